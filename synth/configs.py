@@ -1,0 +1,88 @@
+"""The workloads: projection shapes of the two model stacks and the five cases.
+
+Shapes:
+  BitNet b1.58-2B-4T (QORA-LLM-2B page, "Architecture" table): hidden 2560,
+  30 layers, 20 query / 5 KV heads of 128, FFN 6912.  The seven ternary
+  linears of a layer (the "SubLN Pattern" listing on the same page) are
+  q, k, v, o, gate, up, down.
+  Llama-3.1-8B (the balanced-ternary model card names the model; its
+  dimensions are the published ones): hidden 4096, 32 layers, 32 query /
+  8 KV heads of 128, FFN 14336.
+
+Each projection is (name, out_features N, in_features Kin), weight N x Kin.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+BITNET_2B = {
+    "layers": 30,
+    "proj": [
+        ("q", 2560, 2560),
+        ("k", 640, 2560),
+        ("v", 640, 2560),
+        ("o", 2560, 2560),
+        ("gate", 6912, 2560),
+        ("up", 6912, 2560),
+        ("down", 2560, 6912),
+    ],
+}
+
+LLAMA_8B = {
+    "layers": 32,
+    "proj": [
+        ("q", 4096, 4096),
+        ("k", 1024, 4096),
+        ("v", 1024, 4096),
+        ("o", 4096, 4096),
+        ("gate", 14336, 4096),
+        ("up", 14336, 4096),
+        ("down", 4096, 14336),
+    ],
+}
+
+# Scale layouts and activation types, mirroring the C ABI enums.
+TENSOR, GROUP_F16, CODEBOOK = 0, 1, 2
+F32, BF16, I8 = 0, 1, 2
+
+# Tensor kinds (low 16 bits of the seed key).
+KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS = 1, 2, 3, 4, 5
+
+
+@dataclass(frozen=True)
+class Case:
+    cfg: int                 # 1..5 (5 = prefill int8, 6 = prefill bf16)
+    name: str
+    model: dict | None       # stack, or None for the single tiny linear
+    planes: int
+    group: int               # 0 for per-tensor
+    layout: int
+    x_type: int
+    M: int
+    single: tuple = field(default=None)   # (N, Kin) when model is None
+
+    def projections(self):
+        """[(layer, proj_index, name, N, Kin)] in stack order."""
+        if self.model is None:
+            return [(0, 0, "linear", self.single[0], self.single[1])]
+        out = []
+        for layer in range(self.model["layers"]):
+            for p, (nm, n, kin) in enumerate(self.model["proj"]):
+                out.append((layer, p, nm, n, kin))
+        return out
+
+
+CASES = {
+    "cfg1": Case(1, "tiny single ternary linear 256x512, K=1, g=64, f16 group scales, fp32 x",
+                 None, 1, 64, GROUP_F16, F32, 1, single=(256, 512)),
+    "cfg2": Case(2, "BitNet b1.58-2B decode stack, 30 layers x 7 projections, K=1, per-tensor scale, int8 x",
+                 BITNET_2B, 1, 0, TENSOR, I8, 1),
+    "cfg3": Case(3, "Llama-3.1-8B-shaped decode stack, 32 layers x 7 projections, K=3, g=256, f16 group scales, bf16 x",
+                 LLAMA_8B, 3, 256, GROUP_F16, BF16, 1),
+    "cfg4": Case(4, "balanced-ternary d=3 codec on Llama-3.1-8B shapes, g=16, 27-entry f16 codebook, bf16 x",
+                 LLAMA_8B, 3, 16, CODEBOOK, BF16, 1),
+    "cfg5a": Case(5, "BitNet b1.58-2B prefill stack, M=2048, K=1, per-tensor scale, int8 x",
+                  BITNET_2B, 1, 0, TENSOR, I8, 2048),
+    "cfg5b": Case(6, "Llama-3.1-8B-shaped prefill stack, M=512, K=3, g=256, f16 group scales, bf16 x",
+                  LLAMA_8B, 3, 256, GROUP_F16, BF16, 512),
+}
