@@ -1,0 +1,209 @@
+/*
+ * tq.h -- C ABI of libtq.so: packed ternary-weight matrix-vector (decode) and
+ * skinny matrix-matrix (prefill) products on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (every entry point below computes it or prepares for it):
+ *
+ *   y[m][n] = sum_{k<K} sum_{g<G} S_k[n][g] * sum_{i in group g} t_k[n][i] * x[m][i]
+ *
+ *   t_k[n][i] in {-1, 0, +1}   trit plane k of the N x Kin weight ("Weights use
+ *                              {-1, 0, +1} planes", Tritium page, introduction;
+ *                              plane 0 is the base, the others residual planes)
+ *   S_k[n][g]                  TQ_SCALE_TENSOR:   s_k, one fp32 per plane
+ *                              TQ_SCALE_GROUP_F16: one f16 per plane, row and group
+ *                                of g consecutive inputs (sasori page, "K and g" and
+ *                                "How it works": a sum of K per-group-scaled planes)
+ *                              TQ_SCALE_CODEBOOK: 3^(K-1-k) * cb[idx[n][g]] -- the
+ *                                balanced-ternary codec, K digits per weight, value
+ *                                9 t2 + 3 t1 + t0 for K = 3, 27 levels, a codebook of
+ *                                log-spaced f16 scales and one index per group
+ *                                (Llama-3.1-8B-trit-uniform-d3 card, "Quantization
+ *                                details")
+ *   x                          activations, fp32, bf16 or int8 with a per-token scale
+ *
+ * The weight is stored as trits packed four to a byte, two bits each
+ * (QORA-LLM-2B page, "Ternary GEMV (No Multiplication)"), codes 00 = 0,
+ * 01 = +1, 10 = -1 (11 is never written and reads as 0).  The inner loops
+ * only add or subtract activations; scales are applied once per group, or
+ * once at the end for a per-tensor scale (same section).
+ *
+ * Conventions for every call:
+ *  - A weight is N x Kin (out_features x in_features), as a Linear layer's
+ *    weight; x is [M][Kin] row-major and y is [M][N] row-major fp32.
+ *  - Pointers marked "device" are HIP device pointers owned by the caller;
+ *    the library keeps no reference after the call's work has run and
+ *    allocates no device memory.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    their kernels on it and return without waiting, except tq_pack (see
+ *    there) and tq_gemv_grouped_prepare.
+ *  - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *    Outputs must not alias inputs.
+ *  - Argument, shape, alignment and support errors are returned before
+ *    anything is enqueued.  A failed launch returns TQ_ERR_DEVICE.  Details
+ *    of the last error of the calling thread are in tq_last_error().
+ *  - The calls are thread-safe; calls that overlap on one stream are ordered
+ *    by the stream.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+    TQ_OK = 0,
+    TQ_ERR_ARG = 1,          /* null pointer, bad enum, negative size            */
+    TQ_ERR_SHAPE = 2,        /* Kin % 16, Kin % g, size limits                   */
+    TQ_ERR_ALIGN = 3,        /* device pointer not 16-byte aligned               */
+    TQ_ERR_VALUE = 4,        /* tq_pack: trit outside {-1,0,1}, index >= n_cb,
+                                non-finite scale                                  */
+    TQ_ERR_UNSUPPORTED = 5,  /* valid but not provided (see each call)           */
+    TQ_ERR_DEVICE = 6        /* HIP runtime or launch failure                     */
+} tq_status;
+
+typedef enum tq_scale_layout {
+    TQ_SCALE_TENSOR = 0,     /* canonical scales: fp32 s[K]                           */
+    TQ_SCALE_GROUP_F16 = 1,  /* canonical scales: f16 bits s[K][N][Kin/g]             */
+    TQ_SCALE_CODEBOOK = 2    /* canonical scales: uint8 idx[N][Kin/g] into f16 cb[]   */
+} tq_scale_layout;
+
+typedef enum tq_dtype {
+    TQ_F32 = 0,
+    TQ_BF16 = 1,             /* bits of bfloat16 values, uint16 storage                */
+    TQ_I8 = 2                /* int8 values with an fp32 scale per token (row of x)  */
+} tq_dtype;
+
+/* Shape and format of one packed weight. */
+typedef struct tq_weight_desc {
+    int32_t planes;          /* K, 1..4: trit planes, or digits of the codec          */
+    int32_t group;           /* g in {16,32,64,128,256} for GROUP_F16 and CODEBOOK;
+                                ignored for TENSOR                                      */
+    int32_t scale_layout;    /* tq_scale_layout                                       */
+    int32_t n_codebook;      /* CODEBOOK: entries 1..32 (27 for the d = 3 codec);
+                                ignored otherwise                                       */
+    int64_t out_features;    /* N, 0..2^24                                            */
+    int64_t in_features;     /* Kin, 0..65536, a multiple of 16 and of g              */
+} tq_weight_desc;
+
+int32_t     tq_abi_version(void);
+const char* tq_status_string(int32_t status);
+/* Text of the last error returned on the calling thread ("" if none). */
+const char* tq_last_error(void);
+
+/*
+ * Bytes of the packed blob for `desc` (header, trit planes, scales or codebook
+ * and indices).  The trit planes take K * N * Kin / 4 bytes for N and Kin
+ * multiples of 64 (padding rounds each up to 64 otherwise); GROUP_F16 scales
+ * take 2 bytes per plane, row and group, so the physical bits per weight
+ * approach 2K + 16K/g (the bpw column of the sasori page's "K and g" table).
+ * Pure host arithmetic; needs no GPU.
+ */
+tq_status tq_packed_size(const tq_weight_desc* desc, size_t* bytes);
+
+/*
+ * Pack canonical planes and scales into the opaque device blob.
+ *   trits     device int8 [K][N][Kin], values -1, 0, +1 (digits for CODEBOOK,
+ *             plane 0 the most significant)
+ *   scales    device, canonical layout of desc->scale_layout (see the enum)
+ *   codebook  device f16 bits [n_codebook] for CODEBOOK, NULL otherwise
+ *   blob      device, tq_packed_size(desc) bytes, written in full
+ * Validates every value on the device and synchronizes `stream` to report
+ * TQ_ERR_VALUE (the blob's contents are then unspecified).  Offline step: not
+ * meant for a hot loop.
+ */
+tq_status tq_pack(const tq_weight_desc* desc, const int8_t* trits, const void* scales,
+                  const uint16_t* codebook, void* blob, void* stream);
+
+/*
+ * Inverse of tq_pack: the canonical arrays back from a blob (device pointers,
+ * same layouts as tq_pack's inputs; codebook may be NULL).  Asynchronous.
+ */
+tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8_t* trits, void* scales,
+                    uint16_t* codebook, void* stream);
+
+/*
+ * Per-token absmax int8 quantisation of x [M][Kin] (x_type TQ_F32 or TQ_BF16):
+ *   a_m = max_i |x[m][i]|;   a_m = 0 -> xq = 0 and x_scale[m] = 0;
+ *   otherwise inv = fl32(127 / a_m), xq[m][i] = clamp(rne(fl32(x * inv)), -127, 127)
+ *   and x_scale[m] = fl32(a_m / 127).
+ * xq device int8 [M][Kin], x_scale device fp32 [M].  Non-finite x: unspecified.
+ */
+tq_status tq_act_quant_int8(int64_t M, int64_t in_features, int32_t x_type, const void* x,
+                            int8_t* xq, float* x_scale, void* stream);
+
+/*
+ * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
+ * scale per group).
+ *   x         device [M][Kin] of x_type
+ *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else NULL
+ *   y         device fp32 [M][N]
+ *   acc       optional device int32 [M][N]: the integer accumulator, only for
+ *             TQ_I8 with TQ_SCALE_TENSOR and K = 1 (TQ_ERR_UNSUPPORTED otherwise)
+ * TQ_I8 with TQ_SCALE_TENSOR and K = 1 is bit exact:
+ *   y = fl32(float(acc) * fl32(s_w * x_scale[m])).
+ * Other combinations accumulate in fp32.  M = 0 or N = 0 is a no-op.
+ */
+tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
+                  const void* x, const float* x_scale, float* y, int32_t* acc, void* stream);
+
+/*
+ * Prefill product for any M (matrix-core kernels): same arguments and
+ * results as tq_gemv.  Supported: TQ_I8 with TQ_SCALE_TENSOR and K = 1 (int8
+ * MFMA, int32 accumulate, bit exact as tq_gemv), and TQ_BF16 with
+ * TQ_SCALE_GROUP_F16 (bf16 MFMA, fp32 accumulate per plane and group).
+ */
+tq_status tq_gemm(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
+                  const void* x, const float* x_scale, float* y, int32_t* acc, void* stream);
+
+/*
+ * Many decode products in one launch (a whole layer stack).  All problems
+ * must share K, scale layout, g (when used), x_type and M.
+ */
+typedef struct tq_problem {
+    const tq_weight_desc* desc;   /* host pointer                              */
+    const void* blob;             /* device                                    */
+    const void* x;                /* device [M][Kin]                           */
+    const float* x_scale;         /* device [M] for TQ_I8, else NULL           */
+    float* y;                     /* device [M][N]                             */
+    int32_t* acc;                 /* optional, as in tq_gemv                   */
+} tq_problem;
+
+/* Filled by tq_gemv_grouped_prepare; plain data, may be copied. */
+typedef struct tq_grouped_plan {
+    const void* workspace;        /* device table written by prepare           */
+    int64_t n_items;              /* work items (workgroups) of one run        */
+    int32_t family;               /* kernel family selected at prepare         */
+    int32_t x_type;
+    int32_t M;
+    int32_t waves;                /* waves per workgroup                       */
+    int32_t n_problems;
+    int32_t reserved;
+} tq_grouped_plan;
+
+/* Device workspace bytes that tq_gemv_grouped_prepare needs for these problems. */
+tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,
+                                         size_t* bytes);
+
+/*
+ * Validate the problems, write their descriptor table and the work list
+ * (longest first) into `workspace` (device, caller-owned) and fill `plan`.
+ * Copies host->device on `stream` and synchronizes it.
+ */
+tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                  int32_t x_type, void* workspace, size_t workspace_bytes,
+                                  tq_grouped_plan* plan, void* stream);
+
+/* One launch computing every problem of the plan.  Asynchronous. */
+tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

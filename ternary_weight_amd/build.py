@@ -1,0 +1,81 @@
+"""Build libtq.so (the HIP library) and libtqsynth.so (the input generator) for gfx950.
+
+Each .hip source is compiled separately (in parallel) with hipcc and linked
+into a shared library next to its sources' package.  Run as
+``python -m ternary_weight_amd.build``; ``__graft_entry__.build()`` calls
+``build_all()``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBTQ = os.path.join(PKG, "libtq.so")
+SYNTH_SRC = os.path.join(ROOT, "synth", "synth_kernels.hip")
+LIBSYNTH = os.path.join(ROOT, "synth", "libtqsynth.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
+    "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+    # keep the compiler from forming packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+TQ_SOURCES = ["tq_api.hip", "tq_pack.hip", "tq_act.hip", "tq_gemv.hip", "tq_entry.hip", "tq_gemm.hip"] + [
+    "tq_gemv_%s_m%d.hip" % (x, m) for x in ("f32", "bf16", "i8") for m in (1, 4, 16)]
+
+
+def _compile(src: str, obj: str, extra=()) -> str:
+    os.makedirs(os.path.dirname(obj), exist_ok=True)
+    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
+    return obj
+
+
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed for %s:\n%s" % (out, r.stderr[-4000:]))
+    os.replace(tmp, out)
+
+
+def build_libtq(jobs: int = 0) -> str:
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    objs = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(BUILD_DIR, "tq", s + ".o"))
+                for s in TQ_SOURCES]
+        for f in futs:
+            objs.append(f.result())
+    _link(objs, LIBTQ)
+    return LIBTQ
+
+
+def build_synth() -> str:
+    obj = _compile(SYNTH_SRC, os.path.join(BUILD_DIR, "synth", "synth_kernels.o"))
+    _link([obj], LIBSYNTH)
+    return LIBSYNTH
+
+
+def build_all() -> None:
+    build_libtq()
+    if os.path.exists(SYNTH_SRC):
+        build_synth()
+
+
+if __name__ == "__main__":
+    build_all()
+    print("built", LIBTQ, file=sys.stderr)

@@ -1,0 +1,183 @@
+// libtq: tq_gemv, tq_gemv_grouped_* entry points (validation and dispatch).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+int log2i(int v)
+{
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+bool acc_allowed(const tq_layout& L, int x_type)
+{
+    return x_type == TQ_I8 && L.layout == TQ_SCALE_TENSOR && L.K == 1;
+}
+
+tq_status check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_type, const void* x,
+                     const float* x_scale, const float* y, const int32_t* acc, int64_t max_m)
+{
+    tq_status s;
+    if (x_type != TQ_F32 && x_type != TQ_BF16 && x_type != TQ_I8)
+        return tq_fail(TQ_ERR_ARG, "x_type = %d is not a tq_dtype", x_type);
+    if (M < 0) return tq_fail(TQ_ERR_ARG, "M = %lld is negative", (long long)M);
+    if (M > max_m) return tq_fail(TQ_ERR_UNSUPPORTED, "M = %lld exceeds %lld for this call",
+                                  (long long)M, (long long)max_m);
+    const bool work = M > 0 && L.N > 0;
+    if ((s = tq_check_ptr(blob, "blob", !work))) return s;
+    if ((s = tq_check_ptr(x, "x", !(work && L.Kin > 0)))) return s;
+    if ((s = tq_check_ptr(y, "y", !work))) return s;
+    if (x_type == TQ_I8) {
+        if ((s = tq_check_ptr(x_scale, "x_scale", !work))) return s;
+    }
+    if (acc) {
+        if (!acc_allowed(L, x_type))
+            return tq_fail(TQ_ERR_UNSUPPORTED,
+                           "acc output needs TQ_I8 activations, TQ_SCALE_TENSOR and one plane");
+        if ((s = tq_check_ptr(acc, "acc", true))) return s;
+    }
+    return TQ_OK;
+}
+
+tq_prob_dev make_prob(const tq_layout& L, const void* blob, int64_t M, const void* x,
+                      const float* x_scale, float* y, int32_t* acc)
+{
+    tq_prob_dev P;
+    memset(&P, 0, sizeof P);
+    const uint8_t* b = (const uint8_t*)blob;
+    P.codes = b + L.codes_off;
+    P.scales = b + L.scales_off;
+    P.cb = L.layout == TQ_SCALE_CODEBOOK ? (const uint16_t*)(b + L.cb_off) : nullptr;
+    P.x = x;
+    P.x_scale = x_scale;
+    P.y = y;
+    P.acc = acc;
+    P.N = (int32_t)L.N;
+    P.Kin = (int32_t)L.Kin;
+    P.NC = (int32_t)L.NC;
+    P.NGD = (int32_t)L.NGD;
+    P.NID = (int32_t)L.NID;
+    P.g = L.layout == TQ_SCALE_TENSOR ? 0 : L.g;
+    P.M = (int32_t)M;
+    P.log2g = L.layout == TQ_SCALE_TENSOR ? 0 : log2i(L.g);
+    return P;
+}
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
+                            const void* x, const float* x_scale, float* y, int32_t* acc, void* stream)
+{
+    tq_layout L;
+    tq_status s = tq_check_desc(desc, &L);
+    if (s) return s;
+    if ((s = check_call(L, blob, M, x_type, x, x_scale, y, acc, TQ_MAX_M_GEMV))) return s;
+    if (M == 0 || L.N == 0) return tq_ok();
+    const tq_prob_dev P = make_prob(L, blob, M, x, x_scale, y, acc);
+    if ((s = tq_gemv_launch_single(L, P, x_type, (hipStream_t)stream))) return s;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t count,
+                                                   int64_t M, size_t* bytes)
+{
+    if (!bytes) return tq_fail(TQ_ERR_ARG, "bytes is NULL");
+    if (count < 0 || (count > 0 && !problems)) return tq_fail(TQ_ERR_ARG, "bad problem list");
+    if (M < 0 || M > TQ_MAX_M_GEMV) return tq_fail(TQ_ERR_UNSUPPORTED, "M = %lld not in 0..%d",
+                                                   (long long)M, TQ_MAX_M_GEMV);
+    int64_t items = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        tq_layout L;
+        tq_status s = tq_check_desc(problems[i].desc, &L);
+        if (s) return tq_fail(s, "problem %d: %s", i, tq_last_error());
+        items += L.NB;
+    }
+    *bytes = (size_t)(tq_align256((int64_t)count * (int64_t)sizeof(tq_prob_dev)) + items * 8);
+    if (*bytes == 0) *bytes = 256;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                            int32_t x_type, void* workspace, size_t workspace_bytes,
+                                            tq_grouped_plan* plan, void* stream)
+{
+    if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
+    const int waves_hint = plan->waves;
+    size_t need = 0;
+    tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
+    if (s) return s;
+    if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
+    if (workspace_bytes < need)
+        return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    std::vector<tq_prob_dev> probs((size_t)count);
+    struct Item { int64_t cost; int32_t prob, rb; };
+    std::vector<Item> items;
+    int family = -1, K0 = 0, layout0 = -1, g0 = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const tq_problem& pr = problems[i];
+        tq_layout L;
+        tq_check_desc(pr.desc, &L);
+        if ((s = check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, TQ_MAX_M_GEMV)))
+            return tq_fail(s, "problem %d: %s", i, tq_last_error());
+        if (i == 0) {
+            K0 = L.K;
+            layout0 = L.layout;
+            g0 = L.g;
+        } else if (L.K != K0 || L.layout != layout0 || (L.layout != TQ_SCALE_TENSOR && L.g != g0)) {
+            return tq_fail(TQ_ERR_UNSUPPORTED,
+                           "problem %d: all problems of a plan must share planes, layout and group", i);
+        }
+        probs[(size_t)i] = make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
+        if (M > 0)
+            for (int64_t rb = 0; rb < L.NB; ++rb)
+                items.push_back({L.NC * (int64_t)L.K, i, (int32_t)rb});
+    }
+    if (count > 0 && M > 0) family = tq_gemv_family(x_type, layout0, K0, (int)M);
+    // longest row blocks first, so that the last wave of work is short
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    const int64_t probs_bytes = tq_align256((int64_t)count * (int64_t)sizeof(tq_prob_dev));
+    std::vector<uint8_t> host((size_t)need, 0);
+    if (count > 0) memcpy(host.data(), probs.data(), (size_t)count * sizeof(tq_prob_dev));
+    int32_t* it = (int32_t*)(host.data() + probs_bytes);
+    for (size_t j = 0; j < items.size(); ++j) {
+        it[2 * j] = items[j].prob;
+        it[2 * j + 1] = items[j].rb;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    if ((s = tq_check_hip(hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, st),
+                          "tq_gemv_grouped_prepare copy")))
+        return s;
+    if ((s = tq_check_hip(hipStreamSynchronize(st), "tq_gemv_grouped_prepare synchronize"))) return s;
+    int waves = waves_hint;
+    if (waves < 1 || waves > 16 || (waves & (waves - 1))) waves = 4;
+    plan->workspace = workspace;
+    plan->n_items = (int64_t)items.size();
+    plan->family = family;
+    plan->x_type = x_type;
+    plan->M = (int32_t)M;
+    plan->waves = waves;
+    plan->n_problems = count;
+    plan->reserved = 0;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream)
+{
+    if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
+    if (plan->n_items == 0) return tq_ok();
+    tq_status s;
+    if ((s = tq_check_ptr(plan->workspace, "plan workspace", false))) return s;
+    if (plan->n_items < 0 || plan->n_items > (1ll << 31) - 1 || plan->n_problems < 1)
+        return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
+    if ((s = tq_gemv_launch_grouped(plan->family, plan->waves, plan->workspace, plan->n_problems,
+                                    plan->n_items, (hipStream_t)stream)))
+        return s;
+    return tq_ok();
+}

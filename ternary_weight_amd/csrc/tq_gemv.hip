@@ -1,0 +1,85 @@
+// libtq: decode dispatch -- picks the kernel family and the workgroup shape.
+#include "tq_gemv_impl.h"
+
+namespace {
+
+using namespace tqk;
+
+int mt_index(int M) { return M <= 1 ? 0 : (M <= 4 ? 1 : 2); }
+
+size_t red_bytes(int family, int waves)
+{
+    if (waves <= 1) return 0;
+    const int mti = family % 3, K = (family / 3) % 4 + 1, layout = (family / 12) % 3;
+    const int R = layout != TQ_SCALE_TENSOR ? kMT[mti] : kMT[mti] * K;
+    return (size_t)waves * R * 64 * 4;
+}
+
+const single_fn* single_tab(int xt, int mti)
+{
+    static const single_fn* (*const f[3][3])() = {
+        {single_table_0_0, single_table_0_1, single_table_0_2},
+        {single_table_1_0, single_table_1_1, single_table_1_2},
+        {single_table_2_0, single_table_2_1, single_table_2_2}};
+    return f[xt][mti]();
+}
+
+const grouped_fn* grouped_tab(int xt, int mti)
+{
+    static const grouped_fn* (*const f[3][3])() = {
+        {grouped_table_0_0, grouped_table_0_1, grouped_table_0_2},
+        {grouped_table_1_0, grouped_table_1_1, grouped_table_1_2},
+        {grouped_table_2_0, grouped_table_2_1, grouped_table_2_2}};
+    return f[xt][mti]();
+}
+
+// family = ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + M tier
+single_fn single_of(int family)
+{
+    const int mti = family % 3, rest = family / 3;
+    return single_tab(rest / 12, mti)[rest % 12];
+}
+
+grouped_fn grouped_of(int family)
+{
+    const int mti = family % 3, rest = family / 3;
+    return grouped_tab(rest / 12, mti)[rest % 12];
+}
+
+}  // namespace
+
+int tq_gemv_family(int x_type, int layout, int K, int M)
+{
+    if (x_type < 0 || x_type > 2 || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 || M > 16) return -1;
+    return ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + mt_index(M);
+}
+
+tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
+{
+    const int fam = tq_gemv_family(x_type, L.layout, L.K, P.M);
+    if (fam < 0) return tq_fail(TQ_ERR_UNSUPPORTED, "no decode kernel for this combination");
+    // enough waves to cover the chip: split the columns of each row block
+    const int cpu = (L.layout == TQ_SCALE_TENSOR || L.g <= 64) ? 1 : L.g / 64;
+    const int64_t nunits = (L.NC + cpu - 1) / cpu;
+    int waves = 1;
+    const int64_t target = 4 * (int64_t)tq_device_cus();
+    while (waves < 16 && L.NB * waves < target && nunits >= 4 * waves * 2) waves *= 2;
+    const size_t lds = red_bytes(fam, waves);
+    hipLaunchKernelGGL(single_of(fam), dim3((unsigned)L.NB), dim3(64 * waves), lds, stream, P);
+    return tq_check_launch("tq_gemv");
+}
+
+tq_status tq_gemv_launch_grouped(int family, int waves, const void* workspace, int64_t n_probs,
+                                 int64_t n_items, hipStream_t stream)
+{
+    if (family < 0 || family >= 108) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
+    if (waves < 1 || waves > 16) return tq_fail(TQ_ERR_ARG, "bad plan waves %d", waves);
+    if (n_items <= 0) return tq_ok();
+    const uint8_t* ws = (const uint8_t*)workspace;
+    const tq_prob_dev* probs = (const tq_prob_dev*)ws;
+    const int2* items = (const int2*)(ws + tq_align256(n_probs * (int64_t)sizeof(tq_prob_dev)));
+    const size_t lds = red_bytes(family, waves);
+    hipLaunchKernelGGL(grouped_of(family), dim3((unsigned)n_items), dim3(64 * waves), lds, stream,
+                       probs, items);
+    return tq_check_launch("tq_gemv_grouped_run");
+}

@@ -1,0 +1,8 @@
+// libtq: decode kernels for bf16 activations, up to 16 token(s) per launch
+// (all scale layouts, K = 1..4).
+#include "tq_gemv_impl.h"
+
+namespace tqk {
+const single_fn* single_table_1_2() { return TablesFor<1, 16>::single; }
+const grouped_fn* grouped_table_1_2() { return TablesFor<1, 16>::grouped; }
+}  // namespace tqk

@@ -1,0 +1,530 @@
+#pragma once
+// libtq: decode kernels (M <= 16) -- tq_gemv and tq_gemv_grouped.
+//
+// What is computed is the definition in tq.h: per output row, each trit plane
+// adds or subtracts the activations of its nonzero trits ("the inner GEMV loop
+// uses only addition and subtraction", QORA-LLM-2B page), per-group sums are
+// scaled once at the group's end (sasori page, "K and g"), a per-tensor scale
+// once at the very end (QORA-LLM-2B, "Ternary GEMV (No Multiplication)").
+//
+// Mapping onto CDNA4.  One wave64 owns a block of 64 output rows, one row per
+// lane, so a lane's 16-byte slot of the blob is 64 trits of its own row and a
+// wave-wide load is 1 KiB of contiguous codes (see tq_layout.h).  All lanes
+// of a wave read the same activations, so x is fetched with scalar loads into
+// SGPRs and fed to the vector ALU as a uniform operand; no LDS staging and no
+// cross-lane reduction are needed.  The waves of a workgroup split the columns
+// of the row block (whole groups each) and add their partial sums in LDS in a
+// fixed order at the end.
+//
+// Trit decode, per dword of codes (16 trits):
+//  int8   (w >> 4p) masked to two bits per byte and mapped to {0, +1, -1}
+//         bytes by one v_perm_b32 each (a byte lookup table in the selector's
+//         source operands; for the bits-2..3 field the selector value 8
+//         replicates the sign bit of a source byte, which yields 0xFF), then
+//         one v_dot4_i32_i8 against four int8 activations: about 13 VALU ops
+//         per 16 trits.
+//  bf16   the trit pair (4p+1, 4p+3) of a dword comes from (w >> 2p) & 0x03000300,
+//         the pair (4p, 4p+2) from (w << (8-2p)) & 0x03000300; one v_perm_b32
+//         maps each pair to two bf16 values {0, +2, -2} (low bytes zero), and
+//         one v_dot2_f32_bf16 accumulates t*x for both against the matching
+//         activation pair, which the scalar unit assembles with s_pack.  The
+//         factor 2 is exact and folded into the scale.
+//  fp32   int8 decode as above, converted per trit and accumulated with fma
+//         (t in {-1, 0, 1}, so each fma is an exact add, subtract or no-op).
+#include "tq_internal.h"
+
+#include <algorithm>
+
+namespace tqk {
+
+#define CONST_AS __attribute__((address_space(4)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Loads of wave-uniform data through the constant address space, which the
+// compiler serves with scalar (SMEM) loads into SGPRs.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p)
+{
+    return *(const CONST_AS T*)p;
+}
+
+__device__ __forceinline__ uint32_t ld_uniform_u32(const void* base, int64_t dword)
+{
+    return ((const CONST_AS uint32_t*)base)[dword];
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_uniform_struct(const T* p)
+{
+    static_assert(sizeof(T) % 4 == 0, "dword-sized struct");
+    T v;
+    uint32_t* d = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) d[i] = ld_uniform_u32(p, i);
+    return v;
+}
+
+// int8 trits of columns 4j..4j+3 (j = 0..3) of a 16-column dword of codes.
+__device__ __forceinline__ void decode_i8(uint32_t w, uint32_t t[4])
+{
+    const uint32_t w4 = w >> 4;
+    // bits 0..1 of each byte: selector 0,1,2,3 -> bytes of 0x00FF0100 = 0, +1, -1, 0
+    t[0] = __builtin_amdgcn_perm(0u, 0x00FF0100u, w & 0x03030303u);
+    t[2] = __builtin_amdgcn_perm(0u, 0x00FF0100u, w4 & 0x03030303u);
+    // bits 2..3 of each byte: selector 0 -> 0x00, 4 -> 0x01, 8 -> sign of 0x8000 -> 0xFF, 12 -> 0
+    t[1] = __builtin_amdgcn_perm(0x00000001u, 0x00008000u, w & 0x0C0C0C0Cu);
+    t[3] = __builtin_amdgcn_perm(0x00000001u, 0x00008000u, w4 & 0x0C0C0C0Cu);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+template <int XT>
+struct XUnit;   // activations of one 16-column unit of one token
+
+template <>
+struct XUnit<TQ_I8> {
+    uint32_t v[4];
+    __device__ __forceinline__ void load(const void* x, int64_t elem)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = ld_uniform_u32(x, (elem >> 2) + j);
+    }
+};
+template <>
+struct XUnit<TQ_BF16> {
+    uint32_t v[8];
+    __device__ __forceinline__ void load(const void* x, int64_t elem)
+    {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = ld_uniform_u32(x, (elem >> 1) + j);
+    }
+};
+template <>
+struct XUnit<TQ_F32> {
+    uint32_t v[16];
+    __device__ __forceinline__ void load(const void* x, int64_t elem)
+    {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = ld_uniform_u32(x, elem + j);
+    }
+};
+
+template <int XT>
+struct AccT { using type = float; };
+template <>
+struct AccT<TQ_I8> { using type = int; };
+
+// acc += sum over the 16 columns of one code dword of t * x.
+__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_I8>& x, int& acc)
+{
+    uint32_t t[4];
+    decode_i8(w, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4((int)t[j], (int)x.v[j], acc, false);
+}
+
+__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_BF16>& x, float& acc)
+{
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t x0 = x.v[2 * p], x1 = x.v[2 * p + 1];
+        // columns 4p+1 and 4p+3: high halves; columns 4p and 4p+2: low halves
+        const uint32_t xo = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        const uint32_t xe = (x0 & 0xFFFFu) | (x1 << 16);
+        const uint32_t to = __builtin_amdgcn_perm(0u, 0x00C04000u, (w >> (2 * p)) & 0x03000300u);
+        const uint32_t te = __builtin_amdgcn_perm(0u, 0x00C04000u, (w << (8 - 2 * p)) & 0x03000300u);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, to),
+                                              __builtin_bit_cast(bf16x2_t, xo), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, te),
+                                              __builtin_bit_cast(bf16x2_t, xe), acc, false);
+    }
+}
+
+__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_F32>& x, float& acc)
+{
+    uint32_t t[4];
+    decode_i8(w, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float tf = (float)(int8_t)(t[j] >> (8 * b));
+            acc = fmaf(tf, __uint_as_float(x.v[4 * j + b]), acc);
+        }
+    }
+}
+
+// The trit value encoding's factor: bf16 trits are decoded as +-2.
+template <int XT>
+__device__ __forceinline__ constexpr float enc_scale() { return XT == TQ_BF16 ? 0.5f : 1.0f; }
+
+template <int K>
+__device__ __forceinline__ int codec_combine(const int (&p)[K])
+{
+    int v = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v = v * 3 + p[k];
+    return v;
+}
+
+template <int K>
+__device__ __forceinline__ float codec_combine(const float (&p)[K])
+{
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) v = v * 3.0f + p[k];
+    return v;
+}
+
+// Code (and scale) registers of one 64-column chunk.
+template <int K, int LAYOUT>
+struct Slot {
+    u32x4 w[K];
+    uint32_t sw[LAYOUT == TQ_SCALE_TENSOR ? 1 : K][2];
+};
+
+template <int XT>
+struct XChunk {   // activations of one 64-column chunk of one token (SGPRs)
+    static constexpr int kD = XT == TQ_I8 ? 16 : (XT == TQ_BF16 ? 32 : 64);
+    uint32_t v[kD];
+    __device__ __forceinline__ void load(const void* x, int64_t elem)
+    {
+        const int64_t dw = XT == TQ_I8 ? (elem >> 2) : (XT == TQ_BF16 ? (elem >> 1) : elem);
+#pragma unroll
+        for (int j = 0; j < kD; ++j) v[j] = ld_uniform_u32(x, dw + j);
+    }
+    __device__ __forceinline__ XUnit<XT> unit(int d) const
+    {
+        XUnit<XT> u;
+        constexpr int n = kD / 4;
+#pragma unroll
+        for (int j = 0; j < n; ++j) u.v[j] = v[d * n + j];
+        return u;
+    }
+};
+
+// One row block (64 rows) of one problem, columns split across `nwaves` waves.
+template <int XT, int LAYOUT, int K, int MT>
+struct RowBlock {
+    using A = typename AccT<XT>::type;
+    static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
+    // chunks in flight per wave (codes of K planes each)
+    static constexpr int D = MT > 1 ? 1 : (K == 1 ? 4 : 2);
+    // activations are prefetched a chunk ahead for one token (SGPR budget)
+    static constexpr bool kXPre = MT == 1 && XT != TQ_F32;
+
+    const tq_prob_dev& P;
+    const int rb, lane;
+    A p[MT][K];
+    float out[MT];
+    const GLOBAL_AS u32x4* cp;
+    const GLOBAL_AS uint32_t* sp;
+
+    __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_)
+        : P(P_), rb(rb_), lane(threadIdx.x & 63)
+    {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            out[m] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) p[m][k] = 0;
+        }
+        cp = (const GLOBAL_AS u32x4*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS + lane;
+        sp = (const GLOBAL_AS uint32_t*)P.scales;
+    }
+
+    // scale words needed by the groups that end inside chunk c
+    __device__ __forceinline__ void load_slot(int c, Slot<K, LAYOUT>& s) const
+    {
+#pragma unroll
+        for (int k = 0; k < K; ++k) s.w[k] = __builtin_nontemporal_load(cp + ((int64_t)c * K + k) * TQ_ROWS);
+        if (LAYOUT == TQ_SCALE_GROUP_F16) {
+            const int g = P.g;
+            const int end = std::min((c + 1) * TQ_CHUNK, P.Kin);
+            const int last_pair = ((end >> P.log2g) - 1) >> 1;
+            if (g < 64) {
+                const int first_pair = ((c * TQ_CHUNK) >> P.log2g) >> 1;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    s.sw[k][0] = sp[(((int64_t)rb * P.NGD + first_pair) * K + k) * TQ_ROWS + lane];
+                    s.sw[k][1] = sp[(((int64_t)rb * P.NGD + std::min(first_pair + 1, last_pair)) * K + k) * TQ_ROWS + lane];
+                }
+            } else if ((end & (g - 1)) == 0) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) s.sw[k][0] = sp[(((int64_t)rb * P.NGD + last_pair) * K + k) * TQ_ROWS + lane];
+            }
+        } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
+            const int end = std::min((c + 1) * TQ_CHUNK, P.Kin);
+            const int first_id = ((c * TQ_CHUNK) >> P.log2g) / 6;
+            const int last_id = ((end >> P.log2g) - 1) / 6;
+            s.sw[0][0] = sp[((int64_t)rb * P.NID + first_id) * TQ_ROWS + lane];
+            s.sw[0][1] = sp[((int64_t)rb * P.NID + std::min(first_id + 1, last_id)) * TQ_ROWS + lane];
+        }
+    }
+
+    __device__ __forceinline__ void close_group(int grp, int c, const Slot<K, LAYOUT>& s, const float* cb_lds)
+    {
+        float sc[K];
+        if (LAYOUT == TQ_SCALE_GROUP_F16) {
+            int j = 0;
+            if (P.g < 64) j = (grp >> 1) - (((c * TQ_CHUNK) >> P.log2g) >> 1);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t word = j ? s.sw[k][1] : s.sw[k][0];
+                sc[k] = f16_to_f32((grp & 1) ? (word >> 16) : (word & 0xFFFFu)) * enc_scale<XT>();
+            }
+        } else {
+            const int id = grp / 6;
+            const int j = id - ((c * TQ_CHUNK) >> P.log2g) / 6;
+            const uint32_t word = j ? s.sw[0][1] : s.sw[0][0];
+            const uint32_t idx = (word >> (5 * (grp - 6 * id))) & 31u;
+            sc[0] = cb_lds[idx] * enc_scale<XT>();
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (LAYOUT == TQ_SCALE_GROUP_F16) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) out[m] = fmaf(sc[k], (float)p[m][k], out[m]);
+            } else {
+                out[m] = fmaf(sc[0], (float)codec_combine<K>(p[m]), out[m]);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) p[m][k] = 0;
+        }
+    }
+
+    // Columns of chunk c: `nu` 16-column units (4 for a full chunk).
+    template <bool kFull>
+    __device__ __forceinline__ void compute(int c, int nu, const Slot<K, LAYOUT>& s, const XChunk<XT>* xc,
+                                            const float* cb_lds)
+    {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            if (!kFull && d >= nu) break;
+            const int u = c * 4 + d;
+            uint32_t wd[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) wd[k] = s.w[k][d];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (MT > 1 && m >= P.M) break;
+                XUnit<XT> xu;
+                if (kXPre && kFull) xu = xc->unit(d);
+                else xu.load(P.x, (int64_t)m * P.Kin + (int64_t)u * 16);
+#pragma unroll
+                for (int k = 0; k < K; ++k) accum(wd[k], xu, p[m][k]);
+            }
+            if (kGroup) {
+                const int colend = (u + 1) * 16;
+                if ((colend & (P.g - 1)) == 0) close_group((colend >> P.log2g) - 1, c, s, cb_lds);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void run(int c0, int c1, const float* cb_lds)
+    {
+        const int n16 = P.Kin >> 4;
+        const int cf = std::min(c1, n16 >> 2);   // end of the chunks with all 64 columns valid
+        if (c0 < cf) {
+            Slot<K, LAYOUT> cur[D];
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                if (c0 + j < cf) load_slot(c0 + j, cur[j]);
+            XChunk<XT> xc;
+            if (kXPre) xc.load(P.x, (int64_t)c0 * TQ_CHUNK);
+            for (int c = c0; c < cf; c += D) {
+                Slot<K, LAYOUT> nxt[D];
+#pragma unroll
+                for (int j = 0; j < D; ++j)
+                    if (c + D + j < cf) load_slot(c + D + j, nxt[j]);
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    if (c + j < cf) {
+                        XChunk<XT> xn;
+                        if (kXPre && c + j + 1 < cf) xn.load(P.x, (int64_t)(c + j + 1) * TQ_CHUNK);
+                        compute<true>(c + j, 4, cur[j], &xc, cb_lds);
+                        if (kXPre) xc = xn;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < D; ++j) cur[j] = nxt[j];
+            }
+        }
+        if (cf < c1) {   // the ragged last chunk of the row (Kin % 64 != 0)
+            Slot<K, LAYOUT> s;
+            load_slot(cf, s);
+            compute<false>(cf, n16 - 4 * cf, s, nullptr, cb_lds);
+        }
+    }
+};
+
+template <int XT, int LAYOUT, int K, int MT>
+__device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, const int wave,
+                                         const int nwaves, uint32_t* red, const float* cb_lds)
+{
+    using A = typename AccT<XT>::type;
+    constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
+    const int lane = threadIdx.x & 63;
+    const int NC = P.NC;
+    const int g = P.g;
+    const int M = P.M;
+    const int cpu = (!kGroup || g <= 64) ? 1 : (g >> 6);
+    const int nunits = (NC + cpu - 1) / cpu;
+    const int c0 = ((nunits * wave) / nwaves) * cpu;
+    const int c1 = std::min(((nunits * (wave + 1)) / nwaves) * cpu, NC);
+
+    RowBlock<XT, LAYOUT, K, MT> blk(P, rb);
+    blk.run(c0, c1, cb_lds);
+    auto& p = blk.p;
+    auto& out = blk.out;
+
+    // Partial sums to LDS; wave 0 adds them in wave order and writes y.
+    constexpr int R = kGroup ? MT : MT * K;
+    if (nwaves > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (kGroup) {
+                    red[((wave * R) + m) * 64 + lane] = __float_as_uint(out[m]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const A v = p[m][k];
+                        red[((wave * R) + m * K + k) * 64 + lane] =
+                            XT == TQ_I8 ? (uint32_t)(int)v : __float_as_uint((float)v);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        for (int wv = 1; wv < nwaves; ++wv) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (kGroup) {
+                    out[m] += __uint_as_float(red[((wv * R) + m) * 64 + lane]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const uint32_t bits = red[((wv * R) + m * K + k) * 64 + lane];
+                        if (XT == TQ_I8) p[m][k] += (A)(int)bits;
+                        else p[m][k] += (A)__uint_as_float(bits);
+                    }
+                }
+            }
+        }
+    }
+
+    const int64_t n = (int64_t)rb * TQ_ROWS + lane;
+    if (n >= P.N) return;
+    float ts[K];
+    if (!kGroup) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) ts[k] = ld_uniform(reinterpret_cast<const float*>(P.scales) + k);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m >= M) break;
+        float yv;
+        if (XT == TQ_I8) {
+            const float xs = ld_uniform(P.x_scale + m);
+            if (!kGroup && K == 1) {
+                // bit exact: y = fl(float(acc) * fl(s_w * s_x))
+                const float cm = __fmul_rn(ts[0], xs);
+                yv = __fmul_rn((float)p[m][0], cm);
+                if (P.acc) ((GLOBAL_AS int32_t*)P.acc)[(int64_t)m * P.N + n] = (int)p[m][0];
+            } else if (!kGroup) {
+                float t = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) t = fmaf(ts[k], (float)p[m][k], t);
+                yv = t * xs;
+            } else {
+                yv = out[m] * xs;
+            }
+        } else {
+            if (!kGroup) {
+                float t = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) t = fmaf(ts[k] * enc_scale<XT>(), (float)p[m][k], t);
+                yv = t;
+            } else {
+                yv = out[m];
+            }
+        }
+        ((GLOBAL_AS float*)P.y)[(int64_t)m * P.N + n] = yv;
+    }
+}
+
+template <int XT, int LAYOUT, int K, int MT>
+__device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb)
+{
+    extern __shared__ uint32_t tq_red[];
+    __shared__ float cb_lds[TQ_CB_SLOTS];
+    if (LAYOUT == TQ_SCALE_CODEBOOK) {
+        if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+        __syncthreads();
+    }
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nwaves = (int)(blockDim.x >> 6);
+    rowblock<XT, LAYOUT, K, MT>(P, rb, wave, nwaves, tq_red, cb_lds);
+}
+
+template <int XT, int LAYOUT, int K, int MT>
+__global__ __launch_bounds__(1024) void k_gemv_single(tq_prob_dev P)
+{
+    gemv_body<XT, LAYOUT, K, MT>(P, (int)blockIdx.x);
+}
+
+template <int XT, int LAYOUT, int K, int MT>
+__global__ __launch_bounds__(1024) void k_gemv_grouped(const tq_prob_dev* __restrict__ probs,
+                                                       const int2* __restrict__ items)
+{
+    const int2 it = ld_uniform_struct(items + blockIdx.x);
+    const tq_prob_dev P = ld_uniform_struct(probs + it.x);
+    gemv_body<XT, LAYOUT, K, MT>(P, it.y);
+}
+
+}  // namespace tqk
+
+namespace tqk {
+
+typedef void (*single_fn)(tq_prob_dev);
+typedef void (*grouped_fn)(const tq_prob_dev*, const int2*);
+
+constexpr int kMT[3] = {1, 4, 16};
+// family = ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + M-tier; 36 families per x_type
+constexpr int kPerXT = 36;
+
+// families of one (x_type, M tier): index = layout * 4 + (K - 1)
+template <int F>
+struct FamOf {
+    static constexpr int K = F % 4 + 1;
+    static constexpr int layout = F / 4;
+};
+
+template <int XT, int MT, int... Fs>
+struct TablesXT {
+    static constexpr single_fn single[] = {&k_gemv_single<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
+    static constexpr grouped_fn grouped[] = {&k_gemv_grouped<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
+};
+
+template <int XT, int MT, int... Is>
+constexpr auto make_tables(std::integer_sequence<int, Is...>) { return TablesXT<XT, MT, Is...>{}; }
+
+template <int XT, int MT>
+using TablesFor = decltype(make_tables<XT, MT>(std::make_integer_sequence<int, 12>{}));
+
+// one translation unit per (x_type, M tier) defines its pair of tables
+const single_fn* single_table(int x_type, int mti);
+const grouped_fn* grouped_table(int x_type, int mti);
+#define TQ_DECLARE_TABLES(xt, mti) \
+    const single_fn* single_table_##xt##_##mti(); const grouped_fn* grouped_table_##xt##_##mti();
+TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1) TQ_DECLARE_TABLES(0, 2)
+TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1) TQ_DECLARE_TABLES(1, 2)
+TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1) TQ_DECLARE_TABLES(2, 2)
+
+}  // namespace tqk

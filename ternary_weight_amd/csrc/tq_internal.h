@@ -1,0 +1,48 @@
+// Host-side helpers shared by the libtq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_layout.h"
+
+#define TQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+// Record a message for tq_last_error() on this thread and return `s`.
+tq_status tq_fail(tq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clear the thread's last error; returns TQ_OK.
+tq_status tq_ok();
+
+// Validate a weight descriptor and fill the layout.
+tq_status tq_check_desc(const tq_weight_desc* d, tq_layout* L);
+// Device pointer checks: non-null unless `nullable`, 16-byte aligned.
+tq_status tq_check_ptr(const void* p, const char* name, bool nullable);
+// After a launch: map hipGetLastError() to TQ_ERR_DEVICE.
+tq_status tq_check_launch(const char* what);
+tq_status tq_check_hip(hipError_t e, const char* what);
+
+// The device's compute-unit count (cached per device).
+int tq_device_cus();
+
+// Problem descriptor as the decode kernels read it (host fills, device reads).
+struct tq_prob_dev {
+    const uint8_t* codes;      // blob + codes_off
+    const uint8_t* scales;     // blob + scales_off (indices for CODEBOOK)
+    const uint16_t* cb;        // blob + cb_off (CODEBOOK) or null
+    const void* x;             // [M][Kin]
+    const float* x_scale;      // [M] (I8) or null
+    float* y;                  // [M][N]
+    int32_t* acc;              // optional [M][N]
+    int32_t N, Kin;
+    int32_t NC, NGD;
+    int32_t NID, g;
+    int32_t M, log2g;
+};
+
+// Decode launch shared by tq_gemv and tq_gemv_grouped_run (tq_gemv.hip).
+tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type,
+                                hipStream_t stream);
+tq_status tq_gemv_launch_grouped(int family, int waves, const void* workspace, int64_t n_probs,
+                                 int64_t n_items, hipStream_t stream);
+// Family id of a (x_type, layout, K, M) combination, or -1 if none.
+int tq_gemv_family(int x_type, int layout, int K, int M);

@@ -1,0 +1,312 @@
+// libtq: tq_pack / tq_unpack -- canonical planes and scales <-> device blob.
+//
+// Packing follows the two-bit code of the QORA-LLM-2B page ("Ternary GEMV (No
+// Multiplication)": four trits per byte, two bits each) with 00 = 0, 01 = +1,
+// 10 = -1, in the lane-slot order documented in tq_layout.h.
+#include "tq_internal.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ void k_write_header(tq_blob_header* h, tq_weight_desc d)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        tq_blob_header v = {};
+        v.magic = TQ_BLOB_MAGIC;
+        v.version = TQ_BLOB_VERSION;
+        v.planes = d.planes;
+        v.group = d.scale_layout == TQ_SCALE_TENSOR ? 0 : d.group;
+        v.scale_layout = d.scale_layout;
+        v.n_codebook = d.scale_layout == TQ_SCALE_CODEBOOK ? d.n_codebook : 0;
+        v.out_features = d.out_features;
+        v.in_features = d.in_features;
+        v.pack_status = 0;
+        *h = v;
+    }
+}
+
+__device__ __forceinline__ uint32_t code_of(int8_t t) { return t == 1 ? 1u : (t == -1 ? 2u : 0u); }
+
+// One thread per code dword (16 trits); dword index t is also its offset / 4.
+__global__ void k_pack_codes(const int8_t* __restrict__ trits, uint32_t* __restrict__ codes,
+                             uint32_t* status, int64_t total, int K, int64_t N, int64_t Kin,
+                             int64_t NC)
+{
+    uint32_t bad = 0;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int d = (int)(t & 3);
+        const int lane = (int)((t >> 2) & 63);
+        int64_t rest = t >> 8;
+        const int k = (int)(rest % K);
+        rest /= K;
+        const int64_t c = rest % NC;
+        const int64_t rb = rest / NC;
+        const int64_t n = rb * TQ_ROWS + lane;
+        const int64_t col0 = c * TQ_CHUNK + 16 * d;
+        uint32_t w = 0;
+        if (n < N && col0 < Kin) {
+            const int4 v = *reinterpret_cast<const int4*>(trits + ((int64_t)k * N + n) * Kin + col0);
+            const uint32_t b[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int8_t tv = (int8_t)((b[q >> 2] >> (8 * (q & 3))) & 0xFF);
+                if (tv < -1 || tv > 1) bad |= TQ_PACK_BAD_TRIT;
+                // column 4p + byte b -> byte b, bits 2p..2p+1
+                const int p = q >> 2, byte = q & 3;
+                w |= code_of(tv) << (8 * byte + 2 * p);
+            }
+        }
+        codes[t] = w;
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+__global__ void k_unpack_codes(const uint32_t* __restrict__ codes, int8_t* __restrict__ trits,
+                               int64_t total, int K, int64_t N, int64_t Kin, int64_t NC)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int d = (int)(t & 3);
+        const int lane = (int)((t >> 2) & 63);
+        int64_t rest = t >> 8;
+        const int k = (int)(rest % K);
+        rest /= K;
+        const int64_t c = rest % NC;
+        const int64_t rb = rest / NC;
+        const int64_t n = rb * TQ_ROWS + lane;
+        const int64_t col0 = c * TQ_CHUNK + 16 * d;
+        if (n >= N || col0 >= Kin) continue;
+        const uint32_t w = codes[t];
+        uint32_t b[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int p = q >> 2, byte = q & 3;
+            const uint32_t c2 = (w >> (8 * byte + 2 * p)) & 3u;
+            const int tv = (int)(c2 & 1u) - (int)(c2 >> 1);     // 11 reads as 0
+            b[q >> 2] |= ((uint32_t)(uint8_t)(int8_t)tv) << (8 * (q & 3));
+        }
+        *reinterpret_cast<int4*>(trits + ((int64_t)k * N + n) * Kin + col0) =
+            make_int4((int)b[0], (int)b[1], (int)b[2], (int)b[3]);
+    }
+}
+
+__device__ __forceinline__ bool f16_finite(uint16_t h) { return (h & 0x7C00u) != 0x7C00u; }
+
+// GROUP_F16: one thread per scale dword (two groups).
+__global__ void k_pack_group_scales(const uint16_t* __restrict__ s, uint32_t* __restrict__ out,
+                                    uint32_t* status, int64_t total, int K, int64_t N, int64_t G,
+                                    int64_t NGD, int unpack, uint16_t* __restrict__ s_out)
+{
+    uint32_t bad = 0;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(t & 63);
+        int64_t rest = t >> 6;
+        const int k = (int)(rest % K);
+        rest /= K;
+        const int64_t gd = rest % NGD;
+        const int64_t rb = rest / NGD;
+        const int64_t n = rb * TQ_ROWS + lane;
+        if (!unpack) {
+            uint32_t w = 0;
+            for (int h = 0; h < 2; ++h) {
+                const int64_t grp = 2 * gd + h;
+                if (n < N && grp < G) {
+                    const uint16_t v = s[((int64_t)k * N + n) * G + grp];
+                    if (!f16_finite(v)) bad |= TQ_PACK_BAD_SCALE;
+                    w |= (uint32_t)v << (16 * h);
+                }
+            }
+            out[t] = w;
+        } else {
+            const uint32_t w = out[t];
+            for (int h = 0; h < 2; ++h) {
+                const int64_t grp = 2 * gd + h;
+                if (n < N && grp < G) s_out[((int64_t)k * N + n) * G + grp] = (uint16_t)(w >> (16 * h));
+            }
+        }
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+// CODEBOOK: one thread per index dword (six groups of one row).
+__global__ void k_pack_indices(const uint8_t* __restrict__ idx, uint32_t* __restrict__ out,
+                               uint32_t* status, int64_t total, int64_t N, int64_t G, int64_t NID,
+                               int ncb, int unpack, uint8_t* __restrict__ idx_out)
+{
+    uint32_t bad = 0;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(t & 63);
+        const int64_t rest = t >> 6;
+        const int64_t id = rest % NID;
+        const int64_t rb = rest / NID;
+        const int64_t n = rb * TQ_ROWS + lane;
+        if (!unpack) {
+            uint32_t w = 0;
+            for (int j = 0; j < 6; ++j) {
+                const int64_t grp = 6 * id + j;
+                if (n < N && grp < G) {
+                    const uint32_t v = idx[n * G + grp];
+                    if ((int)v >= ncb) bad |= TQ_PACK_BAD_INDEX;
+                    w |= (v & 31u) << (5 * j);
+                }
+            }
+            out[t] = w;
+        } else {
+            const uint32_t w = out[t];
+            for (int j = 0; j < 6; ++j) {
+                const int64_t grp = 6 * id + j;
+                if (n < N && grp < G) idx_out[n * G + grp] = (uint8_t)((w >> (5 * j)) & 31u);
+            }
+        }
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+// Small copies with checks: TENSOR fp32 scales or the f16 codebook.
+__global__ void k_pack_small(const void* __restrict__ src, void* __restrict__ dst, uint32_t* status,
+                             int n, int slots, int is_f16, int unpack)
+{
+    const int i = threadIdx.x;
+    if (i >= slots) return;
+    if (is_f16) {
+        const uint16_t* s = (const uint16_t*)src;
+        uint16_t* d = (uint16_t*)dst;
+        if (unpack) {
+            if (i < n) d[i] = s[i];
+        } else {
+            const uint16_t v = i < n ? s[i] : 0;
+            if (i < n && !f16_finite(v)) atomicOr(status, TQ_PACK_BAD_SCALE);
+            d[i] = v;
+        }
+    } else {
+        const float* s = (const float*)src;
+        float* d = (float*)dst;
+        if (unpack) {
+            if (i < n) d[i] = s[i];
+        } else {
+            const float v = i < n ? s[i] : 0.0f;
+            if (i < n && !isfinite(v)) atomicOr(status, TQ_PACK_BAD_SCALE);
+            d[i] = v;
+        }
+    }
+}
+
+int grid_for(int64_t total)
+{
+    int64_t b = (total + kBlock - 1) / kBlock;
+    const int64_t cap = (int64_t)tq_device_cus() * 64;
+    if (b > cap) b = cap;
+    return (int)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_pack(const tq_weight_desc* desc, const int8_t* trits, const void* scales,
+                            const uint16_t* codebook, void* blob, void* stream_)
+{
+    tq_layout L;
+    tq_status s = tq_check_desc(desc, &L);
+    if (s) return s;
+    const bool need_trits = L.N > 0 && L.Kin > 0;
+    if ((s = tq_check_ptr(trits, "trits", !need_trits))) return s;
+    if ((s = tq_check_ptr(scales, "scales", L.layout != TQ_SCALE_TENSOR && !need_trits))) return s;
+    if ((s = tq_check_ptr(blob, "blob", false))) return s;
+    if (L.layout == TQ_SCALE_CODEBOOK) {
+        if ((s = tq_check_ptr(codebook, "codebook", false))) return s;
+    }
+    hipStream_t stream = (hipStream_t)stream_;
+    uint8_t* b = (uint8_t*)blob;
+    uint32_t* status = (uint32_t*)(b + TQ_STATUS_OFFSET);
+    // every byte of the blob is defined: padding and unused slots are zero
+    if ((s = tq_check_hip(hipMemsetAsync(blob, 0, (size_t)L.total, stream), "tq_pack clear")))
+        return s;
+    hipLaunchKernelGGL(k_write_header, dim3(1), dim3(64), 0, stream, (tq_blob_header*)b, *desc);
+    if ((s = tq_check_launch("tq_pack header"))) return s;
+    const int64_t ncodes = L.codes_bytes / 4;
+    if (ncodes > 0) {
+        hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(ncodes)), dim3(kBlock), 0, stream, trits,
+                           (uint32_t*)(b + L.codes_off), status, ncodes, L.K, L.N, L.Kin, L.NC);
+        if ((s = tq_check_launch("tq_pack codes"))) return s;
+    }
+    if (L.layout == TQ_SCALE_TENSOR) {
+        hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(64), 0, stream, scales,
+                           (void*)(b + L.scales_off), status, L.K, 64, 0, 0);
+    } else if (L.layout == TQ_SCALE_GROUP_F16) {
+        const int64_t n = L.scales_bytes / 4;
+        if (n > 0)
+            hipLaunchKernelGGL(k_pack_group_scales, dim3(grid_for(n)), dim3(kBlock), 0, stream,
+                               (const uint16_t*)scales, (uint32_t*)(b + L.scales_off), status, n,
+                               L.K, L.N, L.G, L.NGD, 0, (uint16_t*)nullptr);
+    } else {
+        hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(64), 0, stream, (const void*)codebook,
+                           (void*)(b + L.cb_off), status, L.ncb, TQ_CB_SLOTS, 1, 0);
+        const int64_t n = L.scales_bytes / 4;
+        if (n > 0)
+            hipLaunchKernelGGL(k_pack_indices, dim3(grid_for(n)), dim3(kBlock), 0, stream,
+                               (const uint8_t*)scales, (uint32_t*)(b + L.scales_off), status, n,
+                               L.N, L.G, L.NID, L.ncb, 0, (uint8_t*)nullptr);
+    }
+    if ((s = tq_check_launch("tq_pack scales"))) return s;
+    uint32_t host_status = 0;
+    if ((s = tq_check_hip(hipMemcpyAsync(&host_status, status, 4, hipMemcpyDeviceToHost, stream),
+                          "tq_pack status copy")))
+        return s;
+    if ((s = tq_check_hip(hipStreamSynchronize(stream), "tq_pack synchronize"))) return s;
+    if (host_status)
+        return tq_fail(TQ_ERR_VALUE, "tq_pack: invalid input (%s%s%s)",
+                       host_status & TQ_PACK_BAD_TRIT ? "trit outside {-1,0,1} " : "",
+                       host_status & TQ_PACK_BAD_SCALE ? "non-finite scale " : "",
+                       host_status & TQ_PACK_BAD_INDEX ? "codebook index >= n_codebook" : "");
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8_t* trits,
+                              void* scales, uint16_t* codebook, void* stream_)
+{
+    tq_layout L;
+    tq_status s = tq_check_desc(desc, &L);
+    if (s) return s;
+    const bool need = L.N > 0 && L.Kin > 0;
+    if ((s = tq_check_ptr(blob, "blob", false))) return s;
+    if ((s = tq_check_ptr(trits, "trits", !need))) return s;
+    if ((s = tq_check_ptr(scales, "scales", true))) return s;
+    if ((s = tq_check_ptr(codebook, "codebook", true))) return s;
+    hipStream_t stream = (hipStream_t)stream_;
+    const uint8_t* b = (const uint8_t*)blob;
+    const int64_t ncodes = L.codes_bytes / 4;
+    if (ncodes > 0 && trits) {
+        hipLaunchKernelGGL(k_unpack_codes, dim3(grid_for(ncodes)), dim3(kBlock), 0, stream,
+                           (const uint32_t*)(b + L.codes_off), trits, ncodes, L.K, L.N, L.Kin, L.NC);
+        if ((s = tq_check_launch("tq_unpack codes"))) return s;
+    }
+    if (scales) {
+        if (L.layout == TQ_SCALE_TENSOR) {
+            hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(64), 0, stream,
+                               (const void*)(b + L.scales_off), scales, (uint32_t*)nullptr, L.K,
+                               L.K, 0, 1);
+        } else if (L.layout == TQ_SCALE_GROUP_F16) {
+            const int64_t n = L.scales_bytes / 4;
+            if (n > 0)
+                hipLaunchKernelGGL(k_pack_group_scales, dim3(grid_for(n)), dim3(kBlock), 0, stream,
+                                   (const uint16_t*)nullptr, (uint32_t*)(b + L.scales_off),
+                                   (uint32_t*)nullptr, n, L.K, L.N, L.G, L.NGD, 1, (uint16_t*)scales);
+        } else {
+            const int64_t n = L.scales_bytes / 4;
+            if (n > 0)
+                hipLaunchKernelGGL(k_pack_indices, dim3(grid_for(n)), dim3(kBlock), 0, stream,
+                                   (const uint8_t*)nullptr, (uint32_t*)(b + L.scales_off),
+                                   (uint32_t*)nullptr, n, L.N, L.G, L.NID, L.ncb, 1, (uint8_t*)scales);
+        }
+        if ((s = tq_check_launch("tq_unpack scales"))) return s;
+    }
+    if (codebook && L.layout == TQ_SCALE_CODEBOOK) {
+        hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(64), 0, stream, (const void*)(b + L.cb_off),
+                           (void*)codebook, (uint32_t*)nullptr, L.ncb, L.ncb, 1, 1);
+        if ((s = tq_check_launch("tq_unpack codebook"))) return s;
+    }
+    return tq_ok();
+}

@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports what include/tq.h
+declares, and rejects bad arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weight_amd import tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(tq_[a-z0-9_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("tq_pack", "tq_unpack", "tq_gemv", "tq_gemm", "tq_act_quant_int8", "tq_packed_size",
+                 "tq_gemv_grouped_prepare", "tq_gemv_grouped_run"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = tq.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(tq.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert tq.abi_version() == 1
+    assert tq.status_string(0) == "ok"
+    assert tq.status_string(5) == "unsupported combination"
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_descriptor_validation():
+    L = tq.lib()
+    n = ctypes.c_size_t()
+    cases = [
+        (tq.desc(0, 64, 1, 64, 64), tq.ERR_ARG),           # no planes
+        (tq.desc(5, 64, 1, 64, 64), tq.ERR_ARG),           # too many planes
+        (tq.desc(1, 48, 1, 64, 96), tq.ERR_ARG),           # group not a power of two
+        (tq.desc(1, 64, 1, 64, 96), tq.ERR_SHAPE),         # Kin % g
+        (tq.desc(1, 0, 0, 64, 40), tq.ERR_SHAPE),          # Kin % 16
+        (tq.desc(1, 0, 0, -1, 64), tq.ERR_ARG),            # negative
+        (tq.desc(1, 0, 7, 64, 64), tq.ERR_ARG),            # bad layout
+        (tq.desc(3, 16, 2, 64, 64, n_codebook=0), tq.ERR_ARG),
+        (tq.desc(3, 16, 2, 64, 64, n_codebook=33), tq.ERR_ARG),
+        (tq.desc(1, 0, 0, 64, 65536 + 16), tq.ERR_SHAPE),
+    ]
+    for d, want in cases:
+        assert L.tq_packed_size(ctypes.byref(d), ctypes.byref(n)) == want, (d.planes, d.group)
+        assert tq.last_error() != ""
+    assert L.tq_packed_size(ctypes.byref(tq.desc(1, 0, 0, 64, 64)), ctypes.byref(n)) == tq.OK
+    assert tq.last_error() == ""
+
+
+def test_packed_size_accounting():
+    # trits: 2 bits each; GROUP_F16: one f16 per plane, row and group
+    for K, g in ((1, 256), (2, 256), (3, 256), (4, 256), (2, 64), (2, 32)):
+        N, Kin = 4096, 4096
+        size = tq.packed_size(tq.desc(K, g, tq.SCALE_GROUP_F16, N, Kin))
+        bpw = size * 8 / (N * Kin)
+        assert abs(bpw - (2 * K + 16 * K / g)) < 2e-4, (K, g, bpw)
+    # per-tensor: 2K bits per weight plus a header and K fp32
+    size = tq.packed_size(tq.desc(1, 0, tq.SCALE_TENSOR, 2560, 2560))
+    assert size == 256 + 2560 * 2560 // 4 + 256
+    # codebook (d = 3, g = 16): 6 bits of trits plus 5-bit indices, six to a dword
+    size = tq.packed_size(tq.desc(3, 16, tq.SCALE_CODEBOOK, 4096, 4096, n_codebook=27))
+    assert size == 256 + 3 * 4096 * 4096 // 4 + 256 + 4096 * ((256 + 5) // 6) * 4
+    # padding rounds rows and columns to 64
+    assert tq.packed_size(tq.desc(1, 0, 0, 65, 80)) == 256 + 2 * 2 * 1024 + 256
+
+
+def test_call_validation_before_any_device_work():
+    L = tq.lib()
+    d = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 64)
+    good = 0x10000
+    # misaligned device pointers are refused up front
+    assert L.tq_gemv(ctypes.byref(d), good + 4, 1, tq.I8, good, good, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemv(ctypes.byref(d), good, 17, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
+    assert L.tq_gemv(ctypes.byref(d), good, -1, tq.I8, good, good, good, None, None) == tq.ERR_ARG
+    assert L.tq_gemv(ctypes.byref(d), good, 1, 9, good, good, good, None, None) == tq.ERR_ARG
+    assert L.tq_gemv(ctypes.byref(d), None, 1, tq.I8, good, good, good, None, None) == tq.ERR_ARG
+    assert L.tq_gemv(ctypes.byref(d), good, 1, tq.I8, good, None, good, None, None) == tq.ERR_ARG
+    dg = tq.desc(1, 64, tq.SCALE_GROUP_F16, 64, 64)
+    assert L.tq_gemv(ctypes.byref(dg), good, 1, tq.BF16, good, None, good, good, None) == tq.ERR_UNSUPPORTED
+    # empty problems are no-ops that need no pointers
+    assert L.tq_gemv(ctypes.byref(d), None, 0, tq.I8, None, None, None, None, None) == tq.OK
+    d0 = tq.desc(1, 0, tq.SCALE_TENSOR, 0, 64)
+    assert L.tq_gemv(ctypes.byref(d0), None, 4, tq.F32, None, None, None, None, None) == tq.OK
+    assert L.tq_act_quant_int8(3, 40, tq.F32, good, good, good, None) == tq.ERR_SHAPE
+    assert L.tq_act_quant_int8(3, 64, tq.I8, good, good, good, None) == tq.ERR_ARG
+    assert L.tq_act_quant_int8(0, 64, tq.F32, None, None, None, None) == tq.OK
+    assert L.tq_pack(ctypes.byref(tq.desc(1, 0, 0, 64, 64)), good, good, None, good + 8, None) == tq.ERR_ALIGN
+    assert L.tq_pack(ctypes.byref(tq.desc(3, 16, 2, 64, 64, n_codebook=27)), good, good, None, good,
+                     None) == tq.ERR_ARG
+
+
+def test_grouped_validation():
+    d1 = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 64)
+    d3 = tq.desc(3, 256, tq.SCALE_GROUP_F16, 64, 256)
+    good = 0x20000
+    probs = tq.problems([(d1, good, good, good, good, None), (d3, good, good, None, good, None)])
+    n = tq.gemv_grouped_workspace_size(probs, 1)
+    assert n >= 2 * 8
+    with pytest.raises(tq.TQError) as e:
+        tq.gemv_grouped_prepare(probs, 1, tq.I8, good, n, stream=0)
+    assert e.value.status in (tq.ERR_UNSUPPORTED, tq.ERR_ARG)
+    with pytest.raises(tq.TQError) as e:
+        tq.gemv_grouped_workspace_size(probs, 17)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    plan = tq.tq_grouped_plan()
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.OK   # zero items
+    plan.n_items = 5
+    plan.workspace = good
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+
+
+def test_gemm_rejects_unsupported_before_device_work():
+    L = tq.lib()
+    good = 0x30000
+    d = tq.desc(2, 64, tq.SCALE_GROUP_F16, 64, 64)
+    assert L.tq_gemm(ctypes.byref(d), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
