@@ -1,0 +1,508 @@
+"""Benchmark of the packed ternary-weight decode path on one MI355X.
+
+A step is one pass of the hot path over a whole layer stack for one token:
+per-token int8 quantisation of every projection's input (tq_act_quant_int8)
+and the ternary GEMV of all projections in one grouped launch
+(tq_gemv_grouped_run).  The default workload is the BitNet b1.58-2B decode
+stack (30 layers x q,k,v,o,gate,up,down; one trit plane, per-tensor scale,
+int8 activations, int32 accumulate), inputs seeded and synthetic, resident in
+HBM before timing starts.
+
+Prints one JSON line.  `value` is effective HBM bandwidth: the algorithmic
+bytes of a step (packed trits, scales, activations in and out) divided by the
+step time.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synth import device, gen, inputs  # noqa: E402
+from synth.configs import BF16, CASES, CODEBOOK, F32, GROUP_F16, I8, TENSOR  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "ternary_weight_amd", "csrc")
+METRIC = "ternary GEMV effective HBM GB/s (% of peak) at BitNet-2B/Llama-8B shapes, M=1"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--spin-up-ms", type=float, default=150.0,
+                    help="plain streaming reads before the warmup steps: the GPU needs ~20 ms of "
+                         "memory load to leave its idle clocks")
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4"])
+    ap.add_argument("--M", type=int, default=1, help="tokens per step (cfg4: 1, 4 or 16)")
+    ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
+    ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
+    ap.add_argument("--fused", action="store_true",
+                    help="int8 path as one call: fp32 activations quantised inside the grouped product "
+                         "(TQ_F32_Q8); default is two launches, the batched quantiser then the product")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a plain HBM read (torch sum) and copy of 2 GiB as a practical ceiling")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Workload construction (all on the GPU).
+# ---------------------------------------------------------------------------
+class Stack:
+    """Every projection of a case packed in one slab, with its activations and outputs."""
+
+    def __init__(self, case, M: int, fused: bool = True):
+        import torch
+        from ternary_weight_amd import tq
+        self.case, self.M = case, M
+        # int8 activations: quantise inside the product (one launch per step) or as a separate call
+        self.fused = fused and case.x_type == I8
+        self.run_type = tq.F32_Q8 if self.fused else case.x_type
+        self.projs = case.projections()
+        K, g, layout = case.planes, case.group, case.layout
+        ncb = inputs.N_CODEBOOK if layout == CODEBOOK else 0
+        self.descs = [tq.desc(K, g, layout, n, kin, n_codebook=ncb) for (_, _, _, n, kin) in self.projs]
+        sizes = [tq.packed_size(d) for d in self.descs]
+        offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])])
+        self.slab = torch.empty(int(offs[-1]), dtype=torch.uint8, device="cuda")
+        self.blobs = [self.slab[int(offs[i]):int(offs[i]) + sizes[i]] for i in range(len(sizes))]
+        self.blob_bytes = int(offs[-1])
+        # activations grouped by in_features so that quantisation is one launch per width
+        self.widths = sorted({kin for (_, _, _, _, kin) in self.projs})
+        self.rows_of = {w: [i for i, p in enumerate(self.projs) if p[4] == w] for w in self.widths}
+        act_fp = torch.float32 if case.x_type in (F32, I8) else torch.int16
+        self.x_raw = {w: torch.empty((len(self.rows_of[w]) * M, w), dtype=act_fp, device="cuda")
+                      for w in self.widths}
+        unfused_i8 = case.x_type == I8 and not self.fused
+        self.x_q = {w: torch.empty((len(self.rows_of[w]) * M, w), dtype=torch.int8, device="cuda")
+                    for w in self.widths} if unfused_i8 else None
+        self.x_s = {w: torch.empty(len(self.rows_of[w]) * M, dtype=torch.float32, device="cuda")
+                    for w in self.widths} if unfused_i8 else None
+        self.ys = [torch.empty((M, n), dtype=torch.float32, device="cuda") for (_, _, _, n, _) in self.projs]
+        self.slot = {}
+        for w in self.widths:
+            for j, i in enumerate(self.rows_of[w]):
+                self.slot[i] = (w, j)
+        for i, (layer, p, _, n, kin) in enumerate(self.projs):
+            d = device.projection(case, layer, p, n, kin, M=M)
+            tq.pack(self.descs[i], d["trits"], d["scales"], d["codebook"], self.blobs[i])
+            w, j = self.slot[i]
+            self.x_raw[w][j * M:(j + 1) * M].copy_(d["x"])
+            del d
+        torch.cuda.synchronize()
+        # grouped plan over the whole stack
+        items = []
+        for i in range(len(self.projs)):
+            w, j = self.slot[i]
+            if self.x_q is not None:
+                x, xs = self.x_q[w][j * M:(j + 1) * M], self.x_s[w][j * M:(j + 1) * M]
+            else:
+                x, xs = self.x_raw[w][j * M:(j + 1) * M], None
+            items.append((self.descs[i], self.blobs[i], x, xs, self.ys[i], None))
+        self._probs = tq.problems(items)
+        nbytes = tq.gemv_grouped_workspace_size(self._probs, M)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.plan = None
+        self._segments = None
+
+    def prepare(self, waves: int = 0, row_blocks: int = 0):
+        from ternary_weight_amd import tq
+        self.plan = tq.gemv_grouped_prepare(self._probs, self.M, self.run_type, self.ws,
+                                            self.ws.numel(), waves=waves, row_blocks=row_blocks)
+
+    def quantize(self):
+        from ternary_weight_amd import tq
+        if self.x_q is None:
+            return
+        if self._segments is None:
+            self._segments = [(self.x_raw[w].shape[0], w, F32, self.x_raw[w], self.x_q[w], self.x_s[w])
+                              for w in self.widths]
+        tq.act_quant_int8_batch(self._segments)
+
+    def gemv(self):
+        from ternary_weight_amd import tq
+        tq.gemv_grouped_run(self.plan)
+
+    # algorithmic bytes ------------------------------------------------------
+    def gemv_bytes(self) -> int:
+        K, g, layout, M = self.case.planes, self.case.group, self.case.layout, self.M
+        # activations as the product reads them: fp32 when it quantises them itself
+        xsz = 4 if self.fused else {I8: 1, BF16: 2, F32: 4}[self.case.x_type]
+        total = 0
+        for (_, _, _, n, kin) in self.projs:
+            b = K * n * kin // 4                               # packed trits, 2 bits each
+            if layout == TENSOR:
+                b += 4 * K
+            elif layout == GROUP_F16:
+                b += 2 * K * n * (kin // g)                    # one f16 per plane, row, group
+            else:
+                b += (5 * n * (kin // g) + 7) // 8 + 2 * inputs.N_CODEBOOK   # 5-bit index per group
+            b += M * kin * xsz + (4 * M if (self.case.x_type == I8 and not self.fused) else 0)
+            b += 4 * M * n                                     # fp32 y
+            total += b
+        return total
+
+    def quant_bytes(self) -> int:
+        if self.x_q is None:
+            return 0
+        return sum(self.M * kin * (4 + 1) + 4 * self.M for (_, _, _, _, kin) in self.projs)
+
+
+# ---------------------------------------------------------------------------
+# Parity spot check and CPU baseline (oracle).
+# ---------------------------------------------------------------------------
+def rel_err(y, ystar) -> float:
+    """max over tokens of max_n |y - y*| / max(|y*|, rms(y*))."""
+    y, ystar = np.asarray(y, np.float64), np.asarray(ystar, np.float64)
+    worst = 0.0
+    for m in range(ystar.shape[0]):
+        den = np.maximum(np.abs(ystar[m]), np.sqrt(np.mean(ystar[m] ** 2)))
+        den = np.where(den == 0, 1.0, den)
+        worst = max(worst, float(np.max(np.abs(y[m] - ystar[m]) / den)))
+    return worst
+
+
+def spot_check(stack, n_proj=3, rows=64) -> dict:
+    """Rows of a few projections against the oracle on host-regenerated inputs."""
+    import oracle
+    import torch
+    case, M = stack.case, stack.M
+    rng = np.random.default_rng(99)
+    picks = sorted({0, len(stack.projs) - 1, int(rng.integers(len(stack.projs)))})[:n_proj]
+    worst, exact = 0.0, True
+    for i in picks:
+        layer, p, _, n, kin = stack.projs[i]
+        r = np.sort(rng.choice(n, size=min(rows, n), replace=False))
+        h = inputs.projection(case, layer, p, n, kin, rows=r, M=M)
+        y = stack.ys[i].detach().cpu().numpy()[:, r]
+        if case.x_type == I8:
+            q, s = oracle.act_quant_i8(h["x"], F32)
+            out = oracle.gemv_i8(case.planes, case.group, case.layout, h["trits"], h["scales"], q, s,
+                                 h["codebook"])
+            exact &= bool(np.array_equal(y.view(np.uint32), out["y32"].view(np.uint32)))
+        else:
+            ref = oracle.gemv_fp(case.planes, case.group, case.layout, h["trits"], h["scales"], h["x"],
+                                 BF16 if case.x_type == BF16 else F32, h["codebook"])
+            worst = max(worst, rel_err(y, ref))
+    torch.cuda.synchronize()
+    return {"projections": len(picks), "rows_each": rows,
+            "bit_exact" if case.x_type == I8 else "max_rel_err": exact if case.x_type == I8 else worst}
+
+
+def cpu_baseline(stack, seconds: float) -> dict:
+    """The oracle on the host cores, over whole layers of the same stack."""
+    import oracle
+    case, M = stack.case, stack.M
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    orc = oracle.default()
+    per_layer = len(case.model["proj"])
+    layer_inputs = []
+    for (layer, p, _, n, kin) in stack.projs[:per_layer]:
+        layer_inputs.append((n, kin, inputs.projection(case, layer, p, n, kin, M=M)))
+    done_bytes, t0, reps = 0, time.perf_counter(), 0
+    layer_bytes = 0
+    K, g, layout = case.planes, case.group, case.layout
+    for (n, kin, h) in layer_inputs:
+        xsz = {I8: 1, BF16: 2, F32: 4}[case.x_type]
+        layer_bytes += K * n * kin // 4 + M * kin * xsz + 4 * M * n + (M * kin * 5 if case.x_type == I8 else 0)
+        if layout == GROUP_F16:
+            layer_bytes += 2 * K * n * (kin // g)
+    while True:
+        for (n, kin, h) in layer_inputs:
+            if case.x_type == I8:
+                q, s = orc.act_quant_i8(h["x"], F32)
+                orc.gemv_i8(K, g, layout, h["trits"], h["scales"], q, s, h["codebook"], nthreads=threads)
+            else:
+                orc.gemv_fp(K, g, layout, h["trits"], h["scales"], h["x"], case.x_type, h["codebook"],
+                            nthreads=threads)
+        done_bytes += layer_bytes
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "layer 0 of the stack (%d projections), %d repetitions, %.1f s; C oracle, OpenMP over "
+                      "output rows" % (per_layer, reps, el)}
+
+
+def spin_up(ms: float, nbytes: int = 1 << 30):
+    """Keep HBM busy for about `ms` with the harness read kernel (not timed, not a step)."""
+    import torch
+    if ms <= 0:
+        return
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            device.stream_read(buf, sink, 8192)
+        torch.cuda.synchronize()
+    del buf
+
+
+def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 5) -> dict:
+    """A plain streaming read (harness kernel) and a device copy (torch) of known size."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {"bytes": nbytes}
+    for blocks in (2048, 8192):
+        device.stream_read(a, sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            device.stream_read(a, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        out["read_GBs_%d" % blocks] = round(nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    half = nbytes // 2
+    src, dst = a[:half], a[half:]
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBs"] = round(2 * half * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del a
+    return out
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/) and the measured HBM traffic of the kernel.
+# ---------------------------------------------------------------------------
+def kernel_fingerprint() -> str:
+    """Hash of the library sources; traffic measured on other sources is not reused."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "tq.h")]:
+        if f.endswith((".hip", ".h")):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _trace_rows(d):
+    f = glob.glob(os.path.join(d, "*_kernel_trace.csv"))
+    return list(csv.DictReader(open(f[0]))) if f else []
+
+
+def _pmc_means(d):
+    out = {}
+    for f in glob.glob(os.path.join(d, "*_counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            out.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+def summarize(args) -> None:
+    """Write a profiles/*.md summary from rocprofv3 output directories."""
+    kern = args.kernel
+    lines = ["# %s" % args.title, ""]
+    rec = {"kernel": kern, "fingerprint": kernel_fingerprint()}
+    if args.trace_dir:
+        stats = glob.glob(os.path.join(args.trace_dir, "*_kernel_stats.csv"))
+        lines += ["Command: `%s`" % args.trace_cmd, "", "rocprofv3 --kernel-trace --stats, top kernels by total time:", "",
+                  "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        rows = list(csv.DictReader(open(stats[0])))
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+            lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                               float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+            if kern in r["Name"]:
+                rec["avg_us"] = round(float(r["AverageNs"]) / 1e3, 3)
+                rec["calls"] = int(r["Calls"])
+        tr = [r for r in _trace_rows(args.trace_dir) if kern in r["Kernel_Name"]]
+        if tr:
+            tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+            last = tr[-args.timed_launches:] if args.timed_launches else tr
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+            rec["timed_avg_us"] = round(sum(d) / len(d), 3)
+            lines += ["", "Kernel `%s`: average of all %d launches %.2f us; of the last %d (the timed region) %.2f us."
+                      % (kern, len(tr), rec.get("avg_us", float("nan")), len(last), rec["timed_avg_us"])]
+    if args.fetch_dir and args.write_dir:
+        f, w = _pmc_means(args.fetch_dir), _pmc_means(args.write_dir)
+
+        def find(tab, name, counter):
+            for (k, c), v in tab.items():
+                if name in k and c == counter:
+                    return v
+            return None
+        read_kib = find(f, "k_stream_read", "FETCH_SIZE")
+        fill_kib = find(w, "vectorized_elementwise_kernel<16", "WRITE_SIZE")
+        gf, gw = find(f, kern, "FETCH_SIZE"), find(w, kern, "WRITE_SIZE")
+        fetch_factor = (args.read_bytes / 1024) / read_kib[0]
+        write_factor = (args.fill_bytes / 1024) / fill_kib[0]
+        traffic = gf[0] * 1024 * fetch_factor + gw[0] * 1024 * write_factor
+        rec.update({"fetch_kib": round(gf[0], 1), "write_kib": round(gw[0], 1), "fetch_factor": round(fetch_factor, 4),
+                    "write_factor": round(write_factor, 4), "traffic_bytes": int(round(traffic))})
+        lines += ["", "Commands: `%s` (FETCH_SIZE) and the same with `--pmc WRITE_SIZE`." % args.pmc_cmd, "",
+                  "Calibration with kernels of known size in the same run: the harness streaming read of %d bytes "
+                  "reads FETCH_SIZE %.1f KiB (factor %.4f); torch's fill of %d bytes reads WRITE_SIZE %.1f KiB "
+                  "(factor %.4f)." % (args.read_bytes, read_kib[0], fetch_factor, args.fill_bytes, fill_kib[0], write_factor),
+                  "", "Kernel `%s` per launch (%d launches): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB -> HBM traffic "
+                  "%.0f bytes." % (kern, gf[1], gf[0], gw[0], traffic)]
+    lines += ["", "```json", json.dumps(rec), "```", ""]
+    open(args.out, "w").write("\n".join(lines))
+    print("wrote", args.out)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from a profiles/ summary of the current sources, else None."""
+    fp = kernel_fingerprint()
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        text = open(f).read()
+        if "```json" not in text:
+            continue
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        if rec.get("kernel") == kernel and rec.get("fingerprint") == fp and "traffic_bytes" in rec:
+            return rec["traffic_bytes"]
+    return None
+
+
+# ---------------------------------------------------------------------------
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        ap = argparse.ArgumentParser(description="write a profiles/ summary from rocprofv3 output")
+        ap.add_argument("summarize")
+        ap.add_argument("--kernel", required=True)
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--out", required=True)
+        ap.add_argument("--trace-dir")
+        ap.add_argument("--trace-cmd", default="")
+        ap.add_argument("--timed-launches", type=int, default=0)
+        ap.add_argument("--fetch-dir")
+        ap.add_argument("--write-dir")
+        ap.add_argument("--pmc-cmd", default="")
+        ap.add_argument("--read-bytes", type=int, default=4 << 30)
+        ap.add_argument("--fill-bytes", type=int, default=4 << 30)
+        summarize(ap.parse_args())
+        return
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; the multi-GPU path is not built (--gpus %d refused)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    case = CASES[args.config]
+    M = args.M if args.config == "cfg4" else case.M
+    t_build = time.perf_counter()
+    stack = Stack(case, M, fused=args.fused)
+    stack.prepare(args.waves, args.row_blocks)
+    build_s = time.perf_counter() - t_build
+    print("built %s: %d projections, %.1f MB packed, plan %d items x %d blocks x %d waves (%.1f s)"
+          % (args.config, len(stack.projs), stack.blob_bytes / 1e6, stack.plan.n_items,
+             stack.plan.row_blocks, stack.plan.waves, build_s), file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    spin_up(args.spin_up_ms)
+    for _ in range(args.warmup):
+        stack.quantize()
+        stack.gemv()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events only at its two ends
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        stack.quantize()
+        stack.gemv()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    if stack.x_q is None:
+        # one launch per step: the step time is the kernel's launch duration
+        gemv_avg = ms_step
+    else:
+        # the product kernel alone, back to back between one pair of events
+        reps = max(args.steps, 20)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            stack.gemv()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gemv_avg = g0.elapsed_time(g1) / reps
+
+    gbytes, qbytes = stack.gemv_bytes(), stack.quant_bytes()
+    kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
+                                                      1 if M == 1 else (4 if M <= 4 else 16))
+    value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
+    achieved = gbytes / (gemv_avg / 1e3) / 1e9
+
+    ceiling = hbm_ceiling() if args.ceiling else None
+    check = None if args.no_check else spot_check(stack)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(stack, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {I8: "i8", BF16: "bf16", F32: "f32"}[case.x_type],
+        "data": "synthetic (seeded SplitMix64; trits P(0)=0.4, x ~ N(0,1))",
+        "config": {
+            "workload": case.name,
+            "layers": case.model["layers"],
+            "projections": len(stack.projs),
+            "M": M,
+            "planes": case.planes,
+            "group": case.group,
+            "scale_layout": {TENSOR: "tensor", GROUP_F16: "group_f16", CODEBOOK: "codebook"}[case.layout],
+            "step": ("one grouped launch over the stack; fp32 inputs quantised per token to int8 "
+                     "inside it (bit-identical to the separate quantiser)") if stack.fused else
+                    ("act-quant of every projection input + one grouped GEMV launch over the stack"
+                     if case.x_type == I8 else "one grouped GEMV launch over the stack"),
+            "packed_weight_bytes": stack.blob_bytes,
+            "grouped_waves": stack.plan.waves,
+            "grouped_row_blocks": stack.plan.row_blocks,
+        },
+        "tok_per_s_equiv": round(1e3 / ms_step, 1),
+        "gemv_us": round(gemv_avg * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(kernel_name),
+            "kernel": kernel_name,
+            "bytes_per_launch": gbytes,
+        },
+        "cpu_baseline": cpu,
+        "hbm_ceiling": ceiling,
+        "parity_spot_check": check,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -36,8 +36,9 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    their kernels on it and return without waiting, except tq_pack (see
  *    there) and tq_gemv_grouped_prepare.
- *  - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
- *    Outputs must not alias inputs.
+ *  - Alignment (TQ_ERR_ALIGN otherwise): blobs, tq_pack's trits and
+ *    tq_act_quant_int8's x and xq 16 bytes; every other device array 4 bytes
+ *    (2 for f16 codebooks).  Outputs must not alias inputs.
  *  - Argument, shape, alignment and support errors are returned before
  *    anything is enqueued.  A failed launch returns TQ_ERR_DEVICE.  Details
  *    of the last error of the calling thread are in tq_last_error().
@@ -76,7 +77,11 @@ typedef enum tq_scale_layout {
 typedef enum tq_dtype {
     TQ_F32 = 0,
     TQ_BF16 = 1,             /* bits of bfloat16 values, uint16 storage                */
-    TQ_I8 = 2                /* int8 values with an fp32 scale per token (row of x)  */
+    TQ_I8 = 2,               /* int8 values with an fp32 scale per token (row of x)  */
+    TQ_F32_Q8 = 3            /* fp32 values quantised per token to int8 inside the
+                                product, by the rule of tq_act_quant_int8, then
+                                accumulated as TQ_I8 (bit-identical to the two calls);
+                                tq_gemv / tq_gemv_grouped only, M * Kin <= 65536      */
 } tq_dtype;
 
 /* Shape and format of one packed weight. */
@@ -137,15 +142,37 @@ tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8_t* trits,
 tq_status tq_act_quant_int8(int64_t M, int64_t in_features, int32_t x_type, const void* x,
                             int8_t* xq, float* x_scale, void* stream);
 
+/* One activation matrix for tq_act_quant_int8_batch. */
+typedef struct tq_act_segment {
+    int64_t M;                    /* tokens (rows)                              */
+    int64_t in_features;          /* Kin, a multiple of 16                      */
+    int32_t x_type;               /* TQ_F32 or TQ_BF16                          */
+    int32_t reserved;
+    const void* x;                /* device [M][Kin], 16-byte aligned           */
+    int8_t* xq;                   /* device [M][Kin], 16-byte aligned           */
+    float* x_scale;               /* device [M]                                 */
+} tq_act_segment;
+
+#define TQ_ACT_MAX_SEGMENTS 16
+
+/*
+ * tq_act_quant_int8 for up to TQ_ACT_MAX_SEGMENTS matrices in one launch
+ * (e.g. the inputs of every projection of a layer stack, grouped by width).
+ * `segments` is a host array; same per-token rule and results.
+ */
+tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count, void* stream);
+
 /*
  * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
  * scale per group).
  *   x         device [M][Kin] of x_type
- *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else NULL
+ *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else unused
+ *             (TQ_F32_Q8 computes the per-token scales itself)
  *   y         device fp32 [M][N]
  *   acc       optional device int32 [M][N]: the integer accumulator, only for
- *             TQ_I8 with TQ_SCALE_TENSOR and K = 1 (TQ_ERR_UNSUPPORTED otherwise)
- * TQ_I8 with TQ_SCALE_TENSOR and K = 1 is bit exact:
+ *             TQ_I8 / TQ_F32_Q8 with TQ_SCALE_TENSOR and K = 1
+ *             (TQ_ERR_UNSUPPORTED otherwise)
+ * TQ_I8 and TQ_F32_Q8 with TQ_SCALE_TENSOR and K = 1 are bit exact:
  *   y = fl32(float(acc) * fl32(s_w * x_scale[m])).
  * Other combinations accumulate in fp32.  M = 0 or N = 0 is a no-op.
  */
@@ -177,12 +204,16 @@ typedef struct tq_problem {
 /* Filled by tq_gemv_grouped_prepare; plain data, may be copied. */
 typedef struct tq_grouped_plan {
     const void* workspace;        /* device table written by prepare           */
-    int64_t n_items;              /* work items (workgroups) of one run        */
+    int64_t n_items;              /* 64-row blocks over all problems           */
     int32_t family;               /* kernel family selected at prepare         */
     int32_t x_type;
     int32_t M;
-    int32_t waves;                /* waves per workgroup                       */
+    int32_t waves;                /* in: 0 or 1, 2, 4, 8, 16; out: waves that
+                                     split the columns of one 64-row block      */
+    int32_t row_blocks;           /* in: 0 or 1, 2, 4, 8, 16; out: 64-row blocks
+                                     per workgroup (waves * row_blocks <= 16)   */
     int32_t n_problems;
+    int32_t x_lds_bytes;          /* LDS for in-kernel quantised activations   */
     int32_t reserved;
 } tq_grouped_plan;
 
@@ -191,9 +222,14 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
                                          size_t* bytes);
 
 /*
- * Validate the problems, write their descriptor table and the work list
- * (longest first) into `workspace` (device, caller-owned) and fill `plan`.
- * Copies host->device on `stream` and synchronizes it.
+ * Validate the problems, write their descriptor table and the work list into
+ * `workspace` (device, caller-owned) and fill `plan`.  The run is one launch
+ * with one workgroup per item, an item being `row_blocks` consecutive 64-row
+ * blocks of one problem, each split over `waves` waves; items are ordered
+ * longest first.  On entry plan->waves and plan->row_blocks choose the shape
+ * (0 = default: 4 waves, 1 block; with TQ_F32_Q8 1 wave, 4 blocks, so that
+ * a workgroup quantises its activations once for four blocks).  Copies
+ * host->device on `stream` and synchronizes it.
  */
 tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
                                   int32_t x_type, void* workspace, size_t workspace_bytes,

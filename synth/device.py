@@ -29,6 +29,9 @@ def lib():
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_void_p,
                                  ctypes.c_void_p]
         L.synth_fill.restype = ctypes.c_int
+        L.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+        L.synth_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -41,6 +44,15 @@ def fill(kind: int, seed: int, start: int, out, a: float = 0.0, b: float = 0.0, 
     if rc:
         raise RuntimeError("synth_fill failed: hip error %d" % rc)
     return out
+
+
+def stream_read(buf, out, blocks: int = 0, stream=None):
+    """Launch the plain streaming-read kernel over a whole uint8 buffer."""
+    import torch
+    st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = lib().synth_stream_read(buf.data_ptr(), buf.numel() // 16 * 16, out.data_ptr(), blocks, st)
+    if rc:
+        raise RuntimeError("synth_stream_read failed: hip error %d" % rc)
 
 
 def projection(case, layer: int, proj: int, N: int, Kin: int, M=None, device="cuda"):

@@ -31,11 +31,23 @@ COMMON = [
 ]
 
 TQ_SOURCES = ["tq_api.hip", "tq_pack.hip", "tq_act.hip", "tq_gemv.hip", "tq_entry.hip", "tq_gemm.hip"] + [
-    "tq_gemv_%s_m%d.hip" % (x, m) for x in ("f32", "bf16", "i8") for m in (1, 4, 16)]
+    "tq_gemv_%s_m%d.hip" % (x, m) for x in ("f32", "bf16", "i8", "f32q8") for m in (1, 4, 16)]
+
+
+def _deps_mtime() -> float:
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    heads.append(os.path.join(ROOT, "include", "tq.h"))
+    return max(os.path.getmtime(h) for h in heads)
+
+
+INCREMENTAL = False
 
 
 def _compile(src: str, obj: str, extra=()) -> str:
     os.makedirs(os.path.dirname(obj), exist_ok=True)
+    if INCREMENTAL and os.path.exists(obj) and \
+            os.path.getmtime(obj) > max(os.path.getmtime(src), _deps_mtime()):
+        return obj
     cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -77,5 +89,6 @@ def build_all() -> None:
 
 
 if __name__ == "__main__":
+    INCREMENTAL = "--incremental" in sys.argv
     build_all()
     print("built", LIBTQ, file=sys.stderr)

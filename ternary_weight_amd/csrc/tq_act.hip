@@ -5,6 +5,8 @@
 // division and the product are single IEEE fp32 operations (this file is built
 // with -ffp-contract=off; HIP divides fp32 with correct rounding), so the
 // result is bit-identical to any IEEE implementation of the same steps.
+#include <string.h>
+
 #include "tq_internal.h"
 
 namespace {
@@ -27,67 +29,106 @@ __device__ __forceinline__ int8_t quant1(float v, float inv)
     return (int8_t)(int)r;
 }
 
-// One workgroup per token; Kin % 16 == 0 so every row starts 16-byte aligned.
+struct Seg {
+    int64_t row0;        // first global row of the segment
+    int64_t Kin;
+    int32_t x_type, pad;
+    const void* x;
+    int8_t* q;
+    float* s;
+};
+
+struct SegTable {
+    Seg seg[TQ_ACT_MAX_SEGMENTS];
+    int32_t count;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeld = 8;   // 16-byte vectors a thread keeps: one pass for Kin <= 8 * 4 * kThreads
+
+__device__ __forceinline__ float absmax4(f32x4 v)
+{
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ uint32_t quant4(f32x4 v, float inv)
+{
+    return (uint32_t)(uint8_t)quant1(v.x, inv) | ((uint32_t)(uint8_t)quant1(v.y, inv) << 8) |
+           ((uint32_t)(uint8_t)quant1(v.z, inv) << 16) | ((uint32_t)(uint8_t)quant1(v.w, inv) << 24);
+}
+
+// four values of a row as fp32: fp32 loads 16 bytes, bf16 loads 8 bytes
 template <int XT>
-__global__ __launch_bounds__(kThreads) void k_act_quant(const void* __restrict__ x,
-                                                        int8_t* __restrict__ q,
-                                                        float* __restrict__ s, int64_t Kin)
+__device__ __forceinline__ f32x4 load4(const void* row, int i)
+{
+    if (XT == TQ_F32) return reinterpret_cast<const f32x4*>(row)[i];
+    const uint2 w = reinterpret_cast<const uint2*>(row)[i];
+    return f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
+                 bf16_to_f32(w.y >> 16)};
+}
+
+// One workgroup per token (row): a = max|x| (each thread keeps its values in
+// registers when the row fits), then q and s.  Kin % 16 == 0.
+template <int XT>
+__device__ __forceinline__ void quant_row(const void* xrow, int8_t* qrow, float* s_out, int64_t Kin)
 {
     __shared__ float red[kThreads / 64];
-    const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
-    const int64_t n16 = Kin / 16;   // 16-element units
+    const int n4 = (int)(Kin >> 2);
+    const bool held = n4 <= kHeld * kThreads;
+    f32x4 v[kHeld];
     float a = 0.0f;
-    if (XT == TQ_F32) {
-        const float4* xr = reinterpret_cast<const float4*>((const float*)x + m * Kin);
-        for (int64_t u = tid; u < n16 * 4; u += kThreads) {
-            const float4 v = xr[u];
-            a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {
+            const int i = tid + j * kThreads;
+            v[j] = i < n4 ? load4<XT>(xrow, i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            a = fmaxf(a, absmax4(v[j]));
         }
     } else {
-        const uint4* xr = reinterpret_cast<const uint4*>((const uint16_t*)x + m * Kin);
-        for (int64_t u = tid; u < n16 * 2; u += kThreads) {
-            const uint4 v = xr[u];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                a = fmaxf(a, fabsf(bf16_to_f32(w[j] & 0xFFFFu)));
-                a = fmaxf(a, fabsf(bf16_to_f32(w[j] >> 16)));
-            }
-        }
+        for (int i = tid; i < n4; i += kThreads) a = fmaxf(a, absmax4(load4<XT>(xrow, i)));
     }
     a = wave_max(a);
     if ((tid & 63) == 0) red[tid >> 6] = a;
     __syncthreads();
     a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float inv = a > 0.0f ? 127.0f / a : 0.0f;
-    int8_t* qr = q + m * Kin;
-    if (XT == TQ_F32) {
-        const float4* xr = reinterpret_cast<const float4*>((const float*)x + m * Kin);
-        for (int64_t u = tid; u < n16 * 4; u += kThreads) {
-            const float4 v = xr[u];
-            const uint32_t b = (uint32_t)(uint8_t)quant1(v.x, inv) |
-                               ((uint32_t)(uint8_t)quant1(v.y, inv) << 8) |
-                               ((uint32_t)(uint8_t)quant1(v.z, inv) << 16) |
-                               ((uint32_t)(uint8_t)quant1(v.w, inv) << 24);
-            reinterpret_cast<uint32_t*>(qr)[u] = b;
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(qrow);
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < kHeld; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < n4) q4[i] = quant4(v[j], inv);
         }
     } else {
-        const uint4* xr = reinterpret_cast<const uint4*>((const uint16_t*)x + m * Kin);
-        for (int64_t u = tid; u < n16 * 2; u += kThreads) {
-            const uint4 v = xr[u];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[2] = {0, 0};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = (uint8_t)quant1(bf16_to_f32(w[j] & 0xFFFFu), inv);
-                const uint32_t hi = (uint8_t)quant1(bf16_to_f32(w[j] >> 16), inv);
-                o[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
-            }
-            reinterpret_cast<uint2*>(qr)[u] = make_uint2(o[0], o[1]);
-        }
+        for (int i = tid; i < n4; i += kThreads) q4[i] = quant4(load4<XT>(xrow, i), inv);
     }
-    if (tid == 0) s[m] = a > 0.0f ? a / 127.0f : 0.0f;
+    if (tid == 0) *s_out = a > 0.0f ? a / 127.0f : 0.0f;
+}
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void k_act_quant(const void* __restrict__ x, int8_t* __restrict__ q,
+                                                        float* __restrict__ s, int64_t Kin)
+{
+    const int64_t m = blockIdx.x;
+    const size_t esz = XT == TQ_F32 ? 4 : 2;
+    quant_row<XT>((const uint8_t*)x + m * Kin * esz, q + m * Kin, s + m, Kin);
+}
+
+// Several matrices in one launch: workgroup b is global row b.
+__global__ __launch_bounds__(kThreads) void k_act_quant_batch(SegTable T)
+{
+    const int64_t b = blockIdx.x;
+    int j = 0;
+    while (j + 1 < T.count && T.seg[j + 1].row0 <= b) ++j;
+    const Seg& S = T.seg[j];
+    const int64_t m = b - S.row0;
+    if (S.x_type == TQ_F32)
+        quant_row<TQ_F32>((const float*)S.x + m * S.Kin, S.q + m * S.Kin, S.s + m, S.Kin);
+    else
+        quant_row<TQ_BF16>((const uint16_t*)S.x + m * S.Kin, S.q + m * S.Kin, S.s + m, S.Kin);
 }
 
 }  // namespace
@@ -109,7 +150,7 @@ TQ_EXPORT tq_status tq_act_quant_int8(int64_t M, int64_t Kin, int32_t x_type, co
     const bool need = Kin > 0;
     if ((s = tq_check_ptr(x, "x", !need))) return s;
     if ((s = tq_check_ptr(xq, "xq", !need))) return s;
-    if ((s = tq_check_ptr(x_scale, "x_scale", false))) return s;
+    if ((s = tq_check_ptr(x_scale, "x_scale", false, 4))) return s;
     hipStream_t stream = (hipStream_t)stream_;
     if (x_type == TQ_F32)
         hipLaunchKernelGGL(k_act_quant<TQ_F32>, dim3((unsigned)M), dim3(kThreads), 0, stream, x, xq,
@@ -118,5 +159,43 @@ TQ_EXPORT tq_status tq_act_quant_int8(int64_t M, int64_t Kin, int32_t x_type, co
         hipLaunchKernelGGL(k_act_quant<TQ_BF16>, dim3((unsigned)M), dim3(kThreads), 0, stream, x,
                            xq, x_scale, Kin);
     if ((s = tq_check_launch("tq_act_quant_int8"))) return s;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count, void* stream_)
+{
+    tq_status s;
+    if (count < 0 || count > TQ_ACT_MAX_SEGMENTS || (count > 0 && !segments))
+        return tq_fail(TQ_ERR_ARG, "count = %d, must be 0..%d", count, TQ_ACT_MAX_SEGMENTS);
+    SegTable T;
+    memset(&T, 0, sizeof T);
+    int64_t rows = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const tq_act_segment& g = segments[i];
+        if (g.M < 0 || g.in_features < 0)
+            return tq_fail(TQ_ERR_ARG, "segment %d: negative size", i);
+        if (g.x_type != TQ_F32 && g.x_type != TQ_BF16)
+            return tq_fail(TQ_ERR_ARG, "segment %d: x_type = %d, must be TQ_F32 or TQ_BF16", i, g.x_type);
+        if (g.in_features % 16 || g.in_features > TQ_MAX_KIN)
+            return tq_fail(TQ_ERR_SHAPE, "segment %d: in_features = %lld", i, (long long)g.in_features);
+        if (g.M > 0) {
+            const bool need = g.in_features > 0;
+            if ((s = tq_check_ptr(g.x, "segment x", !need))) return s;
+            if ((s = tq_check_ptr(g.xq, "segment xq", !need))) return s;
+            if ((s = tq_check_ptr(g.x_scale, "segment x_scale", false, 4))) return s;
+        }
+        Seg& d = T.seg[T.count++];
+        d.row0 = rows;
+        d.Kin = g.in_features;
+        d.x_type = g.x_type;
+        d.x = g.x;
+        d.q = g.xq;
+        d.s = g.x_scale;
+        rows += g.M;
+    }
+    if (rows > (1ll << 31) - 1) return tq_fail(TQ_ERR_SHAPE, "too many rows");
+    if (rows == 0) return tq_ok();
+    hipLaunchKernelGGL(k_act_quant_batch, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream_, T);
+    if ((s = tq_check_launch("tq_act_quant_int8_batch"))) return s;
     return tq_ok();
 }

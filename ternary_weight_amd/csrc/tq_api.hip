@@ -73,10 +73,11 @@ tq_status tq_check_desc(const tq_weight_desc* d, tq_layout* L)
     return TQ_OK;
 }
 
-tq_status tq_check_ptr(const void* p, const char* name, bool nullable)
+tq_status tq_check_ptr(const void* p, const char* name, bool nullable, int align)
 {
     if (!p) return nullable ? TQ_OK : tq_fail(TQ_ERR_ARG, "%s is NULL", name);
-    if (((uintptr_t)p) & 15) return tq_fail(TQ_ERR_ALIGN, "%s = %p is not 16-byte aligned", name, p);
+    if (((uintptr_t)p) & (uintptr_t)(align - 1))
+        return tq_fail(TQ_ERR_ALIGN, "%s = %p is not %d-byte aligned", name, p, align);
     return TQ_OK;
 }
 

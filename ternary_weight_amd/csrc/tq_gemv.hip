@@ -7,29 +7,32 @@ using namespace tqk;
 
 int mt_index(int M) { return M <= 1 ? 0 : (M <= 4 ? 1 : 2); }
 
-size_t red_bytes(int family, int waves)
+// LDS of the partial sums: one area per wave when a row block is split.
+size_t red_bytes(int family, int split_waves, int total_waves)
 {
-    if (waves <= 1) return 0;
+    if (split_waves <= 1) return 0;
     const int mti = family % 3, K = (family / 3) % 4 + 1, layout = (family / 12) % 3;
     const int R = layout != TQ_SCALE_TENSOR ? kMT[mti] : kMT[mti] * K;
-    return (size_t)waves * R * 64 * 4;
+    return (size_t)total_waves * R * 64 * 4;
 }
 
 const single_fn* single_tab(int xt, int mti)
 {
-    static const single_fn* (*const f[3][3])() = {
+    static const single_fn* (*const f[kXTypes][3])() = {
         {single_table_0_0, single_table_0_1, single_table_0_2},
         {single_table_1_0, single_table_1_1, single_table_1_2},
-        {single_table_2_0, single_table_2_1, single_table_2_2}};
+        {single_table_2_0, single_table_2_1, single_table_2_2},
+        {single_table_3_0, single_table_3_1, single_table_3_2}};
     return f[xt][mti]();
 }
 
 const grouped_fn* grouped_tab(int xt, int mti)
 {
-    static const grouped_fn* (*const f[3][3])() = {
+    static const grouped_fn* (*const f[kXTypes][3])() = {
         {grouped_table_0_0, grouped_table_0_1, grouped_table_0_2},
         {grouped_table_1_0, grouped_table_1_1, grouped_table_1_2},
-        {grouped_table_2_0, grouped_table_2_1, grouped_table_2_2}};
+        {grouped_table_2_0, grouped_table_2_1, grouped_table_2_2},
+        {grouped_table_3_0, grouped_table_3_1, grouped_table_3_2}};
     return f[xt][mti]();
 }
 
@@ -50,7 +53,8 @@ grouped_fn grouped_of(int family)
 
 int tq_gemv_family(int x_type, int layout, int K, int M)
 {
-    if (x_type < 0 || x_type > 2 || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 || M > 16) return -1;
+    if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 || M > 16)
+        return -1;
     return ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + mt_index(M);
 }
 
@@ -64,22 +68,24 @@ tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_
     int waves = 1;
     const int64_t target = 4 * (int64_t)tq_device_cus();
     while (waves < 16 && L.NB * waves < target && nunits >= 4 * waves * 2) waves *= 2;
-    const size_t lds = red_bytes(fam, waves);
+    const size_t lds = red_bytes(fam, waves, waves) + (x_type == TQ_F32_Q8 ? tq_x_lds_bytes(P.M, L.Kin) : 0);
     hipLaunchKernelGGL(single_of(fam), dim3((unsigned)L.NB), dim3(64 * waves), lds, stream, P);
     return tq_check_launch("tq_gemv");
 }
 
-tq_status tq_gemv_launch_grouped(int family, int waves, const void* workspace, int64_t n_probs,
-                                 int64_t n_items, hipStream_t stream)
+tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const void* workspace,
+                                 int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream)
 {
-    if (family < 0 || family >= 108) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
-    if (waves < 1 || waves > 16) return tq_fail(TQ_ERR_ARG, "bad plan waves %d", waves);
+    if (family < 0 || family >= 3 * 4 * 3 * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
+    if (waves < 1 || row_blocks < 1 || waves * row_blocks > 16)
+        return tq_fail(TQ_ERR_ARG, "bad plan shape %d x %d", waves, row_blocks);
     if (n_items <= 0) return tq_ok();
     const uint8_t* ws = (const uint8_t*)workspace;
     const tq_prob_dev* probs = (const tq_prob_dev*)ws;
-    const int2* items = (const int2*)(ws + tq_align256(n_probs * (int64_t)sizeof(tq_prob_dev)));
-    const size_t lds = red_bytes(family, waves);
-    hipLaunchKernelGGL(grouped_of(family), dim3((unsigned)n_items), dim3(64 * waves), lds, stream,
-                       probs, items);
+    const int2* items = (const int2*)(ws + tq_ws_items_off(n_probs));
+    const int total = waves * row_blocks;
+    const size_t lds = red_bytes(family, waves, total) + (size_t)x_lds_bytes;
+    hipLaunchKernelGGL(grouped_of(family), dim3((unsigned)n_items), dim3(64 * total), lds, stream, probs,
+                       items, row_blocks);
     return tq_check_launch("tq_gemv_grouped_run");
 }

@@ -37,8 +37,23 @@
 
 namespace tqk {
 
+// Tuning constants (measured on MI355X; see the design notes).
+#ifndef TQ_Q8_HELD
+#define TQ_Q8_HELD 2          // fp32 activation vectors held per thread while quantising
+#endif
+#ifndef TQ_Q8_EARLY_LOADS
+#define TQ_Q8_EARLY_LOADS 0   // issue the first code loads before quantising
+#endif
+#ifndef TQ_DEPTH_K1
+#define TQ_DEPTH_K1 2         // chunks in flight per wave, one plane
+#endif
+#ifndef TQ_DEPTH_KN
+#define TQ_DEPTH_KN 2         // chunks in flight per wave, several planes
+#endif
+
 #define CONST_AS __attribute__((address_space(4)))
 #define GLOBAL_AS __attribute__((address_space(1)))
+#define LDS_AS __attribute__((address_space(3)))
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -113,10 +128,23 @@ struct XUnit<TQ_F32> {
     }
 };
 
+// fp32 activations quantised to int8 inside the kernel: staged in LDS.
+template <>
+struct XUnit<TQ_F32_Q8> : XUnit<TQ_I8> {
+    __device__ __forceinline__ void load(const void* xq_lds, int64_t elem)
+    {
+        const LDS_AS uint32_t* p = (const LDS_AS uint32_t*)xq_lds + (elem >> 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = p[j];
+    }
+};
+
 template <int XT>
 struct AccT { using type = float; };
 template <>
 struct AccT<TQ_I8> { using type = int; };
+template <>
+struct AccT<TQ_F32_Q8> { using type = int; };
 
 // acc += sum over the 16 columns of one code dword of t * x.
 __device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_I8>& x, int& acc)
@@ -188,11 +216,17 @@ struct Slot {
 };
 
 template <int XT>
-struct XChunk {   // activations of one 64-column chunk of one token (SGPRs)
-    static constexpr int kD = XT == TQ_I8 ? 16 : (XT == TQ_BF16 ? 32 : 64);
+struct XChunk {   // activations of one 64-column chunk of one token (SGPRs, or VGPRs from LDS)
+    static constexpr int kD = (XT == TQ_I8 || XT == TQ_F32_Q8) ? 16 : (XT == TQ_BF16 ? 32 : 64);
     uint32_t v[kD];
     __device__ __forceinline__ void load(const void* x, int64_t elem)
     {
+        if (XT == TQ_F32_Q8) {
+            const LDS_AS uint32_t* p = (const LDS_AS uint32_t*)x + (elem >> 2);
+#pragma unroll
+            for (int j = 0; j < kD; ++j) v[j] = p[j];
+            return;
+        }
         const int64_t dw = XT == TQ_I8 ? (elem >> 2) : (XT == TQ_BF16 ? (elem >> 1) : elem);
 #pragma unroll
         for (int j = 0; j < kD; ++j) v[j] = ld_uniform_u32(x, dw + j);
@@ -213,19 +247,20 @@ struct RowBlock {
     using A = typename AccT<XT>::type;
     static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     // chunks in flight per wave (codes of K planes each)
-    static constexpr int D = MT > 1 ? 1 : (K == 1 ? 4 : 2);
+    static constexpr int D = MT > 1 ? 1 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN);
     // activations are prefetched a chunk ahead for one token (SGPR budget)
     static constexpr bool kXPre = MT == 1 && XT != TQ_F32;
 
     const tq_prob_dev& P;
     const int rb, lane;
+    const void* xsrc;     // activations: global x, or the LDS copy quantised to int8
     A p[MT][K];
     float out[MT];
     const GLOBAL_AS u32x4* cp;
     const GLOBAL_AS uint32_t* sp;
 
-    __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_)
-        : P(P_), rb(rb_), lane(threadIdx.x & 63)
+    __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_)
+        : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_)
     {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -314,7 +349,7 @@ struct RowBlock {
                 if (MT > 1 && m >= P.M) break;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
-                else xu.load(P.x, (int64_t)m * P.Kin + (int64_t)u * 16);
+                else xu.load(xsrc, (int64_t)m * P.Kin + (int64_t)u * 16);
 #pragma unroll
                 for (int k = 0; k < K; ++k) accum(wd[k], xu, p[m][k]);
             }
@@ -325,17 +360,33 @@ struct RowBlock {
         }
     }
 
+    Slot<K, LAYOUT> cur[D];
+    int c0_, c1_, cf_;
+
+    // Issue the loads of the first chunks (before any other set-up work).
+    __device__ __forceinline__ void begin(int c0, int c1)
+    {
+        c0_ = c0;
+        c1_ = c1;
+        cf_ = std::min(c1, (P.Kin >> 4) >> 2);   // end of the chunks with all 64 columns valid
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (c0 + j < cf_) load_slot(c0 + j, cur[j]);
+    }
+
     __device__ __forceinline__ void run(int c0, int c1, const float* cb_lds)
     {
+        begin(c0, c1);
+        finish(cb_lds);
+    }
+
+    __device__ __forceinline__ void finish(const float* cb_lds)
+    {
+        const int c0 = c0_, c1 = c1_, cf = cf_;
         const int n16 = P.Kin >> 4;
-        const int cf = std::min(c1, n16 >> 2);   // end of the chunks with all 64 columns valid
         if (c0 < cf) {
-            Slot<K, LAYOUT> cur[D];
-#pragma unroll
-            for (int j = 0; j < D; ++j)
-                if (c0 + j < cf) load_slot(c0 + j, cur[j]);
             XChunk<XT> xc;
-            if (kXPre) xc.load(P.x, (int64_t)c0 * TQ_CHUNK);
+            if (kXPre) xc.load(xsrc, (int64_t)c0 * TQ_CHUNK);
             for (int c = c0; c < cf; c += D) {
                 Slot<K, LAYOUT> nxt[D];
 #pragma unroll
@@ -345,7 +396,7 @@ struct RowBlock {
                 for (int j = 0; j < D; ++j) {
                     if (c + j < cf) {
                         XChunk<XT> xn;
-                        if (kXPre && c + j + 1 < cf) xn.load(P.x, (int64_t)(c + j + 1) * TQ_CHUNK);
+                        if (kXPre && c + j + 1 < cf) xn.load(xsrc, (int64_t)(c + j + 1) * TQ_CHUNK);
                         compute<true>(c + j, 4, cur[j], &xc, cb_lds);
                         if (kXPre) xc = xn;
                     }
@@ -362,10 +413,89 @@ struct RowBlock {
     }
 };
 
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t quant4(f32x4 v, float inv)
+{
+    // per element: rne(fl(x * inv)) clamped to [-127, 127] -- the steps of tq_act_quant_int8
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t b = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float r = rintf(__fmul_rn(e[j], inv));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        b |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * j);
+    }
+    return b;
+}
+
+// Per-token absmax int8 quantisation of the problem's activations into LDS,
+// by every thread of the workgroup (the same operations as tq_act_quant_int8).
+__device__ __forceinline__ void quantize_to_lds(const tq_prob_dev& P, uint32_t* xq, float* sx, float* wmax)
+{
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int n4 = P.Kin >> 2;
+    constexpr int kHeld = TQ_Q8_HELD;    // 16-byte vectors a thread keeps in registers
+    for (int m = 0; m < P.M; ++m) {
+        const GLOBAL_AS f32x4* xr = (const GLOBAL_AS f32x4*)((const float*)P.x + (int64_t)m * P.Kin);
+        const bool held = kHeld > 0 && n4 <= kHeld * nthr;
+        f32x4 v[kHeld > 0 ? kHeld : 1];
+        float a = 0.0f;
+        if (held) {
+#pragma unroll
+            for (int j = 0; j < kHeld; ++j) {
+                const int i = tid + j * nthr;
+                v[j] = i < n4 ? xr[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < kHeld; ++j)
+                a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+        } else {
+            for (int i = tid; i < n4; i += nthr) {
+                const f32x4 u = xr[i];
+                a = fmaxf(a, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
+            }
+        }
+        a = wave_max(a);
+        if ((tid & 63) == 0) wmax[tid >> 6] = a;
+        __syncthreads();
+        a = wmax[0];
+        for (int w = 1; w < (nthr >> 6); ++w) a = fmaxf(a, wmax[w]);
+        const float inv = a > 0.0f ? 127.0f / a : 0.0f;
+        uint32_t* row = xq + (m * P.Kin >> 2);
+        if (held) {
+#pragma unroll
+            for (int j = 0; j < kHeld; ++j) {
+                const int i = tid + j * nthr;
+                if (i < n4) row[i] = quant4(v[j], inv);
+            }
+        } else {
+            for (int i = tid; i < n4; i += nthr) row[i] = quant4(xr[i], inv);
+        }
+        if (tid == 0) sx[m] = a > 0.0f ? a / 127.0f : 0.0f;
+        __syncthreads();
+    }
+}
+
+// Row block `rb` of one problem; this wave is column split `wave` of `nwaves`.
+// `red` is the row block's own LDS area for the partial sums.  Every wave of
+// the workgroup calls this once (inactive waves with active = false) because
+// it contains a workgroup barrier.
 template <int XT, int LAYOUT, int K, int MT>
 __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, const int wave,
-                                         const int nwaves, uint32_t* red, const float* cb_lds)
+                                         const int nwaves, uint32_t* red, const float* cb_lds,
+                                         const void* xsrc, float* sx_lds, const bool active,
+                                         void* q8_lds = nullptr, float* wmax_lds = nullptr)
 {
+    float* sx_lds_w = sx_lds;
+    constexpr bool kInt = XT == TQ_I8 || XT == TQ_F32_Q8;
     using A = typename AccT<XT>::type;
     constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     const int lane = threadIdx.x & 63;
@@ -374,11 +504,17 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     const int M = P.M;
     const int cpu = (!kGroup || g <= 64) ? 1 : (g >> 6);
     const int nunits = (NC + cpu - 1) / cpu;
-    const int c0 = ((nunits * wave) / nwaves) * cpu;
-    const int c1 = std::min(((nunits * (wave + 1)) / nwaves) * cpu, NC);
+    const int c0 = active ? ((nunits * wave) / nwaves) * cpu : 0;
+    const int c1 = active ? std::min(((nunits * (wave + 1)) / nwaves) * cpu, NC) : 0;
 
-    RowBlock<XT, LAYOUT, K, MT> blk(P, rb);
-    blk.run(c0, c1, cb_lds);
+    RowBlock<XT, LAYOUT, K, MT> blk(P, rb, xsrc);
+    if (XT == TQ_F32_Q8 && !TQ_Q8_EARLY_LOADS) quantize_to_lds(P, (uint32_t*)q8_lds, sx_lds_w, wmax_lds);
+    blk.begin(c0, c1);
+    if (XT == TQ_F32_Q8 && TQ_Q8_EARLY_LOADS) {
+        // the first chunks are in flight while the workgroup quantises the activations
+        quantize_to_lds(P, (uint32_t*)q8_lds, sx_lds_w, wmax_lds);
+    }
+    blk.finish(cb_lds);
     auto& p = blk.p;
     auto& out = blk.out;
 
@@ -395,13 +531,13 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
                     for (int k = 0; k < K; ++k) {
                         const A v = p[m][k];
                         red[((wave * R) + m * K + k) * 64 + lane] =
-                            XT == TQ_I8 ? (uint32_t)(int)v : __float_as_uint((float)v);
+                            kInt ? (uint32_t)(int)v : __float_as_uint((float)v);
                     }
                 }
             }
         }
         __syncthreads();
-        if (wave != 0) return;
+        if (wave != 0 || !active) return;   // split 0 of an active block finishes it
         for (int wv = 1; wv < nwaves; ++wv) {
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -411,7 +547,7 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
 #pragma unroll
                     for (int k = 0; k < K; ++k) {
                         const uint32_t bits = red[((wv * R) + m * K + k) * 64 + lane];
-                        if (XT == TQ_I8) p[m][k] += (A)(int)bits;
+                        if (kInt) p[m][k] += (A)(int)bits;
                         else p[m][k] += (A)__uint_as_float(bits);
                     }
                 }
@@ -420,7 +556,7 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     }
 
     const int64_t n = (int64_t)rb * TQ_ROWS + lane;
-    if (n >= P.N) return;
+    if (!active || n >= P.N) return;
     float ts[K];
     if (!kGroup) {
 #pragma unroll
@@ -430,8 +566,8 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     for (int m = 0; m < MT; ++m) {
         if (m >= M) break;
         float yv;
-        if (XT == TQ_I8) {
-            const float xs = ld_uniform(P.x_scale + m);
+        if (kInt) {
+            const float xs = XT == TQ_F32_Q8 ? sx_lds[m] : ld_uniform(P.x_scale + m);
             if (!kGroup && K == 1) {
                 // bit exact: y = fl(float(acc) * fl(s_w * s_x))
                 const float cm = __fmul_rn(ts[0], xs);
@@ -459,33 +595,53 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     }
 }
 
+// One workgroup: `nrb` row blocks starting at rb0, each split over
+// blockDim / (64 * nrb) waves.
 template <int XT, int LAYOUT, int K, int MT>
-__device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb)
+__device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb)
 {
-    extern __shared__ uint32_t tq_red[];
+    extern __shared__ uint32_t tq_dyn[];     // [reduction areas][int8 activations]
     __shared__ float cb_lds[TQ_CB_SLOTS];
+    __shared__ float sx_lds[TQ_MAX_M_GEMV];
+    __shared__ float wmax[16];
+    constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
+    constexpr int Rw = kGroup ? MT : MT * K;          // partial sums per lane
     if (LAYOUT == TQ_SCALE_CODEBOOK) {
         if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
         __syncthreads();
     }
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwaves = (int)(blockDim.x >> 6);
-    rowblock<XT, LAYOUT, K, MT>(P, rb, wave, nwaves, tq_red, cb_lds);
+    const int S = nwaves / nrb;                       // waves per row block
+    const int r = wave / S, split = wave - r * S;
+    const int rb = rb0 + r;
+    const bool active = rb * TQ_ROWS < P.N;
+    const void* xsrc = P.x;
+    uint32_t* xq = nullptr;
+    if (XT == TQ_F32_Q8) {
+        const int red_words = S > 1 ? nwaves * Rw * 64 : 0;
+        xq = tq_dyn + red_words;
+        xsrc = xq;     // filled inside rowblock, after its first loads are issued
+    }
+    rowblock<XT, LAYOUT, K, MT>(P, rb, split, S, tq_dyn + r * S * Rw * 64, cb_lds, xsrc, sx_lds, active,
+                                xq, wmax);
 }
 
 template <int XT, int LAYOUT, int K, int MT>
 __global__ __launch_bounds__(1024) void k_gemv_single(tq_prob_dev P)
 {
-    gemv_body<XT, LAYOUT, K, MT>(P, (int)blockIdx.x);
+    gemv_body<XT, LAYOUT, K, MT>(P, (int)blockIdx.x, 1);
 }
 
+// A whole stack in one launch: workgroup i takes item i, `nrb` row blocks of
+// one problem (items are ordered longest first by the host).
 template <int XT, int LAYOUT, int K, int MT>
 __global__ __launch_bounds__(1024) void k_gemv_grouped(const tq_prob_dev* __restrict__ probs,
-                                                       const int2* __restrict__ items)
+                                                       const int2* __restrict__ items, int nrb)
 {
     const int2 it = ld_uniform_struct(items + blockIdx.x);
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
-    gemv_body<XT, LAYOUT, K, MT>(P, it.y);
+    gemv_body<XT, LAYOUT, K, MT>(P, it.y, nrb);
 }
 
 }  // namespace tqk
@@ -493,11 +649,12 @@ __global__ __launch_bounds__(1024) void k_gemv_grouped(const tq_prob_dev* __rest
 namespace tqk {
 
 typedef void (*single_fn)(tq_prob_dev);
-typedef void (*grouped_fn)(const tq_prob_dev*, const int2*);
+typedef void (*grouped_fn)(const tq_prob_dev*, const int2*, int);
 
 constexpr int kMT[3] = {1, 4, 16};
 // family = ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + M-tier; 36 families per x_type
 constexpr int kPerXT = 36;
+constexpr int kXTypes = 4;
 
 // families of one (x_type, M tier): index = layout * 4 + (K - 1)
 template <int F>
@@ -526,5 +683,6 @@ const grouped_fn* grouped_table(int x_type, int mti);
 TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1) TQ_DECLARE_TABLES(0, 2)
 TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1) TQ_DECLARE_TABLES(1, 2)
 TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1) TQ_DECLARE_TABLES(2, 2)
+TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1) TQ_DECLARE_TABLES(3, 2)
 
 }  // namespace tqk

@@ -15,8 +15,8 @@ tq_status tq_ok();
 
 // Validate a weight descriptor and fill the layout.
 tq_status tq_check_desc(const tq_weight_desc* d, tq_layout* L);
-// Device pointer checks: non-null unless `nullable`, 16-byte aligned.
-tq_status tq_check_ptr(const void* p, const char* name, bool nullable);
+// Device pointer checks: non-null unless `nullable`, aligned to `align` bytes.
+tq_status tq_check_ptr(const void* p, const char* name, bool nullable, int align = 16);
 // After a launch: map hipGetLastError() to TQ_ERR_DEVICE.
 tq_status tq_check_launch(const char* what);
 tq_status tq_check_hip(hipError_t e, const char* what);
@@ -42,7 +42,12 @@ struct tq_prob_dev {
 // Decode launch shared by tq_gemv and tq_gemv_grouped_run (tq_gemv.hip).
 tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type,
                                 hipStream_t stream);
-tq_status tq_gemv_launch_grouped(int family, int waves, const void* workspace, int64_t n_probs,
-                                 int64_t n_items, hipStream_t stream);
+tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const void* workspace,
+                                 int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream);
+// LDS bytes of M tokens x Kin int8 activations (TQ_F32_Q8), 16-byte rounded.
+static inline size_t tq_x_lds_bytes(int64_t M, int64_t Kin) { return (size_t)((M * Kin + 15) & ~(int64_t)15); }
+// Workspace layout of a grouped plan: problem table, then the items.
+static inline int64_t tq_ws_items_off(int64_t n_probs) { return tq_align256(n_probs * (int64_t)sizeof(tq_prob_dev)); }
+#define TQ_MAX_Q8_LDS 65536
 // Family id of a (x_type, layout, K, M) combination, or -1 if none.
 int tq_gemv_family(int x_type, int layout, int K, int M);

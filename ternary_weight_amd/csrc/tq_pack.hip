@@ -213,10 +213,10 @@ TQ_EXPORT tq_status tq_pack(const tq_weight_desc* desc, const int8_t* trits, con
     if (s) return s;
     const bool need_trits = L.N > 0 && L.Kin > 0;
     if ((s = tq_check_ptr(trits, "trits", !need_trits))) return s;
-    if ((s = tq_check_ptr(scales, "scales", L.layout != TQ_SCALE_TENSOR && !need_trits))) return s;
+    if ((s = tq_check_ptr(scales, "scales", L.layout != TQ_SCALE_TENSOR && !need_trits, 4))) return s;
     if ((s = tq_check_ptr(blob, "blob", false))) return s;
     if (L.layout == TQ_SCALE_CODEBOOK) {
-        if ((s = tq_check_ptr(codebook, "codebook", false))) return s;
+        if ((s = tq_check_ptr(codebook, "codebook", false, 2))) return s;
     }
     hipStream_t stream = (hipStream_t)stream_;
     uint8_t* b = (uint8_t*)blob;
@@ -273,8 +273,8 @@ TQ_EXPORT tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8
     const bool need = L.N > 0 && L.Kin > 0;
     if ((s = tq_check_ptr(blob, "blob", false))) return s;
     if ((s = tq_check_ptr(trits, "trits", !need))) return s;
-    if ((s = tq_check_ptr(scales, "scales", true))) return s;
-    if ((s = tq_check_ptr(codebook, "codebook", true))) return s;
+    if ((s = tq_check_ptr(scales, "scales", true, 4))) return s;
+    if ((s = tq_check_ptr(codebook, "codebook", true, 2))) return s;
     hipStream_t stream = (hipStream_t)stream_;
     const uint8_t* b = (const uint8_t*)blob;
     const int64_t ncodes = L.codes_bytes / 4;

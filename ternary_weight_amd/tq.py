@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libtq.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_UNSUPPORTED, ERR_DEVICE = range(7)
 SCALE_TENSOR, SCALE_GROUP_F16, SCALE_CODEBOOK = 0, 1, 2
-F32, BF16, I8 = 0, 1, 2
+F32, BF16, I8, F32_Q8 = 0, 1, 2, 3
 
 
 class TQError(RuntimeError):
@@ -43,10 +43,17 @@ class tq_problem(ctypes.Structure):
                 ("acc", ctypes.c_void_p)]
 
 
+class tq_act_segment(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("in_features", ctypes.c_int64), ("x_type", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("x", ctypes.c_void_p), ("xq", ctypes.c_void_p),
+                ("x_scale", ctypes.c_void_p)]
+
+
 class tq_grouped_plan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("n_items", ctypes.c_int64),
                 ("family", ctypes.c_int32), ("x_type", ctypes.c_int32), ("M", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("n_problems", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
+                ("n_problems", ctypes.c_int32), ("x_lds_bytes", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
 
@@ -61,6 +68,7 @@ SIGNATURES = {
     "tq_pack": ([_DESC, _VP, _VP, _VP, _VP, _VP], _I32),
     "tq_unpack": ([_DESC, _VP, _VP, _VP, _VP, _VP], _I32),
     "tq_act_quant_int8": ([_I64, _I64, _I32, _VP, _VP, _VP, _VP], _I32),
+    "tq_act_quant_int8_batch": ([ctypes.POINTER(tq_act_segment), _I32, _VP], _I32),
     "tq_gemv": ([_DESC, _VP, _I64, _I32, _VP, _VP, _VP, _VP, _VP], _I32),
     "tq_gemm": ([_DESC, _VP, _I64, _I32, _VP, _VP, _VP, _VP, _VP], _I32),
     "tq_gemv_grouped_workspace_size": ([ctypes.POINTER(tq_problem), _I32, _I64,
@@ -150,6 +158,14 @@ def act_quant_int8(M, in_features, x_type, x, xq, x_scale, stream=None):
                                    _stream(stream)), "tq_act_quant_int8")
 
 
+def act_quant_int8_batch(segments, stream=None):
+    """segments: (M, in_features, x_type, x, xq, x_scale) tuples, one launch for all."""
+    arr = (tq_act_segment * max(len(segments), 1))()
+    for i, (M, kin, xt, x, xq, xs) in enumerate(segments):
+        arr[i] = tq_act_segment(M, kin, xt, 0, _ptr(x), _ptr(xq), _ptr(xs))
+    _check(lib().tq_act_quant_int8_batch(arr, len(segments), _stream(stream)), "tq_act_quant_int8_batch")
+
+
 def gemv(d, blob, M, x_type, x, x_scale, y, acc=None, stream=None):
     _check(lib().tq_gemv(ctypes.byref(d), _ptr(blob), M, x_type, _ptr(x), _ptr(x_scale), _ptr(y),
                          _ptr(acc), _stream(stream)), "tq_gemv")
@@ -177,9 +193,11 @@ def gemv_grouped_workspace_size(probs, M) -> int:
     return n.value
 
 
-def gemv_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, waves=0, stream=None):
+def gemv_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, waves=0, row_blocks=0,
+                         stream=None):
     plan = tq_grouped_plan()
     plan.waves = waves
+    plan.row_blocks = row_blocks
     _check(lib().tq_gemv_grouped_prepare(probs, len(probs), M, x_type, _ptr(workspace),
                                          workspace_bytes, ctypes.byref(plan), _stream(stream)),
            "tq_gemv_grouped_prepare")

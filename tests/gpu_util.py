@@ -18,6 +18,7 @@ def dev(a):
     """numpy -> cuda tensor (u16 travels as int16 bits)."""
     t = torch()
     a = np.ascontiguousarray(a)
+    assert a.dtype != np.float64, "device arrays here are fp32 / bf16 / integer"
     if a.dtype == np.uint16:
         a = a.view(np.int16)
     return t.from_numpy(a).to("cuda")

@@ -134,3 +134,31 @@ def test_gemm_rejects_unsupported_before_device_work():
     good = 0x30000
     d = tq.desc(2, 64, tq.SCALE_GROUP_F16, 64, 64)
     assert L.tq_gemm(ctypes.byref(d), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
+
+
+def test_fused_int8_activation_limits():
+    L = tq.lib()
+    good = 0x40000
+    d = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 8192)
+    # M * Kin beyond the workgroup's LDS copy
+    assert L.tq_gemv(ctypes.byref(d), good, 16, tq.F32_Q8, good, None, good, None, None) == tq.ERR_UNSUPPORTED
+    # fp32 activations are read 16 bytes at a time
+    assert L.tq_gemv(ctypes.byref(d), good, 1, tq.F32_Q8, good + 4, None, good, None, None) == tq.ERR_ALIGN
+    dg = tq.desc(1, 64, tq.SCALE_GROUP_F16, 64, 64)
+    assert L.tq_gemv(ctypes.byref(dg), good, 1, tq.F32_Q8, good, None, good, good, None) == tq.ERR_UNSUPPORTED
+
+
+def test_act_quant_batch_validation():
+    L = tq.lib()
+    good = 0x50000
+    seg = (tq.tq_act_segment * 17)()
+    assert L.tq_act_quant_int8_batch(seg, 17, None) == tq.ERR_ARG
+    seg[0] = tq.tq_act_segment(2, 40, tq.F32, 0, good, good, good)
+    assert L.tq_act_quant_int8_batch(seg, 1, None) == tq.ERR_SHAPE
+    seg[0] = tq.tq_act_segment(2, 64, tq.I8, 0, good, good, good)
+    assert L.tq_act_quant_int8_batch(seg, 1, None) == tq.ERR_ARG
+    seg[0] = tq.tq_act_segment(2, 64, tq.F32, 0, good + 8, good, good)
+    assert L.tq_act_quant_int8_batch(seg, 1, None) == tq.ERR_ALIGN
+    seg[0] = tq.tq_act_segment(0, 64, tq.F32, 0, None, None, None)
+    assert L.tq_act_quant_int8_batch(seg, 1, None) == tq.OK
+    assert L.tq_act_quant_int8_batch(None, 0, None) == tq.OK

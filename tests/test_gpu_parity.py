@@ -12,6 +12,8 @@ import pytest
 
 import oracle
 from oracle import BF16, CODEBOOK, F32, GROUP_F16, I8, TENSOR
+
+F32_Q8 = 3   # fp32 activations quantised to int8 inside the product
 from synth import gen
 
 from tests.gpu_util import TOL, dev, gemv, host, pack, read_blob, rel_err, torch
@@ -165,16 +167,17 @@ for layout in (TENSOR, GROUP_F16, CODEBOOK):
 
 
 @pytest.mark.parametrize("layout,K,g", FP_CASES)
-@pytest.mark.parametrize("x_type", [F32, BF16, I8])
+@pytest.mark.parametrize("x_type", [F32, BF16, I8, F32_Q8])
 def test_gemv_all_formats(layout, K, g, x_type):
     rng = np.random.default_rng(K * 1000 + g + 7 * layout + 31 * x_type)
     N, Kin = 192, 1024 + (256 if g <= 256 else 0)
     for M in (1, 3, 16):
         trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
         d, blob = pack(K, g, layout, trits, scales, cb)
-        if x_type == I8:
-            q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
-            y = gemv(d, blob, I8, q, s)
+        if x_type in (I8, F32_Q8):
+            xf = rand_x(M, Kin, F32, rng)
+            q, s = oracle.act_quant_i8(xf)
+            y = gemv(d, blob, I8, q, s) if x_type == I8 else gemv(d, blob, F32_Q8, xf)
             ref = oracle.gemv_i8(K, g, layout, trits, scales, q, s, cb)
             if layout == TENSOR and K == 1:
                 assert np.array_equal(y.view(np.uint32), ref["y32"].view(np.uint32))
@@ -280,9 +283,10 @@ def test_deterministic_repeat():
 # Grouped launch.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("x_type,K,g,layout,M", [(I8, 1, 0, TENSOR, 1), (BF16, 3, 256, GROUP_F16, 1),
-                                                  (BF16, 3, 16, CODEBOOK, 4), (F32, 2, 64, GROUP_F16, 2)])
-@pytest.mark.parametrize("waves", [1, 4, 16])
-def test_grouped_matches_oracle(x_type, K, g, layout, M, waves):
+                                                  (BF16, 3, 16, CODEBOOK, 4), (F32, 2, 64, GROUP_F16, 2),
+                                                  (F32_Q8, 1, 0, TENSOR, 1), (F32_Q8, 1, 0, TENSOR, 4)])
+@pytest.mark.parametrize("waves,row_blocks", [(0, 0), (1, 1), (4, 1), (16, 1), (1, 4), (2, 2), (2, 8), (1, 16)])
+def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
     from ternary_weight_amd import tq
     t = torch()
     shapes = [(640, 2560), (64, 256), (2560, 512), (130, 768), (96, 6912)]
@@ -290,9 +294,10 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves):
     for i, (N, Kin) in enumerate(shapes):
         trits, scales, cb = rand_problem(K, g, layout, N, Kin)
         d, blob = pack(K, g, layout, trits, scales, cb)
-        if x_type == I8:
-            q, s = oracle.act_quant_i8(rand_x(M, Kin, F32))
-            xd, sd = dev(q), dev(s)
+        if x_type in (I8, F32_Q8):
+            xf = rand_x(M, Kin, F32)
+            q, s = oracle.act_quant_i8(xf)
+            xd, sd = (dev(q), dev(s)) if x_type == I8 else (dev(xf), None)
             r = oracle.gemv_i8(K, g, layout, trits, scales, q, s, cb)
             refs.append(r["y32"] if layout == TENSOR and K == 1 else r["y64"])
         else:
@@ -306,12 +311,56 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves):
     probs = tq.problems(items)
     nbytes = tq.gemv_grouped_workspace_size(probs, M)
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
-    plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves)
-    assert plan.n_items == sum((N + 63) // 64 for N, _ in shapes) and plan.waves == waves
+    plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
+    R = plan.row_blocks
+    assert plan.n_items == sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes)
+    if waves:
+        assert (plan.waves, plan.row_blocks) == (waves, row_blocks)
     tq.gemv_grouped_run(plan)
     t.cuda.synchronize()
     for y, r in zip(ys, refs):
-        if x_type == I8 and layout == TENSOR and K == 1:
+        if x_type in (I8, F32_Q8) and layout == TENSOR and K == 1:
             assert np.array_equal(host(y).view(np.uint32), r.view(np.uint32))
         else:
             assert rel_err(host(y), r) <= TOL
+
+
+@pytest.mark.parametrize("N,Kin,M", [(2560, 2560, 1), (640, 2560, 1), (2560, 6912, 1), (130, 80, 3),
+                                     (64, 4096, 16), (200, 65536, 1), (64, 16, 1)])
+def test_fused_quantisation_is_bit_identical(N, Kin, M):
+    """fp32 x quantised inside the product == tq_act_quant_int8 then the int8 product."""
+    trits, scales, _ = rand_problem(1, 0, TENSOR, N, Kin)
+    x = (rand_x(M, Kin, F32) * 10.0 ** float(RNG.integers(-3, 4))).astype(np.float32)
+    if M > 2:
+        x[1] = 0.0
+    q, s = oracle.act_quant_i8(x)
+    d, blob = pack(1, 0, TENSOR, trits, scales)
+    y, acc = gemv(d, blob, F32_Q8, x, want_acc=True)
+    ref = oracle.gemv_i8(1, 0, TENSOR, trits, scales, q, s)
+    assert np.array_equal(acc, ref["acc"].astype(np.int32))
+    assert np.array_equal(y.view(np.uint32), ref["y32"].view(np.uint32))
+
+
+def test_act_quant_batch_bit_exact():
+    from ternary_weight_amd import tq
+    t = torch()
+    segs, want, keep = [], [], []
+    for (M, Kin, xt) in [(180, 2560, F32), (30, 6912, F32), (3, 16, BF16), (0, 64, F32), (5, 40000, F32),
+                         (2, 4096, BF16)]:
+        v = RNG.standard_normal((M, Kin)) * 10.0 ** RNG.uniform(-5, 5, size=(M, 1))
+        if M > 1:
+            v[0] = 0.0
+        x = gen.bf16_bits(v) if xt == BF16 else v.astype(np.float32)
+        xd = dev(x)
+        qd = t.full((M, Kin), 99, dtype=t.int8, device="cuda")
+        sd = t.full((M,), -1.0, dtype=t.float32, device="cuda")
+        keep.append((xd, qd, sd))
+        segs.append((M, Kin, xt, xd, qd, sd))
+        want.append(oracle.act_quant_i8(x, xt) if M else None)
+    tq.act_quant_int8_batch(segs)
+    t.cuda.synchronize()
+    for (xd, qd, sd), w in zip(keep, want):
+        if w is None:
+            continue
+        assert np.array_equal(host(qd), w[0])
+        assert np.array_equal(host(sd).view(np.uint32), w[1].view(np.uint32))
