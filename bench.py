@@ -211,7 +211,9 @@ def cpu_baseline(stack, seconds: float) -> dict:
     case, M = stack.case, stack.M
     threads = min(len(os.sched_getaffinity(0)), 16)
     orc = oracle.default()
-    per_layer = len(case.model["proj"])
+    # layer 0 of the stack (its first four projections for the 8B-shaped stacks, to keep the
+    # host-side input generation short)
+    per_layer = len(case.model["proj"]) if case.planes == 1 else 4
     layer_inputs = []
     for (layer, p, _, n, kin) in stack.projs[:per_layer]:
         layer_inputs.append((n, kin, inputs.projection(case, layer, p, n, kin, M=M)))
@@ -223,6 +225,8 @@ def cpu_baseline(stack, seconds: float) -> dict:
         layer_bytes += K * n * kin // 4 + M * kin * xsz + 4 * M * n + (M * kin * 5 if case.x_type == I8 else 0)
         if layout == GROUP_F16:
             layer_bytes += 2 * K * n * (kin // g)
+        elif layout == CODEBOOK:
+            layer_bytes += (5 * n * (kin // g) + 7) // 8 + 2 * inputs.N_CODEBOOK
     while True:
         for (n, kin, h) in layer_inputs:
             if case.x_type == I8:
@@ -237,8 +241,8 @@ def cpu_baseline(stack, seconds: float) -> dict:
         if el >= seconds:
             break
     return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "layer 0 of the stack (%d projections), %d repetitions, %.1f s; C oracle, OpenMP over "
-                      "output rows" % (per_layer, reps, el)}
+            "sample": "layer 0 of the stack (first %d projections), %d repetitions, %.1f s; C oracle, "
+                      "OpenMP over output rows" % (per_layer, reps, el)}
 
 
 def spin_up(ms: float, nbytes: int = 1 << 30):

@@ -124,9 +124,11 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
     const int pow2[] = {1, 2, 4, 8, 16};
     auto is_shape = [&](int v) { for (int p : pow2) if (v == p) return true; return false; };
     int waves = plan->waves, row_blocks = plan->row_blocks;
-    if (!is_shape(waves) || !is_shape(row_blocks) || waves * row_blocks > 16) {
+    const bool hinted = is_shape(waves) && is_shape(row_blocks) && waves * row_blocks <= 16;
+    if (!hinted) {
+        // bf16: the trit table fills 64 KiB of LDS, so two 16-wave workgroups per compute unit
         waves = x_type == TQ_F32_Q8 ? 1 : 4;
-        row_blocks = x_type == TQ_F32_Q8 ? 4 : 1;
+        row_blocks = x_type == TQ_F32_Q8 ? 4 : (x_type == TQ_BF16 ? 4 : 1);
     }
     size_t need = 0;
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
@@ -155,13 +157,29 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
         }
         probs[(size_t)i] = make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
         if (x_type == TQ_F32_Q8) x_lds = std::max(x_lds, tq_x_lds_bytes(M, L.Kin));
-        if (M > 0)
-            for (int64_t rb = 0; rb < L.NB; rb += row_blocks) {
-                const int64_t nb = std::min<int64_t>(row_blocks, L.NB - rb);
-                items.push_back({nb * L.NC * (int64_t)L.K, i, (int32_t)rb});
-            }
     }
-    if (count > 0 && M > 0) family = tq_gemv_family(x_type, layout0, K0, (int)M);
+    if (count > 0 && M > 0) {
+        family = tq_gemv_family(x_type, layout0, K0, (int)M);
+        // a shape whose partial sums overflow the workgroup's LDS: the default
+        // one gives up the column split first, a requested one is refused
+        auto lds = [&](int w, int rbs) { return tq_gemv_lds_bytes(family, w, w * rbs, x_lds); };
+        if (lds(waves, row_blocks) > TQ_MAX_WG_LDS) {
+            if (hinted) return tq_fail(TQ_ERR_UNSUPPORTED, "plan shape %d x %d needs more LDS than a "
+                                       "workgroup has", waves, row_blocks);
+            while (waves > 1 && lds(waves, row_blocks) > TQ_MAX_WG_LDS) waves /= 2;
+            while (row_blocks > 1 && lds(waves, row_blocks) > TQ_MAX_WG_LDS) row_blocks /= 2;
+            if (lds(waves, row_blocks) > TQ_MAX_WG_LDS)
+                return tq_fail(TQ_ERR_UNSUPPORTED, "decode needs more LDS than a workgroup has");
+        }
+        for (int32_t i = 0; i < count; ++i) {
+            const tq_prob_dev& P = probs[(size_t)i];
+            const int64_t NB = (P.N + 63) / 64;
+            for (int64_t rb = 0; rb < NB; rb += row_blocks) {
+                const int64_t nb = std::min<int64_t>(row_blocks, NB - rb);
+                items.push_back({nb * P.NC * (int64_t)K0, i, (int32_t)rb});
+            }
+        }
+    }
     // longest items first, so that the last workgroups to start are short
     std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
     std::vector<uint8_t> host((size_t)need, 0);

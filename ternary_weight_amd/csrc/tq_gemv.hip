@@ -51,6 +51,13 @@ grouped_fn grouped_of(int family)
 
 }  // namespace
 
+size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_lds_bytes)
+{
+    const int x_type = family / 36;
+    const size_t fixed = (x_type == TQ_BF16 ? (size_t)kLutBytes : 0) + 1024;
+    return fixed + red_bytes(family, split_waves, total_waves) + x_lds_bytes;
+}
+
 int tq_gemv_family(int x_type, int layout, int K, int M)
 {
     if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 || M > 16)
@@ -68,7 +75,12 @@ tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_
     int waves = 1;
     const int64_t target = 4 * (int64_t)tq_device_cus();
     while (waves < 16 && L.NB * waves < target && nunits >= 4 * waves * 2) waves *= 2;
-    const size_t lds = red_bytes(fam, waves, waves) + (x_type == TQ_F32_Q8 ? tq_x_lds_bytes(P.M, L.Kin) : 0);
+    if (x_type == TQ_BF16) waves = 16;   // the 64 KiB trit table is shared by up to 16 waves
+    const size_t x_lds = x_type == TQ_F32_Q8 ? tq_x_lds_bytes(P.M, L.Kin) : 0;
+    while (waves > 1 && tq_gemv_lds_bytes(fam, waves, waves, x_lds) > TQ_MAX_WG_LDS) waves /= 2;
+    if (tq_gemv_lds_bytes(fam, waves, waves, x_lds) > TQ_MAX_WG_LDS)
+        return tq_fail(TQ_ERR_UNSUPPORTED, "decode needs more LDS than a workgroup has");
+    const size_t lds = red_bytes(fam, waves, waves) + x_lds;
     hipLaunchKernelGGL(single_of(fam), dim3((unsigned)L.NB), dim3(64 * waves), lds, stream, P);
     return tq_check_launch("tq_gemv");
 }
@@ -84,6 +96,9 @@ tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const vo
     const tq_prob_dev* probs = (const tq_prob_dev*)ws;
     const int2* items = (const int2*)(ws + tq_ws_items_off(n_probs));
     const int total = waves * row_blocks;
+    if (tq_gemv_lds_bytes(family, waves, total, (size_t)x_lds_bytes) > TQ_MAX_WG_LDS)
+        return tq_fail(TQ_ERR_UNSUPPORTED, "plan shape %d x %d needs more LDS than a workgroup has", waves,
+                       row_blocks);
     const size_t lds = red_bytes(family, waves, total) + (size_t)x_lds_bytes;
     hipLaunchKernelGGL(grouped_of(family), dim3((unsigned)n_items), dim3(64 * total), lds, stream, probs,
                        items, row_blocks);

@@ -48,7 +48,7 @@ namespace tqk {
 #define TQ_DEPTH_K1 2         // chunks in flight per wave, one plane
 #endif
 #ifndef TQ_DEPTH_KN
-#define TQ_DEPTH_KN 2         // chunks in flight per wave, several planes
+#define TQ_DEPTH_KN 1         // chunks in flight per wave, several planes
 #endif
 
 #define CONST_AS __attribute__((address_space(4)))
@@ -155,20 +155,63 @@ __device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_I8>& x, int& ac
     for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4((int)t[j], (int)x.v[j], acc, false);
 }
 
-__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_BF16>& x, float& acc)
+// bf16 activations: a lookup table in LDS maps one code byte (the trits of
+// columns b, 4+b, 8+b, 12+b of a 16-column dword) to four bf16 values in
+// {0, +1, -1}, as the pairs (t_b, t_4+b) and (t_8+b, t_12+b).  The table has
+// 32 copies, lane l reading copy l % 32, so that the 8-byte reads of a wave
+// never share a bank.  Entry e, copy c sits at byte offset e * 256 + c * 8, so
+// one v_perm_b32 builds the address: byte 1 = the code byte, byte 0 = c * 8.
+constexpr int kLutBytes = 256 * 256;
+
+struct BfPairs {   // activation pairs of one 16-column unit, matching the table's pairs
+    uint32_t a[4], b[4];
+};
+
+__device__ __forceinline__ BfPairs bf_pairs(const XUnit<TQ_BF16>& x)
+{
+    // x.v[j] holds columns 2j (low half) and 2j+1 (high half)
+    BfPairs p;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t x0 = x.v[b >> 1], x4 = x.v[2 + (b >> 1)], x8 = x.v[4 + (b >> 1)], x12 = x.v[6 + (b >> 1)];
+        if (b & 1) {
+            p.a[b] = (x0 >> 16) | (x4 & 0xFFFF0000u);
+            p.b[b] = (x8 >> 16) | (x12 & 0xFFFF0000u);
+        } else {
+            p.a[b] = (x0 & 0xFFFFu) | (x4 << 16);
+            p.b[b] = (x8 & 0xFFFFu) | (x12 << 16);
+        }
+    }
+    return p;
+}
+
+__device__ __forceinline__ void accum_lut(uint32_t w, const BfPairs& xp, float& acc,
+                                          const LDS_AS uint8_t* lut, uint32_t copyoff)
 {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t x0 = x.v[2 * p], x1 = x.v[2 * p + 1];
-        // columns 4p+1 and 4p+3: high halves; columns 4p and 4p+2: low halves
-        const uint32_t xo = (x0 >> 16) | (x1 & 0xFFFF0000u);
-        const uint32_t xe = (x0 & 0xFFFFu) | (x1 << 16);
-        const uint32_t to = __builtin_amdgcn_perm(0u, 0x00C04000u, (w >> (2 * p)) & 0x03000300u);
-        const uint32_t te = __builtin_amdgcn_perm(0u, 0x00C04000u, (w << (8 - 2 * p)) & 0x03000300u);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, to),
-                                              __builtin_bit_cast(bf16x2_t, xo), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, te),
-                                              __builtin_bit_cast(bf16x2_t, xe), acc, false);
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, copyoff, 0x0C0C0400u | ((4u + b) << 8));
+        const LDS_AS uint32_t* t = (const LDS_AS uint32_t*)(lut + addr);
+        const uint32_t t0 = t[0], t1 = t[1];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t0),
+                                              __builtin_bit_cast(bf16x2_t, xp.a[b]), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t1),
+                                              __builtin_bit_cast(bf16x2_t, xp.b[b]), acc, false);
+    }
+}
+
+// Fill the table (all threads of the workgroup; the caller synchronises).
+__device__ __forceinline__ void fill_bf16_lut(uint8_t* lut)
+{
+    for (int i = threadIdx.x; i < 256 * 32; i += blockDim.x) {
+        const uint32_t e = (uint32_t)i >> 5, c = (uint32_t)i & 31u;
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t code = (e >> (2 * q)) & 3u;
+            h[q] = code == 1u ? 0x3F80u : (code == 2u ? 0xBF80u : 0u);
+        }
+        *(uint2*)(lut + e * 256 + c * 8) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
 }
 
@@ -186,9 +229,9 @@ __device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_F32>& x, float&
     }
 }
 
-// The trit value encoding's factor: bf16 trits are decoded as +-2.
+// Factor of the decoded trit values (all paths decode exactly +-1).
 template <int XT>
-__device__ __forceinline__ constexpr float enc_scale() { return XT == TQ_BF16 ? 0.5f : 1.0f; }
+__device__ __forceinline__ constexpr float enc_scale() { return 1.0f; }
 
 template <int K>
 __device__ __forceinline__ int codec_combine(const int (&p)[K])
@@ -248,19 +291,23 @@ struct RowBlock {
     static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     // chunks in flight per wave (codes of K planes each)
     static constexpr int D = MT > 1 ? 1 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN);
+    static_assert(XT != TQ_BF16 || sizeof(typename AccT<XT>::type) == 4, "bf16 accumulates in fp32");
     // activations are prefetched a chunk ahead for one token (SGPR budget)
-    static constexpr bool kXPre = MT == 1 && XT != TQ_F32;
+    static constexpr bool kXPre = MT == 1 && (XT == TQ_I8 || XT == TQ_F32_Q8);
 
     const tq_prob_dev& P;
     const int rb, lane;
     const void* xsrc;     // activations: global x, or the LDS copy quantised to int8
+    const LDS_AS uint8_t* lut;   // bf16 trit table (TQ_BF16)
+    uint32_t copyoff;
     A p[MT][K];
     float out[MT];
     const GLOBAL_AS u32x4* cp;
     const GLOBAL_AS uint32_t* sp;
 
-    __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_)
-        : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_)
+    __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_, const uint8_t* lut_)
+        : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_), lut((const LDS_AS uint8_t*)lut_),
+          copyoff((uint32_t)(threadIdx.x & 31) * 8u)
     {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -350,8 +397,14 @@ struct RowBlock {
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
                 else xu.load(xsrc, (int64_t)m * P.Kin + (int64_t)u * 16);
+                if constexpr (XT == TQ_BF16) {
+                    const BfPairs xp = bf_pairs(xu);
 #pragma unroll
-                for (int k = 0; k < K; ++k) accum(wd[k], xu, p[m][k]);
+                    for (int k = 0; k < K; ++k) accum_lut(wd[k], xp, p[m][k], lut, copyoff);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < K; ++k) accum(wd[k], xu, p[m][k]);
+                }
             }
             if (kGroup) {
                 const int colend = (u + 1) * 16;
@@ -492,7 +545,7 @@ template <int XT, int LAYOUT, int K, int MT>
 __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, const int wave,
                                          const int nwaves, uint32_t* red, const float* cb_lds,
                                          const void* xsrc, float* sx_lds, const bool active,
-                                         void* q8_lds = nullptr, float* wmax_lds = nullptr)
+                                         void* q8_lds, float* wmax_lds, const uint8_t* lut)
 {
     float* sx_lds_w = sx_lds;
     constexpr bool kInt = XT == TQ_I8 || XT == TQ_F32_Q8;
@@ -507,7 +560,7 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     const int c0 = active ? ((nunits * wave) / nwaves) * cpu : 0;
     const int c1 = active ? std::min(((nunits * (wave + 1)) / nwaves) * cpu, NC) : 0;
 
-    RowBlock<XT, LAYOUT, K, MT> blk(P, rb, xsrc);
+    RowBlock<XT, LAYOUT, K, MT> blk(P, rb, xsrc, lut);
     if (XT == TQ_F32_Q8 && !TQ_Q8_EARLY_LOADS) quantize_to_lds(P, (uint32_t*)q8_lds, sx_lds_w, wmax_lds);
     blk.begin(c0, c1);
     if (XT == TQ_F32_Q8 && TQ_Q8_EARLY_LOADS) {
@@ -604,12 +657,12 @@ __device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb
     __shared__ float cb_lds[TQ_CB_SLOTS];
     __shared__ float sx_lds[TQ_MAX_M_GEMV];
     __shared__ float wmax[16];
+    __shared__ __attribute__((aligned(16))) uint8_t lut[XT == TQ_BF16 ? kLutBytes : 16];
     constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     constexpr int Rw = kGroup ? MT : MT * K;          // partial sums per lane
-    if (LAYOUT == TQ_SCALE_CODEBOOK) {
-        if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
-        __syncthreads();
-    }
+    if (LAYOUT == TQ_SCALE_CODEBOOK && threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+    if (XT == TQ_BF16) fill_bf16_lut(lut);
+    if (LAYOUT == TQ_SCALE_CODEBOOK || XT == TQ_BF16) __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwaves = (int)(blockDim.x >> 6);
     const int S = nwaves / nrb;                       // waves per row block
@@ -624,7 +677,7 @@ __device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb
         xsrc = xq;     // filled inside rowblock, after its first loads are issued
     }
     rowblock<XT, LAYOUT, K, MT>(P, rb, split, S, tq_dyn + r * S * Rw * 64, cb_lds, xsrc, sx_lds, active,
-                                xq, wmax);
+                                xq, wmax, lut);
 }
 
 template <int XT, int LAYOUT, int K, int MT>

@@ -49,5 +49,10 @@ static inline size_t tq_x_lds_bytes(int64_t M, int64_t Kin) { return (size_t)((M
 // Workspace layout of a grouped plan: problem table, then the items.
 static inline int64_t tq_ws_items_off(int64_t n_probs) { return tq_align256(n_probs * (int64_t)sizeof(tq_prob_dev)); }
 #define TQ_MAX_Q8_LDS 65536
+// LDS of one workgroup on gfx950, and what a decode launch asks for: the
+// kernel's static arrays (the bf16 trit table; 1 KiB covers the small ones),
+// the partial sums of split row blocks and the int8 copy of x.
+#define TQ_MAX_WG_LDS 163840
+size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_lds_bytes);
 // Family id of a (x_type, layout, K, M) combination, or -1 if none.
 int tq_gemv_family(int x_type, int layout, int K, int M);

@@ -162,3 +162,20 @@ def test_act_quant_batch_validation():
     seg[0] = tq.tq_act_segment(0, 64, tq.F32, 0, None, None, None)
     assert L.tq_act_quant_int8_batch(seg, 1, None) == tq.OK
     assert L.tq_act_quant_int8_batch(None, 0, None) == tq.OK
+
+
+def test_grouped_shape_must_fit_the_workgroup_lds():
+    # bf16 decode keeps a 64 KiB trit table in LDS; 16 split waves of a
+    # 4-plane, 16-token per-tensor problem would add 256 KiB of partial sums
+    d = tq.desc(4, 0, tq.SCALE_TENSOR, 64, 256)
+    good = 0x60000
+    probs = tq.problems([(d, good, good, None, good, None)])
+    n = tq.gemv_grouped_workspace_size(probs, 16)
+    with pytest.raises(tq.TQError) as e:
+        tq.gemv_grouped_prepare(probs, 16, tq.BF16, good, n, waves=16, row_blocks=1, stream=0)
+    assert e.value.status == tq.ERR_UNSUPPORTED and "LDS" in str(e.value)
+    plan = tq.tq_grouped_plan(workspace=good, n_items=1, family=-1)
+    for fam_x in (tq.BF16, tq.I8):
+        plan.family = ((fam_x * 3 + 0) * 4 + 3) * 3 + 2     # x type, per-tensor, 4 planes, 16 tokens
+        plan.waves, plan.row_blocks, plan.n_problems = 16, 1, 1
+        assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_UNSUPPORTED
