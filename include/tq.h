@@ -6,13 +6,14 @@
  *
  *   y[m][n] = sum_{k<K} sum_{g<G} S_k[n][g] * sum_{i in group g} t_k[n][i] * x[m][i]
  *
- *   t_k[n][i] in {-1, 0, +1}   trit plane k of the N x Kin weight ("Weights use
- *                              {-1, 0, +1} planes", Tritium page, introduction;
- *                              plane 0 is the base, the others residual planes)
+ *   t_k[n][i] in {-1, 0, +1}   trit plane k of the N x Kin weight (Tritium page,
+ *                              introduction: a base plane plus residual planes,
+ *                              each with values -1, 0 or +1; plane 0 is the base)
  *   S_k[n][g]                  TQ_SCALE_TENSOR:   s_k, one fp32 per plane
  *                              TQ_SCALE_GROUP_F16: one f16 per plane, row and group
  *                                of g consecutive inputs (sasori page, "K and g" and
- *                                "How it works": a sum of K per-group-scaled planes)
+ *                                "How it works": the weight is the sum of its K
+ *                                planes, each scaled group by group)
  *                              TQ_SCALE_CODEBOOK: 3^(K-1-k) * cb[idx[n][g]] -- the
  *                                balanced-ternary codec, K digits per weight, value
  *                                9 t2 + 3 t1 + t0 for K = 3, 27 levels, a codebook of

@@ -9,21 +9,23 @@
  *
  *   y[m][n] = sum_k sum_g S_k[n][g] * sum_{i in group g} t_k[n][i] * x[m][i]
  *
- * - "Weights use {-1, 0, +1} planes; one plane is the compact base model;
- *   additional residual planes" (Tritium page, introduction): planes are
- *   summed, plane 0 first.
- * - "a sum of K per-group-scaled trit-planes" with one f16 scale per plane
- *   per group of g weights along the row (sasori page, "How it works" and the
+ * - The weight is a base plane of values -1, 0, +1 plus residual planes of
+ *   the same kind (Tritium page, introduction): planes are summed, plane 0
+ *   first.
+ * - Each plane is scaled group by group before the planes are added, with
+ *   one f16 scale per plane per group of g weights along the row (sasori
+ *   page, "How it works" and the
  *   "K and g" table, whose bits-per-weight figures 2K + 16K/g only add up
  *   with one f16 per plane per group).
  * - A per-tensor scale applied once at the end ("Ternary GEMV (No
  *   Multiplication)" section of the QORA-LLM-2B page).
  * - The balanced-ternary codec: d = 3 digits give 27 levels, value
- *   9 t2 + 3 t1 + t0, group size 16 and a 27-entry log-spaced scale codebook
+ *   9 t2 + 3 t1 + t0, groups of 16 weights whose scale is one of 27
+ *   log-spaced f16 values
  *   (Llama-3.1-8B-trit-uniform-d3 card, "Quantization details").  Plane p
  *   carries the digit of weight 3^(K-1-p), so S_p[n][g] = 3^(K-1-p) cb[idx].
  * - The result equals the dense product with the dequantised weight, the
- *   "fake-quant" that the sasori kernel "reproduces bit-exactly" (sasori page,
+ *   fake-quant result that the sasori kernel is said to match bit for bit (sasori page,
  *   "g (group-size)") and the FP16-dequantised checkpoint of the model card
  *   ("Quick load").
  *

@@ -8,7 +8,7 @@ Canonical layouts (the ones the C ABI's pack call and the oracle take):
   x         fp32 or bf16 bits   [M][Kin]
 
 Value recipes, as the workloads state them or, where they are silent, the
-plainest reading (listed with reasons in the design notes):
+plainest reading that the rest supports:
   trits     P(-1) = P(+1) = 0.3, P(0) = 0.4
   digits    uniform over {-1, 0, +1}
   TENSOR    log-uniform [1e-3, 1e-1], one draw per plane, rounded to fp32

@@ -2,8 +2,8 @@
 // libtq: decode kernels (M <= 16) -- tq_gemv and tq_gemv_grouped.
 //
 // What is computed is the definition in tq.h: per output row, each trit plane
-// adds or subtracts the activations of its nonzero trits ("the inner GEMV loop
-// uses only addition and subtraction", QORA-LLM-2B page), per-group sums are
+// adds or subtracts the activations of its nonzero trits, with no multiply by
+// a weight in the inner loop (QORA-LLM-2B page), per-group sums are
 // scaled once at the group's end (sasori page, "K and g"), a per-tensor scale
 // once at the very end (QORA-LLM-2B, "Ternary GEMV (No Multiplication)").
 //
@@ -23,12 +23,13 @@
 //         replicates the sign bit of a source byte, which yields 0xFF), then
 //         one v_dot4_i32_i8 against four int8 activations: about 13 VALU ops
 //         per 16 trits.
-//  bf16   the trit pair (4p+1, 4p+3) of a dword comes from (w >> 2p) & 0x03000300,
-//         the pair (4p, 4p+2) from (w << (8-2p)) & 0x03000300; one v_perm_b32
-//         maps each pair to two bf16 values {0, +2, -2} (low bytes zero), and
-//         one v_dot2_f32_bf16 accumulates t*x for both against the matching
-//         activation pair, which the scalar unit assembles with s_pack.  The
-//         factor 2 is exact and folded into the scale.
+//  bf16   a table in LDS maps each code byte (four trits) to four bf16 values
+//         {0, +1, -1} (8 bytes); one v_perm_b32 builds the byte address from
+//         the code byte and the lane's copy offset, one 8-byte LDS read fetches
+//         the four values and two v_dot2_f32_bf16 accumulate them against the
+//         matching activation pairs, which the scalar unit assembles with
+//         s_pack.  The table is 256 entries x 32 copies (64 KiB): 32 lanes read
+//         32 different copies, so a wave's read has no bank conflicts.
 //  fp32   int8 decode as above, converted per trit and accumulated with fma
 //         (t in {-1, 0, 1}, so each fma is an exact add, subtract or no-op).
 #include "tq_internal.h"
@@ -37,7 +38,7 @@
 
 namespace tqk {
 
-// Tuning constants (measured on MI355X; see the design notes).
+// Tuning constants (measured on MI355X).
 #ifndef TQ_Q8_HELD
 #define TQ_Q8_HELD 2          // fp32 activation vectors held per thread while quantising
 #endif
