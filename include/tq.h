@@ -181,10 +181,19 @@ tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_t M, int32
                   const void* x, const float* x_scale, float* y, int32_t* acc, void* stream);
 
 /*
- * Prefill product for any M (matrix-core kernels): same arguments and
- * results as tq_gemv.  Supported: TQ_I8 with TQ_SCALE_TENSOR and K = 1 (int8
- * MFMA, int32 accumulate, bit exact as tq_gemv), and TQ_BF16 with
- * TQ_SCALE_GROUP_F16 (bf16 MFMA, fp32 accumulate per plane and group).
+ * Prefill product for any M (matrix-core kernels: the trits of each 16 x 16
+ * weight tile are decoded in registers to the MFMA operand type, the MFMA
+ * accumulates one plane and group at a time, and the group's scale is applied
+ * once when the group ends).  Same arguments and results as tq_gemv, with:
+ *   x_type    TQ_I8 (int8 MFMA, int32 accumulate) or TQ_BF16 (bf16 MFMA,
+ *             fp32 accumulate); TQ_F32 and TQ_F32_Q8 are TQ_ERR_UNSUPPORTED
+ *   layout    TQ_SCALE_TENSOR, or TQ_SCALE_GROUP_F16 with g a multiple of the
+ *             MFMA step (64 columns for TQ_I8, 32 for TQ_BF16); TQ_SCALE_CODEBOOK
+ *             is TQ_ERR_UNSUPPORTED
+ *   x         device, 16-byte aligned (rows are read 16 bytes at a time)
+ *   M         0 .. 2^24
+ * TQ_I8 with TQ_SCALE_TENSOR and K = 1 is bit exact, as in tq_gemv:
+ *   acc = sum_i t[n][i] * xq[m][i] (int32), y = fl32(float(acc) * fl32(s_w * x_scale[m])).
  */
 tq_status tq_gemm(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
                   const void* x, const float* x_scale, float* y, int32_t* acc, void* stream);
@@ -238,6 +247,24 @@ tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int
 
 /* One launch computing every problem of the plan.  Asynchronous. */
 tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);
+
+/*
+ * Many prefill products (tq_gemm) in one launch, e.g. every projection of a
+ * layer stack.  All problems must share K, scale layout and x_type; M is
+ * common.  The work list holds one item per 32 FM x 32 FN output tile (128 x
+ * 256 for TQ_I8 with one plane and a per-tensor scale, else 128 x 128), longest
+ * problems first.  The plan is the decode one's struct: on return waves = 4
+ * and row_blocks = 64-row blocks per tile; tq_gemv_grouped_run refuses it.
+ */
+tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,
+                                         int32_t x_type, size_t* bytes);
+/* Validate, write the problem table and work list to `workspace` (device),
+   fill `plan`.  Copies host->device on `stream` and synchronizes it. */
+tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                  int32_t x_type, void* workspace, size_t workspace_bytes,
+                                  tq_grouped_plan* plan, void* stream);
+/* One launch computing every problem of the plan.  Asynchronous. */
+tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,9 +7,7 @@
 
 #include "tq_internal.h"
 
-namespace {
-
-int log2i(int v)
+static int log2i(int v)
 {
     int r = 0;
     while ((1 << r) < v) ++r;
@@ -17,20 +15,21 @@ int log2i(int v)
 }
 
 // Prefix the thread's last error message with the problem index.
-tq_status fail_problem(tq_status s, int32_t i)
+tq_status tq_fail_problem(tq_status s, int32_t i)
 {
     char msg[512];
     snprintf(msg, sizeof msg, "%s", tq_last_error());
     return tq_fail(s, "problem %d: %s", (int)i, msg);
 }
 
-bool acc_allowed(const tq_layout& L, int x_type)
+static bool acc_allowed(const tq_layout& L, int x_type)
 {
     return (x_type == TQ_I8 || x_type == TQ_F32_Q8) && L.layout == TQ_SCALE_TENSOR && L.K == 1;
 }
 
-tq_status check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_type, const void* x,
-                     const float* x_scale, const float* y, const int32_t* acc, int64_t max_m)
+tq_status tq_check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_type, const void* x,
+                        const float* x_scale, const float* y, const int32_t* acc, int64_t max_m,
+                        int x_align)
 {
     tq_status s;
     if (x_type != TQ_F32 && x_type != TQ_BF16 && x_type != TQ_I8 && x_type != TQ_F32_Q8)
@@ -40,7 +39,7 @@ tq_status check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_
                                   (long long)M, (long long)max_m);
     const bool work = M > 0 && L.N > 0;
     if ((s = tq_check_ptr(blob, "blob", !work))) return s;
-    if ((s = tq_check_ptr(x, "x", !(work && L.Kin > 0), x_type == TQ_F32_Q8 ? 16 : 4))) return s;
+    if ((s = tq_check_ptr(x, "x", !(work && L.Kin > 0), x_type == TQ_F32_Q8 ? 16 : x_align))) return s;
     if (x_type == TQ_F32_Q8 && (int64_t)tq_x_lds_bytes(M, L.Kin) > TQ_MAX_Q8_LDS)
         return tq_fail(TQ_ERR_UNSUPPORTED, "TQ_F32_Q8 needs M * in_features <= %d (LDS); got %lld",
                        TQ_MAX_Q8_LDS, (long long)(M * L.Kin));
@@ -57,7 +56,7 @@ tq_status check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_
     return TQ_OK;
 }
 
-tq_prob_dev make_prob(const tq_layout& L, const void* blob, int64_t M, const void* x,
+tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const void* x,
                       const float* x_scale, float* y, int32_t* acc)
 {
     tq_prob_dev P;
@@ -81,7 +80,6 @@ tq_prob_dev make_prob(const tq_layout& L, const void* blob, int64_t M, const voi
     return P;
 }
 
-}  // namespace
 
 TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
                             const void* x, const float* x_scale, float* y, int32_t* acc, void* stream)
@@ -89,9 +87,9 @@ TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_
     tq_layout L;
     tq_status s = tq_check_desc(desc, &L);
     if (s) return s;
-    if ((s = check_call(L, blob, M, x_type, x, x_scale, y, acc, TQ_MAX_M_GEMV))) return s;
+    if ((s = tq_check_call(L, blob, M, x_type, x, x_scale, y, acc, TQ_MAX_M_GEMV))) return s;
     if (M == 0 || L.N == 0) return tq_ok();
-    const tq_prob_dev P = make_prob(L, blob, M, x, x_scale, y, acc);
+    const tq_prob_dev P = tq_make_prob(L, blob, M, x, x_scale, y, acc);
     if ((s = tq_gemv_launch_single(L, P, x_type, (hipStream_t)stream))) return s;
     return tq_ok();
 }
@@ -107,7 +105,7 @@ TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, i
     for (int32_t i = 0; i < count; ++i) {
         tq_layout L;
         tq_status s = tq_check_desc(problems[i].desc, &L);
-        if (s) return fail_problem(s, i);
+        if (s) return tq_fail_problem(s, i);
         items += L.NB;
     }
     // problems, then one (problem, first row block) item per workgroup (at most one per block)
@@ -145,8 +143,8 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
         const tq_problem& pr = problems[i];
         tq_layout L;
         tq_check_desc(pr.desc, &L);
-        if ((s = check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, TQ_MAX_M_GEMV)))
-            return fail_problem(s, i);
+        if ((s = tq_check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, TQ_MAX_M_GEMV)))
+            return tq_fail_problem(s, i);
         if (i == 0) {
             K0 = L.K;
             layout0 = L.layout;
@@ -155,7 +153,7 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
             return tq_fail(TQ_ERR_UNSUPPORTED,
                            "problem %d: all problems of a plan must share planes, layout and group", i);
         }
-        probs[(size_t)i] = make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
+        probs[(size_t)i] = tq_make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
         if (x_type == TQ_F32_Q8) x_lds = std::max(x_lds, tq_x_lds_bytes(M, L.Kin));
     }
     if (count > 0 && M > 0) {

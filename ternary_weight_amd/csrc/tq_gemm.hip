@@ -1,12 +1,176 @@
-// libtq: tq_gemm -- prefill product on the matrix cores (MFMA).
-#include "tq_internal.h"
+// libtq: tq_gemm and tq_gemm_grouped_* -- prefill product on the matrix
+// cores (validation and dispatch; the kernels are in tq_gemm_impl.h).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tq_gemm_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxM = 1 << 24;
+constexpr int kFamilyBase = 1000;   // grouped plans of tq_gemm carry family >= this
+
+// Kernel for (x_type, layout, K, g), or null with the reason recorded.
+const tq_gemm_kernel* gemm_kernel(const tq_layout& L, int x_type)
+{
+    if (x_type != TQ_I8 && x_type != TQ_BF16) {
+        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm takes TQ_I8 or TQ_BF16 activations (got %d)", x_type);
+        return nullptr;
+    }
+    if (L.layout == TQ_SCALE_CODEBOOK) {
+        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: TQ_SCALE_CODEBOOK is decode-only (tq_gemv)");
+        return nullptr;
+    }
+    const int step = x_type == TQ_I8 ? 64 : 32;   // columns per MFMA step
+    if (L.layout == TQ_SCALE_GROUP_F16 && L.g % step != 0) {
+        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: group size %d below the %d-column MFMA step of this x_type",
+                L.g, step);
+        return nullptr;
+    }
+    const tq_gemm_kernel (*t)[4] = x_type == TQ_I8 ? tq_gemm_table_i8() : tq_gemm_table_bf16();
+    return &t[L.layout == TQ_SCALE_GROUP_F16 ? 1 : 0][L.K - 1];
+}
+
+int gemm_family(const tq_layout& L, int x_type)
+{
+    return kFamilyBase + (((x_type == TQ_BF16 ? 1 : 0) * 2 + (L.layout == TQ_SCALE_GROUP_F16 ? 1 : 0)) * 4 + L.K - 1);
+}
+
+const tq_gemm_kernel* kernel_of_family(int family)
+{
+    const int f = family - kFamilyBase;
+    if (f < 0 || f >= 16) return nullptr;
+    const tq_gemm_kernel (*t)[4] = (f >> 3) ? tq_gemm_table_bf16() : tq_gemm_table_i8();
+    return &t[(f >> 2) & 1][f & 3];
+}
+
+int64_t tiles_of(const tq_gemm_kernel& k, int64_t M, int64_t N, int64_t* tiles_m)
+{
+    const int64_t tm = (M + 32 * k.fm - 1) / (32 * k.fm);
+    const int64_t tn = (N + 32 * k.fn - 1) / (32 * k.fn);
+    if (tiles_m) *tiles_m = tm;
+    return tm * tn;
+}
+
+}  // namespace
 
 TQ_EXPORT tq_status tq_gemm(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
                             const void* x, const float* x_scale, float* y, int32_t* acc, void* stream)
 {
-    (void)blob; (void)M; (void)x_type; (void)x; (void)x_scale; (void)y; (void)acc; (void)stream;
     tq_layout L;
     tq_status s = tq_check_desc(desc, &L);
     if (s) return s;
-    return tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: not available in this build");
+    if ((s = tq_check_call(L, blob, M, x_type, x, x_scale, y, acc, kMaxM, 16))) return s;
+    const tq_gemm_kernel* k = gemm_kernel(L, x_type);
+    if (!k) return TQ_ERR_UNSUPPORTED;
+    if (M == 0 || L.N == 0) return tq_ok();
+    int64_t tiles_m = 0;
+    const int64_t tiles = tiles_of(*k, M, L.N, &tiles_m);
+    if (tiles > INT32_MAX) return tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: %lld tiles exceed one launch", (long long)tiles);
+    const tq_prob_dev P = tq_make_prob(L, blob, M, x, x_scale, y, acc);
+    hipLaunchKernelGGL(k->single, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, P, (int)tiles_m);
+    if ((s = tq_check_launch("tq_gemm"))) return s;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,
+                                                   int32_t x_type, size_t* bytes)
+{
+    if (!bytes) return tq_fail(TQ_ERR_ARG, "bytes is NULL");
+    if (count < 0 || (count > 0 && !problems)) return tq_fail(TQ_ERR_ARG, "bad problem list");
+    if (M < 0 || M > kMaxM) return tq_fail(TQ_ERR_UNSUPPORTED, "M = %lld not in 0..%lld", (long long)M,
+                                           (long long)kMaxM);
+    int64_t items = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        tq_layout L;
+        tq_status s = tq_check_desc(problems[i].desc, &L);
+        if (s) return tq_fail_problem(s, i);
+        const tq_gemm_kernel* k = gemm_kernel(L, x_type);
+        if (!k) return tq_fail_problem(TQ_ERR_UNSUPPORTED, i);
+        items += tiles_of(*k, M, L.N, nullptr);
+    }
+    if (items > INT32_MAX) return tq_fail(TQ_ERR_UNSUPPORTED, "%lld tiles exceed one launch", (long long)items);
+    *bytes = (size_t)(tq_ws_items_off(count) + tq_align256(items * 8));
+    if (*bytes == 0) *bytes = 256;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                            int32_t x_type, void* workspace, size_t workspace_bytes,
+                                            tq_grouped_plan* plan, void* stream)
+{
+    if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
+    size_t need = 0;
+    tq_status s = tq_gemm_grouped_workspace_size(problems, count, M, x_type, &need);
+    if (s) return s;
+    if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
+    if (workspace_bytes < need)
+        return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    std::vector<tq_prob_dev> probs((size_t)count);
+    struct Item { int64_t cost; int32_t prob, tile; };
+    std::vector<Item> items;
+    int family = -1;
+    const tq_gemm_kernel* k0 = nullptr;
+    for (int32_t i = 0; i < count; ++i) {
+        const tq_problem& pr = problems[i];
+        tq_layout L;
+        tq_check_desc(pr.desc, &L);
+        if ((s = tq_check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, kMaxM, 16)))
+            return tq_fail_problem(s, i);
+        const tq_gemm_kernel* k = gemm_kernel(L, x_type);
+        if (i == 0) {
+            family = gemm_family(L, x_type);
+            k0 = k;
+        } else if (gemm_family(L, x_type) != family) {
+            return tq_fail(TQ_ERR_UNSUPPORTED,
+                           "problem %d: all problems of a plan must share planes, layout and x_type", i);
+        }
+        probs[(size_t)i] = tq_make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
+        if (M > 0) {
+            const int64_t n = tiles_of(*k, M, L.N, nullptr);
+            for (int64_t t = 0; t < n; ++t) items.push_back({L.Kin * (int64_t)L.K, i, (int32_t)t});
+        }
+    }
+    // longest problems first, so that the last workgroups to start are short
+    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    std::vector<uint8_t> host(need, 0);
+    if (count > 0) memcpy(host.data(), probs.data(), (size_t)count * sizeof(tq_prob_dev));
+    int32_t* it = (int32_t*)(host.data() + tq_ws_items_off(count));
+    for (size_t j = 0; j < items.size(); ++j) {
+        it[2 * j] = items[j].prob;
+        it[2 * j + 1] = items[j].tile;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    if ((s = tq_check_hip(hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, st),
+                          "tq_gemm_grouped_prepare copy")))
+        return s;
+    if ((s = tq_check_hip(hipStreamSynchronize(st), "tq_gemm_grouped_prepare synchronize"))) return s;
+    memset(plan, 0, sizeof *plan);
+    plan->workspace = workspace;
+    plan->n_items = (int64_t)items.size();
+    plan->family = family;
+    plan->x_type = x_type;
+    plan->M = (int32_t)M;
+    plan->waves = 4;
+    plan->row_blocks = k0 ? k0->fn / 2 : 0;
+    plan->n_problems = count;
+    return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream)
+{
+    if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
+    if (plan->n_items == 0) return tq_ok();
+    tq_status s;
+    if ((s = tq_check_ptr(plan->workspace, "plan workspace", false))) return s;
+    const tq_gemm_kernel* k = kernel_of_family(plan->family);
+    if (!k || plan->n_items < 0 || plan->n_items > INT32_MAX || plan->n_problems < 1)
+        return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemm_grouped_prepare");
+    const uint8_t* ws = (const uint8_t*)plan->workspace;
+    hipLaunchKernelGGL(k->grouped, dim3((unsigned)plan->n_items), dim3(256), 0, (hipStream_t)stream,
+                       (const tq_prob_dev*)ws, (const int2*)(ws + tq_ws_items_off(plan->n_problems)));
+    if ((s = tq_check_launch("tq_gemm_grouped_run"))) return s;
+    return tq_ok();
 }

@@ -39,6 +39,17 @@ struct tq_prob_dev {
     int32_t M, log2g;
 };
 
+// Call validation shared by the entry points (tq_entry.hip): x_type, M in
+// 0..max_m, pointers (x aligned to x_align bytes), the acc restriction.
+tq_status tq_check_call(const tq_layout& L, const void* blob, int64_t M, int32_t x_type, const void* x,
+                        const float* x_scale, const float* y, const int32_t* acc, int64_t max_m,
+                        int x_align = 4);
+// The device-side descriptor of one problem.
+tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const void* x,
+                         const float* x_scale, float* y, int32_t* acc);
+// Prefix the thread's last error message with a problem index.
+tq_status tq_fail_problem(tq_status s, int32_t i);
+
 // Decode launch shared by tq_gemv and tq_gemv_grouped_run (tq_gemv.hip).
 tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type,
                                 hipStream_t stream);

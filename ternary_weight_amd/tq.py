@@ -76,6 +76,11 @@ SIGNATURES = {
     "tq_gemv_grouped_prepare": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32, _VP,
                                  ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_gemv_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
+    "tq_gemm_grouped_workspace_size": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32,
+                                        ctypes.POINTER(ctypes.c_size_t)], _I32),
+    "tq_gemm_grouped_prepare": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32, _VP,
+                                 ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
+    "tq_gemm_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
 }
 
 _lib = None
@@ -206,3 +211,22 @@ def gemv_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, waves=0, 
 
 def gemv_grouped_run(plan, stream=None):
     _check(lib().tq_gemv_grouped_run(ctypes.byref(plan), _stream(stream)), "tq_gemv_grouped_run")
+
+
+def gemm_grouped_workspace_size(probs, M, x_type) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tq_gemm_grouped_workspace_size(probs, len(probs), M, x_type, ctypes.byref(n)),
+           "tq_gemm_grouped_workspace_size")
+    return n.value
+
+
+def gemm_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, stream=None):
+    plan = tq_grouped_plan()
+    _check(lib().tq_gemm_grouped_prepare(probs, len(probs), M, x_type, _ptr(workspace),
+                                         workspace_bytes, ctypes.byref(plan), _stream(stream)),
+           "tq_gemm_grouped_prepare")
+    return plan
+
+
+def gemm_grouped_run(plan, stream=None):
+    _check(lib().tq_gemm_grouped_run(ctypes.byref(plan), _stream(stream)), "tq_gemm_grouped_run")

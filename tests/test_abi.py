@@ -132,8 +132,38 @@ def test_grouped_validation():
 def test_gemm_rejects_unsupported_before_device_work():
     L = tq.lib()
     good = 0x30000
-    d = tq.desc(2, 64, tq.SCALE_GROUP_F16, 64, 64)
-    assert L.tq_gemm(ctypes.byref(d), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
+    g32 = tq.desc(2, 32, tq.SCALE_GROUP_F16, 64, 64)      # below the int8 MFMA step of 64 columns
+    assert L.tq_gemm(ctypes.byref(g32), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
+    cb = tq.desc(3, 16, tq.SCALE_CODEBOOK, 64, 64, n_codebook=27)
+    assert L.tq_gemm(ctypes.byref(cb), good, 64, tq.BF16, good, None, good, None, None) == tq.ERR_UNSUPPORTED
+    d = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 64)
+    for xt in (tq.F32, tq.F32_Q8):
+        assert L.tq_gemm(ctypes.byref(d), good, 64, xt, good, None, good, None, None) == tq.ERR_UNSUPPORTED
+    # x is read 16 bytes at a time; M is bounded; acc only for the bit-exact combination
+    assert L.tq_gemm(ctypes.byref(d), good, 64, tq.I8, good + 4, good, good, None, None) == tq.ERR_ALIGN
+    assert L.tq_gemm(ctypes.byref(d), good, (1 << 24) + 1, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
+    assert L.tq_gemm(ctypes.byref(g32), good, 64, tq.BF16, good, None, good, good, None) == tq.ERR_UNSUPPORTED
+    assert L.tq_gemm(ctypes.byref(d), None, 0, tq.I8, None, None, None, None, None) == tq.OK
+
+
+def test_gemm_grouped_validation():
+    d1 = tq.desc(1, 0, tq.SCALE_TENSOR, 640, 2560)
+    d3 = tq.desc(3, 256, tq.SCALE_GROUP_F16, 640, 2560)
+    good = 0x70000
+    n = tq.gemm_grouped_workspace_size(tq.problems([(d1, good, good, good, good, None)]), 2048, tq.I8)
+    # one 128 x 256 tile item per output tile (16 x 3), after the problem table
+    assert n == 256 + ((16 * 3 * 8 + 255) // 256) * 256
+    mixed = tq.problems([(d1, good, good, good, good, None), (d3, good, good, good, good, None)])
+    with pytest.raises(tq.TQError) as e:
+        tq.gemm_grouped_prepare(mixed, 64, tq.I8, good, 1 << 20, stream=0)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    with pytest.raises(tq.TQError) as e:
+        tq.gemm_grouped_workspace_size(mixed, 64, tq.F32)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    plan = tq.tq_grouped_plan(workspace=good, n_items=3, family=5, n_problems=1)
+    assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a decode family
+    plan.family = 1000
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a prefill family
 
 
 def test_fused_int8_activation_limits():

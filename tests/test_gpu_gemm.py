@@ -1,0 +1,197 @@
+"""GPU parity of the prefill product (tq_gemm, tq_gemm_grouped_*) against the
+CPU oracle, through the C ABI.
+
+Bars as for decode: bit-exact y and int32 accumulator for int8 activations
+with one plane and a per-tensor scale; the per-token relative error
+max_n |y - y*| / max(|y*|, rms(y*)) <= 1e-3 against the fp64 oracle otherwise.
+Sizes span several 128 x 256 (or 128 x 128) output tiles with ragged edges in
+M, N and Kin.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import BF16, CODEBOOK, F32, GROUP_F16, I8, TENSOR
+from tests.gpu_util import TOL, dev, gemv, host, pack, rel_err, torch
+from tests.test_gpu_parity import rand_problem, rand_x
+
+pytestmark = pytest.mark.gpu
+
+
+def check_i8(K, g, layout, trits, scales, d, blob, q, s, exact):
+    ref = oracle.gemv_i8(K, g, layout, trits, scales, q, s)
+    if exact:
+        y, acc = gemv(d, blob, I8, q, s, want_acc=True, gemm=True)
+        assert np.array_equal(acc.astype(np.int64), ref["acc"].reshape(acc.shape))
+        assert np.array_equal(y.view(np.uint32), ref["y32"].view(np.uint32))
+    else:
+        y = gemv(d, blob, I8, q, s, gemm=True)
+        assert rel_err(y, ref["y64"]) <= TOL
+
+
+@pytest.mark.parametrize("N,Kin,M", [
+    (256, 512, 128), (200, 80, 17), (640, 2560, 300), (64, 64, 1), (513, 1024, 129), (1, 16, 5),
+])
+def test_gemm_i8_tensor_bit_exact(N, Kin, M):
+    rng = np.random.default_rng(N * 7 + Kin + M)
+    trits, scales, _ = rand_problem(1, 0, TENSOR, N, Kin, rng)
+    d, blob = pack(1, 0, TENSOR, trits, scales)
+    q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+    check_i8(1, 0, TENSOR, trits, scales, d, blob, q, s, exact=True)
+
+
+def test_gemm_i8_extreme_accumulators():
+    # every trit +1 against x at +-127: |acc| = 127 * Kin, the largest the format allows here
+    N, Kin, M = 130, 4096, 70
+    trits = np.ones((1, N, Kin), dtype=np.int8)
+    trits[0, 1::2] = -1
+    scales = np.array([0.0123], dtype=np.float32)
+    d, blob = pack(1, 0, TENSOR, trits, scales)
+    x = np.full((M, Kin), 3.5, dtype=np.float32)
+    x[1::2] = -3.5
+    q, s = oracle.act_quant_i8(x)
+    assert np.abs(q).max() == 127
+    check_i8(1, 0, TENSOR, trits, scales, d, blob, q, s, exact=True)
+
+
+@pytest.mark.parametrize("K,g,layout", [
+    (2, 0, TENSOR), (3, 0, TENSOR), (4, 0, TENSOR),
+    (1, 64, GROUP_F16), (3, 128, GROUP_F16), (2, 256, GROUP_F16), (4, 64, GROUP_F16),
+])
+def test_gemm_i8_other_layouts(K, g, layout):
+    rng = np.random.default_rng(K * 100 + g + layout)
+    N, Kin, M = 200, 768, 140
+    trits, scales, _ = rand_problem(K, g, layout, N, Kin, rng)
+    d, blob = pack(K, g, layout, trits, scales)
+    q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+    check_i8(K, g, layout, trits, scales, d, blob, q, s, exact=False)
+
+
+@pytest.mark.parametrize("K,g,layout", [
+    (1, 0, TENSOR), (3, 0, TENSOR), (1, 32, GROUP_F16), (3, 256, GROUP_F16), (2, 64, GROUP_F16),
+    (4, 128, GROUP_F16), (3, 32, GROUP_F16),
+])
+@pytest.mark.parametrize("N,Kin,M", [(200, 768, 140), (64, 256, 1), (300, 1280, 37)])
+def test_gemm_bf16(K, g, layout, N, Kin, M):
+    rng = np.random.default_rng(K * 1000 + g + N + M)
+    trits, scales, _ = rand_problem(K, g, layout, N, Kin, rng)
+    d, blob = pack(K, g, layout, trits, scales)
+    x = rand_x(M, Kin, BF16, rng)
+    y = gemv(d, blob, BF16, x, gemm=True)
+    ref = oracle.gemv_fp(K, g, layout, trits, scales, x, BF16)
+    err = rel_err(y, ref)
+    assert err <= TOL, err
+    assert err <= 1e-5          # fp32 accumulation is far inside the bar
+
+
+def test_gemm_ragged_kin_tail():
+    # Kin not a multiple of the MFMA step: the last step is part padding
+    rng = np.random.default_rng(5)
+    for (Kin, xt) in ((80, I8), (48, BF16), (16, I8), (16, BF16), (1040, I8)):
+        N, M = 70, 33
+        trits, scales, _ = rand_problem(1, 0, TENSOR, N, Kin, rng)
+        d, blob = pack(1, 0, TENSOR, trits, scales)
+        if xt == I8:
+            q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+            check_i8(1, 0, TENSOR, trits, scales, d, blob, q, s, exact=True)
+        else:
+            x = rand_x(M, Kin, BF16, rng)
+            assert rel_err(gemv(d, blob, BF16, x, gemm=True), oracle.gemv_fp(1, 0, TENSOR, trits, scales, x, BF16)) <= TOL
+
+
+def test_gemm_one_hot_indexing():
+    # x = e_j picks column j: y[j][n] = s[n][j / g] * t[n][j] exactly, for every
+    # j of a row of two groups and every n of two weight tiles
+    N, Kin = 96, 128
+    rng = np.random.default_rng(9)
+    trits, scales, _ = rand_problem(1, 64, GROUP_F16, N, Kin, rng)
+    d, blob = pack(1, 64, GROUP_F16, trits, scales)
+    x = np.zeros((Kin, Kin), dtype=np.float32)
+    np.fill_diagonal(x, 1.0)
+    from synth import gen
+    y = gemv(d, blob, BF16, gen.bf16_bits(x), gemm=True)
+    s = np.array([[oracle.f16_to_f64(int(h)) for h in row] for row in scales[0]])   # [N][G]
+    want = (s[:, np.arange(Kin) // 64] * trits[0]).T                                   # [Kin][N]
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_gemm_matches_gemv_at_small_m():
+    # the two kernel families agree where both apply (int8: bit for bit)
+    rng = np.random.default_rng(11)
+    N, Kin, M = 320, 2560, 3
+    trits, scales, _ = rand_problem(1, 0, TENSOR, N, Kin, rng)
+    d, blob = pack(1, 0, TENSOR, trits, scales)
+    q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+    a = gemv(d, blob, I8, q, s, want_acc=True)
+    b = gemv(d, blob, I8, q, s, want_acc=True, gemm=True)
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32)) and np.array_equal(a[1], b[1])
+
+
+def test_gemm_unsupported_and_empty():
+    from ternary_weight_amd import tq
+    t = torch()
+    trits, scales, cb = rand_problem(3, 16, CODEBOOK, 64, 64)
+    d, blob = pack(3, 16, CODEBOOK, trits, scales, cb)
+    x = dev(rand_x(4, 64, BF16))
+    y = t.zeros((4, 64), dtype=t.float32, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.gemm(d, blob, 4, BF16, x, None, y)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    trits, scales, _ = rand_problem(1, 32, GROUP_F16, 64, 64)
+    d, blob = pack(1, 32, GROUP_F16, trits, scales)
+    xq = t.zeros((4, 64), dtype=t.int8, device="cuda")
+    xs = t.ones(4, dtype=t.float32, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.gemm(d, blob, 4, I8, xq, xs, y)          # g = 32 is below the int8 MFMA step
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    with pytest.raises(tq.TQError) as e:
+        tq.gemm(d, blob, 4, F32, t.zeros((4, 64), device="cuda"), None, y)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+    tq.gemm(d, blob, 0, BF16, None, None, None)       # M = 0: no-op
+    t.cuda.synchronize()
+
+
+def test_gemm_deterministic():
+    rng = np.random.default_rng(21)
+    trits, scales, _ = rand_problem(3, 256, GROUP_F16, 700, 2048, rng)
+    d, blob = pack(3, 256, GROUP_F16, trits, scales)
+    x = rand_x(100, 2048, BF16, rng)
+    a = gemv(d, blob, BF16, x, gemm=True)
+    b = gemv(d, blob, BF16, x, gemm=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("xt,K,g,layout", [(I8, 1, 0, TENSOR), (BF16, 3, 256, GROUP_F16), (I8, 2, 64, GROUP_F16)])
+def test_gemm_grouped_equals_single(xt, K, g, layout):
+    from ternary_weight_amd import tq
+    t = torch()
+    rng = np.random.default_rng(31 + K)
+    M = 77
+    shapes = [(256, 512), (64, 1024), (700, 256), (130, 768)]
+    keep, items, want = [], [], []
+    for (N, Kin) in shapes:
+        trits, scales, _ = rand_problem(K, g, layout, N, Kin, rng)
+        d, blob = pack(K, g, layout, trits, scales)
+        if xt == I8:
+            q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+            xd, xs = dev(q), dev(s)
+        else:
+            xd, xs = dev(rand_x(M, Kin, BF16, rng)), None
+        y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+        keep.append((d, blob, xd, xs, y))
+        items.append((d, blob, xd, xs, y, None))
+        want.append(gemv(d, blob, xt, xd, xs, gemm=True))
+    probs = tq.problems(items)
+    n = tq.gemm_grouped_workspace_size(probs, M, xt)
+    ws = t.empty(n, dtype=t.uint8, device="cuda")
+    plan = tq.gemm_grouped_prepare(probs, M, xt, ws, n)
+    for _ in range(2):
+        tq.gemm_grouped_run(plan)
+        t.cuda.synchronize()
+        for (d, blob, xd, xs, y), w in zip(keep, want):
+            assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
+    # a decode plan is refused by the prefill run and the other way round
+    with pytest.raises(tq.TQError):
+        tq.gemv_grouped_run(plan)
