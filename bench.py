@@ -36,6 +36,9 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "ternary_weight_amd", "csrc")
 METRIC = "ternary GEMV effective HBM GB/s (% of peak) at BitNet-2B/Llama-8B shapes, M=1"
+METRIC_PREFILL = "ternary prefill GEMM effective TOP/s (MFMA utilisation) at BitNet-2B/Llama-8B shapes"
+MFMA_PEAK_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 
 
 def parse():
@@ -46,7 +49,8 @@ def parse():
     ap.add_argument("--spin-up-ms", type=float, default=150.0,
                     help="plain streaming reads before the warmup steps: the GPU needs ~20 ms of "
                          "memory load to leave its idle clocks")
-    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4"])
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b"],
+                    help="cfg2-4: decode stacks (tq_gemv_grouped_*); cfg5a/b: prefill stacks (tq_gemm_grouped_*)")
     ap.add_argument("--M", type=int, default=1, help="tokens per step (cfg4: 1, 4 or 16)")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
@@ -71,8 +75,9 @@ class Stack:
         import torch
         from ternary_weight_amd import tq
         self.case, self.M = case, M
+        self.prefill = M > 16          # matrix-core product (tq_gemm) instead of the decode kernels
         # int8 activations: quantise inside the product (one launch per step) or as a separate call
-        self.fused = fused and case.x_type == I8
+        self.fused = fused and case.x_type == I8 and not self.prefill
         self.run_type = tq.F32_Q8 if self.fused else case.x_type
         self.projs = case.projections()
         K, g, layout = case.planes, case.group, case.layout
@@ -116,13 +121,17 @@ class Stack:
                 x, xs = self.x_raw[w][j * M:(j + 1) * M], None
             items.append((self.descs[i], self.blobs[i], x, xs, self.ys[i], None))
         self._probs = tq.problems(items)
-        nbytes = tq.gemv_grouped_workspace_size(self._probs, M)
+        nbytes = (tq.gemm_grouped_workspace_size(self._probs, M, self.run_type) if self.prefill
+                  else tq.gemv_grouped_workspace_size(self._probs, M))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.plan = None
         self._segments = None
 
     def prepare(self, waves: int = 0, row_blocks: int = 0):
         from ternary_weight_amd import tq
+        if self.prefill:
+            self.plan = tq.gemm_grouped_prepare(self._probs, self.M, self.run_type, self.ws, self.ws.numel())
+            return
         self.plan = tq.gemv_grouped_prepare(self._probs, self.M, self.run_type, self.ws,
                                             self.ws.numel(), waves=waves, row_blocks=row_blocks)
 
@@ -137,7 +146,11 @@ class Stack:
 
     def gemv(self):
         from ternary_weight_amd import tq
-        tq.gemv_grouped_run(self.plan)
+        (tq.gemm_grouped_run if self.prefill else tq.gemv_grouped_run)(self.plan)
+
+    def ops(self) -> int:
+        """Algorithmic operations of the product: 2 M N Kin per plane (multiply-add counted as two)."""
+        return sum(2 * self.M * n * kin * self.case.planes for (_, _, _, n, kin) in self.projs)
 
     # algorithmic bytes ------------------------------------------------------
     def gemv_bytes(self) -> int:
@@ -205,10 +218,40 @@ def spot_check(stack, n_proj=3, rows=64) -> dict:
             "bit_exact" if case.x_type == I8 else "max_rel_err": exact if case.x_type == I8 else worst}
 
 
+def cpu_baseline_prefill(stack, seconds: float, tokens: int = 32) -> dict:
+    """The oracle on the host cores: the first projection of the stack for its first `tokens` tokens,
+    repeated for about `seconds`, as operations per second."""
+    import oracle
+    case = stack.case
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    orc = oracle.default()
+    layer, p, name, n, kin = stack.projs[0]
+    h = inputs.projection(case, layer, p, n, kin, M=tokens)
+    K, g, layout = case.planes, case.group, case.layout
+    ops, reps, t0 = 0, 0, time.perf_counter()
+    while True:
+        if case.x_type == I8:
+            q, s = orc.act_quant_i8(h["x"], F32)
+            orc.gemv_i8(K, g, layout, h["trits"], h["scales"], q, s, h["codebook"], nthreads=threads)
+        else:
+            orc.gemv_fp(K, g, layout, h["trits"], h["scales"], h["x"], case.x_type, h["codebook"], nthreads=threads)
+        ops += 2 * tokens * n * kin * K
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(ops / el / 1e12, 6), "unit": "TOP/s" if case.x_type == I8 else "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "projection %s of layer 0 (%d x %d, %d plane(s)) for the first %d tokens, %d repetitions, "
+                      "%.1f s; C oracle, OpenMP over output rows" % (name, n, kin, K, tokens, reps, el)}
+
+
 def cpu_baseline(stack, seconds: float) -> dict:
     """The oracle on the host cores, over whole layers of the same stack."""
     import oracle
     case, M = stack.case, stack.M
+    if stack.prefill:
+        return cpu_baseline_prefill(stack, seconds)
     threads = min(len(os.sched_getaffinity(0)), 16)
     orc = oracle.default()
     # layer 0 of the stack (its first four projections for the 8B-shaped stacks, to keep the
@@ -450,19 +493,29 @@ def main():
         gemv_avg = g0.elapsed_time(g1) / reps
 
     gbytes, qbytes = stack.gemv_bytes(), stack.quant_bytes()
-    kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
-                                                      1 if M == 1 else (4 if M <= 4 else 16))
-    value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
-    achieved = gbytes / (gemv_avg / 1e3) / 1e9
+    if stack.prefill:
+        fm_fn = (4, 8) if (case.x_type == I8 and case.layout == TENSOR and case.planes == 1) else (4, 4)
+        kernel_name = "k_gemm_grouped<%d, %d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes, *fm_fn)
+        ops = stack.ops()
+        value = ops / (ms_step / 1e3) / 1e12
+        achieved = ops / (gemv_avg / 1e3) / 1e12
+        peak = MFMA_PEAK_I8_TOPS if case.x_type == I8 else MFMA_PEAK_BF16_TFLOPS
+        unit = "TOP/s" if case.x_type == I8 else "TFLOP/s"
+    else:
+        kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
+                                                          1 if M == 1 else (4 if M <= 4 else 16))
+        value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
+        achieved = gbytes / (gemv_avg / 1e3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
 
     ceiling = hbm_ceiling() if args.ceiling else None
     check = None if args.no_check else spot_check(stack)
     cpu = None if args.no_cpu_baseline else cpu_baseline(stack, args.cpu_seconds)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_PREFILL if stack.prefill else METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -480,7 +533,9 @@ def main():
             "planes": case.planes,
             "group": case.group,
             "scale_layout": {TENSOR: "tensor", GROUP_F16: "group_f16", CODEBOOK: "codebook"}[case.layout],
-            "step": ("one grouped launch over the stack; fp32 inputs quantised per token to int8 "
+            "step": ("act-quant of every projection input + one grouped MFMA GEMM launch over the stack"
+                     if case.x_type == I8 else "one grouped MFMA GEMM launch over the stack") if stack.prefill else
+                    ("one grouped launch over the stack; fp32 inputs quantised per token to int8 "
                      "inside it (bit-identical to the separate quantiser)") if stack.fused else
                     ("act-quant of every projection input + one grouped GEMV launch over the stack"
                      if case.x_type == I8 else "one grouped GEMV launch over the stack"),
@@ -488,17 +543,19 @@ def main():
             "grouped_waves": stack.plan.waves,
             "grouped_row_blocks": stack.plan.row_blocks,
         },
-        "tok_per_s_equiv": round(1e3 / ms_step, 1),
+        "tok_per_s_equiv": round(M * 1e3 / ms_step, 1),
         "gemv_us": round(gemv_avg * 1e3, 2),
         "roofline": {
-            "bound": "hbm",
+            "bound": "mfma" if stack.prefill else "hbm",
             "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(kernel_name),
             "kernel": kernel_name,
             "bytes_per_launch": gbytes,
+            **({"ops_per_launch": stack.ops(),
+                "effective_hbm_GBs": round(gbytes / (gemv_avg / 1e3) / 1e9, 1)} if stack.prefill else {}),
         },
         "cpu_baseline": cpu,
         "hbm_ceiling": ceiling,
