@@ -151,8 +151,8 @@ __device__ __forceinline__ void accum_lut(uint32_t w, const BfPairs& xp, float& 
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const uint32_t addr = __builtin_amdgcn_perm(w, copyoff, 0x0C0C0400u | ((4u + b) << 8));
-        const LDS_AS uint32_t* t = (const LDS_AS uint32_t*)(lut + addr);
-        const uint32_t t0 = t[0], t1 = t[1];
+        const uint64_t t = *(const LDS_AS uint64_t*)(lut + addr);
+        const uint32_t t0 = (uint32_t)t, t1 = (uint32_t)(t >> 32);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t0),
                                               __builtin_bit_cast(bf16x2_t, xp.a[b]), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t1),
@@ -171,7 +171,8 @@ __device__ __forceinline__ void fill_bf16_lut(uint8_t* lut)
             const uint32_t code = (e >> (2 * q)) & 3u;
             h[q] = code == 1u ? 0x3F80u : (code == 2u ? 0xBF80u : 0u);
         }
-        *(uint2*)(lut + e * 256 + c * 8) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *(LDS_AS uint64_t*)(lut + e * 256 + c * 8) =
+            (uint64_t)(h[0] | (h[1] << 16)) | ((uint64_t)(h[2] | (h[3] << 16)) << 32);
     }
 }
 
