@@ -238,7 +238,8 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * blocks of one problem, each split over `waves` waves; items are ordered
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
  * (0 = default: 4 waves, 1 block; with TQ_F32_Q8 1 wave, 4 blocks, so that
- * a workgroup quantises its activations once for four blocks).  Copies
+ * a workgroup quantises its activations once for four blocks; with TQ_BF16
+ * 1 wave, 16 blocks, so that 16 blocks share the workgroup's trit table).  Copies
  * host->device on `stream` and synchronizes it.
  */
 tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,

@@ -124,9 +124,9 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
     int waves = plan->waves, row_blocks = plan->row_blocks;
     const bool hinted = is_shape(waves) && is_shape(row_blocks) && waves * row_blocks <= 16;
     if (!hinted) {
-        // bf16: the trit table fills 64 KiB of LDS, so two 16-wave workgroups per compute unit
-        waves = x_type == TQ_F32_Q8 ? 1 : 4;
-        row_blocks = x_type == TQ_F32_Q8 ? 4 : (x_type == TQ_BF16 ? 4 : 1);
+        // bf16: the trit table fills 64 KiB of LDS, so 16 one-wave row blocks share it
+        waves = (x_type == TQ_F32_Q8 || x_type == TQ_BF16) ? 1 : 4;
+        row_blocks = x_type == TQ_F32_Q8 ? 4 : (x_type == TQ_BF16 ? 16 : 1);
     }
     size_t need = 0;
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);

@@ -52,6 +52,9 @@ namespace tqk {
 #ifndef TQ_DEPTH_KN
 #define TQ_DEPTH_KN 1         // chunks in flight per wave, several planes
 #endif
+#ifndef TQ_DEPTH_BF16
+#define TQ_DEPTH_BF16 2       // chunks in flight per wave, bf16 activations (table decode)
+#endif
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -251,7 +254,7 @@ struct RowBlock {
     using A = typename AccT<XT>::type;
     static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     // chunks in flight per wave (codes of K planes each)
-    static constexpr int D = MT > 1 ? 1 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN);
+    static constexpr int D = MT > 1 ? 1 : (XT == TQ_BF16 ? TQ_DEPTH_BF16 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN));
     static_assert(XT != TQ_BF16 || sizeof(typename AccT<XT>::type) == 4, "bf16 accumulates in fp32");
     // activations are prefetched a chunk ahead for one token (SGPR budget)
     static constexpr bool kXPre = MT == 1 && (XT == TQ_I8 || XT == TQ_F32_Q8);
