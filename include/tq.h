@@ -165,7 +165,9 @@ tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count,
 
 /*
  * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
- * scale per group).
+ * scale per group).  With TQ_BF16 and M >= 8 (and x 16-byte aligned) the
+ * product runs on the matrix cores instead, as tq_gemm does; the results meet
+ * the same bound.
  *   x         device [M][Kin] of x_type
  *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else unused
  *             (TQ_F32_Q8 computes the per-token scales itself)
@@ -187,9 +189,10 @@ tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_t M, int32
  * once when the group ends).  Same arguments and results as tq_gemv, with:
  *   x_type    TQ_I8 (int8 MFMA, int32 accumulate) or TQ_BF16 (bf16 MFMA,
  *             fp32 accumulate); TQ_F32 and TQ_F32_Q8 are TQ_ERR_UNSUPPORTED
- *   layout    TQ_SCALE_TENSOR, or TQ_SCALE_GROUP_F16 with g a multiple of the
- *             MFMA step (64 columns for TQ_I8, 32 for TQ_BF16); TQ_SCALE_CODEBOOK
- *             is TQ_ERR_UNSUPPORTED
+ *   layout    TQ_I8: TQ_SCALE_TENSOR, or TQ_SCALE_GROUP_F16 with g a multiple of
+ *             the 64-column int8 MFMA step.  TQ_BF16: every layout and group
+ *             size (32-column steps where g allows, else 16-column steps, one
+ *             per group of 16).  Other combinations are TQ_ERR_UNSUPPORTED.
  *   x         device, 16-byte aligned (rows are read 16 bytes at a time)
  *   M         0 .. 2^24
  * TQ_I8 with TQ_SCALE_TENSOR and K = 1 is bit exact, as in tq_gemv:
@@ -233,7 +236,9 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
 
 /*
  * Validate the problems, write their descriptor table and the work list into
- * `workspace` (device, caller-owned) and fill `plan`.  The run is one launch
+ * `workspace` (device, caller-owned) and fill `plan`.  With TQ_BF16, M >= 8
+ * and every x 16-byte aligned the plan is a matrix-core plan (as from
+ * tq_gemm_grouped_prepare; the shape hints are then unused).  The run is one launch
  * with one workgroup per item, an item being `row_blocks` consecutive 64-row
  * blocks of one problem, each split over `waves` waves; items are ordered
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
@@ -252,9 +257,9 @@ tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);
 /*
  * Many prefill products (tq_gemm) in one launch, e.g. every projection of a
  * layer stack.  All problems must share K, scale layout and x_type; M is
- * common.  The work list holds one item per 32 FM x 32 FN output tile (128 x
- * 256 for TQ_I8 with one plane and a per-tensor scale, else 128 x 128), longest
- * problems first.  The plan is the decode one's struct: on return waves = 4
+ * common.  The work list holds one item per output tile (128 tokens x 256 rows
+ * for TQ_I8 with one plane and a per-tensor scale, 16 x 256 for TQ_BF16 with
+ * M <= 16, else 128 x 128), longest problems first.  The plan is the decode one's struct: on return waves = 4
  * and row_blocks = 64-row blocks per tile; tq_gemv_grouped_run refuses it.
  */
 tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,

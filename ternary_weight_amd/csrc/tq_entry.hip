@@ -90,7 +90,11 @@ TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_
     if ((s = tq_check_call(L, blob, M, x_type, x, x_scale, y, acc, TQ_MAX_M_GEMV))) return s;
     if (M == 0 || L.N == 0) return tq_ok();
     const tq_prob_dev P = tq_make_prob(L, blob, M, x, x_scale, y, acc);
-    if ((s = tq_gemv_launch_single(L, P, x_type, (hipStream_t)stream))) return s;
+    if (tq_gemv_uses_mfma(x_type, M, x))
+        s = tq_gemm_launch(L, P, x_type, (hipStream_t)stream);
+    else
+        s = tq_gemv_launch_single(L, P, x_type, (hipStream_t)stream);
+    if (s) return s;
     return tq_ok();
 }
 
@@ -131,6 +135,10 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
     size_t need = 0;
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
     if (s) return s;
+    // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte loads
+    bool mfma = count > 0;
+    for (int32_t i = 0; i < count; ++i) mfma = mfma && tq_gemv_uses_mfma(x_type, M, problems[i].x);
+    if (mfma) return tq_gemm_grouped_prepare(problems, count, M, x_type, workspace, workspace_bytes, plan, stream);
     if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
     if (workspace_bytes < need)
         return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -213,6 +221,7 @@ TQ_EXPORT tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* strea
     if ((s = tq_check_ptr(plan->workspace, "plan workspace", false))) return s;
     if (plan->n_items < 0 || plan->n_items > (1ll << 31) - 1 || plan->n_problems < 1)
         return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
+    if (plan->family >= 1000) return tq_gemm_grouped_run(plan, stream);   // matrix-core plan
     if (plan->x_lds_bytes < 0 || plan->x_lds_bytes > TQ_MAX_Q8_LDS)
         return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
     if ((s = tq_gemv_launch_grouped(plan->family, plan->waves, plan->row_blocks, plan->workspace,

@@ -12,49 +12,72 @@ namespace {
 constexpr int64_t kMaxM = 1 << 24;
 constexpr int kFamilyBase = 1000;   // grouped plans of tq_gemm carry family >= this
 
-// Kernel for (x_type, layout, K, g), or null with the reason recorded.
-const tq_gemm_kernel* gemm_kernel(const tq_layout& L, int x_type)
+int gemm_row(const tq_layout& L, int x_type)
+{
+    if (L.layout == TQ_SCALE_TENSOR) return TQ_GEMM_ROW_TENSOR;
+    if (L.layout == TQ_SCALE_CODEBOOK) return TQ_GEMM_ROW_CODEBOOK;
+    if (x_type == TQ_BF16 && L.g % 32 != 0) return TQ_GEMM_ROW_GROUP16;
+    return TQ_GEMM_ROW_GROUP;
+}
+
+// Kernel tables: 0 int8, 1 bf16, 2 bf16 with at most 16 tokens.
+int table_index(int x_type, int64_t M) { return x_type == TQ_I8 ? 0 : (M <= TQ_MAX_M_GEMV ? 2 : 1); }
+
+const tq_gemm_kernel (*gemm_table(int index))[4]
+{
+    return index == 0 ? tq_gemm_table_i8() : (index == 1 ? tq_gemm_table_bf16() : tq_gemm_table_bf16_skinny());
+}
+
+// Kernel for (x_type, layout, K, g, M), or null with the reason recorded.
+const tq_gemm_kernel* gemm_kernel(const tq_layout& L, int x_type, int64_t M)
 {
     if (x_type != TQ_I8 && x_type != TQ_BF16) {
         tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm takes TQ_I8 or TQ_BF16 activations (got %d)", x_type);
         return nullptr;
     }
-    if (L.layout == TQ_SCALE_CODEBOOK) {
-        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: TQ_SCALE_CODEBOOK is decode-only (tq_gemv)");
+    const tq_gemm_kernel* k = &gemm_table(table_index(x_type, M))[gemm_row(L, x_type)][L.K - 1];
+    if (!k->single || (L.layout != TQ_SCALE_TENSOR && L.g % k->step != 0)) {
+        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: no matrix-core kernel for this scale layout and group size %d "
+                "with x_type %d (int8 steps are 64 columns)", L.g, x_type);
         return nullptr;
     }
-    const int step = x_type == TQ_I8 ? 64 : 32;   // columns per MFMA step
-    if (L.layout == TQ_SCALE_GROUP_F16 && L.g % step != 0) {
-        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: group size %d below the %d-column MFMA step of this x_type",
-                L.g, step);
-        return nullptr;
-    }
-    const tq_gemm_kernel (*t)[4] = x_type == TQ_I8 ? tq_gemm_table_i8() : tq_gemm_table_bf16();
-    return &t[L.layout == TQ_SCALE_GROUP_F16 ? 1 : 0][L.K - 1];
+    return k;
 }
 
-int gemm_family(const tq_layout& L, int x_type)
+int gemm_family(const tq_layout& L, int x_type, int64_t M)
 {
-    return kFamilyBase + (((x_type == TQ_BF16 ? 1 : 0) * 2 + (L.layout == TQ_SCALE_GROUP_F16 ? 1 : 0)) * 4 + L.K - 1);
+    return kFamilyBase + (table_index(x_type, M) * TQ_GEMM_ROWS + gemm_row(L, x_type)) * 4 + L.K - 1;
 }
 
 const tq_gemm_kernel* kernel_of_family(int family)
 {
     const int f = family - kFamilyBase;
-    if (f < 0 || f >= 16) return nullptr;
-    const tq_gemm_kernel (*t)[4] = (f >> 3) ? tq_gemm_table_bf16() : tq_gemm_table_i8();
-    return &t[(f >> 2) & 1][f & 3];
+    if (f < 0 || f >= 3 * TQ_GEMM_ROWS * 4) return nullptr;
+    const tq_gemm_kernel* k = &gemm_table(f / (TQ_GEMM_ROWS * 4))[(f / 4) % TQ_GEMM_ROWS][f % 4];
+    return k->single ? k : nullptr;
 }
 
 int64_t tiles_of(const tq_gemm_kernel& k, int64_t M, int64_t N, int64_t* tiles_m)
 {
-    const int64_t tm = (M + 32 * k.fm - 1) / (32 * k.fm);
-    const int64_t tn = (N + 32 * k.fn - 1) / (32 * k.fn);
+    const int64_t rows_m = 16 * k.fm * k.wm, rows_n = 16 * k.fn * (4 / k.wm);
+    const int64_t tm = (M + rows_m - 1) / rows_m;
+    const int64_t tn = (N + rows_n - 1) / rows_n;
     if (tiles_m) *tiles_m = tm;
     return tm * tn;
 }
 
 }  // namespace
+
+tq_status tq_gemm_launch(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
+{
+    const tq_gemm_kernel* k = gemm_kernel(L, x_type, P.M);
+    if (!k) return TQ_ERR_UNSUPPORTED;
+    int64_t tiles_m = 0;
+    const int64_t tiles = tiles_of(*k, P.M, L.N, &tiles_m);
+    if (tiles > INT32_MAX) return tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: %lld tiles exceed one launch", (long long)tiles);
+    hipLaunchKernelGGL(k->single, dim3((unsigned)tiles), dim3(256), 0, stream, P, (int)tiles_m);
+    return tq_check_launch("tq_gemm");
+}
 
 TQ_EXPORT tq_status tq_gemm(const tq_weight_desc* desc, const void* blob, int64_t M, int32_t x_type,
                             const void* x, const float* x_scale, float* y, int32_t* acc, void* stream)
@@ -63,15 +86,10 @@ TQ_EXPORT tq_status tq_gemm(const tq_weight_desc* desc, const void* blob, int64_
     tq_status s = tq_check_desc(desc, &L);
     if (s) return s;
     if ((s = tq_check_call(L, blob, M, x_type, x, x_scale, y, acc, kMaxM, 16))) return s;
-    const tq_gemm_kernel* k = gemm_kernel(L, x_type);
-    if (!k) return TQ_ERR_UNSUPPORTED;
+    if (!gemm_kernel(L, x_type, M)) return TQ_ERR_UNSUPPORTED;
     if (M == 0 || L.N == 0) return tq_ok();
-    int64_t tiles_m = 0;
-    const int64_t tiles = tiles_of(*k, M, L.N, &tiles_m);
-    if (tiles > INT32_MAX) return tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: %lld tiles exceed one launch", (long long)tiles);
     const tq_prob_dev P = tq_make_prob(L, blob, M, x, x_scale, y, acc);
-    hipLaunchKernelGGL(k->single, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream, P, (int)tiles_m);
-    if ((s = tq_check_launch("tq_gemm"))) return s;
+    if ((s = tq_gemm_launch(L, P, x_type, (hipStream_t)stream))) return s;
     return tq_ok();
 }
 
@@ -87,7 +105,7 @@ TQ_EXPORT tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, i
         tq_layout L;
         tq_status s = tq_check_desc(problems[i].desc, &L);
         if (s) return tq_fail_problem(s, i);
-        const tq_gemm_kernel* k = gemm_kernel(L, x_type);
+        const tq_gemm_kernel* k = gemm_kernel(L, x_type, M);
         if (!k) return tq_fail_problem(TQ_ERR_UNSUPPORTED, i);
         items += tiles_of(*k, M, L.N, nullptr);
     }
@@ -119,11 +137,11 @@ TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t 
         tq_check_desc(pr.desc, &L);
         if ((s = tq_check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, kMaxM, 16)))
             return tq_fail_problem(s, i);
-        const tq_gemm_kernel* k = gemm_kernel(L, x_type);
+        const tq_gemm_kernel* k = gemm_kernel(L, x_type, M);
         if (i == 0) {
-            family = gemm_family(L, x_type);
+            family = gemm_family(L, x_type, M);
             k0 = k;
-        } else if (gemm_family(L, x_type) != family) {
+        } else if (gemm_family(L, x_type, M) != family) {
             return tq_fail(TQ_ERR_UNSUPPORTED,
                            "problem %d: all problems of a plan must share planes, layout and x_type", i);
         }
@@ -154,7 +172,7 @@ TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t 
     plan->x_type = x_type;
     plan->M = (int32_t)M;
     plan->waves = 4;
-    plan->row_blocks = k0 ? k0->fn / 2 : 0;
+    plan->row_blocks = k0 ? k0->fn * (4 / k0->wm) / 4 : 0;
     plan->n_problems = count;
     return tq_ok();
 }

@@ -12,14 +12,17 @@
 // per-tensor scale is applied once at the very end (QORA-LLM-2B page,
 // "Ternary GEMV (No Multiplication)").
 //
-// Mapping onto CDNA4.  A workgroup is 2 x 2 waves; a wave owns FM x FN tiles
-// of 16 x 16 outputs (16 FM tokens by 16 FN weight rows).  Per step a wave
+// Mapping onto CDNA4.  A workgroup is 4 waves, 2 x 2 (tokens x weight rows)
+// for prefill or 1 x 4 for a few tokens; a wave owns FM x FN tiles of
+// 16 x 16 outputs (16 FM tokens by 16 FN weight rows).  Per step a wave
 // loads, for each token tile, 16 bytes per lane of x (row = lane % 16, the
 // lane group q = lane / 16 takes one quarter of the step's columns) and, for
 // each weight tile, one dword of codes per lane: in the blob (tq_layout.h) a
 // dword is 16 consecutive columns of one row, exactly the quarter-step of the
 // int8 MFMA v_mfma_i32_16x16x64_i8 (64 columns per step), or a half dword for
-// the bf16 MFMA v_mfma_f32_16x16x32_bf16 (32 columns per step).  Each decoded
+// the bf16 MFMA v_mfma_f32_16x16x32_bf16 (32 columns per step), or a quarter
+// dword for v_mfma_f32_16x16x16_bf16 (16 columns per step: one group of the
+// d = 3 codec, whose scale is applied after each step).  Each decoded
 // weight tile is reused by the FM token tiles, each token tile by the FN
 // weight tiles.  x is read straight from global memory (the workgroup's other
 // waves and neighbouring workgroups hit it in L1/L2); there is no LDS.
@@ -40,27 +43,36 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 2 x 2 waves
 
-template <int XT>
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The MFMA of one step of KS columns for activation type XT: operand
+// fragments (16 tokens or 16 weight rows by KS columns, KS / 4 columns per
+// lane group), partial-sum type, and the decode of the lane's columns from
+// its dword of codes.
+template <int XT, int KS>
 struct Mfma;
 
 template <>
-struct Mfma<TQ_I8> {
-    static constexpr int kStep = 64;        // columns per MFMA
+struct Mfma<TQ_I8, 64> {
+    using Frag = u32x4;
     using Part = i32x4;
-    static __device__ __forceinline__ Part run(u32x4 a, u32x4 b, Part c)
+    static __device__ __forceinline__ Part run(Frag a, Frag b, Part c)
     {
         return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
                                                      c, 0, 0, 0);
     }
     // int8 trits of the lane's 16 columns: the whole dword
-    static __device__ __forceinline__ u32x4 decode(uint32_t w, int /*half*/)
+    static __device__ __forceinline__ Frag decode(uint32_t w, int /*q*/)
     {
         uint32_t t[4];
         decode_i8(w, t);
-        return u32x4{t[0], t[1], t[2], t[3]};
+        return Frag{t[0], t[1], t[2], t[3]};
     }
-    // the decoded trits are exactly +-1
-    static constexpr float kScale = 1.0f;
+    // lane group q reads dword q of the step's 64-column chunk
+    static __device__ __forceinline__ int chunk(int ks) { return ks; }
+    static __device__ __forceinline__ int dword(int /*ks*/, int q) { return q; }
+    static constexpr float kScale = 1.0f;   // the decoded trits are exactly +-1
 };
 
 // Two bf16 values {0, +2, -2} from the codes in bytes `b` and `b + 1` of a
@@ -77,32 +89,67 @@ __device__ __forceinline__ uint32_t bf16_pair(uint32_t f)
 }
 
 template <>
-struct Mfma<TQ_BF16> {
-    static constexpr int kStep = 32;
+struct Mfma<TQ_BF16, 32> {
+    using Frag = u32x4;
     using Part = f32x4;
-    static __device__ __forceinline__ Part run(u32x4 a, u32x4 b, Part c)
+    static __device__ __forceinline__ Part run(Frag a, Frag b, Part c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        c, 0, 0, 0);
     }
-    // bf16 trits (times 2) of 8 consecutive columns: half `half` of the dword
-    // (columns 8 half .. 8 half + 7 = fields 2 half and 2 half + 1)
-    static __device__ __forceinline__ u32x4 decode(uint32_t w, int half)
+    // bf16 trits (times 2) of 8 consecutive columns: half q & 1 of the dword
+    // (columns 8h .. 8h + 7 = fields 2h and 2h + 1)
+    static __device__ __forceinline__ Frag decode(uint32_t w, int q)
     {
+        const int half = q & 1;
         const uint32_t lo = (w >> (4 * half)) & 0x03030303u;        // columns 8h + b
         const uint32_t hi = (w >> (4 * half + 2)) & 0x03030303u;    // columns 8h + 4 + b
-        return u32x4{bf16_pair<0>(lo), bf16_pair<2>(lo), bf16_pair<0>(hi), bf16_pair<2>(hi)};
+        return Frag{bf16_pair<0>(lo), bf16_pair<2>(lo), bf16_pair<0>(hi), bf16_pair<2>(hi)};
     }
+    static __device__ __forceinline__ int chunk(int ks) { return ks >> 1; }
+    static __device__ __forceinline__ int dword(int ks, int q) { return 2 * (ks & 1) + (q >> 1); }
     static constexpr float kScale = 0.5f;   // undo the factor 2 of the decoded values
 };
 
-// One workgroup tile (32 FM tokens x 32 FN weight rows) of one problem.
-template <int XT, int LAYOUT, int K, int FM, int FN>
-__device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
+// 16 columns per step: one dword of codes, lane group q taking field q
+// (columns 4q .. 4q + 3).  A step is exactly one group of 16, the group size
+// of the d = 3 codec.
+template <>
+struct Mfma<TQ_BF16, 16> {
+    using Frag = u32x2;
+    using Part = f32x4;
+    static __device__ __forceinline__ Part run(Frag a, Frag b, Part c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                         c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ Frag decode(uint32_t w, int q)
+    {
+        const uint32_t f = (w >> (2 * q)) & 0x03030303u;            // columns 4q + b
+        return Frag{bf16_pair<0>(f), bf16_pair<2>(f)};
+    }
+    static __device__ __forceinline__ int chunk(int ks) { return ks >> 2; }
+    static __device__ __forceinline__ int dword(int ks, int /*q*/) { return ks & 3; }
+    static constexpr float kScale = 0.5f;
+};
+
+template <typename F>
+__device__ __forceinline__ F zero_frag()
 {
-    using MF = Mfma<XT>;
+    F z;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(F) / 4); ++i) z[i] = 0u;
+    return z;
+}
+
+// One workgroup tile of one problem: WM x (4 / WM) waves, each with FM x FN
+// tiles of 16 x 16, so 16 FM WM tokens by 16 FN (4 / WM) weight rows.
+template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
+__device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, const LDS_AS float* cb_lds)
+{
+    using MF = Mfma<XT, KS>;
     using Part = typename MF::Part;
-    constexpr int KS = MF::kStep;
+    using Frag = typename MF::Frag;
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
     // int8, one plane, per-tensor scale: the int32 sum is the result
@@ -112,8 +159,9 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
     const int r = lane & 15, q = lane >> 4;
     const int M = P.M, N = P.N, Kin = P.Kin, NC = P.NC;
     const int NB = (N + 63) >> 6;
-    const int m0 = tm * (32 * FM) + (wave & 1) * (16 * FM);
-    const int n0 = tn * (32 * FN) + (wave >> 1) * (16 * FN);
+    static_assert(WM == 1 || WM == 2, "waves along the tokens");
+    const int m0 = tm * (16 * FM * WM) + (wave % WM) * (16 * FM);
+    const int n0 = tn * (16 * FN * (4 / WM)) + (wave / WM) * (16 * FN);
 
     // x rows of the lane (rows past M repeat row M - 1; their results are not stored)
     const uint8_t* xrow[FM];
@@ -148,31 +196,55 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
             if (!kDirect) acc[kDirect ? 0 : fm][kDirect ? 0 : fn] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    auto load = [&](int seg, int k, int j, u32x4 (&a)[FM], uint32_t (&w)[FN]) {
+    // the scale word of a (segment, plane) block: two f16 group scales, or six
+    // 5-bit codebook indices; fetched with the block's first step
+    constexpr bool kWord = !kDirect && LAYOUT != TQ_SCALE_TENSOR;
+    const uint8_t* srow[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + 16 * fn + r;
+        const int rb = min(n >> 6, NB - 1);
+        srow[fn] = P.scales + (LAYOUT == TQ_SCALE_CODEBOOK ? ((int64_t)rb * P.NID * 64 + (n & 63)) * 4
+                                                           : ((int64_t)rb * P.NGD * K * 64 + (n & 63)) * 4);
+    }
+    auto load_word = [&](int seg, int k, uint32_t (&sw)[FN]) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            sw[fn] = *(const GLOBAL_AS uint32_t*)(srow[fn] + (LAYOUT == TQ_SCALE_CODEBOOK
+                                                                  ? (int64_t)(seg / 6) * 256
+                                                                  : ((int64_t)(seg >> 1) * K + k) * 256));
+    };
+
+    auto load = [&](int seg, int k, int j, Frag (&a)[FM], uint32_t (&w)[FN]) {
         const int ks = seg * seg_steps + j;                     // MFMA step along the row
         const int col = ks * KS;
         const bool in = col + q * QCOLS < Kin;                  // Kin % 16 == 0: all or nothing
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            a[fm] = in ? *(const GLOBAL_AS u32x4*)(xrow[fm] + (int64_t)col * ESZ) : u32x4{0u, 0u, 0u, 0u};
-        const int c = XT == TQ_I8 ? ks : ks >> 1;               // 64-column chunk
-        const int dw = XT == TQ_I8 ? q : 2 * (ks & 1) + (q >> 1);
+            a[fm] = in ? *(const GLOBAL_AS Frag*)(xrow[fm] + (int64_t)col * ESZ) : zero_frag<Frag>();
+        const int c = MF::chunk(ks);                            // 64-column chunk
+        const int dw = MF::dword(ks, q);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             w[fn] = *(const GLOBAL_AS uint32_t*)(crow[fn] + ((int64_t)c * K + k) * 1024 + dw * 4);
     };
 
-    u32x4 a_nxt[FM];
-    uint32_t w_nxt[FN];
+    Frag a_nxt[FM];
+    uint32_t w_nxt[FN], sw_nxt[FN], sw[FN];
     int seg = 0, k = 0, j = 0;
     load(0, 0, 0, a_nxt, w_nxt);
+    if (kWord) load_word(0, 0, sw_nxt);
     for (int t = 0; t < total; ++t) {
-        u32x4 a[FM];
+        Frag a[FM];
         uint32_t w[FN];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) a[fm] = a_nxt[fm];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) w[fn] = w_nxt[fn];
+        if (kWord && j == 0) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) sw[fn] = sw_nxt[fn];
+        }
         const int cseg = seg, ck = k, cj = j;
         if (++j == seg_steps) {
             j = 0;
@@ -181,7 +253,10 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
                 ++seg;
             }
         }
-        if (t + 1 < total) load(seg, k, j, a_nxt, w_nxt);
+        if (t + 1 < total) {
+            load(seg, k, j, a_nxt, w_nxt);
+            if (kWord && j == 0) load_word(seg, k, sw_nxt);
+        }
 
         // scales of this (segment, plane) for the lane's weight rows
         float sc[FN];
@@ -190,20 +265,23 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
             for (int fn = 0; fn < FN; ++fn) {
                 if (LAYOUT == TQ_SCALE_TENSOR) {
                     sc[fn] = ld_uniform(((const float*)P.scales) + ck) * MF::kScale;
+                } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
+                    // digit plane ck weighs 3^(K-1-ck); the group's scale is cb[idx[n][group]]
+                    const uint32_t idx = (sw[fn] >> (5 * (cseg % 6))) & 31u;
+                    float wgt = 1.0f;
+#pragma unroll
+                    for (int i = 1; i < K; ++i)
+                        if (i < K - ck) wgt *= 3.0f;
+                    sc[fn] = cb_lds[idx] * (wgt * MF::kScale);
                 } else {
-                    const int n = n0 + 16 * fn + r;
-                    const int rb = min(n >> 6, NB - 1);
-                    const uint32_t word = *(const GLOBAL_AS uint32_t*)(P.scales +
-                        ((((int64_t)rb * P.NGD + (cseg >> 1)) * K + ck) * 64 + (n & 63)) * 4);
-                    sc[fn] = f16_to_f32((cseg & 1) ? (word >> 16) : (word & 0xFFFFu)) * MF::kScale;
+                    sc[fn] = f16_to_f32((cseg & 1) ? (sw[fn] >> 16) : (sw[fn] & 0xFFFFu)) * MF::kScale;
                 }
             }
         }
 
-        const int half = XT == TQ_I8 ? 0 : (q & 1);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const u32x4 b = MF::decode(w[fn], half);
+            const Frag b = MF::decode(w[fn], q);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, part[fm][fn]);
         }
@@ -223,8 +301,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
     }
 
     // epilogue: lane holds weight row n = n0 + 16 fn + r of tokens m0 + 16 fm + 4 q + e
-    float sw = 0.0f;
-    if (kDirect) sw = ld_uniform((const float*)P.scales);
+    float s_w = 0.0f;
+    if (kDirect) s_w = ld_uniform((const float*)P.scales);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -233,7 +311,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
             if (m >= M) continue;
             float xs = 1.0f;
             if (XT == TQ_I8) xs = P.x_scale[m];
-            const float cm = kDirect ? sw * xs : xs;   // fl32(s_w * x_scale[m]), one rounding
+            const float cm = kDirect ? s_w * xs : xs;   // fl32(s_w * x_scale[m]), one rounding
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int n = n0 + 16 * fn + r;
@@ -252,21 +330,34 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn)
     }
 }
 
-template <int XT, int LAYOUT, int K, int FM, int FN>
+// The codebook as fp32 in LDS (codec layout only).
+template <int LAYOUT>
+__device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_lds)
+{
+    if (LAYOUT != TQ_SCALE_CODEBOOK) return;
+    if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+    __syncthreads();
+}
+
+template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
 __global__ __launch_bounds__(kThreads) void k_gemm_single(tq_prob_dev P, int tiles_m)
 {
+    __shared__ float cb_lds[TQ_CB_SLOTS];
+    stage_codebook<LAYOUT>(P, cb_lds);
     const int tile = blockIdx.x;
-    gemm_tile<XT, LAYOUT, K, FM, FN>(P, tile % tiles_m, tile / tiles_m);
+    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, tile % tiles_m, tile / tiles_m, (const LDS_AS float*)cb_lds);
 }
 
 // Grouped: item i = (problem, tile); tiles of a problem run token-tile fastest.
-template <int XT, int LAYOUT, int K, int FM, int FN>
+template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
 __global__ __launch_bounds__(kThreads) void k_gemm_grouped(const tq_prob_dev* probs, const int2* items)
 {
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
-    const int tiles_m = (P.M + 32 * FM - 1) / (32 * FM);
-    gemm_tile<XT, LAYOUT, K, FM, FN>(P, it.y % tiles_m, it.y / tiles_m);
+    __shared__ float cb_lds[TQ_CB_SLOTS];
+    stage_codebook<LAYOUT>(P, cb_lds);
+    const int tiles_m = (P.M + 16 * FM * WM - 1) / (16 * FM * WM);
+    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, it.y % tiles_m, it.y / tiles_m, (const LDS_AS float*)cb_lds);
 }
 
 }  // namespace tqm

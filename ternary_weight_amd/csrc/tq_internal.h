@@ -50,6 +50,18 @@ tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const 
 // Prefix the thread's last error message with a problem index.
 tq_status tq_fail_problem(tq_status s, int32_t i);
 
+// bf16 decode with at least this many tokens runs on the matrix cores (the
+// prefill kernels' one-tile variant) when x is 16-byte aligned.
+#ifndef TQ_BF16_MFMA_MIN_M
+#define TQ_BF16_MFMA_MIN_M 8
+#endif
+static inline bool tq_gemv_uses_mfma(int x_type, int64_t M, const void* x)
+{
+    return x_type == TQ_BF16 && M >= TQ_BF16_MFMA_MIN_M && ((uintptr_t)x & 15) == 0;
+}
+// Matrix-core launch of one problem (tq_gemm.hip); the arguments are checked.
+tq_status tq_gemm_launch(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream);
+
 // Decode launch shared by tq_gemv and tq_gemv_grouped_run (tq_gemv.hip).
 tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type,
                                 hipStream_t stream);

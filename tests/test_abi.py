@@ -135,7 +135,7 @@ def test_gemm_rejects_unsupported_before_device_work():
     g32 = tq.desc(2, 32, tq.SCALE_GROUP_F16, 64, 64)      # below the int8 MFMA step of 64 columns
     assert L.tq_gemm(ctypes.byref(g32), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
     cb = tq.desc(3, 16, tq.SCALE_CODEBOOK, 64, 64, n_codebook=27)
-    assert L.tq_gemm(ctypes.byref(cb), good, 64, tq.BF16, good, None, good, None, None) == tq.ERR_UNSUPPORTED
+    assert L.tq_gemm(ctypes.byref(cb), good, 64, tq.I8, good, good, good, None, None) == tq.ERR_UNSUPPORTED
     d = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 64)
     for xt in (tq.F32, tq.F32_Q8):
         assert L.tq_gemm(ctypes.byref(d), good, 64, xt, good, None, good, None, None) == tq.ERR_UNSUPPORTED
@@ -162,8 +162,11 @@ def test_gemm_grouped_validation():
     assert e.value.status == tq.ERR_UNSUPPORTED
     plan = tq.tq_grouped_plan(workspace=good, n_items=3, family=5, n_problems=1)
     assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a decode family
-    plan.family = 1000
-    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a prefill family
+    plan.family = 1000 + 3 * 4 * 4                                                 # past the last family
+    assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    plan.family = 1000 + 2 * 4 + 0                                                 # int8 with groups of 16: none
+    assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
 
 
 def test_fused_int8_activation_limits():
@@ -197,9 +200,10 @@ def test_act_quant_batch_validation():
 def test_grouped_shape_must_fit_the_workgroup_lds():
     # bf16 decode keeps a 64 KiB trit table in LDS; 16 split waves of a
     # 4-plane, 16-token per-tensor problem would add 256 KiB of partial sums
+    # (x only 4-byte aligned keeps the vector-ALU kernels, which the shape hints are for)
     d = tq.desc(4, 0, tq.SCALE_TENSOR, 64, 256)
     good = 0x60000
-    probs = tq.problems([(d, good, good, None, good, None)])
+    probs = tq.problems([(d, good, good + 4, None, good, None)])
     n = tq.gemv_grouped_workspace_size(probs, 16)
     with pytest.raises(tq.TQError) as e:
         tq.gemv_grouped_prepare(probs, 16, tq.BF16, good, n, waves=16, row_blocks=1, stream=0)

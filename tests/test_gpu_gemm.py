@@ -71,16 +71,18 @@ def test_gemm_i8_other_layouts(K, g, layout):
 
 @pytest.mark.parametrize("K,g,layout", [
     (1, 0, TENSOR), (3, 0, TENSOR), (1, 32, GROUP_F16), (3, 256, GROUP_F16), (2, 64, GROUP_F16),
-    (4, 128, GROUP_F16), (3, 32, GROUP_F16),
+    (4, 128, GROUP_F16), (3, 32, GROUP_F16), (2, 16, GROUP_F16), (3, 16, CODEBOOK), (3, 32, CODEBOOK),
+    (2, 64, CODEBOOK), (1, 16, CODEBOOK),
 ])
-@pytest.mark.parametrize("N,Kin,M", [(200, 768, 140), (64, 256, 1), (300, 1280, 37)])
+@pytest.mark.parametrize("N,Kin,M", [(200, 768, 140), (64, 256, 1), (300, 1280, 37), (130, 512, 16), (70, 512, 5)])
 def test_gemm_bf16(K, g, layout, N, Kin, M):
+    # M <= 16 runs the one-tile (1 x 4 waves) kernels, larger M the 2 x 2 ones
     rng = np.random.default_rng(K * 1000 + g + N + M)
-    trits, scales, _ = rand_problem(K, g, layout, N, Kin, rng)
-    d, blob = pack(K, g, layout, trits, scales)
+    trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
+    d, blob = pack(K, g, layout, trits, scales, cb)
     x = rand_x(M, Kin, BF16, rng)
     y = gemv(d, blob, BF16, x, gemm=True)
-    ref = oracle.gemv_fp(K, g, layout, trits, scales, x, BF16)
+    ref = oracle.gemv_fp(K, g, layout, trits, scales, x, BF16, cb)
     err = rel_err(y, ref)
     assert err <= TOL, err
     assert err <= 1e-5          # fp32 accumulation is far inside the bar
@@ -134,15 +136,14 @@ def test_gemm_unsupported_and_empty():
     t = torch()
     trits, scales, cb = rand_problem(3, 16, CODEBOOK, 64, 64)
     d, blob = pack(3, 16, CODEBOOK, trits, scales, cb)
-    x = dev(rand_x(4, 64, BF16))
+    xq = t.zeros((4, 64), dtype=t.int8, device="cuda")
+    xs = t.ones(4, dtype=t.float32, device="cuda")
     y = t.zeros((4, 64), dtype=t.float32, device="cuda")
     with pytest.raises(tq.TQError) as e:
-        tq.gemm(d, blob, 4, BF16, x, None, y)
+        tq.gemm(d, blob, 4, I8, xq, xs, y)           # the codec's groups of 16 are below the int8 step
     assert e.value.status == tq.ERR_UNSUPPORTED
     trits, scales, _ = rand_problem(1, 32, GROUP_F16, 64, 64)
     d, blob = pack(1, 32, GROUP_F16, trits, scales)
-    xq = t.zeros((4, 64), dtype=t.int8, device="cuda")
-    xs = t.ones(4, dtype=t.float32, device="cuda")
     with pytest.raises(tq.TQError) as e:
         tq.gemm(d, blob, 4, I8, xq, xs, y)          # g = 32 is below the int8 MFMA step
     assert e.value.status == tq.ERR_UNSUPPORTED
@@ -192,6 +193,43 @@ def test_gemm_grouped_equals_single(xt, K, g, layout):
         t.cuda.synchronize()
         for (d, blob, xd, xs, y), w in zip(keep, want):
             assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
-    # a decode plan is refused by the prefill run and the other way round
-    with pytest.raises(tq.TQError):
-        tq.gemv_grouped_run(plan)
+    # the decode run executes a matrix-core plan too (it prepares them for bf16 with several tokens)
+    for (d, blob, xd, xs, y) in keep:
+        y.fill_(float("nan"))
+    tq.gemv_grouped_run(plan)
+    t.cuda.synchronize()
+    for (d, blob, xd, xs, y), w in zip(keep, want):
+        assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
+
+
+@pytest.mark.parametrize("layout,K,g", [(CODEBOOK, 3, 16), (GROUP_F16, 3, 256), (GROUP_F16, 2, 16)])
+@pytest.mark.parametrize("M", [8, 9, 16])
+def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
+    """tq_gemv and the grouped decode plan route bf16 with several tokens to the
+    one-tile matrix-core kernels; both agree with the oracle, the grouped plan
+    bit for bit with the single call."""
+    from ternary_weight_amd import tq
+    t = torch()
+    rng = np.random.default_rng(M * 10 + g + K)
+    shapes = [(1024, 512), (320, 1024), (96, 256)]
+    keep, items, want = [], [], []
+    for (N, Kin) in shapes:
+        trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
+        d, blob = pack(K, g, layout, trits, scales, cb)
+        x = rand_x(M, Kin, BF16, rng)
+        y1 = gemv(d, blob, BF16, x)
+        assert rel_err(y1, oracle.gemv_fp(K, g, layout, trits, scales, x, BF16, cb)) <= TOL
+        xd = dev(x)
+        y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+        keep.append((d, blob, xd, y))
+        items.append((d, blob, xd, None, y, None))
+        want.append(y1)
+    probs = tq.problems(items)
+    n = tq.gemv_grouped_workspace_size(probs, M)
+    ws = t.empty(n, dtype=t.uint8, device="cuda")
+    plan = tq.gemv_grouped_prepare(probs, M, BF16, ws, n)
+    assert plan.family >= 1000                       # a matrix-core plan
+    tq.gemv_grouped_run(plan)
+    t.cuda.synchronize()
+    for (d, blob, xd, y), w in zip(keep, want):
+        assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))

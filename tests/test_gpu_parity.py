@@ -171,7 +171,7 @@ for layout in (TENSOR, GROUP_F16, CODEBOOK):
 def test_gemv_all_formats(layout, K, g, x_type):
     rng = np.random.default_rng(K * 1000 + g + 7 * layout + 31 * x_type)
     N, Kin = 192, 1024 + (256 if g <= 256 else 0)
-    for M in (1, 3, 16):
+    for M in (1, 3, 4, 16):
         trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
         d, blob = pack(K, g, layout, trits, scales, cb)
         if x_type in (I8, F32_Q8):
@@ -312,10 +312,15 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
     nbytes = tq.gemv_grouped_workspace_size(probs, M)
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
-    R = plan.row_blocks
-    assert plan.n_items == sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes)
-    if waves:
-        assert (plan.waves, plan.row_blocks) == (waves, row_blocks)
+    if plan.family >= 1000:
+        # a matrix-core plan (bf16 with several tokens): one item per 16-token x 256-row tile
+        assert x_type == BF16 and M > 1
+        assert plan.n_items == sum((N + 255) // 256 for N, _ in shapes)
+    else:
+        R = plan.row_blocks
+        assert plan.n_items == sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes)
+        if waves:
+            assert (plan.waves, plan.row_blocks) == (waves, row_blocks)
     tq.gemv_grouped_run(plan)
     t.cuda.synchronize()
     for y, r in zip(ys, refs):
