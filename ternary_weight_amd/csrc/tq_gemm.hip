@@ -41,6 +41,17 @@ const tq_gemm_kernel* gemm_kernel(const tq_layout& L, int x_type, int64_t M)
                 "with x_type %d (int8 steps are 64 columns)", L.g, x_type);
         return nullptr;
     }
+    // the kernels address x, the codes and the scales with 32-bit offsets,
+    // including the rows a partial tile reads past M and N
+    const int64_t lim = (int64_t)UINT32_MAX;
+    const int64_t xb = (M + 16 * k->fm * k->wm) * L.Kin * (x_type == TQ_I8 ? 1 : 2);
+    const int64_t cb = (L.NB + 4 * k->fn) * L.NC * L.K * 1024;
+    const int64_t sb = (L.NB + 4 * k->fn) * (L.layout == TQ_SCALE_CODEBOOK ? L.NID : L.NGD * L.K) * 256;
+    if (xb > lim || cb > lim || sb > lim) {
+        tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: an operand exceeds 4 GiB (x %lld, codes %lld bytes)", (long long)xb,
+                (long long)cb);
+        return nullptr;
+    }
     return k;
 }
 

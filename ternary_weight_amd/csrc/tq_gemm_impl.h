@@ -71,7 +71,8 @@ struct Mfma<TQ_I8, 64> {
     }
     // lane group q reads dword q of the step's 64-column chunk
     static __device__ __forceinline__ int chunk(int ks) { return ks; }
-    static __device__ __forceinline__ int dword(int /*ks*/, int q) { return q; }
+    static __device__ __forceinline__ int dword_lane(int q) { return q; }
+    static __device__ __forceinline__ int dword_step(int /*ks*/) { return 0; }
     static constexpr float kScale = 1.0f;   // the decoded trits are exactly +-1
 };
 
@@ -107,7 +108,8 @@ struct Mfma<TQ_BF16, 32> {
         return Frag{bf16_pair<0>(lo), bf16_pair<2>(lo), bf16_pair<0>(hi), bf16_pair<2>(hi)};
     }
     static __device__ __forceinline__ int chunk(int ks) { return ks >> 1; }
-    static __device__ __forceinline__ int dword(int ks, int q) { return 2 * (ks & 1) + (q >> 1); }
+    static __device__ __forceinline__ int dword_lane(int q) { return q >> 1; }
+    static __device__ __forceinline__ int dword_step(int ks) { return 2 * (ks & 1); }
     static constexpr float kScale = 0.5f;   // undo the factor 2 of the decoded values
 };
 
@@ -129,7 +131,8 @@ struct Mfma<TQ_BF16, 16> {
         return Frag{bf16_pair<0>(f), bf16_pair<2>(f)};
     }
     static __device__ __forceinline__ int chunk(int ks) { return ks >> 2; }
-    static __device__ __forceinline__ int dword(int ks, int /*q*/) { return ks & 3; }
+    static __device__ __forceinline__ int dword_lane(int /*q*/) { return 0; }
+    static __device__ __forceinline__ int dword_step(int ks) { return ks & 3; }
     static constexpr float kScale = 0.5f;
 };
 
@@ -144,6 +147,49 @@ __device__ __forceinline__ F zero_frag()
 
 // One workgroup tile of one problem: WM x (4 / WM) waves, each with FM x FN
 // tiles of 16 x 16, so 16 FM WM tokens by 16 FN (4 / WM) weight rows.
+// Loads through buffer resources: a 32-bit per-lane offset plus an SGPR
+// offset per step, no address arithmetic in the loop, and reads past the
+// resource's size return zero (rows past M, row blocks past N).  The host
+// keeps every operand of a launch below 4 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+template <typename F>
+__device__ __forceinline__ F buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ u32x4 buffer_load<u32x4>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ u32x2 buffer_load<u32x2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ uint32_t buffer_load<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Position in the step sequence: segment (a group, or the whole row for a
+// per-tensor scale), then plane, then the segment's MFMA steps.
+struct Cursor {
+    int seg, k, j;
+    __device__ __forceinline__ void advance(int seg_steps, int K)
+    {
+        if (++j == seg_steps) {
+            j = 0;
+            if (++k == K) {
+                k = 0;
+                ++seg;
+            }
+        }
+    }
+};
+
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
 __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, const LDS_AS float* cb_lds)
 {
@@ -152,8 +198,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     using Frag = typename MF::Frag;
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
+    constexpr int NBUF = 3;                               // steps in flight (loads issued 2 steps ahead)
     // int8, one plane, per-tensor scale: the int32 sum is the result
     constexpr bool kDirect = XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1;
+    // the scale word of a (segment, plane) block: two f16 group scales, or six 5-bit codebook indices
+    constexpr bool kWord = !kDirect && LAYOUT != TQ_SCALE_TENSOR;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -163,24 +212,21 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     const int m0 = tm * (16 * FM * WM) + (wave % WM) * (16 * FM);
     const int n0 = tn * (16 * FN * (4 / WM)) + (wave / WM) * (16 * FN);
 
-    // x rows of the lane (rows past M repeat row M - 1; their results are not stored)
-    const uint8_t* xrow[FM];
+    const __amdgpu_buffer_rsrc_t rx = rsrc(P.x, (int64_t)M * Kin * ESZ);
+    const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, (int64_t)NB * NC * K * 1024);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)NB * P.NID * 256
+                                                                                 : (int64_t)NB * P.NGD * K * 256);
+    uint32_t xoff[FM], coff[FN], soff[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-        const int row = min(m0 + 16 * fm + r, M - 1);
-        xrow[fm] = (const uint8_t*)P.x + ((int64_t)row * Kin + q * QCOLS) * ESZ;
-    }
-    // code slots of the lane's weight rows (rows past the last block read block 0; not stored)
-    const uint8_t* crow[FN];
+    for (int fm = 0; fm < FM; ++fm) xoff[fm] = ((uint32_t)(m0 + 16 * fm + r) * Kin + q * QCOLS) * ESZ;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-        const int n = n0 + 16 * fn + r;
-        const int rb = n >> 6;
-        crow[fn] = P.codes + (rb < NB ? ((int64_t)rb * NC * K * 64 + (n & 63)) * 16 : 0);
+        const uint32_t n = n0 + 16 * fn + r;
+        coff[fn] = ((n >> 6) * NC * K * 64 + (n & 63)) * 16 + MF::dword_lane(q) * 4;
+        soff[fn] = LAYOUT == TQ_SCALE_CODEBOOK ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4
+                                               : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
     }
 
-    // Steps: segment (group, or the whole row for a per-tensor scale), then
-    // plane, then the segment's MFMA steps.
     const int nks = (Kin + KS - 1) / KS;                       // MFMA steps per row
     const int seg_steps = LAYOUT == TQ_SCALE_TENSOR ? nks : P.g / KS;
     const int nseg = LAYOUT == TQ_SCALE_TENSOR ? 1 : Kin / P.g;
@@ -196,107 +242,91 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             if (!kDirect) acc[kDirect ? 0 : fm][kDirect ? 0 : fn] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    // the scale word of a (segment, plane) block: two f16 group scales, or six
-    // 5-bit codebook indices; fetched with the block's first step
-    constexpr bool kWord = !kDirect && LAYOUT != TQ_SCALE_TENSOR;
-    const uint8_t* srow[FN];
+    // Columns of x past Kin in a ragged last step read the next row (or zero
+    // past the end); the codes there are padding (zero trits), so they add 0.
+    Frag abuf[NBUF][FM];
+    uint32_t wbuf[NBUF][FN], swbuf[NBUF][FN];
+    auto load = [&](const Cursor& c, Frag (&a)[FM], uint32_t (&w)[FN], uint32_t (&sw)[FN]) {
+        const int ks = c.seg * seg_steps + c.j;                 // MFMA step along the row
+        const uint32_t xs = (uint32_t)ks * (KS * ESZ);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const int n = n0 + 16 * fn + r;
-        const int rb = min(n >> 6, NB - 1);
-        srow[fn] = P.scales + (LAYOUT == TQ_SCALE_CODEBOOK ? ((int64_t)rb * P.NID * 64 + (n & 63)) * 4
-                                                           : ((int64_t)rb * P.NGD * K * 64 + (n & 63)) * 4);
-    }
-    auto load_word = [&](int seg, int k, uint32_t (&sw)[FN]) {
+        for (int fm = 0; fm < FM; ++fm) a[fm] = buffer_load<Frag>(rx, xoff[fm], xs);
+        const uint32_t cs = ((uint32_t)MF::chunk(ks) * K + c.k) * 1024 + MF::dword_step(ks) * 4;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            sw[fn] = *(const GLOBAL_AS uint32_t*)(srow[fn] + (LAYOUT == TQ_SCALE_CODEBOOK
-                                                                  ? (int64_t)(seg / 6) * 256
-                                                                  : ((int64_t)(seg >> 1) * K + k) * 256));
+        for (int fn = 0; fn < FN; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
+        if (kWord) {   // the block's word, with every step (no branch around a load)
+            const uint32_t ss = LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(c.seg / 6) * 256
+                                                            : ((uint32_t)(c.seg >> 1) * K + c.k) * 256;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) sw[fn] = buffer_load<uint32_t>(rs, soff[fn], ss);
+        }
     };
-
-    auto load = [&](int seg, int k, int j, Frag (&a)[FM], uint32_t (&w)[FN]) {
-        const int ks = seg * seg_steps + j;                     // MFMA step along the row
-        const int col = ks * KS;
-        const bool in = col + q * QCOLS < Kin;                  // Kin % 16 == 0: all or nothing
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            a[fm] = in ? *(const GLOBAL_AS Frag*)(xrow[fm] + (int64_t)col * ESZ) : zero_frag<Frag>();
-        const int c = MF::chunk(ks);                            // 64-column chunk
-        const int dw = MF::dword(ks, q);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            w[fn] = *(const GLOBAL_AS uint32_t*)(crow[fn] + ((int64_t)c * K + k) * 1024 + dw * 4);
-    };
-
-    Frag a_nxt[FM];
-    uint32_t w_nxt[FN], sw_nxt[FN], sw[FN];
-    int seg = 0, k = 0, j = 0;
-    load(0, 0, 0, a_nxt, w_nxt);
-    if (kWord) load_word(0, 0, sw_nxt);
-    for (int t = 0; t < total; ++t) {
-        Frag a[FM];
-        uint32_t w[FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) a[fm] = a_nxt[fm];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) w[fn] = w_nxt[fn];
-        if (kWord && j == 0) {
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sw[fn] = sw_nxt[fn];
-        }
-        const int cseg = seg, ck = k, cj = j;
-        if (++j == seg_steps) {
-            j = 0;
-            if (++k == K) {
-                k = 0;
-                ++seg;
-            }
-        }
-        if (t + 1 < total) {
-            load(seg, k, j, a_nxt, w_nxt);
-            if (kWord && j == 0) load_word(seg, k, sw_nxt);
-        }
-
-        // scales of this (segment, plane) for the lane's weight rows
-        float sc[FN];
-        if (!kDirect && cj == seg_steps - 1) {
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                if (LAYOUT == TQ_SCALE_TENSOR) {
-                    sc[fn] = ld_uniform(((const float*)P.scales) + ck) * MF::kScale;
-                } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
-                    // digit plane ck weighs 3^(K-1-ck); the group's scale is cb[idx[n][group]]
-                    const uint32_t idx = (sw[fn] >> (5 * (cseg % 6))) & 31u;
-                    float wgt = 1.0f;
-#pragma unroll
-                    for (int i = 1; i < K; ++i)
-                        if (i < K - ck) wgt *= 3.0f;
-                    sc[fn] = cb_lds[idx] * (wgt * MF::kScale);
-                } else {
-                    sc[fn] = f16_to_f32((cseg & 1) ? (sw[fn] >> 16) : (sw[fn] & 0xFFFFu)) * MF::kScale;
-                }
-            }
-        }
-
+    auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&sw)[FN]) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const Frag b = MF::decode(w[fn], q);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, part[fm][fn]);
         }
+        if (kDirect || c.j != seg_steps - 1) return;
+        // the block's scale for the lane's weight rows, applied once
+        float sc[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            if (LAYOUT == TQ_SCALE_TENSOR) {
+                sc[fn] = ld_uniform(((const float*)P.scales) + c.k) * MF::kScale;
+            } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
+                // digit plane k weighs 3^(K-1-k); the group's scale is cb[idx[n][group]]
+                const uint32_t idx = (sw[fn] >> (5 * (c.seg % 6))) & 31u;
+                float wgt = 1.0f;
+#pragma unroll
+                for (int i = 1; i < K; ++i)
+                    if (i < K - c.k) wgt *= 3.0f;
+                sc[fn] = cb_lds[idx] * (wgt * MF::kScale);
+            } else {
+                sc[fn] = f16_to_f32((c.seg & 1) ? (sw[fn] >> 16) : (sw[fn] & 0xFFFFu)) * MF::kScale;
+            }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e] =
+                        fmaf(sc[fn], (float)part[fm][fn][e], acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e]);
+                part[fm][fn] = Part{0, 0, 0, 0};
+            }
+    };
 
-        if (!kDirect && cj == seg_steps - 1) {
+    // Step s lives in buffer s % NBUF; loads run NBUF - 1 steps ahead of the
+    // MFMAs.  No load sits under a branch, so the compiler's wait counts see
+    // exactly which loads a step needs.  Loads past the last step read beyond
+    // the data (zeros or unused bytes) and are never consumed.
+    Cursor ld{0, 0, 0}, cp{0, 0, 0};
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+    for (int u = 0; u + 1 < NBUF; ++u) {
+        load(ld, abuf[u], wbuf[u], swbuf[u]);
+        ld.advance(seg_steps, K);
+    }
+    int t = 0;
+    for (; t + NBUF <= total; t += NBUF) {
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
+        for (int u = 0; u < NBUF; ++u) {
+            constexpr int kAhead = NBUF - 1;
+            const int v = (u + kAhead) % NBUF;
+            load(ld, abuf[v], wbuf[v], swbuf[v]);
+            ld.advance(seg_steps, K);
+            __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's MFMAs
+            compute(cp, abuf[u], wbuf[u], swbuf[u]);
+            cp.advance(seg_steps, K);
+        }
+    }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e] =
-                            fmaf(sc[fn], (float)part[fm][fn][e], acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e]);
-                    part[fm][fn] = Part{0, 0, 0, 0};
-                }
+    for (int u = 0; u + 1 < NBUF; ++u) {   // the last total % NBUF steps, already loaded
+        if (t + u < total) {
+            compute(cp, abuf[u], wbuf[u], swbuf[u]);
+            cp.advance(seg_steps, K);
         }
     }
 
