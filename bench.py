@@ -338,13 +338,27 @@ def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 5) -> dict:
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries (profiles/) and the measured HBM traffic of the kernel.
 # ---------------------------------------------------------------------------
-def kernel_fingerprint() -> str:
-    """Hash of the library sources; traffic measured on other sources is not reused."""
+# Sources that make up each kernel family (the traffic of a kernel is reused
+# only while none of them has changed).
+_COMMON_SOURCES = ["tq_decode.h", "tq_internal.h", "tq_layout.h"]
+_FAMILY_SOURCES = {
+    "k_gemv": ["tq_gemv_impl.h", "tq_gemv.hip", "tq_entry.hip"],
+    "k_gemm": ["tq_gemm_impl.h", "tq_gemm_kernels.h", "tq_gemm.hip"],
+}
+
+
+def kernel_fingerprint(kernel: str) -> str:
+    """Hash of the sources of the kernel's family (and the header of the ABI)."""
+    fam = next((k for k in _FAMILY_SOURCES if kernel.startswith(k)), None)
+    files = _COMMON_SOURCES + (_FAMILY_SOURCES[fam] if fam else [])
+    prefix = {"k_gemv": "tq_gemv_", "k_gemm": "tq_gemm_"}.get(fam)
+    if prefix:
+        files += sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, prefix + "*.hip")))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "tq.h")]:
-        if f.endswith((".hip", ".h")):
-            h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+    for f in sorted(set(files)):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "tq.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -365,7 +379,7 @@ def summarize(args) -> None:
     """Write a profiles/*.md summary from rocprofv3 output directories."""
     kern = args.kernel
     lines = ["# %s" % args.title, ""]
-    rec = {"kernel": kern, "fingerprint": kernel_fingerprint()}
+    rec = {"kernel": kern, "fingerprint": kernel_fingerprint(kern)}
     if args.trace_dir:
         stats = glob.glob(os.path.join(args.trace_dir, "*_kernel_stats.csv"))
         lines += ["Command: `%s`" % args.trace_cmd, "", "rocprofv3 --kernel-trace --stats, top kernels by total time:", "",
@@ -414,7 +428,7 @@ def summarize(args) -> None:
 
 def measured_traffic(kernel: str):
     """HBM bytes per launch from a profiles/ summary of the current sources, else None."""
-    fp = kernel_fingerprint()
+    fp = kernel_fingerprint(kernel)
     for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         text = open(f).read()
         if "```json" not in text:
