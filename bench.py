@@ -508,8 +508,8 @@ def main():
 
     gbytes, qbytes = stack.gemv_bytes(), stack.quant_bytes()
     if stack.prefill:
-        fm_fn = (4, 8) if (case.x_type == I8 and case.layout == TENSOR and case.planes == 1) else (4, 4)
-        kernel_name = "k_gemm_grouped<%d, %d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes, *fm_fn)
+        step = 64 if case.x_type == I8 else (32 if case.layout == TENSOR or case.group % 32 == 0 else 16)
+        kernel_name = "k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, case.layout, case.planes, step)
         ops = stack.ops()
         value = ops / (ms_step / 1e3) / 1e12
         achieved = ops / (gemv_avg / 1e3) / 1e12

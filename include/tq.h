@@ -257,9 +257,8 @@ tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);
 /*
  * Many prefill products (tq_gemm) in one launch, e.g. every projection of a
  * layer stack.  All problems must share K, scale layout and x_type; M is
- * common.  The work list holds one item per output tile (128 tokens x 256 rows
- * for TQ_I8 with one plane and a per-tensor scale, 16 x 256 for TQ_BF16 with
- * M <= 16, else 128 x 128), longest problems first.  The plan is the decode one's struct: on return waves = 4
+ * common.  The work list holds one item per output tile (16 tokens x 256 rows
+ * for TQ_BF16 with M <= 16, else 128 x 128), longest problems first.  The plan is the decode one's struct: on return waves = 4
  * and row_blocks = 64-row blocks per tile; tq_gemv_grouped_run refuses it.
  */
 tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,

@@ -41,7 +41,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;   // 2 x 2 waves
+constexpr int kThreads = 256;   // 4 waves
+#ifndef TQ_GEMM_WAVES_PER_SIMD
+#define TQ_GEMM_WAVES_PER_SIMD 2   // register budget: two waves per SIMD, so that one
+                                   // wave's trit decode overlaps the other's MFMAs
+#endif
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -198,11 +202,18 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     using Frag = typename MF::Frag;
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
-    constexpr int NBUF = 3;                               // steps in flight (loads issued 2 steps ahead)
+    constexpr int NBUF = 4;                               // steps in flight (loads issued 3 steps ahead)
     // int8, one plane, per-tensor scale: the int32 sum is the result
     constexpr bool kDirect = XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1;
     // the scale word of a (segment, plane) block: two f16 group scales, or six 5-bit codebook indices
     constexpr bool kWord = !kDirect && LAYOUT != TQ_SCALE_TENSOR;
+    // x through LDS: the 2 x 2 kernels whose step is 64 bytes of a row (int8,
+    // or 32 bf16 columns).  The workgroup loads its 16 FM WM rows once per
+    // step, 16 bytes per thread and chunk, and every wave reads its fragments
+    // from there instead of loading them again.
+    constexpr int TM = 16 * FM * WM;
+    constexpr bool kLds = WM == 2 && KS * ESZ == 64 && TM * 4 % kThreads == 0;
+    constexpr int XCH = kLds ? TM * 4 / kThreads : 1;     // 16-byte chunks per thread and step
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -219,6 +230,23 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     uint32_t xoff[FM], coff[FN], soff[FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) xoff[fm] = ((uint32_t)(m0 + 16 * fm + r) * Kin + q * QCOLS) * ESZ;
+    // LDS staging: chunk id = thread + 256 i holds row id / 4, 16-byte column
+    // chunk id % 4; a row's four chunks are stored XOR-swizzled by (row / 4) % 4
+    // so that the 16 rows one fragment read touches fall in distinct banks
+    uint32_t xoffl[XCH], xlds_w[XCH];
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+        const uint32_t id = threadIdx.x + kThreads * i, R = id >> 2, c = id & 3;
+        xoffl[i] = ((uint32_t)(tm * TM + R) * Kin) * ESZ + 16 * c;
+        xlds_w[i] = R * 64 + 16 * (c ^ ((R >> 2) & 3));
+    }
+    uint32_t xlds_r[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const uint32_t R = (wave % WM) * (16 * FM) + 16 * fm + r;
+        xlds_r[fm] = R * 64 + 16 * (q ^ ((R >> 2) & 3));
+    }
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[kLds ? 2 : 1][kLds ? TM * 64 : 16];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const uint32_t n = n0 + 16 * fn + r;
@@ -244,13 +272,19 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
 
     // Columns of x past Kin in a ragged last step read the next row (or zero
     // past the end); the codes there are padding (zero trits), so they add 0.
-    Frag abuf[NBUF][FM];
+    constexpr int AREG = kLds ? XCH : FM;                  // x registers per step buffer
+    Frag abuf[NBUF][AREG];
     uint32_t wbuf[NBUF][FN], swbuf[NBUF][FN];
-    auto load = [&](const Cursor& c, Frag (&a)[FM], uint32_t (&w)[FN], uint32_t (&sw)[FN]) {
+    auto load = [&](const Cursor& c, Frag (&a)[AREG], uint32_t (&w)[FN], uint32_t (&sw)[FN]) {
         const int ks = c.seg * seg_steps + c.j;                 // MFMA step along the row
         const uint32_t xs = (uint32_t)ks * (KS * ESZ);
+        if (kLds) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) a[fm] = buffer_load<Frag>(rx, xoff[fm], xs);
+            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rx, xoffl[i], xs);
+        } else {
+#pragma unroll
+            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rx, xoff[i], xs);
+        }
         const uint32_t cs = ((uint32_t)MF::chunk(ks) * K + c.k) * 1024 + MF::dword_step(ks) * 4;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
@@ -262,6 +296,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         }
     };
     auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&sw)[FN]) {
+        static_assert(sizeof(a) == FM * sizeof(Frag), "fragments");
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const Frag b = MF::decode(w[fn], q);
@@ -303,31 +338,57 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // MFMAs.  No load sits under a branch, so the compiler's wait counts see
     // exactly which loads a step needs.  Loads past the last step read beyond
     // the data (zeros or unused bytes) and are never consumed.
+    // LDS stage of a step (double buffered): write the thread's chunks, and
+    // read a wave's fragments.  One barrier per step separates them: before
+    // it every wave has written stage t % 2 and finished reading stage
+    // (t + 1) % 2, which is written next.
+    auto lds_write = [&](int stage, const Frag (&a)[AREG]) {
+#pragma unroll
+        for (int i = 0; i < AREG; ++i) *(LDS_AS Frag*)((LDS_AS uint8_t*)xlds[stage] + xlds_w[i]) = a[i];
+    };
+    auto lds_read = [&](int stage, Frag (&a)[FM]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) a[fm] = *(const LDS_AS Frag*)((const LDS_AS uint8_t*)xlds[stage] + xlds_r[fm]);
+    };
+    auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // one step: the loads of step t + NBUF - 1, then (LDS path) the staging of
+    // step t + 1, then the MFMAs of step t
+    auto step = [&](int u, Cursor& ld, Cursor& cp, bool issue) {
+        constexpr int kAhead = NBUF - 1;
+        const int v = (u + kAhead) % NBUF;
+        if (issue) {
+            load(ld, abuf[v], wbuf[v], swbuf[v]);
+            ld.advance(seg_steps, K);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's MFMAs
+        if constexpr (kLds) {
+            Frag a[FM];
+            barrier();
+            lds_write((u + 1) & 1, abuf[(u + 1) % NBUF]);
+            lds_read(u & 1, a);
+            compute(cp, a, wbuf[u], swbuf[u]);
+        } else {
+            compute(cp, abuf[u], wbuf[u], swbuf[u]);
+        }
+        cp.advance(seg_steps, K);
+    };
+
     Cursor ld{0, 0, 0}, cp{0, 0, 0};
 #pragma unroll
     for (int u = 0; u + 1 < NBUF; ++u) {
         load(ld, abuf[u], wbuf[u], swbuf[u]);
         ld.advance(seg_steps, K);
     }
+    if constexpr (kLds) lds_write(0, abuf[0]);
+    static_assert(!kLds || NBUF % 2 == 0, "stage parity follows the buffer index");
     int t = 0;
     for (; t + NBUF <= total; t += NBUF) {
 #pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-            constexpr int kAhead = NBUF - 1;
-            const int v = (u + kAhead) % NBUF;
-            load(ld, abuf[v], wbuf[v], swbuf[v]);
-            ld.advance(seg_steps, K);
-            __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's MFMAs
-            compute(cp, abuf[u], wbuf[u], swbuf[u]);
-            cp.advance(seg_steps, K);
-        }
+        for (int u = 0; u < NBUF; ++u) step(u, ld, cp, true);
     }
 #pragma unroll
     for (int u = 0; u + 1 < NBUF; ++u) {   // the last total % NBUF steps, already loaded
-        if (t + u < total) {
-            compute(cp, abuf[u], wbuf[u], swbuf[u]);
-            cp.advance(seg_steps, K);
-        }
+        if (t + u < total) step(u, ld, cp, false);
     }
 
     // epilogue: lane holds weight row n = n0 + 16 fn + r of tokens m0 + 16 fm + 4 q + e
@@ -370,7 +431,7 @@ __device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_l
 }
 
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
-__global__ __launch_bounds__(kThreads) void k_gemm_single(tq_prob_dev P, int tiles_m)
+__global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_single(tq_prob_dev P, int tiles_m)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
     stage_codebook<LAYOUT>(P, cb_lds);
@@ -380,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_single(tq_prob_dev P, int til
 
 // Grouped: item i = (problem, tile); tiles of a problem run token-tile fastest.
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
-__global__ __launch_bounds__(kThreads) void k_gemm_grouped(const tq_prob_dev* probs, const int2* items)
+__global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_grouped(const tq_prob_dev* probs, const int2* items)
 {
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);

@@ -4,8 +4,8 @@ CPU oracle, through the C ABI.
 Bars as for decode: bit-exact y and int32 accumulator for int8 activations
 with one plane and a per-tensor scale; the per-token relative error
 max_n |y - y*| / max(|y*|, rms(y*)) <= 1e-3 against the fp64 oracle otherwise.
-Sizes span several 128 x 256 (or 128 x 128) output tiles with ragged edges in
-M, N and Kin.
+Sizes span several 128 x 128 output tiles (16 x 256 for bf16 with M <= 16)
+with ragged edges in M, N and Kin.
 """
 from __future__ import annotations
 
