@@ -214,6 +214,15 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int TM = 16 * FM * WM;
     constexpr bool kLds = WM == 2 && KS * ESZ == 64 && TM * 4 % kThreads == 0;
     constexpr int XCH = kLds ? TM * 4 / kThreads : 1;     // 16-byte chunks per thread and step
+    // The codes go through LDS as well: the workgroup's TN rows' code dwords
+    // of a step are CW per row (the whole 16-byte slot for int8, half of it
+    // for bf16), loaded CPT consecutive dwords per thread.  Read in the MFMA
+    // fragment layout straight from global memory, 16 lanes of a load would
+    // sit 16 bytes apart, which costs the L1 about one access per two lanes.
+    constexpr int TN = 16 * FN * (4 / WM);
+    constexpr int CW = kLds ? (XT == TQ_I8 ? 4 : 2) : 1;
+    constexpr int CPT = kLds ? TN * CW / kThreads : 1;
+    static_assert(!kLds || (CPT >= 1 && CW % CPT == 0), "code dwords per thread");
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -231,22 +240,41 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) xoff[fm] = ((uint32_t)(m0 + 16 * fm + r) * Kin + q * QCOLS) * ESZ;
     // LDS staging: chunk id = thread + 256 i holds row id / 4, 16-byte column
-    // chunk id % 4; a row's four chunks are stored XOR-swizzled by (row / 4) % 4
-    // so that the 16 rows one fragment read touches fall in distinct banks
+    // chunk id % 4; a row's four chunks are stored XOR-swizzled by (row / 2) % 4,
+    // so that the 8 lanes of one 128-byte LDS pass (32 banks of 4 bytes), rows
+    // R .. R + 7 of one chunk, fall in distinct banks, for reads and writes
     uint32_t xoffl[XCH], xlds_w[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
         const uint32_t id = threadIdx.x + kThreads * i, R = id >> 2, c = id & 3;
         xoffl[i] = ((uint32_t)(tm * TM + R) * Kin) * ESZ + 16 * c;
-        xlds_w[i] = R * 64 + 16 * (c ^ ((R >> 2) & 3));
+        xlds_w[i] = R * 64 + 16 * (c ^ ((R >> 1) & 3));
     }
     uint32_t xlds_r[FM];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const uint32_t R = (wave % WM) * (16 * FM) + 16 * fm + r;
-        xlds_r[fm] = R * 64 + 16 * (q ^ ((R >> 2) & 3));
+        xlds_r[fm] = R * 64 + 16 * (q ^ ((R >> 1) & 3));
     }
     __shared__ __attribute__((aligned(16))) uint8_t xlds[kLds ? 2 : 1][kLds ? TM * 64 : 16];
+    // code stage: row R's dword d at R * CW + ((d + rot(R)) % CW), the int8
+    // rotation rot = 2 ((R / 8) % 2) putting the 32 lanes of one LDS pass
+    // (rows R .. R + 15, two dwords each) in distinct banks
+    __shared__ __attribute__((aligned(16))) uint32_t clds[kLds ? 2 : 1][kLds ? TN * CW : 4];
+    uint32_t ccoff = 0, clds_w = 0, clds_r[FN];
+    {
+        const uint32_t T = threadIdx.x, R = T * CPT / CW, d0 = T * CPT % CW;
+        const uint32_t n = tn * TN + R;
+        const uint32_t rot = CW == 4 ? 2 * ((R >> 3) & 1) : 0;
+        ccoff = ((n >> 6) * NC * K * 64 + (n & 63)) * 16 + d0 * 4;
+        clds_w = R * CW + ((d0 + rot) % CW);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const uint32_t Rr = (wave / WM) * (16 * FN) + 16 * fn + r;
+            const uint32_t rotr = CW == 4 ? 2 * ((Rr >> 3) & 1) : 0;
+            clds_r[fn] = Rr * CW + ((MF::dword_lane(q) + rotr) % CW);
+        }
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
         const uint32_t n = n0 + 16 * fn + r;
@@ -273,9 +301,10 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // Columns of x past Kin in a ragged last step read the next row (or zero
     // past the end); the codes there are padding (zero trits), so they add 0.
     constexpr int AREG = kLds ? XCH : FM;                  // x registers per step buffer
+    constexpr int WREG = kLds ? CPT : FN;                  // code registers per step buffer
     Frag abuf[NBUF][AREG];
-    uint32_t wbuf[NBUF][FN], swbuf[NBUF][FN];
-    auto load = [&](const Cursor& c, Frag (&a)[AREG], uint32_t (&w)[FN], uint32_t (&sw)[FN]) {
+    uint32_t wbuf[NBUF][WREG], swbuf[NBUF][FN];
+    auto load = [&](const Cursor& c, Frag (&a)[AREG], uint32_t (&w)[WREG], uint32_t (&sw)[FN]) {
         const int ks = c.seg * seg_steps + c.j;                 // MFMA step along the row
         const uint32_t xs = (uint32_t)ks * (KS * ESZ);
         if (kLds) {
@@ -286,8 +315,18 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rx, xoff[i], xs);
         }
         const uint32_t cs = ((uint32_t)MF::chunk(ks) * K + c.k) * 1024 + MF::dword_step(ks) * 4;
+        if constexpr (kLds) {
+            if constexpr (CPT == 2) {
+                const u32x2 v = buffer_load<u32x2>(rc, ccoff, cs);
+                w[0] = v[0];
+                w[CPT - 1] = v[1];
+            } else {
+                w[0] = buffer_load<uint32_t>(rc, ccoff, cs);
+            }
+        } else {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
+            for (int fn = 0; fn < WREG; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
+        }
         if (kWord) {   // the block's word, with every step (no branch around a load)
             const uint32_t ss = LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(c.seg / 6) * 256
                                                             : ((uint32_t)(c.seg >> 1) * K + c.k) * 256;
@@ -342,13 +381,20 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // read a wave's fragments.  One barrier per step separates them: before
     // it every wave has written stage t % 2 and finished reading stage
     // (t + 1) % 2, which is written next.
-    auto lds_write = [&](int stage, const Frag (&a)[AREG]) {
+    auto lds_write = [&](int stage, const Frag (&a)[AREG], const uint32_t (&w)[WREG]) {
 #pragma unroll
         for (int i = 0; i < AREG; ++i) *(LDS_AS Frag*)((LDS_AS uint8_t*)xlds[stage] + xlds_w[i]) = a[i];
+        if constexpr (CPT == 2) {
+            *(LDS_AS u32x2*)((LDS_AS uint32_t*)clds[stage] + clds_w) = u32x2{w[0], w[CPT - 1]};
+        } else {
+            ((LDS_AS uint32_t*)clds[stage])[clds_w] = w[0];
+        }
     };
-    auto lds_read = [&](int stage, Frag (&a)[FM]) {
+    auto lds_read = [&](int stage, Frag (&a)[FM], uint32_t (&w)[FN]) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) a[fm] = *(const LDS_AS Frag*)((const LDS_AS uint8_t*)xlds[stage] + xlds_r[fm]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) w[fn] = ((const LDS_AS uint32_t*)clds[stage])[clds_r[fn]];
     };
     auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     // one step: the loads of step t + NBUF - 1, then (LDS path) the staging of
@@ -363,10 +409,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's MFMAs
         if constexpr (kLds) {
             Frag a[FM];
+            uint32_t w[FN];
             barrier();
-            lds_write((u + 1) & 1, abuf[(u + 1) % NBUF]);
-            lds_read(u & 1, a);
-            compute(cp, a, wbuf[u], swbuf[u]);
+            lds_write((u + 1) & 1, abuf[(u + 1) % NBUF], wbuf[(u + 1) % NBUF]);
+            lds_read(u & 1, a, w);
+            compute(cp, a, w, swbuf[u]);
         } else {
             compute(cp, abuf[u], wbuf[u], swbuf[u]);
         }
@@ -379,7 +426,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         load(ld, abuf[u], wbuf[u], swbuf[u]);
         ld.advance(seg_steps, K);
     }
-    if constexpr (kLds) lds_write(0, abuf[0]);
+    if constexpr (kLds) lds_write(0, abuf[0], wbuf[0]);
     static_assert(!kLds || NBUF % 2 == 0, "stage parity follows the buffer index");
     int t = 0;
     for (; t + NBUF <= total; t += NBUF) {
