@@ -48,6 +48,45 @@ __device__ __forceinline__ void decode_i8(uint32_t w, uint32_t t[4])
     t[3] = __builtin_amdgcn_perm(0x00000001u, 0x00008000u, w4 & 0x0C0C0C0Cu);
 }
 
+// Buffer resources: a 32-bit per-lane offset (VGPR) plus a wave-uniform
+// offset (SGPR) from a base; a lane whose VGPR offset is at or past the
+// resource's size reads zeros without touching memory.  The SGPR offset is
+// kept inside the data wherever the load's result is used, since only the
+// VGPR offset is certain to take part in the range check.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kOffNone = 0x80000000u;   // VGPR offset that reads zero (resources are < 2 GiB)
+constexpr int kCacheNT = 2;                  // cache policy: non-temporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+template <typename F, int kPolicy = 0>
+__device__ __forceinline__ F buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ u32x4 buffer_load<u32x4, 0>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ u32x4 buffer_load<u32x4, kCacheNT>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCacheNT));
+}
+template <>
+__device__ __forceinline__ u32x2 buffer_load<u32x2, 0>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ uint32_t buffer_load<uint32_t, 0>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 }  // namespace tqk

@@ -14,18 +14,18 @@
 //
 // Mapping onto CDNA4.  A workgroup is 4 waves, 2 x 2 (tokens x weight rows)
 // for prefill or 1 x 4 for a few tokens; a wave owns FM x FN tiles of
-// 16 x 16 outputs (16 FM tokens by 16 FN weight rows).  Per step a wave
-// loads, for each token tile, 16 bytes per lane of x (row = lane % 16, the
-// lane group q = lane / 16 takes one quarter of the step's columns) and, for
-// each weight tile, one dword of codes per lane: in the blob (tq_layout.h) a
-// dword is 16 consecutive columns of one row, exactly the quarter-step of the
-// int8 MFMA v_mfma_i32_16x16x64_i8 (64 columns per step), or a half dword for
-// the bf16 MFMA v_mfma_f32_16x16x32_bf16 (32 columns per step), or a quarter
-// dword for v_mfma_f32_16x16x16_bf16 (16 columns per step: one group of the
-// d = 3 codec, whose scale is applied after each step).  Each decoded
-// weight tile is reused by the FM token tiles, each token tile by the FN
-// weight tiles.  x is read straight from global memory (the workgroup's other
-// waves and neighbouring workgroups hit it in L1/L2); there is no LDS.
+// 16 x 16 outputs (16 FM tokens by 16 FN weight rows).  An MFMA's operands
+// are 16 rows by one step of columns, each lane holding row lane % 16 and
+// the quarter q = lane / 16 of the step's columns: for x, 16 bytes; for the
+// weights, one dword of codes (in the blob, tq_layout.h, a dword is 16
+// consecutive columns of one row), exactly the quarter-step of the int8 MFMA
+// v_mfma_i32_16x16x64_i8 (64 columns per step), or a half dword for the bf16
+// MFMA v_mfma_f32_16x16x32_bf16 (32 columns per step), or a quarter dword for
+// v_mfma_f32_16x16x16_bf16 (16 columns per step: one group of the d = 3
+// codec, whose scale is applied after each step).  Each decoded weight tile
+// is reused by the FM token tiles, each token tile by the FN weight tiles.
+// In the 2 x 2 kernels the workgroup stages each step's x tile and code
+// dwords in LDS once, and the waves read their fragments from there.
 //
 // Result tile layout of a 16 x 16 MFMA: lane l holds column l % 16 (a weight
 // row n) of rows 4 (l / 16) + e, e = 0..3 (tokens m).
@@ -39,7 +39,6 @@ using namespace tqk;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 waves
 #ifndef TQ_GEMM_WAVES_PER_SIMD
@@ -47,7 +46,6 @@ constexpr int kThreads = 256;   // 4 waves
                                    // wave's trit decode overlaps the other's MFMAs
 #endif
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // The MFMA of one step of KS columns for activation type XT: operand
@@ -151,33 +149,10 @@ __device__ __forceinline__ F zero_frag()
 
 // One workgroup tile of one problem: WM x (4 / WM) waves, each with FM x FN
 // tiles of 16 x 16, so 16 FM WM tokens by 16 FN (4 / WM) weight rows.
-// Loads through buffer resources: a 32-bit per-lane offset plus an SGPR
-// offset per step, no address arithmetic in the loop, and reads past the
-// resource's size return zero (rows past M, row blocks past N).  The host
-// keeps every operand of a launch below 4 GiB.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
-}
-
-template <typename F>
-__device__ __forceinline__ F buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
-template <>
-__device__ __forceinline__ u32x4 buffer_load<u32x4>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-template <>
-__device__ __forceinline__ u32x2 buffer_load<u32x2>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-template <>
-__device__ __forceinline__ uint32_t buffer_load<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-
+// Loads through buffer resources: a 32-bit per-lane offset plus a uniform
+// offset per step, no address arithmetic in the loop, and lanes whose offset
+// is past the resource's size read zero (rows past M, row blocks past N).
+// The host keeps every operand of a launch below 4 GiB.
 // Position in the step sequence: segment (a group, or the whole row for a
 // per-tensor scale), then plane, then the segment's MFMA steps.
 struct Cursor {
@@ -232,7 +207,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     const int m0 = tm * (16 * FM * WM) + (wave % WM) * (16 * FM);
     const int n0 = tn * (16 * FN * (4 / WM)) + (wave / WM) * (16 * FN);
 
-    const __amdgpu_buffer_rsrc_t rx = rsrc(P.x, (int64_t)M * Kin * ESZ);
+    const int64_t xbytes = (int64_t)M * Kin * ESZ;
     const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, (int64_t)NB * NC * K * 1024);
     const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)NB * P.NID * 256
                                                                                  : (int64_t)NB * P.NGD * K * 256);
@@ -304,15 +279,22 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int WREG = kLds ? CPT : FN;                  // code registers per step buffer
     Frag abuf[NBUF][AREG];
     uint32_t wbuf[NBUF][WREG], swbuf[NBUF][FN];
-    auto load = [&](const Cursor& c, Frag (&a)[AREG], uint32_t (&w)[WREG], uint32_t (&sw)[FN]) {
+    auto load = [&](const Cursor& cur, Frag (&a)[AREG], uint32_t (&w)[WREG], uint32_t (&sw)[FN]) {
+        // a cursor past the last step (the prefetch runs ahead of the end)
+        // loads the last step again: the data is in cache and never used
+        const bool past = cur.seg >= nseg;
+        const Cursor c{past ? nseg - 1 : cur.seg, past ? K - 1 : cur.k, past ? seg_steps - 1 : cur.j};
         const int ks = c.seg * seg_steps + c.j;                 // MFMA step along the row
         const uint32_t xs = (uint32_t)ks * (KS * ESZ);
+        // x through a window from the step's first column to the end of x, so
+        // that the columns of a ragged last step past the last row read zeros
+        const __amdgpu_buffer_rsrc_t rxs = rsrc((const uint8_t*)P.x + xs, xbytes - xs);
         if (kLds) {
 #pragma unroll
-            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rx, xoffl[i], xs);
+            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rxs, xoffl[i], 0);
         } else {
 #pragma unroll
-            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rx, xoff[i], xs);
+            for (int i = 0; i < AREG; ++i) a[i] = buffer_load<Frag>(rxs, xoff[i], 0);
         }
         const uint32_t cs = ((uint32_t)MF::chunk(ks) * K + c.k) * 1024 + MF::dword_step(ks) * 4;
         if constexpr (kLds) {
@@ -375,8 +357,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
 
     // Step s lives in buffer s % NBUF; loads run NBUF - 1 steps ahead of the
     // MFMAs.  No load sits under a branch, so the compiler's wait counts see
-    // exactly which loads a step needs.  Loads past the last step read beyond
-    // the data (zeros or unused bytes) and are never consumed.
+    // exactly which loads a step needs.  Loads issued past the last step
+    // repeat the last step's addresses and are never consumed.
     // LDS stage of a step (double buffered): write the thread's chunks, and
     // read a wave's fragments.  One barrier per step separates them: before
     // it every wave has written stage t % 2 and finished reading stage

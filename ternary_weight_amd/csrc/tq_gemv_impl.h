@@ -36,6 +36,7 @@
 #include "tq_decode.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tqk {
 
@@ -55,8 +56,6 @@ namespace tqk {
 #ifndef TQ_DEPTH_BF16
 #define TQ_DEPTH_BF16 2       // chunks in flight per wave, bf16 activations (table decode)
 #endif
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
@@ -130,6 +129,27 @@ struct BfPairs {   // activation pairs of one 16-column unit, matching the table
     uint32_t a[4], b[4];
 };
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Two 16-bit halves of wave-uniform dwords into one (the scalar unit's
+// s_pack_ll_b32_b16 and s_pack_hh_b32_b16): low halves, or high halves, of a
+// and b.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, u16x2{(unsigned short)a, (unsigned short)b});
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b)
+{
+    // written out: the compiler forms it as two shifts and s_pack_ll.  The
+    // operands are uniform; readfirstlane only moves one the compiler keeps
+    // in a VGPR to an SGPR (and vanishes when it is in one already).
+    uint32_t r;
+    asm("s_pack_hh_b32_b16 %0, %1, %2"
+        : "=s"(r)
+        : "s"(__builtin_amdgcn_readfirstlane((int)a)), "s"(__builtin_amdgcn_readfirstlane((int)b)));
+    return r;
+}
+
 __device__ __forceinline__ BfPairs bf_pairs(const XUnit<TQ_BF16>& x)
 {
     // x.v[j] holds columns 2j (low half) and 2j+1 (high half)
@@ -138,11 +158,11 @@ __device__ __forceinline__ BfPairs bf_pairs(const XUnit<TQ_BF16>& x)
     for (int b = 0; b < 4; ++b) {
         const uint32_t x0 = x.v[b >> 1], x4 = x.v[2 + (b >> 1)], x8 = x.v[4 + (b >> 1)], x12 = x.v[6 + (b >> 1)];
         if (b & 1) {
-            p.a[b] = (x0 >> 16) | (x4 & 0xFFFF0000u);
-            p.b[b] = (x8 >> 16) | (x12 & 0xFFFF0000u);
+            p.a[b] = pack_hi(x0, x4);
+            p.b[b] = pack_hi(x8, x12);
         } else {
-            p.a[b] = (x0 & 0xFFFFu) | (x4 << 16);
-            p.b[b] = (x8 & 0xFFFFu) | (x12 << 16);
+            p.a[b] = pack_lo(x0, x4);
+            p.b[b] = pack_lo(x8, x12);
         }
     }
     return p;
@@ -209,9 +229,9 @@ __device__ __forceinline__ int codec_combine(const int (&p)[K])
 template <int K>
 __device__ __forceinline__ float codec_combine(const float (&p)[K])
 {
-    float v = 0.0f;
+    float v = p[0];
 #pragma unroll
-    for (int k = 0; k < K; ++k) v = v * 3.0f + p[k];
+    for (int k = 1; k < K; ++k) v = fmaf(v, 3.0f, p[k]);
     return v;
 }
 
@@ -266,8 +286,8 @@ struct RowBlock {
     uint32_t copyoff;
     A p[MT][K];
     float out[MT];
-    const GLOBAL_AS u32x4* cp;
-    const GLOBAL_AS uint32_t* sp;
+    const uint8_t* cbase;   // this row block's codes
+    const uint8_t* sbase;   // this row block's scale words
 
     __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_, const uint8_t* lut_)
         : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_), lut((const LDS_AS uint8_t*)lut_),
@@ -279,39 +299,78 @@ struct RowBlock {
 #pragma unroll
             for (int k = 0; k < K; ++k) p[m][k] = 0;
         }
-        cp = (const GLOBAL_AS u32x4*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS + lane;
-        sp = (const GLOBAL_AS uint32_t*)P.scales;
+        cbase = (const uint8_t*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS * 16;
+        sbase = (const uint8_t*)P.scales +
+                (LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)rb * P.NID : (int64_t)rb * P.NGD * K) * TQ_ROWS * 4;
     }
 
-    // scale words needed by the groups that end inside chunk c
-    __device__ __forceinline__ void load_slot(int c, Slot<K, LAYOUT>& s) const
+    // A buffer resource over `bytes` bytes at `base + off` (no bytes when the
+    // load is not needed: its lanes then read zeros and touch no memory).
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const uint8_t* base, int64_t off, bool need,
+                                                                  int bytes)
     {
+        return rsrc(base + off, need ? bytes : 0);
+    }
+
+    // Codes of chunk c (K planes) and the scale words needed by the groups
+    // that end inside it.  Every load is issued whatever c is, so that no
+    // load sits under a branch (the compiler would then wait for all loads
+    // in flight at the join); chunks at or past c1 read zeros.
+    __device__ __forceinline__ void load_slot(int c_, Slot<K, LAYOUT>& s) const
+    {
+        const int c = __builtin_amdgcn_readfirstlane(c_);   // wave-uniform: keep its arithmetic scalar
+        const bool valid = c < c1_;
+        const __amdgpu_buffer_rsrc_t rc = window(cbase, (int64_t)c * K * TQ_ROWS * 16, valid, K * TQ_ROWS * 16);
 #pragma unroll
-        for (int k = 0; k < K; ++k) s.w[k] = __builtin_nontemporal_load(cp + ((int64_t)c * K + k) * TQ_ROWS);
+        for (int k = 0; k < K; ++k) s.w[k] = buffer_load<u32x4, kCacheNT>(rc, lane * 16, k * TQ_ROWS * 16);
+        constexpr int kWordRow = TQ_ROWS * 4;   // one scale word per row of the block
         if (LAYOUT == TQ_SCALE_GROUP_F16) {
             const int g = P.g;
             const int end = std::min((c + 1) * TQ_CHUNK, P.Kin);
             const int last_pair = ((end >> P.log2g) - 1) >> 1;
             if (g < 64) {
                 const int first_pair = ((c * TQ_CHUNK) >> P.log2g) >> 1;
+                const int second = std::min(first_pair + 1, last_pair);
+                const __amdgpu_buffer_rsrc_t r0 = window(sbase, (int64_t)first_pair * K * kWordRow, valid, K * kWordRow);
+                const __amdgpu_buffer_rsrc_t r1 = window(sbase, (int64_t)second * K * kWordRow, valid, K * kWordRow);
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
-                    s.sw[k][0] = sp[(((int64_t)rb * P.NGD + first_pair) * K + k) * TQ_ROWS + lane];
-                    s.sw[k][1] = sp[(((int64_t)rb * P.NGD + std::min(first_pair + 1, last_pair)) * K + k) * TQ_ROWS + lane];
+                    s.sw[k][0] = buffer_load<uint32_t>(r0, lane * 4, k * kWordRow);
+                    s.sw[k][1] = buffer_load<uint32_t>(r1, lane * 4, k * kWordRow);
                 }
-            } else if ((end & (g - 1)) == 0) {
+            } else {
+                const bool ends = (end & (g - 1)) == 0;   // a group ends in this chunk
+                const __amdgpu_buffer_rsrc_t r0 =
+                    window(sbase, (int64_t)last_pair * K * kWordRow, valid && ends, K * kWordRow);
 #pragma unroll
-                for (int k = 0; k < K; ++k) s.sw[k][0] = sp[(((int64_t)rb * P.NGD + last_pair) * K + k) * TQ_ROWS + lane];
+                for (int k = 0; k < K; ++k) s.sw[k][0] = buffer_load<uint32_t>(r0, lane * 4, k * kWordRow);
             }
         } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
             const int end = std::min((c + 1) * TQ_CHUNK, P.Kin);
             const int first_id = ((c * TQ_CHUNK) >> P.log2g) / 6;
             const int last_id = ((end >> P.log2g) - 1) / 6;
-            s.sw[0][0] = sp[((int64_t)rb * P.NID + first_id) * TQ_ROWS + lane];
-            s.sw[0][1] = sp[((int64_t)rb * P.NID + std::min(first_id + 1, last_id)) * TQ_ROWS + lane];
+            const int second = std::min(first_id + 1, last_id);
+            s.sw[0][0] = buffer_load<uint32_t>(window(sbase, (int64_t)first_id * kWordRow, valid, kWordRow), lane * 4, 0);
+            s.sw[0][1] = buffer_load<uint32_t>(window(sbase, (int64_t)second * kWordRow, valid, kWordRow), lane * 4, 0);
         }
     }
 
+    // Scale the finished group's partial sums q into out; sc: the group's
+    // scale per plane (GROUP), or its codebook scale (CODEBOOK).
+    __device__ __forceinline__ void apply_group(const float (&sc)[K], const A (&q)[MT][K])
+    {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (LAYOUT == TQ_SCALE_GROUP_F16) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) out[m] = fmaf(sc[k], (float)q[m][k], out[m]);
+            } else {
+                out[m] = fmaf(sc[0], (float)codec_combine<K>(q[m]), out[m]);
+            }
+        }
+    }
+
+    // Group grp ends inside chunk c: its scale, applied to p, which restarts.
     __device__ __forceinline__ void close_group(int grp, int c, const Slot<K, LAYOUT>& s, const float* cb_lds)
     {
         float sc[K];
@@ -330,51 +389,89 @@ struct RowBlock {
             const uint32_t idx = (word >> (5 * (grp - 6 * id))) & 31u;
             sc[0] = cb_lds[idx] * enc_scale<XT>();
         }
+        apply_group(sc, p);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (LAYOUT == TQ_SCALE_GROUP_F16) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) out[m] = fmaf(sc[k], (float)p[m][k], out[m]);
-            } else {
-                out[m] = fmaf(sc[0], (float)codec_combine<K>(p[m]), out[m]);
-            }
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int k = 0; k < K; ++k) p[m][k] = 0;
+    }
+
+    // g = 16: unit d of chunk c is group 4 c + d.  In the chunk's words the
+    // group-f16 scales of unit d are the half d % 2 of word d / 2; the
+    // codebook index is field pos = (4 c) % 6 + d of the first word (of the
+    // second from pos 6 on), with pos0 = (4 c) % 6.
+    template <int d>
+    __device__ __forceinline__ void scales_g16(const Slot<K, LAYOUT>& s, uint32_t pos0, const float* cb_lds,
+                                               float (&sc)[K]) const
+    {
+        if (LAYOUT == TQ_SCALE_GROUP_F16) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const uint32_t word = s.sw[k][d >> 1];
+                sc[k] = f16_to_f32((d & 1) ? (word >> 16) : (word & 0xFFFFu)) * enc_scale<XT>();
+            }
+        } else {
+            const uint32_t pos = pos0 + d;
+            const bool second = pos >= 6;
+            const uint32_t word = second ? s.sw[0][1] : s.sw[0][0];
+            const uint32_t idx = (word >> (5 * (second ? pos - 6 : pos))) & 31u;
+            sc[0] = cb_lds[idx] * enc_scale<XT>();
         }
     }
 
     // Columns of chunk c: `nu` 16-column units (4 for a full chunk).
-    template <bool kFull>
-    __device__ __forceinline__ void compute(int c, int nu, const Slot<K, LAYOUT>& s, const XChunk<XT>* xc,
+    // kG16: the group size is 16, so each unit is one group and its sums
+    // start from zero in fresh registers.
+    template <bool kFull, bool kG16>
+    __device__ __forceinline__ void compute(int c_, int nu, const Slot<K, LAYOUT>& s, const XChunk<XT>* xc,
                                             const float* cb_lds)
     {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            if (!kFull && d >= nu) break;
+        const int c = __builtin_amdgcn_readfirstlane(c_);   // wave-uniform: keep its arithmetic scalar
+        const uint32_t pos0 = kG16 && LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(4 * c) % 6u : 0u;
+        const auto unit = [&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            if (!kFull && d >= nu) return;
             const int u = c * 4 + d;
             uint32_t wd[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) wd[k] = s.w[k][d];
+            A q[MT][K];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if (MT > 1 && m >= P.M) break;
+#pragma unroll
+                for (int k = 0; k < K; ++k) q[m][k] = kG16 ? (A)0 : p[m][k];
+                if (MT > 1 && m >= P.M) continue;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
                 else xu.load(xsrc, (int64_t)m * P.Kin + (int64_t)u * 16);
                 if constexpr (XT == TQ_BF16) {
                     const BfPairs xp = bf_pairs(xu);
 #pragma unroll
-                    for (int k = 0; k < K; ++k) accum_lut(wd[k], xp, p[m][k], lut, copyoff);
+                    for (int k = 0; k < K; ++k) accum_lut(wd[k], xp, q[m][k], lut, copyoff);
                 } else {
 #pragma unroll
-                    for (int k = 0; k < K; ++k) accum(wd[k], xu, p[m][k]);
+                    for (int k = 0; k < K; ++k) accum(wd[k], xu, q[m][k]);
                 }
             }
-            if (kGroup) {
-                const int colend = (u + 1) * 16;
-                if ((colend & (P.g - 1)) == 0) close_group((colend >> P.log2g) - 1, c, s, cb_lds);
+            if constexpr (kG16) {
+                float sc[K];
+                scales_g16<d>(s, pos0, cb_lds, sc);
+                apply_group(sc, q);
+            } else {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int k = 0; k < K; ++k) p[m][k] = q[m][k];
+                if (kGroup) {
+                    const int colend = (u + 1) * 16;
+                    if ((colend & (P.g - 1)) == 0) close_group((colend >> P.log2g) - 1, c, s, cb_lds);
+                }
             }
-        }
+        };
+        unit(std::integral_constant<int, 0>{});
+        unit(std::integral_constant<int, 1>{});
+        unit(std::integral_constant<int, 2>{});
+        unit(std::integral_constant<int, 3>{});
     }
 
     Slot<K, LAYOUT> cur[D];
@@ -387,8 +484,7 @@ struct RowBlock {
         c1_ = c1;
         cf_ = std::min(c1, (P.Kin >> 4) >> 2);   // end of the chunks with all 64 columns valid
 #pragma unroll
-        for (int j = 0; j < D; ++j)
-            if (c0 + j < cf_) load_slot(c0 + j, cur[j]);
+        for (int j = 0; j < D; ++j) load_slot(c0 + j, cur[j]);
     }
 
     __device__ __forceinline__ void run(int c0, int c1, const float* cb_lds)
@@ -399,33 +495,48 @@ struct RowBlock {
 
     __device__ __forceinline__ void finish(const float* cb_lds)
     {
+        if (kGroup && P.g == 16) run_chunks<true>(cb_lds);
+        else run_chunks<false>(cb_lds);
+    }
+
+    // The full chunks c0 .. cf - 1, D at a time, the next D loading while
+    // one set computes (two register sets in turn, so no copies), then the
+    // ragged last chunk of the row (Kin % 64 != 0).
+    template <bool kG16>
+    __device__ __forceinline__ void run_chunks(const float* cb_lds)
+    {
         const int c0 = c0_, c1 = c1_, cf = cf_;
         const int n16 = P.Kin >> 4;
         if (c0 < cf) {
             XChunk<XT> xc;
             if (kXPre) xc.load(xsrc, (int64_t)c0 * TQ_CHUNK);
-            for (int c = c0; c < cf; c += D) {
-                Slot<K, LAYOUT> nxt[D];
-#pragma unroll
-                for (int j = 0; j < D; ++j)
-                    if (c + D + j < cf) load_slot(c + D + j, nxt[j]);
+            Slot<K, LAYOUT> nxt[D];
+            auto run = [&](int c, const Slot<K, LAYOUT> (&set)[D]) {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
                     if (c + j < cf) {
                         XChunk<XT> xn;
                         if (kXPre && c + j + 1 < cf) xn.load(xsrc, (int64_t)(c + j + 1) * TQ_CHUNK);
-                        compute<true>(c + j, 4, cur[j], &xc, cb_lds);
+                        compute<true, kG16>(c + j, 4, set[j], &xc, cb_lds);
                         if (kXPre) xc = xn;
                     }
                 }
+            };
+            for (int c = c0;; c += 2 * D) {
 #pragma unroll
-                for (int j = 0; j < D; ++j) cur[j] = nxt[j];
+                for (int j = 0; j < D; ++j) load_slot(c + D + j, nxt[j]);
+                run(c, cur);
+                if (c + D >= cf) break;
+#pragma unroll
+                for (int j = 0; j < D; ++j) load_slot(c + 2 * D + j, cur[j]);
+                run(c + D, nxt);
+                if (c + 2 * D >= cf) break;
             }
         }
-        if (cf < c1) {   // the ragged last chunk of the row (Kin % 64 != 0)
+        if (cf < c1) {
             Slot<K, LAYOUT> s;
             load_slot(cf, s);
-            compute<false>(cf, n16 - 4 * cf, s, nullptr, cb_lds);
+            compute<false, kG16>(cf, n16 - 4 * cf, s, nullptr, cb_lds);
         }
     }
 };
