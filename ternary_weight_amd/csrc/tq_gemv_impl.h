@@ -108,13 +108,19 @@ struct AccT<TQ_I8> { using type = int; };
 template <>
 struct AccT<TQ_F32_Q8> { using type = int; };
 
+// The trits of one 16-column code dword, decoded once and shared by every
+// token: int8 values (integer and fp32 paths), or the four 8-byte entries of
+// the bf16 table (below).
+template <int XT>
+struct Trits { uint32_t t[4]; };
+template <>
+struct Trits<TQ_BF16> { uint64_t t[4]; };
+
 // acc += sum over the 16 columns of one code dword of t * x.
-__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_I8>& x, int& acc)
+__device__ __forceinline__ void accum(const Trits<TQ_I8>& t, const XUnit<TQ_I8>& x, int& acc)
 {
-    uint32_t t[4];
-    decode_i8(w, t);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4((int)t[j], (int)x.v[j], acc, false);
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4((int)t.t[j], (int)x.v[j], acc, false);
 }
 
 // bf16 activations: a lookup table in LDS maps one code byte (the trits of
@@ -168,14 +174,37 @@ __device__ __forceinline__ BfPairs bf_pairs(const XUnit<TQ_BF16>& x)
     return p;
 }
 
-__device__ __forceinline__ void accum_lut(uint32_t w, const BfPairs& xp, float& acc,
-                                          const LDS_AS uint8_t* lut, uint32_t copyoff)
+__device__ __forceinline__ Trits<TQ_BF16> lut_lookup(uint32_t w, const LDS_AS uint8_t* lut, uint32_t copyoff)
+{
+    Trits<TQ_BF16> r;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, copyoff, 0x0C0C0400u | ((4u + b) << 8));
+        r.t[b] = *(const LDS_AS uint64_t*)(lut + addr);
+    }
+    return r;
+}
+
+// One token: the table reads interleaved with their dot products.
+__device__ __forceinline__ void accum_lut(uint32_t w, const BfPairs& xp, float& acc, const LDS_AS uint8_t* lut,
+                                          uint32_t copyoff)
 {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const uint32_t addr = __builtin_amdgcn_perm(w, copyoff, 0x0C0C0400u | ((4u + b) << 8));
         const uint64_t t = *(const LDS_AS uint64_t*)(lut + addr);
-        const uint32_t t0 = (uint32_t)t, t1 = (uint32_t)(t >> 32);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (uint32_t)t),
+                                              __builtin_bit_cast(bf16x2_t, xp.a[b]), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (uint32_t)(t >> 32)),
+                                              __builtin_bit_cast(bf16x2_t, xp.b[b]), acc, false);
+    }
+}
+
+__device__ __forceinline__ void accum(const Trits<TQ_BF16>& t, const BfPairs& xp, float& acc)
+{
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t t0 = (uint32_t)t.t[b], t1 = (uint32_t)(t.t[b] >> 32);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t0),
                                               __builtin_bit_cast(bf16x2_t, xp.a[b]), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t1),
@@ -199,15 +228,13 @@ __device__ __forceinline__ void fill_bf16_lut(uint8_t* lut)
     }
 }
 
-__device__ __forceinline__ void accum(uint32_t w, const XUnit<TQ_F32>& x, float& acc)
+__device__ __forceinline__ void accum(const Trits<TQ_F32>& t, const XUnit<TQ_F32>& x, float& acc)
 {
-    uint32_t t[4];
-    decode_i8(w, t);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const float tf = (float)(int8_t)(t[j] >> (8 * b));
+            const float tf = (float)(int8_t)(t.t[j] >> (8 * b));
             acc = fmaf(tf, __uint_as_float(x.v[4 * j + b]), acc);
         }
     }
@@ -432,25 +459,42 @@ struct RowBlock {
             constexpr int d = decltype(dc)::value;
             if (!kFull && d >= nu) return;
             const int u = c * 4 + d;
-            uint32_t wd[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) wd[k] = s.w[k][d];
+            using TX = Trits<XT == TQ_F32_Q8 ? TQ_I8 : XT>;
+            auto decode = [&](int k) {
+                TX t;
+                if constexpr (XT == TQ_BF16) t = lut_lookup(s.w[k][d], lut, copyoff);
+                else decode_i8(s.w[k][d], t.t);
+                return t;
+            };
             A q[MT][K];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
 #pragma unroll
                 for (int k = 0; k < K; ++k) q[m][k] = kG16 ? (A)0 : p[m][k];
-                if (MT > 1 && m >= P.M) continue;
+            }
+            // one token: each plane decoded right before its sums; several:
+            // the unit's trits decoded once, then every token's sums
+            TX t[MT > 1 ? K : 1];
+            if constexpr (MT > 1) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) t[k] = decode(k);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (MT > 1 && m >= P.M) break;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
                 else xu.load(xsrc, (int64_t)m * P.Kin + (int64_t)u * 16);
                 if constexpr (XT == TQ_BF16) {
                     const BfPairs xp = bf_pairs(xu);
 #pragma unroll
-                    for (int k = 0; k < K; ++k) accum_lut(wd[k], xp, q[m][k], lut, copyoff);
+                    for (int k = 0; k < K; ++k) {
+                        if constexpr (MT > 1) accum(t[k], xp, q[m][k]);
+                        else accum_lut(s.w[k][d], xp, q[m][k], lut, copyoff);
+                    }
                 } else {
 #pragma unroll
-                    for (int k = 0; k < K; ++k) accum(wd[k], xu, q[m][k]);
+                    for (int k = 0; k < K; ++k) accum(MT > 1 ? t[k] : decode(k), xu, q[m][k]);
                 }
             }
             if constexpr (kG16) {
