@@ -69,6 +69,13 @@ class Oracle:
         L.oracle_f16_to_f64.restype = ctypes.c_double
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_rms_norm.argtypes = [i64, vp, vp, ctypes.c_float, vp]
+        L.oracle_rms_norm.restype = i32
+        L.oracle_relu2_mul.argtypes = [i64, vp, vp, vp]
+        L.oracle_relu2_mul.restype = i32
+        L.oracle_bitnet_layer.argtypes = [i64, i64, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                          vp, vp]
+        L.oracle_bitnet_layer.restype = i32
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = i32
         self.L = L
@@ -125,6 +132,43 @@ class Oracle:
             raise OracleError("oracle_gemv_i8 failed with status %d" % rc)
         return {"acc": acc, "y64": y64, "y32": y32}
 
+    def rms_norm(self, x, w, eps):
+        """fp32 RMSNorm of the vector x with weight w."""
+        x, w = _c(x, np.float32).reshape(-1), _c(w, np.float32).reshape(-1)
+        out = np.zeros_like(x)
+        rc = self.L.oracle_rms_norm(len(x), _p(x), _p(w), float(eps), _p(out))
+        if rc:
+            raise OracleError("oracle_rms_norm failed with status %d" % rc)
+        return out
+
+    def relu2_mul(self, g, u):
+        g, u = _c(g, np.float32).reshape(-1), _c(u, np.float32).reshape(-1)
+        out = np.zeros_like(g)
+        rc = self.L.oracle_relu2_mul(len(g), _p(g), _p(u), _p(out))
+        if rc:
+            raise OracleError("oracle_relu2_mul failed with status %d" % rc)
+        return out
+
+    def bitnet_layer(self, dims, trits, s_w, norms, x):
+        """One decode-chain layer for the first token.
+
+        dims: (hidden, inter, n_heads, n_kv, head_dim, eps); trits: 7 int8
+        [N][Kin] arrays (q, k, v, o, gate, up, down); s_w: their 7 fp32
+        scales; norms: (input, attention-sub, post-attention, FFN-sub) fp32
+        weights.  Returns (x after the layer, q|k|v fp32)."""
+        hidden, inter, nh, nkv, hd, eps = dims
+        ts = [_c(t, np.int8).reshape(t.shape[-2], t.shape[-1]) for t in trits]
+        ptrs = (ctypes.c_void_p * 7)(*[t.ctypes.data for t in ts])
+        sw = np.ascontiguousarray(s_w, dtype=np.float32)
+        ns = [_c(n, np.float32) for n in norms]
+        x = np.array(x, dtype=np.float32).reshape(-1)
+        qkv = np.zeros((nh + 2 * nkv) * hd, dtype=np.float32)
+        rc = self.L.oracle_bitnet_layer(hidden, inter, nh, nkv, hd, float(eps), ctypes.cast(ptrs, ctypes.c_void_p),
+                                        _p(sw), _p(ns[0]), _p(ns[1]), _p(ns[2]), _p(ns[3]), _p(x), _p(qkv))
+        if rc:
+            raise OracleError("oracle_bitnet_layer failed with status %d" % rc)
+        return x, qkv
+
     def f16_to_f64(self, h: int) -> float:
         return self.L.oracle_f16_to_f64(int(h))
 
@@ -155,6 +199,18 @@ def gemv_i8(*a, **k):
 
 def act_quant_i8(*a, **k):
     return default().act_quant_i8(*a, **k)
+
+
+def rms_norm(*a, **k):
+    return default().rms_norm(*a, **k)
+
+
+def relu2_mul(*a, **k):
+    return default().relu2_mul(*a, **k)
+
+
+def bitnet_layer(*a, **k):
+    return default().bitnet_layer(*a, **k)
 
 
 def f16_to_f64(h: int) -> float:

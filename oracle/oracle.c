@@ -39,6 +39,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -281,4 +282,124 @@ int oracle_gemv_i8(int K, int g, int layout, int n_cb, int64_t N, int64_t Kin,
         }
     }
     return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * One BitNet b1.58 layer as a decode chain for one token (QORA-LLM-2B page,
+ * "SubLN Pattern" listing, and its "Architecture" table for the head
+ * counts): every ternary linear takes its input quantised to int8 per token
+ * (the int8 path above, one plane and a per-tensor scale), and the steps run
+ * in the listing's order.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * RMSNorm (the listing's input, attention-sub, post-attention and FFN-sub
+ * norms): out_i = x_i / sqrt(mean(x^2) + eps) * w_i.  The sum of squares is
+ * taken in fp64 (each square exact), the mean rounded once to fp32, and the
+ * rest is single fp32 operations:
+ *   ms = fl32(ss / n);  r = fl(1 / fl(sqrt(fl(ms + eps))));  out_i = fl(fl(x_i * r) * w_i).
+ */
+int oracle_rms_norm(int64_t n, const float* x, const float* w, float eps, float* out)
+{
+    int64_t i;
+    double ss = 0.0;
+    float ms, r;
+    if (n <= 0 || !x || !w || !out) return OR_ERR_ARG;
+    for (i = 0; i < n; ++i) {
+        if (!isfinite(x[i]) || !isfinite(w[i])) return OR_ERR_VALUE;
+        ss += (double)x[i] * (double)x[i];
+    }
+    ms = (float)(ss / (double)n);
+    r = 1.0f / sqrtf(ms + eps);
+    for (i = 0; i < n; ++i) out[i] = (x[i] * r) * w[i];
+    return OR_OK;
+}
+
+/* The FFN's squared-ReLU gate times the up projection (same listing):
+ * out_i = fl(fl(g'_i * g'_i) * u_i) with g'_i = max(0, g_i). */
+int oracle_relu2_mul(int64_t n, const float* g, const float* u, float* out)
+{
+    int64_t i;
+    if (n < 0 || (n > 0 && (!g || !u || !out))) return OR_ERR_ARG;
+    for (i = 0; i < n; ++i) {
+        float a = g[i] > 0.0f ? g[i] : 0.0f;
+        out[i] = (a * a) * u[i];
+    }
+    return OR_OK;
+}
+
+/* y = fl32 result of one ternary linear (one plane, per-tensor scale s_w) on
+ * the int8 quantisation of x: the int8 path above. */
+static int linear_i8(int64_t N, int64_t Kin, const int8_t* trits, float s_w, const float* x,
+                     float* y, int8_t* q_tmp)
+{
+    float sx;
+    int rc = oracle_act_quant_i8(1, Kin, OR_F32, x, q_tmp, &sx);
+    if (rc) return rc;
+    return oracle_gemv_i8(1, 0, OR_TENSOR, 0, N, Kin, trits, &s_w, 0, 1, q_tmp, &sx, 0, 0, y, 0);
+}
+
+/*
+ * One layer for the first token of a sequence (position 0).  With a single
+ * cached key the attention softmax has one weight, 1, so each query head's
+ * output is the value vector of its KV head: query head h reads KV head
+ * h / (n_heads / n_kv), the consecutive grouping of grouped-query attention.
+ * RoPE, q and k then leave the output unchanged; q, k and v are still
+ * computed and returned (qkv), as a decode step stores k and v.
+ *
+ *   h  = RMSNorm(x, w_in);            q, k, v = W_q h, W_k h, W_v h
+ *   a  = repeat(v);  a = RMSNorm(a, w_attn_sub);  x1 = x + W_o a
+ *   h2 = RMSNorm(x1, w_post);         g, u = W_gate h2, W_up h2
+ *   f  = RMSNorm(relu2(g) * u, w_ffn_sub);  x <- x1 + W_down f
+ *
+ * trits[p], s_w[p]: projection p in the order q, k, v, o, gate, up, down,
+ * int8 [N][Kin] and its per-tensor scale.  x: [hidden], updated in place.
+ * qkv (optional): [(n_heads + 2 n_kv) * head_dim], q then k then v.
+ */
+int oracle_bitnet_layer(int64_t hidden, int64_t inter, int n_heads, int n_kv, int head_dim, float eps,
+                        const int8_t* const* trits, const float* s_w, const float* w_in,
+                        const float* w_attn_sub, const float* w_post, const float* w_ffn_sub,
+                        float* x, float* qkv)
+{
+    const int64_t nq = (int64_t)n_heads * head_dim, nkv = (int64_t)n_kv * head_dim;
+    const int64_t big = hidden > inter ? (hidden > nq ? hidden : nq) : (inter > nq ? inter : nq);
+    int64_t i;
+    int rc = OR_OK;
+    float *h, *q, *k, *v, *a, *o, *x1, *g, *u, *f, *d;
+    int8_t* qt;
+    if (hidden <= 0 || inter <= 0 || n_heads <= 0 || n_kv <= 0 || head_dim <= 0) return OR_ERR_ARG;
+    if (n_heads % n_kv != 0 || nq != hidden) return OR_ERR_SHAPE;
+    h = (float*)malloc(sizeof(float) * (size_t)(big * 8 + nq + 2 * nkv));
+    qt = (int8_t*)malloc((size_t)big);
+    if (!h || !qt) {
+        free(h);
+        free(qt);
+        return OR_ERR_ARG;
+    }
+    q = h + big; k = q + nq; v = k + nkv; a = v + nkv; o = a + big; x1 = o + big;
+    g = x1 + big; u = g + big; f = u + big; d = f + big;
+
+    if ((rc = oracle_rms_norm(hidden, x, w_in, eps, h))) goto done;
+    if ((rc = linear_i8(nq, hidden, trits[0], s_w[0], h, q, qt))) goto done;
+    if ((rc = linear_i8(nkv, hidden, trits[1], s_w[1], h, k, qt))) goto done;
+    if ((rc = linear_i8(nkv, hidden, trits[2], s_w[2], h, v, qt))) goto done;
+    for (i = 0; i < nq; ++i) {
+        const int64_t head = i / head_dim, kvh = head / (n_heads / n_kv);
+        a[i] = v[kvh * head_dim + i % head_dim];
+    }
+    if ((rc = oracle_rms_norm(nq, a, w_attn_sub, eps, a))) goto done;
+    if ((rc = linear_i8(hidden, nq, trits[3], s_w[3], a, o, qt))) goto done;
+    for (i = 0; i < hidden; ++i) x1[i] = x[i] + o[i];
+    if ((rc = oracle_rms_norm(hidden, x1, w_post, eps, h))) goto done;
+    if ((rc = linear_i8(inter, hidden, trits[4], s_w[4], h, g, qt))) goto done;
+    if ((rc = linear_i8(inter, hidden, trits[5], s_w[5], h, u, qt))) goto done;
+    if ((rc = oracle_relu2_mul(inter, g, u, f))) goto done;
+    if ((rc = oracle_rms_norm(inter, f, w_ffn_sub, eps, f))) goto done;
+    if ((rc = linear_i8(hidden, inter, trits[6], s_w[6], f, d, qt))) goto done;
+    for (i = 0; i < hidden; ++i) x[i] = x1[i] + d[i];
+    if (qkv) memcpy(qkv, q, sizeof(float) * (size_t)(nq + 2 * nkv));
+done:
+    free(h);
+    free(qt);
+    return rc;
 }

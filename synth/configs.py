@@ -46,7 +46,7 @@ TENSOR, GROUP_F16, CODEBOOK = 0, 1, 2
 F32, BF16, I8 = 0, 1, 2
 
 # Tensor kinds (low 16 bits of the seed key).
-KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS = 1, 2, 3, 4, 5
+KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS, KIND_NORM = 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -85,4 +85,49 @@ CASES = {
                   BITNET_2B, 1, 0, TENSOR, I8, 2048),
     "cfg5b": Case(6, "Llama-3.1-8B-shaped prefill stack, M=512, K=3, g=256, f16 group scales, bf16 x",
                   LLAMA_8B, 3, 256, GROUP_F16, BF16, 512),
+}
+
+
+@dataclass(frozen=True)
+class Chain:
+    """BitNet b1.58 layers run back to back as one decode chain for one token.
+
+    The layer is the QORA-LLM-2B page's "SubLN Pattern" listing: input
+    RMSNorm, q/k/v, attention, attention-sub RMSNorm, o, residual;
+    post-attention RMSNorm, gate/up, squared ReLU, FFN-sub RMSNorm, down,
+    residual.  The projections' weights follow the BitNet decode stack's
+    recipe (one plane, per-tensor scale) and, with ``weights_cfg`` = 2 and the
+    BitNet shapes, are the very tensors of that stack.
+    """
+    cfg: int
+    name: str
+    layers: int
+    hidden: int
+    inter: int
+    n_heads: int
+    n_kv: int
+    head_dim: int
+    weights_cfg: int
+    eps: float = 1e-5
+
+    def proj_shapes(self):
+        """[(name, N, Kin)] in the order q, k, v, o, gate, up, down."""
+        nq, nkv = self.n_heads * self.head_dim, self.n_kv * self.head_dim
+        return [("q", nq, self.hidden), ("k", nkv, self.hidden), ("v", nkv, self.hidden),
+                ("o", self.hidden, nq), ("gate", self.inter, self.hidden), ("up", self.inter, self.hidden),
+                ("down", self.hidden, self.inter)]
+
+    def dims(self):
+        return (self.hidden, self.inter, self.n_heads, self.n_kv, self.head_dim, self.eps)
+
+    def norm_sizes(self):
+        """Lengths of the four RMSNorm weights: input, attention-sub, post-attention, FFN-sub."""
+        return (self.hidden, self.n_heads * self.head_dim, self.hidden, self.inter)
+
+
+CHAINS = {
+    "chain": Chain(7, "BitNet b1.58-2B decode chain, 30 layers, one token at position 0",
+                   30, 2560, 6912, 20, 5, 128, weights_cfg=2),
+    "chain_small": Chain(8, "BitNet-shaped decode chain at small sizes, 6 layers",
+                         6, 256, 704, 4, 2, 64, weights_cfg=8),
 }

@@ -25,7 +25,7 @@ import numpy as np
 
 from . import gen
 from .configs import (BF16, CODEBOOK, F32, GROUP_F16, I8, KIND_DIGITS,
-                      KIND_INDEX, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
+                      KIND_INDEX, KIND_NORM, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
 
 N_CODEBOOK = 27
 
@@ -122,6 +122,29 @@ def projection(case, layer: int, proj: int, N: int, Kin: int, rows=None, M=None)
     return d
 
 
-__all__ = ["projection", "activations", "plane_values", "plane_values_full", "group_scales",
+def chain_projection(chain, layer: int, proj: int) -> dict:
+    """Projection ``proj`` (q, k, v, o, gate, up, down) of a chain layer:
+    trits int8 [1][N][Kin] and the per-tensor scale fp32 [1], drawn as the
+    BitNet decode stack draws them (its seeds when weights_cfg is 2)."""
+    _, N, Kin = chain.proj_shapes()[proj]
+    s = seeds(chain.weights_cfg, layer, proj)
+    return {"trits": plane_values_full(s["trits"], 1, N, Kin), "scales": tensor_scales(s["scales"], 1),
+            "N": N, "Kin": Kin}
+
+
+def chain_norm(chain, layer: int, which: int) -> np.ndarray:
+    """RMSNorm weight ``which`` (0 input, 1 attention-sub, 2 post-attention,
+    3 FFN-sub) of a chain layer: fp32 uniform over [0.5, 1.5)."""
+    n = chain.norm_sizes()[which]
+    seed = gen.tensor_seed(chain.cfg, layer, which, KIND_NORM)
+    return (0.5 + gen.uniform(seed, 0, n)).astype(np.float32)
+
+
+def chain_input(chain) -> np.ndarray:
+    """The token's hidden state entering layer 0: fp32 N(0, 1) [hidden]."""
+    return gen.normal(gen.tensor_seed(chain.cfg, 0, 0, KIND_X), 0, chain.hidden).astype(np.float32)
+
+
+__all__ = ["projection", "chain_projection", "chain_norm", "chain_input", "activations", "plane_values", "plane_values_full", "group_scales",
            "tensor_scales", "codebook_indices", "seeds", "N_CODEBOOK",
            "TENSOR", "GROUP_F16", "CODEBOOK", "F32", "BF16", "I8"]
