@@ -258,8 +258,9 @@ tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);
  * Many prefill products (tq_gemm) in one launch, e.g. every projection of a
  * layer stack.  All problems must share K, scale layout and x_type; M is
  * common.  The work list holds one item per output tile (16 tokens x 256 rows
- * for TQ_BF16 with M <= 16, else 128 x 128), longest problems first.  The plan is the decode one's struct: on return waves = 4
- * and row_blocks = 64-row blocks per tile; tq_gemv_grouped_run refuses it.
+ * for TQ_BF16 with M <= 16, else 128 x 128), longest problems first.  The
+ * plan is the decode one's struct: on return waves = 4 and row_blocks =
+ * 64-row blocks per tile; tq_gemv_grouped_run runs it as well.
  */
 tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, int32_t count, int64_t M,
                                          int32_t x_type, size_t* bytes);
@@ -270,6 +271,99 @@ tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int
                                   tq_grouped_plan* plan, void* stream);
 /* One launch computing every problem of the plan.  Asynchronous. */
 tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream);
+
+/*
+ * Decode chain: BitNet b1.58 layers run back to back for one token in one
+ * persistent launch, in the order of the QORA-LLM-2B page's "SubLN Pattern"
+ * listing (head counts from its "Architecture" table).  Per layer, with x
+ * the token's hidden state:
+ *
+ *   h  = RMSNorm(x, norm[0]);            q, k, v = W_q h, W_k h, W_v h
+ *   a  = attention(q, k, v);             x1 = x + W_o RMSNorm(a, norm[1])
+ *   h2 = RMSNorm(x1, norm[2]);           g, u = W_gate h2, W_up h2
+ *   x  = x1 + W_down RMSNorm(relu2(g) * u, norm[3]),   relu2(z) = max(0, z)^2
+ *
+ * The token is at position 0: attention over its single cached key has
+ * softmax weight 1, so each query head's output is the value vector of its
+ * KV group (query head h reads KV head h / (n_heads / n_kv_heads)); q and k
+ * do not reach x but are computed and returned, as a decode step stores its
+ * keys and values.
+ *
+ * Arithmetic, step by step (the CPU oracle's, bit for bit):
+ *  - every ternary linear runs on the int8 path: its input is quantised per
+ *    token by tq_act_quant_int8's rule, and its output is
+ *    fl(float(acc) * fl(s_w * s_x)) with acc the exact int32 sum;
+ *  - RMSNorm: the sum of squares in fp64, the mean rounded once to fp32,
+ *    r = fl(1 / fl(sqrt(fl(mean + eps)))), out_i = fl(fl(v_i * r) * w_i);
+ *  - relu2(g) * u = fl(fl(g' * g') * u), g' = max(g, 0); the residual adds
+ *    are single fp32 adds.
+ * The fp64 sums of squares are added in another order than the oracle's;
+ * the fp32 mean can differ only when the exact sum lies within ~1e-14
+ * relative of an fp32 rounding boundary.
+ */
+typedef struct tq_bitnet_dims {
+    int32_t hidden;               /* model width; n_heads * head_dim == hidden  */
+    int32_t intermediate;         /* FFN width                                  */
+    int32_t n_heads;              /* query heads                                */
+    int32_t n_kv_heads;           /* KV heads, dividing n_heads                 */
+    int32_t head_dim;
+    float eps;                    /* RMSNorm epsilon                            */
+} tq_bitnet_dims;
+
+/* One layer's weights, all device pointers owned by the caller. */
+typedef struct tq_bitnet_layer {
+    /* blobs packed by tq_pack with planes = 1, TQ_SCALE_TENSOR, shapes (N x Kin)
+       q: n_heads*head_dim x hidden, k and v: n_kv_heads*head_dim x hidden,
+       o: hidden x n_heads*head_dim, gate and up: intermediate x hidden,
+       down: hidden x intermediate -- in that order                            */
+    const void* w[7];
+    /* fp32 RMSNorm weights: input [hidden], attention-sub [hidden],
+       post-attention [hidden], FFN-sub [intermediate]                         */
+    const float* norm[4];
+} tq_bitnet_layer;
+
+/* Filled by tq_bitnet_chain_prepare; plain data, may be copied. */
+typedef struct tq_chain_plan {
+    void* workspace;              /* device: layer table and chain state        */
+    int32_t n_layers;
+    int32_t workgroups;           /* in: 0 (default) or a count; out: the grid  */
+    tq_bitnet_dims dims;
+    int32_t reserved[4];
+} tq_chain_plan;
+
+/* Device workspace bytes that tq_bitnet_chain_prepare needs. */
+tq_status tq_bitnet_chain_workspace_size(const tq_bitnet_dims* dims, int32_t n_layers, size_t* bytes);
+
+/*
+ * Validate the dimensions and the layers (`layers` is a host array of
+ * n_layers; each blob's header is read back to check its shape and format),
+ * write the layer table into `workspace` (device, caller-owned, kept for the
+ * plan's lifetime) and clear the chain state.  Widths up to 16384, each a
+ * multiple of 16.  plan->workgroups on entry: 0 for one workgroup per
+ * compute unit, else the grid to use (at most what fits the GPU at once).
+ * Copies host->device on `stream` and synchronizes it.
+ */
+tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq_bitnet_layer* layers,
+                                  int32_t n_layers, void* workspace, size_t workspace_bytes,
+                                  tq_chain_plan* plan, void* stream);
+
+/*
+ * Run every layer of the plan on one token.  x: device fp32 [hidden], the
+ * hidden state entering the first layer on entry and leaving the last on
+ * return.  qkv: optional device fp32 [n_layers][(n_heads + 2 n_kv_heads) *
+ * head_dim], each layer's q, k and v.  One cooperative launch (all
+ * workgroups resident, synchronising at the four phase boundaries of each
+ * layer) after a small reset launch.  Asynchronous; runs on one stream at a
+ * time per workspace.
+ */
+tq_status tq_bitnet_chain_run(const tq_chain_plan* plan, float* x, float* qkv, void* stream);
+
+/*
+ * Synchronize `stream` and report whether the plan's last run completed:
+ * TQ_ERR_DEVICE if a phase barrier gave up waiting (the grid was not all
+ * resident) -- x is then undefined.
+ */
+tq_status tq_bitnet_chain_status(const tq_chain_plan* plan, void* stream);
 
 #ifdef __cplusplus
 }

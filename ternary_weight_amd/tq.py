@@ -57,6 +57,20 @@ class tq_grouped_plan(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class tq_bitnet_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class tq_bitnet_layer(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p * 7), ("norm", ctypes.c_void_p * 4)]
+
+
+class tq_chain_plan(ctypes.Structure):
+    _fields_ = [("workspace", ctypes.c_void_p), ("n_layers", ctypes.c_int32),
+                ("workgroups", ctypes.c_int32), ("dims", tq_bitnet_dims), ("reserved", ctypes.c_int32 * 4)]
+
+
 # Every symbol the header declares, with its ctypes signature.
 _VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _DESC = ctypes.POINTER(tq_weight_desc)
@@ -81,6 +95,12 @@ SIGNATURES = {
     "tq_gemm_grouped_prepare": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32, _VP,
                                  ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_gemm_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
+    "tq_bitnet_chain_workspace_size": ([ctypes.POINTER(tq_bitnet_dims), _I32, ctypes.POINTER(ctypes.c_size_t)],
+                                       _I32),
+    "tq_bitnet_chain_prepare": ([ctypes.POINTER(tq_bitnet_dims), ctypes.POINTER(tq_bitnet_layer), _I32, _VP,
+                                 ctypes.c_size_t, ctypes.POINTER(tq_chain_plan), _VP], _I32),
+    "tq_bitnet_chain_run": ([ctypes.POINTER(tq_chain_plan), _VP, _VP, _VP], _I32),
+    "tq_bitnet_chain_status": ([ctypes.POINTER(tq_chain_plan), _VP], _I32),
 }
 
 _lib = None
@@ -230,3 +250,38 @@ def gemm_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, stream=No
 
 def gemm_grouped_run(plan, stream=None):
     _check(lib().tq_gemm_grouped_run(ctypes.byref(plan), _stream(stream)), "tq_gemm_grouped_run")
+
+
+def bitnet_dims(hidden: int, intermediate: int, n_heads: int, n_kv_heads: int, head_dim: int,
+                eps: float) -> tq_bitnet_dims:
+    return tq_bitnet_dims(hidden, intermediate, n_heads, n_kv_heads, head_dim, eps)
+
+
+def bitnet_chain_workspace_size(dims: tq_bitnet_dims, n_layers: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tq_bitnet_chain_workspace_size(ctypes.byref(dims), n_layers, ctypes.byref(n)),
+           "tq_bitnet_chain_workspace_size")
+    return n.value
+
+
+def bitnet_chain_prepare(dims: tq_bitnet_dims, layers, workspace, workspace_bytes, workgroups=0, stream=None):
+    """layers: one (7 blobs q, k, v, o, gate, up, down; 4 norm weights) pair per layer."""
+    arr = (tq_bitnet_layer * len(layers))()
+    for i, (ws, ns) in enumerate(layers):
+        for p in range(7):
+            arr[i].w[p] = _ptr(ws[p])
+        for j in range(4):
+            arr[i].norm[j] = _ptr(ns[j])
+    plan = tq_chain_plan()
+    plan.workgroups = workgroups
+    _check(lib().tq_bitnet_chain_prepare(ctypes.byref(dims), arr, len(layers), _ptr(workspace), workspace_bytes,
+                                         ctypes.byref(plan), _stream(stream)), "tq_bitnet_chain_prepare")
+    return plan
+
+
+def bitnet_chain_run(plan, x, qkv=None, stream=None):
+    _check(lib().tq_bitnet_chain_run(ctypes.byref(plan), _ptr(x), _ptr(qkv), _stream(stream)), "tq_bitnet_chain_run")
+
+
+def bitnet_chain_status(plan, stream=None):
+    _check(lib().tq_bitnet_chain_status(ctypes.byref(plan), _stream(stream)), "tq_bitnet_chain_status")

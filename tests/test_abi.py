@@ -213,3 +213,25 @@ def test_grouped_shape_must_fit_the_workgroup_lds():
         plan.family = ((fam_x * 3 + 0) * 4 + 3) * 3 + 2     # x type, per-tensor, 4 planes, 16 tokens
         plan.waves, plan.row_blocks, plan.n_problems = 16, 1, 1
         assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_UNSUPPORTED
+
+
+def test_chain_workspace_size_validation():
+    """tq_bitnet_chain_workspace_size checks the dimensions on the host."""
+    ok = tq.bitnet_dims(2560, 6912, 20, 5, 128, 1e-5)
+    n1 = tq.bitnet_chain_workspace_size(ok, 1)
+    n30 = tq.bitnet_chain_workspace_size(ok, 30)
+    assert n30 > n1 > 0 and n1 % 256 == 0
+    bad = [
+        (tq.bitnet_dims(2560, 6912, 20, 6, 128, 1e-5), tq.ERR_SHAPE),      # 20 % 6
+        (tq.bitnet_dims(2560, 6912, 16, 4, 128, 1e-5), tq.ERR_SHAPE),      # heads * dim != hidden
+        (tq.bitnet_dims(2560, 6900, 20, 5, 128, 1e-5), tq.ERR_SHAPE),      # width % 16
+        (tq.bitnet_dims(20480, 6912, 160, 5, 128, 1e-5), tq.ERR_UNSUPPORTED),   # wider than LDS holds
+        (tq.bitnet_dims(2560, 6912, 20, 5, 128, float("nan")), tq.ERR_VALUE),
+    ]
+    for d, status in bad:
+        with pytest.raises(tq.TQError) as e:
+            tq.bitnet_chain_workspace_size(d, 1)
+        assert e.value.status == status
+    with pytest.raises(tq.TQError) as e:
+        tq.bitnet_chain_workspace_size(ok, 0)
+    assert e.value.status == tq.ERR_ARG
