@@ -30,13 +30,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from synth import device, gen, inputs  # noqa: E402
-from synth.configs import BF16, CASES, CODEBOOK, F32, GROUP_F16, I8, TENSOR  # noqa: E402
+from synth.configs import BF16, CASES, CHAINS, CODEBOOK, F32, GROUP_F16, I8, TENSOR  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "ternary_weight_amd", "csrc")
 METRIC = "ternary GEMV effective HBM GB/s (% of peak) at BitNet-2B/Llama-8B shapes, M=1"
 METRIC_PREFILL = "ternary prefill GEMM effective TOP/s (MFMA utilisation) at BitNet-2B/Llama-8B shapes"
+METRIC_CHAIN = "BitNet-2B decode chain effective HBM GB/s (% of peak), one token through every layer"
 MFMA_PEAK_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
 MFMA_PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 
@@ -49,8 +50,10 @@ def parse():
     ap.add_argument("--spin-up-ms", type=float, default=150.0,
                     help="plain streaming reads before the warmup steps: the GPU needs ~20 ms of "
                          "memory load to leave its idle clocks")
-    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b"],
-                    help="cfg2-4: decode stacks (tq_gemv_grouped_*); cfg5a/b: prefill stacks (tq_gemm_grouped_*)")
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b", "chain"],
+                    help="cfg2-4: decode stacks (tq_gemv_grouped_*); cfg5a/b: prefill stacks (tq_gemm_grouped_*); "
+                         "chain: the BitNet b1.58-2B layers as a dependent decode chain (tq_bitnet_chain_*)")
+    ap.add_argument("--workgroups", type=int, default=0, help="chain: grid of the persistent launch (0 = default)")
     ap.add_argument("--M", type=int, default=1, help="tokens per step (cfg4: 1, 4 or 16)")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
@@ -344,6 +347,7 @@ _COMMON_SOURCES = ["tq_decode.h", "tq_internal.h", "tq_layout.h"]
 _FAMILY_SOURCES = {
     "k_gemv": ["tq_gemv_impl.h", "tq_gemv.hip", "tq_entry.hip"],
     "k_gemm": ["tq_gemm_impl.h", "tq_gemm_kernels.h", "tq_gemm.hip"],
+    "k_bitnet_chain": ["tq_chain.hip", "tq_gemv_impl.h"],
 }
 
 
@@ -462,6 +466,9 @@ def main():
         print("bench.py measures one GPU only; the multi-GPU path is not built (--gpus %d refused)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.config == "chain":
+        main_chain(args)
+        return
     import torch
     case = CASES[args.config]
     M = args.M if args.config == "cfg4" else case.M
@@ -516,8 +523,12 @@ def main():
         peak = MFMA_PEAK_I8_TOPS if case.x_type == I8 else MFMA_PEAK_BF16_TFLOPS
         unit = "TOP/s" if case.x_type == I8 else "TFLOP/s"
     else:
-        kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
-                                                          1 if M == 1 else (4 if M <= 4 else 16))
+        if stack.plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
+            ks = 32 if case.layout == TENSOR or case.group % 32 == 0 else 16
+            kernel_name = "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (stack.run_type, case.layout, case.planes, ks)
+        else:
+            kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
+                                                              1 if M == 1 else (4 if M <= 4 else 16))
         value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
         achieved = gbytes / (gemv_avg / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
@@ -573,6 +584,150 @@ def main():
         },
         "cpu_baseline": cpu,
         "hbm_ceiling": ceiling,
+        "parity_spot_check": check,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+# The decode chain: one token through every BitNet layer, dependencies kept.
+# ---------------------------------------------------------------------------
+def chain_bytes(chain, blob_bytes: int) -> int:
+    """Algorithmic bytes of one token through the chain: the packed trits and
+    scales of every projection, the RMSNorm weights, and each phase's input
+    read and output written once (fp32)."""
+    sizes = chain.norm_sizes()
+    per_layer = 4 * sum(sizes)                                       # norm weights
+    nqkv = (chain.n_heads + 2 * chain.n_kv) * chain.head_dim
+    per_layer += 4 * (chain.hidden + nqkv)                           # QKV: x in, q|k|v out
+    per_layer += 4 * (chain.n_kv * chain.head_dim + 2 * chain.hidden)   # O: v in, x in, x1 out
+    per_layer += 4 * (chain.hidden + chain.inter)                    # GU: x1 in, act out
+    per_layer += 4 * (chain.inter + 2 * chain.hidden)                # DOWN: act in, x1 in, x out
+    trits = sum(n * kin // 4 + 4 for (_, n, kin) in chain.proj_shapes()) * chain.layers
+    return trits + per_layer * chain.layers
+
+
+def chain_spot_check(chain, blobs, norms_dev, dims) -> dict:
+    """The first layer on its own plan, against the oracle on host-regenerated inputs."""
+    import oracle
+    import torch
+    from ternary_weight_amd import tq
+    nbytes = tq.bitnet_chain_workspace_size(dims, 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    plan = tq.bitnet_chain_prepare(dims, [(blobs[0:7], norms_dev[0])], ws, nbytes)
+    x = torch.from_numpy(inputs.chain_input(chain)).cuda()
+    tq.bitnet_chain_run(plan, x)
+    tq.bitnet_chain_status(plan)
+    ws_ = [inputs.chain_projection(chain, 0, p) for p in range(7)]
+    norms = [inputs.chain_norm(chain, 0, j) for j in range(4)]
+    ref, _ = oracle.bitnet_layer(chain.dims(), [w["trits"][0] for w in ws_],
+                                 np.array([w["scales"][0] for w in ws_], dtype=np.float32), norms,
+                                 inputs.chain_input(chain))
+    got = x.cpu().numpy()
+    return {"layers": 1, "bit_exact": bool(np.array_equal(got.view(np.uint32), ref.view(np.uint32)))}
+
+
+def chain_cpu_baseline(chain, seconds: float) -> dict:
+    import oracle
+    orc = oracle.default()
+    ws_ = [inputs.chain_projection(chain, 0, p) for p in range(7)]
+    trits = [w["trits"][0] for w in ws_]
+    s_w = np.array([w["scales"][0] for w in ws_], dtype=np.float32)
+    norms = [inputs.chain_norm(chain, 0, j) for j in range(4)]
+    x = inputs.chain_input(chain)
+    layer_bytes = chain_bytes(chain, 0) / chain.layers
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.bitnet_layer(chain.dims(), trits, s_w, norms, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(layer_bytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "layer 0 of the chain, %d repetitions, %.1f s (%.2f tokens/s over %d layers); C oracle, "
+                      "one thread" % (reps, el, reps / el / chain.layers, chain.layers)}
+
+
+def main_chain(args):
+    import torch
+    from ternary_weight_amd import tq
+    chain = CHAINS["chain"]
+    t_build = time.perf_counter()
+    # the decode stack's packed projections are the chain's weights (same seeds and recipe)
+    stack = Stack(CASES["cfg2"], 1, fused=False)
+    assert len(stack.blobs) == 7 * chain.layers
+    norms_dev = [[torch.from_numpy(inputs.chain_norm(chain, l, j)).cuda() for j in range(4)]
+                 for l in range(chain.layers)]
+    dims = tq.bitnet_dims(*chain.dims())
+    nbytes = tq.bitnet_chain_workspace_size(dims, chain.layers)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    layers = [(stack.blobs[7 * l:7 * l + 7], norms_dev[l]) for l in range(chain.layers)]
+    plan = tq.bitnet_chain_prepare(dims, layers, ws, nbytes, workgroups=args.workgroups)
+    x0 = torch.from_numpy(inputs.chain_input(chain)).cuda()
+    x = x0.clone()
+    print("built chain: %d layers, %.1f MB packed, %d workgroups (%.1f s)"
+          % (chain.layers, stack.blob_bytes / 1e6, plan.workgroups, time.perf_counter() - t_build),
+          file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    spin_up(args.spin_up_ms)
+    for _ in range(args.warmup):
+        tq.bitnet_chain_run(plan, x)
+    tq.bitnet_chain_status(plan)
+    # timed region: K tokens, each through every layer (the state carries over
+    # from token to token; the work does not depend on its values)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        tq.bitnet_chain_run(plan, x)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tq.bitnet_chain_status(plan)
+    ms_step = start.elapsed_time(end) / args.steps
+    gbytes = chain_bytes(chain, stack.blob_bytes)
+    value = gbytes / (ms_step / 1e3) / 1e9
+    check = None if args.no_check else chain_spot_check(chain, stack.blobs, norms_dev, dims)
+    cpu = None if args.no_cpu_baseline else chain_cpu_baseline(chain, args.cpu_seconds)
+    kernel_name = "k_bitnet_chain"
+    out = {
+        "metric": METRIC_CHAIN,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded SplitMix64; the BitNet decode stack's weights, RMSNorm weights U[0.5, 1.5), "
+                "x ~ N(0,1))",
+        "config": {
+            "workload": chain.name,
+            "layers": chain.layers,
+            "M": 1,
+            "step": "one token through every layer: a reset launch and one cooperative launch (4 phases per layer, "
+                    "grid barrier between phases)",
+            "packed_weight_bytes": stack.blob_bytes,
+            "workgroups": plan.workgroups,
+        },
+        "tok_per_s": round(1e3 / ms_step, 1),
+        "us_per_layer": round(ms_step * 1e3 / chain.layers, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(value, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(kernel_name),
+            "kernel": kernel_name,
+            "bytes_per_launch": gbytes,
+        },
+        "cpu_baseline": cpu,
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }

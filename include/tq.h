@@ -338,9 +338,9 @@ tq_status tq_bitnet_chain_workspace_size(const tq_bitnet_dims* dims, int32_t n_l
  * Validate the dimensions and the layers (`layers` is a host array of
  * n_layers; each blob's header is read back to check its shape and format),
  * write the layer table into `workspace` (device, caller-owned, kept for the
- * plan's lifetime) and clear the chain state.  Widths up to 16384, each a
- * multiple of 16.  plan->workgroups on entry: 0 for one workgroup per
- * compute unit, else the grid to use (at most what fits the GPU at once).
+ * plan's lifetime) and clear the chain state.  Widths up to 8192, each a
+ * multiple of 16.  plan->workgroups on entry: 0 for one workgroup per two
+ * compute units, else the grid to use (at most what fits the GPU at once).
  * Copies host->device on `stream` and synchronizes it.
  */
 tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq_bitnet_layer* layers,

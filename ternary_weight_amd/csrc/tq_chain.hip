@@ -45,7 +45,7 @@ using namespace tqk;
 
 constexpr int kThreads = 512;            // 8 waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxWidth = 16384;         // longest phase input held in LDS
+constexpr int kMaxWidth = 8192;          // longest phase input (held in registers, 16 per thread)
 constexpr uint32_t kSpinLimit = 1u << 22;   // barrier polls before giving up (~seconds)
 
 enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3 };
@@ -80,7 +80,25 @@ struct ChainDev {
 
 // ---------------------------------------------------------------------------
 // Device side.
+//
+// Data that one workgroup writes and others read (the phase outputs and the
+// hidden state) moves only through agent-scope accesses, which reach memory
+// past the per-XCD L2s (sc1): so no cache needs writing back or invalidating
+// at a barrier -- a barrier only waits for the workgroup's own stores to
+// complete before it arrives.  Everything else the kernel reads is
+// read-only for the whole launch and stays cached.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float ld_shared(const float* p)
+{
+    return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_shared(float* p, float v)
+{
+    __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores and atomics have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 struct Item {
     int proj;           // projection of waves 0 .. kWaves/2 - 1 (GU) or of all waves
     int rb;             // 64-row block within the projection
@@ -89,9 +107,8 @@ struct Item {
     int off;            // first accumulator row of the block (of gate for GU)
 };
 
-__device__ __forceinline__ Item item_of(const ChainDev& C, int ph, int item)
+__device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, int ph, int item)
 {
-    const PhaseDev& P = C.ph[ph];
     Item it;
     it.group = item / P.splits;
     it.split = item - it.group * P.splits;
@@ -113,21 +130,23 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, int ph, int item)
 }
 
 // Grid barrier number `index` (0-based over the run).  Returns false when it
-// gave up, or when another workgroup did (every wait is bounded).
+// gave up, or when another workgroup did (every wait is bounded).  Every
+// wave has waited for its phase's stores before (at the end of its items),
+// so that the loads issued for the next phase meanwhile are not waited for.
 __device__ bool grid_sync(const ChainDev& C, uint32_t index, int* flag_lds)
 {
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t target = (index + 1) * (uint32_t)C.G;
-        __hip_atomic_fetch_add(C.bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(C.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
         int ok = 1;
-        while (__hip_atomic_load(C.bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (__hip_atomic_load(C.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             if (__hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
                 ok = 0;
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(1);
             if (++spins >= kSpinLimit) {
                 __hip_atomic_store(C.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
@@ -137,7 +156,6 @@ __device__ bool grid_sync(const ChainDev& C, uint32_t index, int* flag_lds)
         *flag_lds = ok;
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return *flag_lds != 0;
 }
 
@@ -151,28 +169,45 @@ __device__ __forceinline__ double wave_sum_f64(double v)
 // Input element i of a phase (global memory written by the previous phase).
 __device__ __forceinline__ float phase_input(const ChainDev& C, int ph, const float* x, int i)
 {
-    if (ph == PH_QKV) return x[i];
-    if (ph == PH_GU) return C.x1[i];
-    if (ph == PH_DOWN) return C.act[i];
+    if (ph == PH_QKV) return ld_shared(x + i);
+    if (ph == PH_GU) return ld_shared(C.x1 + i);
+    if (ph == PH_DOWN) return ld_shared(C.act + i);
     // O: repeat(v): query head h reads KV head h / (n_heads / n_kv)
     const int head = i / C.head_dim, d = i - head * C.head_dim;
     const int kvh = head / (C.n_heads / C.n_kv);
-    return C.qkv[C.nq + C.nkv + kvh * C.head_dim + d];
+    return ld_shared(C.qkv + C.nq + C.nkv + kvh * C.head_dim + d);
 }
 
 // RMSNorm of the phase input with weight w, then the per-token absmax int8
 // quantisation, into LDS (xq, zero-padded to whole 64-column chunks) and
-// *sx.  The steps are tq.h's; every workgroup computes the same bytes.
-__device__ void norm_quant(const ChainDev& C, int ph, const float* x, const float* w, int n, float* vin,
-                           int8_t* xq, float* sx, double* red_d, float* red_f)
+// *sx.  The steps are tq.h's; every workgroup computes the same bytes.  A
+// thread holds its kPer inputs and weights in registers, all loads issued
+// before the first use.
+constexpr int kPer = kMaxWidth / kThreads;
+
+__device__ __forceinline__ void load_norm_weight(const float* w, int n, float (&wt)[kPer])
+{
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        wt[j] = i < n ? w[i] : 0.0f;
+    }
+}
+
+__device__ void norm_quant(const ChainDev& C, int ph, const float* x, const float* w, int n, int8_t* xq,
+                           float* sx, double* red_d, float* red_f)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    double ss = 0.0;
-    for (int i = tid; i < n; i += kThreads) {
-        const float v = phase_input(C, ph, x, i);
-        vin[i] = v;
-        ss += (double)v * (double)v;
+    float v[kPer], wt[kPer];
+    load_norm_weight(w, n, wt);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kThreads;
+        v[j] = i < n ? phase_input(C, ph, x, i) : 0.0f;
     }
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) ss += (double)v[j] * (double)v[j];
     ss = wave_sum_f64(ss);
     if (lane == 0) red_d[wave] = ss;
     __syncthreads();
@@ -181,10 +216,10 @@ __device__ void norm_quant(const ChainDev& C, int ph, const float* x, const floa
     const float ms = (float)(ss / (double)n);
     const float r = 1.0f / sqrtf(ms + C.eps);
     float a = 0.0f;
-    for (int i = tid; i < n; i += kThreads) {
-        const float h = __fmul_rn(__fmul_rn(vin[i], r), w[i]);
-        vin[i] = h;
-        a = fmaxf(a, fabsf(h));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        v[j] = __fmul_rn(__fmul_rn(v[j], r), wt[j]);   // zero past n
+        a = fmaxf(a, fabsf(v[j]));
     }
     a = wave_max(a);
     if (lane == 0) red_f[wave] = a;
@@ -193,20 +228,24 @@ __device__ void norm_quant(const ChainDev& C, int ph, const float* x, const floa
     for (int k = 1; k < kWaves; ++k) a = fmaxf(a, red_f[k]);
     const float inv = a > 0.0f ? 127.0f / a : 0.0f;
     const int npad = (n + TQ_CHUNK - 1) / TQ_CHUNK * TQ_CHUNK;
-    for (int i = tid; i < npad; i += kThreads) {
-        int8_t q = 0;
-        if (i < n) {
-            float t = rintf(__fmul_rn(vin[i], inv));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < npad) {
+            float t = rintf(__fmul_rn(v[j], inv));
             t = fminf(fmaxf(t, -127.0f), 127.0f);
-            q = (int8_t)(int)t;
+            xq[i] = (int8_t)(int)t;
         }
-        xq[i] = q;
     }
     if (tid == 0) *sx = a > 0.0f ? a / 127.0f : 0.0f;
     __syncthreads();
 }
 
-using RB = RowBlock<TQ_F32_Q8, TQ_SCALE_TENSOR, 1, 1>;
+#ifndef TQ_CHAIN_DEPTH
+#define TQ_CHAIN_DEPTH 2     // chunks in flight per wave (measured: 4, 6 and 8 were no faster; the
+                             // phase time is in the barrier, the input's round trip and the stores)
+#endif
+using RB = RowBlock<TQ_F32_Q8, TQ_SCALE_TENSOR, 1, 1, TQ_CHAIN_DEPTH>;
 
 // The chunk range of this wave within an item: split s of the block's NC
 // chunks, then this wave's share among `nw` waves.
@@ -220,7 +259,6 @@ __device__ __forceinline__ void wave_range(int NC, int splits, int s, int nw, in
 __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __restrict__ Cp, float* x, float* qkv_out)
 {
     const ChainDev C = ld_uniform_struct(Cp);
-    __shared__ float vin[kMaxWidth];
     __shared__ __attribute__((aligned(16))) int8_t xq[kMaxWidth];
     __shared__ int32_t red[kWaves][64];
     __shared__ double red_d[kWaves];
@@ -233,15 +271,14 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
 
     for (int l = 0; l < C.n_layers; ++l) {
         const LayerDev& Ld = C.layers[l];
-#pragma unroll
         for (int ph = 0; ph < 4; ++ph) {
-            const PhaseDev P = C.ph[ph];
+            const PhaseDev P = ld_uniform_struct(&Cp->ph[ph]);
             // GU: waves 0..3 run gate, 4..7 up; else all waves one projection
             const int nw = ph == PH_GU ? kWaves / 2 : kWaves;
             const int wp = ph == PH_GU ? wave / nw : 0;
             const int ws = wave - wp * nw;
             const int first = blockIdx.x;
-            Item it = item_of(C, ph, first < P.items ? first : 0);
+            Item it = item_of(C, P, ph, first < P.items ? first : 0);
             const tq_prob_dev& Pp = Ld.p[it.proj + wp];
             int c0 = 0, c1 = 0;
             if (first < P.items) wave_range(Pp.NC, P.splits, it.split, nw, ws, &c0, &c1);
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
             if (l > 0 || ph > 0) {
                 if (!grid_sync(C, nbar++, &flag)) return;
             }
-            norm_quant(C, ph, x, Ld.norm[ph], P.width, vin, xq, &sx_lds, red_d, (float*)red_f);
+            norm_quant(C, ph, x, Ld.norm[ph], P.width, xq, &sx_lds, red_d, (float*)red_f);
             const float sx = sx_lds;
             for (int item = first; item < P.items; item += C.G) {
                 int part;
@@ -258,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     blk.finish(nullptr);
                     part = blk.p[0][0];
                 } else {
-                    it = item_of(C, ph, item);
+                    it = item_of(C, P, ph, item);
                     const tq_prob_dev& Pq = Ld.p[it.proj + wp];
                     wave_range(Pq.NC, P.splits, it.split, nw, ws, &c0, &c1);
                     RB b2(Pq, it.rb, xq, nullptr);
@@ -279,13 +316,13 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     if (P.splits > 1) {
                         __hip_atomic_fetch_add(C.acc + ra, sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         if (ph == PH_GU) __hip_atomic_fetch_add(C.acc + rbw, sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        wait_stores();     // the partial sums are in before the count says so
                         uint32_t old = 0;
                         if (lane == 0)
-                            old = __hip_atomic_fetch_add(C.cnt + it.group, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                            old = __hip_atomic_fetch_add(C.cnt + it.group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         old = __shfl(old, 0, 64);
                         last = old == (uint32_t)P.splits - 1;
                         if (last) {
-                            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                             sa = __hip_atomic_exchange(C.acc + ra, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             if (ph == PH_GU) sb = __hip_atomic_exchange(C.acc + rbw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             if (lane == 0) __hip_atomic_store(C.cnt + it.group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -297,23 +334,24 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                         const float ca = __fmul_rn(ld_uniform((const float*)Pa.scales), sx);
                         const float ya = __fmul_rn((float)sa, ca);
                         if (ph == PH_QKV) {
-                            C.qkv[it.off + lane] = ya;
+                            st_shared(C.qkv + it.off + lane, ya);
                             if (qkv_out) qkv_out[(int64_t)l * (C.nq + 2 * C.nkv) + it.off + lane] = ya;
                         } else if (ph == PH_O) {
-                            C.x1[n] = x[n] + ya;
+                            st_shared(C.x1 + n, __fadd_rn(ld_shared(x + n), ya));
                         } else if (ph == PH_GU) {
                             const tq_prob_dev& Pb = Ld.p[W_UP];
                             const float cb = __fmul_rn(ld_uniform((const float*)Pb.scales), sx);
                             const float u = __fmul_rn((float)sb, cb);
                             const float g = fmaxf(ya, 0.0f);
-                            C.act[n] = __fmul_rn(__fmul_rn(g, g), u);
+                            st_shared(C.act + n, __fmul_rn(__fmul_rn(g, g), u));
                         } else {
-                            x[n] = C.x1[n] + ya;
+                            st_shared(x + n, __fadd_rn(ld_shared(C.x1 + n), ya));
                         }
                     }
                 }
                 __syncthreads();
             }
+            wait_stores();    // this phase's outputs are in memory before the barrier
         }
     }
 }
@@ -455,7 +493,10 @@ TQ_EXPORT tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq
     int G = plan->workgroups;
     const int lim = grid_limit();
     if (lim <= 0) return tq_fail(TQ_ERR_DEVICE, "no occupancy for the chain kernel");
-    if (G <= 0) G = std::min(lim, tq_device_cus());
+    // default: one workgroup per two compute units -- enough items for every
+    // phase of the BitNet shapes, and a cheaper barrier than one per unit
+    // (measured 1.64 ms per token against 2.0 ms with 256)
+    if (G <= 0) G = std::min(lim, std::max(1, tq_device_cus() / 2));
     if (G > lim) return tq_fail(TQ_ERR_UNSUPPORTED, "%d workgroups requested, %d fit at once", G, lim);
 
     uint8_t* ws = (uint8_t*)workspace;

@@ -296,15 +296,18 @@ struct XChunk {   // activations of one 64-column chunk of one token (SGPRs, or 
 };
 
 // One row block (64 rows) of one problem, columns split across `nwaves` waves.
-template <int XT, int LAYOUT, int K, int MT>
+// kDepth: chunks in flight per wave (0: the decode kernels' tuned depth).
+template <int XT, int LAYOUT, int K, int MT, int kDepth = 0>
 struct RowBlock {
     using A = typename AccT<XT>::type;
     static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     // chunks in flight per wave (codes of K planes each)
-    static constexpr int D = MT > 1 ? 1 : (XT == TQ_BF16 ? TQ_DEPTH_BF16 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN));
+    static constexpr int D = kDepth > 0 ? kDepth
+                           : (MT > 1 ? 1 : (XT == TQ_BF16 ? TQ_DEPTH_BF16 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN)));
     static_assert(XT != TQ_BF16 || sizeof(typename AccT<XT>::type) == 4, "bf16 accumulates in fp32");
-    // activations are prefetched a chunk ahead for one token (SGPR budget)
-    static constexpr bool kXPre = MT == 1 && (XT == TQ_I8 || XT == TQ_F32_Q8);
+    // activations are prefetched a chunk ahead for one token (SGPR budget);
+    // not with an explicit depth (the chain reads its x from LDS as it goes)
+    static constexpr bool kXPre = kDepth == 0 && MT == 1 && (XT == TQ_I8 || XT == TQ_F32_Q8);
 
     const tq_prob_dev& P;
     const int rb, lane;
