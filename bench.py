@@ -710,8 +710,8 @@ def main_chain(args):
             "workload": chain.name,
             "layers": chain.layers,
             "M": 1,
-            "step": "one token through every layer: a reset launch and one cooperative launch (4 phases per layer, "
-                    "grid barrier between phases)",
+            "step": "one token through every layer: a reset launch and one cooperative launch (4 phases per layer; "
+                    "a phase waits until the blocks it reads are written)",
             "packed_weight_bytes": stack.blob_bytes,
             "workgroups": plan.workgroups,
         },

@@ -352,15 +352,15 @@ tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq_bitnet_la
  * hidden state entering the first layer on entry and leaving the last on
  * return.  qkv: optional device fp32 [n_layers][(n_heads + 2 n_kv_heads) *
  * head_dim], each layer's q, k and v.  One cooperative launch (all
- * workgroups resident, synchronising at the four phase boundaries of each
- * layer) after a small reset launch.  Asynchronous; runs on one stream at a
- * time per workspace.
+ * workgroups resident; a phase waits until the output blocks it reads have
+ * been written) after a small reset launch.  Asynchronous; runs on one
+ * stream at a time per workspace.
  */
 tq_status tq_bitnet_chain_run(const tq_chain_plan* plan, float* x, float* qkv, void* stream);
 
 /*
  * Synchronize `stream` and report whether the plan's last run completed:
- * TQ_ERR_DEVICE if a phase barrier gave up waiting (the grid was not all
+ * TQ_ERR_DEVICE if a wait between phases gave up (the grid was not all
  * resident) -- x is then undefined.
  */
 tq_status tq_bitnet_chain_status(const tq_chain_plan* plan, void* stream);

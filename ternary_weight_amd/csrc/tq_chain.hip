@@ -12,13 +12,17 @@
 //   O     o of RMSNorm(repeat(v))            -> x1 = x + .
 //   GU    gate and up of RMSNorm(x1)         -> act = relu2(gate) * up
 //   DOWN  down of RMSNorm(act)               -> x = x1 + .
-// Every phase needs the whole of the previous one's output (a norm is a
-// reduction over the vector), so the grid synchronises between phases.  The
-// launch is cooperative (all workgroups resident) and each workgroup:
-//   1. issues the code loads of its first item of the phase -- weights do
-//      not depend on the activations, so they stream in while the
-//      workgroup waits at the barrier;
-//   2. waits at the grid barrier;
+// A phase needs the whole of the vector it normalises (a norm is a
+// reduction over it), so it waits until every output block of the phase it
+// reads has been written: each block's last writer counts it in a per-layer
+// counter once its stores are complete.  O needs only v, so the QKV phase
+// produces v first and O starts while q and k are still being computed.
+// The launch is cooperative (all workgroups resident; every wait is on
+// blocks of an earlier phase, so none can be circular) and each workgroup,
+// for each phase in which it has an item:
+//   1. issues the code loads of its first item -- weights do not depend on
+//      the activations, so they stream in while the workgroup waits;
+//   2. waits for the blocks it reads;
 //   3. reads the phase's input vector (a few KiB, from L2/HBM), takes its
 //      RMSNorm and int8 quantisation into LDS -- every workgroup does this
 //      itself, in the same order, so all hold the same bytes and no extra
@@ -29,8 +33,8 @@
 //      kernels' row-block loop, one row per lane).  The waves' partial sums
 //      meet in LDS; with S > 1 the splits of a block meet in an int32
 //      accumulator in global memory (exact, any order) and the last split
-//      to arrive, counted with an atomic per block, applies the epilogue and
-//      clears the accumulator and the count for the next phase.
+//      to arrive, counted with an atomic per block, applies the epilogue,
+//      clears the accumulator and the count, and counts the block done.
 #include <string.h>
 
 #include <algorithm>
@@ -46,7 +50,7 @@ using namespace tqk;
 constexpr int kThreads = 512;            // 8 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxWidth = 8192;          // longest phase input (held in registers, 16 per thread)
-constexpr uint32_t kSpinLimit = 1u << 22;   // barrier polls before giving up (~seconds)
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls of one wait before giving up (~seconds)
 
 enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3 };
 enum { W_Q = 0, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN };
@@ -74,8 +78,8 @@ struct ChainDev {
     float* act;         // [inter]
     int32_t* acc;       // [max(nq + 2 nkv, hidden, 2 inter)] split partial sums, kept zero
     uint32_t* cnt;      // [max groups] arrivals per block, kept zero
-    uint32_t* bar;      // grid barrier counter
-    int32_t* err;       // set when a barrier gives up
+    uint32_t* done;     // [n_layers][5] blocks written: QKV, v, O, GU, DOWN
+    int32_t* err;       // set when a wait gives up
 };
 
 // ---------------------------------------------------------------------------
@@ -112,14 +116,14 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, in
     Item it;
     it.group = item / P.splits;
     it.split = item - it.group * P.splits;
-    if (ph == PH_QKV) {
+    if (ph == PH_QKV) {   // v first (O waits for it alone), then k, then q
         int g = it.group;
-        if (g < C.nb_q) {
-            it.proj = W_Q; it.rb = g; it.off = g * 64;
-        } else if (g < C.nb_q + C.nb_kv) {
-            it.proj = W_K; it.rb = g - C.nb_q; it.off = C.nq + it.rb * 64;
+        if (g < C.nb_kv) {
+            it.proj = W_V; it.rb = g; it.off = C.nq + C.nkv + g * 64;
+        } else if (g < 2 * C.nb_kv) {
+            it.proj = W_K; it.rb = g - C.nb_kv; it.off = C.nq + it.rb * 64;
         } else {
-            it.proj = W_V; it.rb = g - C.nb_q - C.nb_kv; it.off = C.nq + C.nkv + it.rb * 64;
+            it.proj = W_Q; it.rb = g - 2 * C.nb_kv; it.off = it.rb * 64;
         }
     } else {
         it.proj = ph == PH_O ? W_O : (ph == PH_GU ? W_GATE : W_DOWN);
@@ -129,19 +133,17 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, in
     return it;
 }
 
-// Grid barrier number `index` (0-based over the run).  Returns false when it
-// gave up, or when another workgroup did (every wait is bounded).  Every
-// wave has waited for its phase's stores before (at the end of its items),
-// so that the loads issued for the next phase meanwhile are not waited for.
-__device__ bool grid_sync(const ChainDev& C, uint32_t index, int* flag_lds)
+enum { DONE_QKV = 0, DONE_V = 1, DONE_O = 2, DONE_GU = 3, DONE_DOWN = 4, DONE_N = 5 };
+
+// Wait until counter ctr reaches target.  Returns false when the wait gave
+// up, or another workgroup's did (every wait is bounded).
+__device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t target, int* flag_lds)
 {
-    __syncthreads();
+    __syncthreads();   // every thread has read the previous wait's flag
     if (threadIdx.x == 0) {
-        const uint32_t target = (index + 1) * (uint32_t)C.G;
-        __hip_atomic_fetch_add(C.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
         int ok = 1;
-        while (__hip_atomic_load(C.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             if (__hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
                 ok = 0;
                 break;
@@ -267,7 +269,6 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    uint32_t nbar = 0;
 
     for (int l = 0; l < C.n_layers; ++l) {
         const LayerDev& Ld = C.layers[l];
@@ -278,15 +279,28 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
             const int wp = ph == PH_GU ? wave / nw : 0;
             const int ws = wave - wp * nw;
             const int first = blockIdx.x;
-            Item it = item_of(C, P, ph, first < P.items ? first : 0);
+            if (first >= P.items) continue;      // no item in this phase
+            Item it = item_of(C, P, ph, first);
             const tq_prob_dev& Pp = Ld.p[it.proj + wp];
             int c0 = 0, c1 = 0;
-            if (first < P.items) wave_range(Pp.NC, P.splits, it.split, nw, ws, &c0, &c1);
+            wave_range(Pp.NC, P.splits, it.split, nw, ws, &c0, &c1);
             RB blk(Pp, it.rb, xq, nullptr);
-            blk.begin(c0, c1);     // the codes stream in during the barrier
-            if (l > 0 || ph > 0) {
-                if (!grid_sync(C, nbar++, &flag)) return;
+            blk.begin(c0, c1);     // the codes stream in during the wait
+            uint32_t* dl = C.done + l * DONE_N;
+            bool ok = true;
+            if (ph == PH_QKV) {
+                if (l > 0) ok = wait_count(C, dl - DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].groups, &flag);
+            } else if (ph == PH_O) {
+                ok = wait_count(C, dl + DONE_V, (uint32_t)C.nb_kv, &flag);
+            } else if (ph == PH_GU) {
+                // x1 complete; and every QKV block, so that no workgroup still
+                // reads x when DOWN rewrites it
+                ok = wait_count(C, dl + DONE_O, (uint32_t)C.ph[PH_O].groups, &flag) &&
+                     wait_count(C, dl + DONE_QKV, (uint32_t)C.ph[PH_QKV].groups, &flag);
+            } else {
+                ok = wait_count(C, dl + DONE_GU, (uint32_t)C.ph[PH_GU].groups, &flag);
             }
+            if (!ok) return;
             norm_quant(C, ph, x, Ld.norm[ph], P.width, xq, &sx_lds, red_d, (float*)red_f);
             const float sx = sx_lds;
             for (int item = first; item < P.items; item += C.G) {
@@ -348,10 +362,18 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                             st_shared(x + n, __fadd_rn(ld_shared(C.x1 + n), ya));
                         }
                     }
+                    if (last) {   // the block is written: count it once its stores are complete
+                        wait_stores();
+                        if (lane == 0) {
+                            const int c = ph == PH_QKV ? DONE_QKV : (ph == PH_O ? DONE_O : (ph == PH_GU ? DONE_GU : DONE_DOWN));
+                            __hip_atomic_fetch_add(dl + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (ph == PH_QKV && it.proj == W_V)
+                                __hip_atomic_fetch_add(dl + DONE_V, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
                 }
                 __syncthreads();
             }
-            wait_stores();    // this phase's outputs are in memory before the barrier
         }
     }
 }
@@ -361,10 +383,8 @@ __global__ void k_chain_reset(ChainDev* C, int acc_n, int cnt_n)
     const ChainDev c = *C;
     for (int i = threadIdx.x; i < acc_n; i += blockDim.x) c.acc[i] = 0;
     for (int i = threadIdx.x; i < cnt_n; i += blockDim.x) c.cnt[i] = 0;
-    if (threadIdx.x == 0) {
-        *c.bar = 0;
-        *c.err = 0;
-    }
+    for (int i = threadIdx.x; i < c.n_layers * DONE_N; i += blockDim.x) c.done[i] = 0;
+    if (threadIdx.x == 0) *c.err = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -372,7 +392,7 @@ __global__ void k_chain_reset(ChainDev* C, int acc_n, int cnt_n)
 // ---------------------------------------------------------------------------
 struct Sizes {
     int64_t nq, nkv, acc_n, cnt_n;
-    int64_t off_layers, off_qkv, off_x1, off_act, off_acc, off_cnt, off_bar, total;
+    int64_t off_layers, off_qkv, off_x1, off_act, off_acc, off_cnt, off_done, off_err, total;
 };
 
 tq_status check_dims(const tq_bitnet_dims* d, int32_t n_layers)
@@ -415,8 +435,10 @@ Sizes sizes_of(const tq_bitnet_dims* d, int32_t n_layers)
     o = tq_align256(o + 4 * s.acc_n);
     s.off_cnt = o;
     o = tq_align256(o + 4 * s.cnt_n);
-    s.off_bar = o;   // barrier counter, then the error flag
-    s.total = tq_align256(o + 8);
+    s.off_done = o;
+    o = tq_align256(o + 4 * (int64_t)n_layers * DONE_N);
+    s.off_err = o;
+    s.total = tq_align256(o + 4);
     return s;
 }
 
@@ -534,8 +556,8 @@ TQ_EXPORT tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq
     c.act = (float*)(ws + z.off_act);
     c.acc = (int32_t*)(ws + z.off_acc);
     c.cnt = (uint32_t*)(ws + z.off_cnt);
-    c.bar = (uint32_t*)(ws + z.off_bar);
-    c.err = (int32_t*)(ws + z.off_bar + 4);
+    c.done = (uint32_t*)(ws + z.off_done);
+    c.err = (int32_t*)(ws + z.off_err);
     std::vector<uint8_t> host((size_t)z.off_qkv, 0);
     memcpy(host.data(), &c, sizeof c);
     memcpy(host.data() + z.off_layers, ld.data(), ld.size() * sizeof(LayerDev));
@@ -581,10 +603,10 @@ TQ_EXPORT tq_status tq_bitnet_chain_status(const tq_chain_plan* plan, void* stre
     const Sizes z = sizes_of(&plan->dims, plan->n_layers);
     int32_t err = 0;
     tq_status s;
-    if ((s = tq_check_hip(hipMemcpyAsync(&err, (const uint8_t*)plan->workspace + z.off_bar + 4, 4,
+    if ((s = tq_check_hip(hipMemcpyAsync(&err, (const uint8_t*)plan->workspace + z.off_err, 4,
                                          hipMemcpyDeviceToHost, st), "tq_bitnet_chain_status copy")))
         return s;
     if ((s = tq_check_hip(hipStreamSynchronize(st), "tq_bitnet_chain_status synchronize"))) return s;
-    if (err) return tq_fail(TQ_ERR_DEVICE, "a chain barrier gave up waiting (the grid was not all resident)");
+    if (err) return tq_fail(TQ_ERR_DEVICE, "a chain wait gave up (the grid was not all resident)");
     return tq_ok();
 }
