@@ -689,6 +689,7 @@ def main_chain(args):
     ms_step = start.elapsed_time(end) / args.steps
     gbytes = chain_bytes(chain, stack.blob_bytes)
     value = gbytes / (ms_step / 1e3) / 1e9
+    ceiling = hbm_ceiling() if args.ceiling else None
     check = None if args.no_check else chain_spot_check(chain, stack.blobs, norms_dev, dims)
     cpu = None if args.no_cpu_baseline else chain_cpu_baseline(chain, args.cpu_seconds)
     kernel_name = "k_bitnet_chain"
@@ -728,6 +729,7 @@ def main_chain(args):
             "bytes_per_launch": gbytes,
         },
         "cpu_baseline": cpu,
+        "hbm_ceiling": ceiling,
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }
