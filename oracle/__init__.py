@@ -76,6 +76,10 @@ class Oracle:
         L.oracle_bitnet_layer.argtypes = [i64, i64, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp,
                                           vp, vp]
         L.oracle_bitnet_layer.restype = i32
+        L.oracle_ternarize.argtypes = [i32, i32, i32, i32, i64, i64, vp, vp, vp, vp]
+        L.oracle_ternarize.restype = i32
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = i32
         self.L = L
@@ -169,6 +173,27 @@ class Oracle:
             raise OracleError("oracle_bitnet_layer failed with status %d" % rc)
         return x, qkv
 
+    def ternarize(self, K, g, layout, w, codebook=None):
+        """(trits int8 [K][N][Kin], canonical scales) fitted to the fp32 weight w [N][Kin]."""
+        w = _c(w, np.float32)
+        N, Kin = w.shape
+        codebook = _c(codebook, np.uint16)
+        ncb = 0 if codebook is None else len(codebook)
+        trits = np.zeros((K, N, Kin), dtype=np.int8)
+        if layout == TENSOR:
+            scales = np.zeros(K, dtype=np.float32)
+        elif layout == GROUP_F16:
+            scales = np.zeros((K, N, Kin // g), dtype=np.uint16)
+        else:
+            scales = np.zeros((N, Kin // g), dtype=np.uint8)
+        rc = self.L.oracle_ternarize(K, g, layout, ncb, N, Kin, _p(w), _p(codebook), _p(trits), _p(scales))
+        if rc:
+            raise OracleError("oracle_ternarize failed with status %d" % rc)
+        return trits, scales
+
+    def f32_to_f16(self, f: float) -> int:
+        return self.L.oracle_f32_to_f16(float(f))
+
     def f16_to_f64(self, h: int) -> float:
         return self.L.oracle_f16_to_f64(int(h))
 
@@ -211,6 +236,10 @@ def relu2_mul(*a, **k):
 
 def bitnet_layer(*a, **k):
     return default().bitnet_layer(*a, **k)
+
+
+def ternarize(*a, **k):
+    return default().ternarize(*a, **k)
 
 
 def f16_to_f64(h: int) -> float:

@@ -403,3 +403,207 @@ done:
     free(qt);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Ternarizer: the step before packing -- a dense weight fit into K trit
+ * planes (sasori page, "How it works & paper": each matrix is fit on its
+ * own into a sum of K per-group-scaled trit-planes, weight-only) or into
+ * the balanced-ternary codec (d3 card, "Quantization details": uniform
+ * post-training quantisation, 27 levels, groups of 16, a 27-entry
+ * log-spaced scale codebook).
+ * ------------------------------------------------------------------------ */
+
+/* fp32 -> IEEE binary16 bits, round to nearest even; magnitudes above the
+ * largest finite half saturate to it (65504). */
+uint16_t oracle_f32_to_f16(float f)
+{
+    double a = fabs((double)f);
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    int e;
+    double m, q;
+    uint32_t bits;
+    if (a >= 65504.0) return (uint16_t)(sign | 0x7BFFu);
+    if (a < ldexp(1.0, -24) * 0.5) return sign;              /* rounds to zero (ties to even) */
+    e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e -= 1;                             /* guard the log */
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    if (e < -14) {                                             /* subnormal: multiples of 2^-24 */
+        q = nearbyint(a / ldexp(1.0, -24));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    m = a / ldexp(1.0, e);                                     /* in [1, 2) */
+    q = nearbyint((m - 1.0) * 1024.0);                         /* 10 mantissa bits, ties to even */
+    if (q == 1024.0) {
+        q = 0.0;
+        e += 1;
+    }
+    if (e > 15) return (uint16_t)(sign | 0x7BFFu);
+    bits = ((uint32_t)(e + 15) << 10) | (uint32_t)q;
+    return (uint16_t)(sign | bits);
+}
+
+/* The balanced-ternary digits of q in [-(3^K - 1)/2, (3^K - 1)/2]: q =
+ * sum_d 3^d t_d with t_d in {-1, 0, 1}; digit d written to dig[d]. */
+static void balanced_digits(int q, int K, int8_t* dig)
+{
+    int d;
+    for (d = 0; d < K; ++d) {
+        int r = ((q % 3) + 3) % 3;                /* 0, 1, 2 */
+        int t = r == 2 ? -1 : r;
+        dig[d] = (int8_t)t;
+        q = (q - t) / 3;
+    }
+}
+
+/*
+ * Fit w [N][Kin] (fp32) into trits [K][N][Kin] and canonical scales.
+ *
+ * TQ_SCALE_GROUP_F16 and TQ_SCALE_TENSOR -- greedy residual planes:
+ *   R = w;  for k = 0 .. K-1, per group (g consecutive inputs of a row; the
+ *   whole tensor for TENSOR):
+ *     a = mean |R| over the group                  (the absmean of BitNet b1.58)
+ *     t = a > 0 ? clamp(rint(fl(R / a)), -1, 1) : 0
+ *     s = mean |R| over the entries with t != 0     (the least-squares scale
+ *                                                    of the plane t; 0 if none)
+ *     R = fl(R - s t)
+ *   Sums are fp64 (row by row in index order; for TENSOR the row sums then
+ *   added in row order), divided in fp64 and rounded to fp32; s is then
+ *   rounded to f16 for GROUP_F16 (ties to even, saturating at 65504), and
+ *   the rounded s is what the residual uses.  A plane never increases a
+ *   group's squared error (s is optimal for t, and s = 0 would leave it).
+ *
+ * TQ_SCALE_CODEBOOK -- uniform quantisation onto L = (3^K - 1) / 2 levels a
+ * side with a scale from the codebook (ascending) per group:
+ *   a = max |w|;  c = fl(a / L);  idx = the first entry with cb[idx] >= c
+ *   (the last if none);  q = clamp(rint(fl(w / cb[idx])), -L, L);
+ *   digits of q in balanced ternary, plane p holding the digit of 3^(K-1-p).
+ */
+int oracle_ternarize(int K, int g, int layout, int n_cb, int64_t N, int64_t Kin, const float* w,
+                     const uint16_t* codebook, int8_t* trits, void* scales)
+{
+    int64_t n, i, G;
+    int rc = check_desc(K, g, layout, n_cb, N, Kin);
+    if (rc) return rc;
+    for (i = 0; i < N * Kin; ++i)
+        if (!isfinite(w[i])) return OR_ERR_VALUE;
+    if (layout == OR_CODEBOOK) {
+        const int L = (K == 1) ? 1 : (K == 2 ? 4 : (K == 3 ? 13 : 40));
+        int j;
+        for (j = 0; j + 1 < n_cb; ++j)
+            if (!(oracle_f16_to_f64(codebook[j]) < oracle_f16_to_f64(codebook[j + 1]))) return OR_ERR_VALUE;
+        if (!(oracle_f16_to_f64(codebook[0]) > 0.0)) return OR_ERR_VALUE;
+        G = Kin / g;
+        for (n = 0; n < N; ++n) {
+            int64_t grp;
+            for (grp = 0; grp < G; ++grp) {
+                float a = 0.0f, c, s;
+                int idx = n_cb - 1;
+                for (i = grp * g; i < (grp + 1) * g; ++i)
+                    if (fabsf(w[n * Kin + i]) > a) a = fabsf(w[n * Kin + i]);
+                c = a / (float)L;
+                for (j = 0; j < n_cb; ++j) {
+                    if ((float)oracle_f16_to_f64(codebook[j]) >= c) {
+                        idx = j;
+                        break;
+                    }
+                }
+                ((uint8_t*)scales)[n * G + grp] = (uint8_t)idx;
+                s = (float)oracle_f16_to_f64(codebook[idx]);
+                for (i = grp * g; i < (grp + 1) * g; ++i) {
+                    float q = rintf(w[n * Kin + i] / s);
+                    int8_t dig[4];
+                    int p;
+                    if (q > (float)L) q = (float)L;
+                    if (q < -(float)L) q = -(float)L;
+                    balanced_digits((int)q, K, dig);
+                    for (p = 0; p < K; ++p) trits[((int64_t)p * N + n) * Kin + i] = dig[K - 1 - p];
+                }
+            }
+        }
+        return OR_OK;
+    }
+    {
+        float* R = (float*)malloc(sizeof(float) * (size_t)(N * Kin));
+        double* rowsum = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        int k;
+        const int64_t gs = layout == OR_TENSOR ? Kin : g;
+        if (!R || !rowsum) {
+            free(R);
+            free(rowsum);
+            return OR_ERR_ARG;
+        }
+        G = layout == OR_TENSOR ? 1 : Kin / g;
+        memcpy(R, w, sizeof(float) * (size_t)(N * Kin));
+        for (k = 0; k < K; ++k) {
+            /* per group: the absmean a, the plane t, then its scale s */
+            for (n = 0; n < N; ++n) {
+                int64_t grp;
+                for (grp = 0; grp < G; ++grp) {
+                    double sum = 0.0, sum_nz = 0.0;
+                    int64_t nz = 0;
+                    float a, sc;
+                    if (layout == OR_TENSOR) break;
+                    for (i = grp * gs; i < (grp + 1) * gs; ++i) sum += fabs((double)R[n * Kin + i]);
+                    a = (float)(sum / (double)gs);
+                    for (i = grp * gs; i < (grp + 1) * gs; ++i) {
+                        float t = 0.0f;
+                        if (a > 0.0f) {
+                            t = rintf(R[n * Kin + i] / a);
+                            if (t > 1.0f) t = 1.0f;
+                            if (t < -1.0f) t = -1.0f;
+                        }
+                        trits[((int64_t)k * N + n) * Kin + i] = (int8_t)t;
+                        if (t != 0.0f) {
+                            sum_nz += fabs((double)R[n * Kin + i]);
+                            nz += 1;
+                        }
+                    }
+                    sc = nz > 0 ? (float)(sum_nz / (double)nz) : 0.0f;
+                    {
+                        const uint16_t h = oracle_f32_to_f16(sc);
+                        ((uint16_t*)scales)[((int64_t)k * N + n) * G + grp] = h;
+                        sc = (float)oracle_f16_to_f64(h);
+                    }
+                    for (i = grp * gs; i < (grp + 1) * gs; ++i)
+                        R[n * Kin + i] = R[n * Kin + i] - sc * (float)trits[((int64_t)k * N + n) * Kin + i];
+                }
+            }
+            if (layout == OR_TENSOR) {
+                double tot = 0.0, tot_nz = 0.0;
+                int64_t nz = 0;
+                float a, sc;
+                for (n = 0; n < N; ++n) {
+                    double sr = 0.0;
+                    for (i = 0; i < Kin; ++i) sr += fabs((double)R[n * Kin + i]);
+                    rowsum[n] = sr;
+                }
+                for (n = 0; n < N; ++n) tot += rowsum[n];
+                a = (N * Kin > 0) ? (float)(tot / (double)(N * Kin)) : 0.0f;
+                for (n = 0; n < N; ++n) {
+                    double sr = 0.0;
+                    for (i = 0; i < Kin; ++i) {
+                        float t = 0.0f;
+                        if (a > 0.0f) {
+                            t = rintf(R[n * Kin + i] / a);
+                            if (t > 1.0f) t = 1.0f;
+                            if (t < -1.0f) t = -1.0f;
+                        }
+                        trits[((int64_t)k * N + n) * Kin + i] = (int8_t)t;
+                        if (t != 0.0f) {
+                            sr += fabs((double)R[n * Kin + i]);
+                            nz += 1;
+                        }
+                    }
+                    rowsum[n] = sr;
+                }
+                for (n = 0; n < N; ++n) tot_nz += rowsum[n];
+                sc = nz > 0 ? (float)(tot_nz / (double)nz) : 0.0f;
+                ((float*)scales)[k] = sc;
+                for (i = 0; i < N * Kin; ++i) R[i] = R[i] - sc * (float)trits[(int64_t)k * N * Kin + i];
+            }
+        }
+        free(R);
+        free(rowsum);
+    }
+    return OR_OK;
+}
