@@ -273,6 +273,40 @@ tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int
 tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream);
 
 /*
+ * Ternarizer: fit a dense fp32 weight w [N][Kin] (device) into the canonical
+ * arrays that tq_pack takes -- trits int8 [K][N][Kin] and scales (device) --
+ * before packing.  Each matrix is fit on its own, weight-only (sasori page,
+ * "How it works & paper": a sum of K per-group-scaled trit-planes; d3 card,
+ * "Quantization details": uniform quantisation onto 27 levels with a
+ * 27-entry log-spaced scale codebook).  By scale layout:
+ *
+ *  TQ_SCALE_GROUP_F16, TQ_SCALE_TENSOR -- greedy residual planes.  R = w; for
+ *  k = 0 .. K-1, per group (g inputs of a row; the whole tensor for TENSOR):
+ *    a = mean |R|;  t = a > 0 ? clamp(rint(fl(R / a)), -1, 1) : 0;
+ *    s = mean of |R| where t != 0 (the least-squares scale of t; 0 if none);
+ *    R = fl(R - s t).
+ *  Sums are fp64 in index order (TENSOR: each row, then the row sums in row
+ *  order), divided in fp64 and rounded to fp32; GROUP_F16 rounds s to f16
+ *  (ties to even, saturating at 65504) and uses the rounded value after.
+ *  No plane increases any group's squared error.
+ *
+ *  TQ_SCALE_CODEBOOK -- codebook (device f16 [n_codebook], positive and
+ *  ascending, checked) per group of g: a = max |w|, L = (3^K - 1) / 2
+ *  levels a side, idx = the first entry >= fl(a / L) (the last if none),
+ *  q = clamp(rint(fl(w / cb[idx])), -L, L) written as balanced-ternary
+ *  digits, plane p holding the digit of 3^(K-1-p) (p = 0: t2 for K = 3);
+ *  scales = idx as uint8 [N][Kin / g].
+ *
+ * The results equal the CPU oracle's bit for bit.  workspace: device bytes
+ * from tq_ternarize_workspace_size (TENSOR only; NULL and 0 otherwise).
+ * Non-finite weights are out of contract.  An offline call: CODEBOOK reads
+ * the codebook back and synchronizes `stream`; the rest is asynchronous.
+ */
+tq_status tq_ternarize_workspace_size(const tq_weight_desc* desc, size_t* bytes);
+tq_status tq_ternarize(const tq_weight_desc* desc, const float* w, const uint16_t* codebook, int8_t* trits,
+                       void* scales, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode chain: BitNet b1.58 layers run back to back for one token in one
  * persistent launch, in the order of the QORA-LLM-2B page's "SubLN Pattern"
  * listing (head counts from its "Architecture" table).  Per layer, with x

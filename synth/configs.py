@@ -46,7 +46,7 @@ TENSOR, GROUP_F16, CODEBOOK = 0, 1, 2
 F32, BF16, I8 = 0, 1, 2
 
 # Tensor kinds (low 16 bits of the seed key).
-KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS, KIND_NORM = 1, 2, 3, 4, 5, 6
+KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS, KIND_NORM, KIND_DENSE = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclass(frozen=True)

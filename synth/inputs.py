@@ -25,7 +25,7 @@ import numpy as np
 
 from . import gen
 from .configs import (BF16, CODEBOOK, F32, GROUP_F16, I8, KIND_DIGITS,
-                      KIND_INDEX, KIND_NORM, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
+                      KIND_DENSE, KIND_INDEX, KIND_NORM, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
 
 N_CODEBOOK = 27
 
@@ -145,6 +145,13 @@ def chain_input(chain) -> np.ndarray:
     return gen.normal(gen.tensor_seed(chain.cfg, 0, 0, KIND_X), 0, chain.hidden).astype(np.float32)
 
 
-__all__ = ["projection", "chain_projection", "chain_norm", "chain_input", "activations", "plane_values", "plane_values_full", "group_scales",
+def dense_weight(cfg: int, layer: int, proj: int, N: int, Kin: int, sigma: float = 0.02) -> np.ndarray:
+    """A dense fp32 weight [N][Kin] to ternarize: N(0, sigma^2) (the scale of a
+    trained LLM linear's weights; no trained weights exist here)."""
+    seed = gen.tensor_seed(cfg, layer, proj, KIND_DENSE)
+    return (gen.normal(seed, 0, N * Kin) * sigma).astype(np.float32).reshape(N, Kin)
+
+
+__all__ = ["projection", "dense_weight", "chain_projection", "chain_norm", "chain_input", "activations", "plane_values", "plane_values_full", "group_scales",
            "tensor_scales", "codebook_indices", "seeds", "N_CODEBOOK",
            "TENSOR", "GROUP_F16", "CODEBOOK", "F32", "BF16", "I8"]

@@ -95,6 +95,8 @@ SIGNATURES = {
     "tq_gemm_grouped_prepare": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32, _VP,
                                  ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_gemm_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
+    "tq_ternarize_workspace_size": ([_DESC, ctypes.POINTER(ctypes.c_size_t)], _I32),
+    "tq_ternarize": ([_DESC, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP], _I32),
     "tq_bitnet_chain_workspace_size": ([ctypes.POINTER(tq_bitnet_dims), _I32, ctypes.POINTER(ctypes.c_size_t)],
                                        _I32),
     "tq_bitnet_chain_prepare": ([ctypes.POINTER(tq_bitnet_dims), ctypes.POINTER(tq_bitnet_layer), _I32, _VP,
@@ -285,3 +287,14 @@ def bitnet_chain_run(plan, x, qkv=None, stream=None):
 
 def bitnet_chain_status(plan, stream=None):
     _check(lib().tq_bitnet_chain_status(ctypes.byref(plan), _stream(stream)), "tq_bitnet_chain_status")
+
+
+def ternarize_workspace_size(d: tq_weight_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().tq_ternarize_workspace_size(ctypes.byref(d), ctypes.byref(n)), "tq_ternarize_workspace_size")
+    return n.value
+
+
+def ternarize(d: tq_weight_desc, w, trits, scales, codebook=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().tq_ternarize(ctypes.byref(d), _ptr(w), _ptr(codebook), _ptr(trits), _ptr(scales), _ptr(workspace),
+                              workspace_bytes, _stream(stream)), "tq_ternarize")

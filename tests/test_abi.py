@@ -235,3 +235,15 @@ def test_chain_workspace_size_validation():
     with pytest.raises(tq.TQError) as e:
         tq.bitnet_chain_workspace_size(ok, 0)
     assert e.value.status == tq.ERR_ARG
+
+
+def test_ternarize_workspace_and_validation():
+    """tq_ternarize_workspace_size and the host-side checks of tq_ternarize."""
+    assert tq.ternarize_workspace_size(tq.desc(3, 256, tq.SCALE_GROUP_F16, 4096, 4096)) == 0
+    assert tq.ternarize_workspace_size(tq.desc(1, 0, tq.SCALE_TENSOR, 4096, 4096)) >= 4096 * 16
+    with pytest.raises(tq.TQError) as e:
+        tq.ternarize_workspace_size(tq.desc(3, 48, tq.SCALE_GROUP_F16, 64, 256))    # 256 % 48
+    assert e.value.status in (tq.ERR_SHAPE, tq.ERR_ARG)
+    with pytest.raises(tq.TQError) as e:
+        tq.ternarize(tq.desc(3, 64, tq.SCALE_GROUP_F16, 64, 256), None, None, None, stream=0)
+    assert e.value.status == tq.ERR_ARG
