@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--spin-up-ms", type=float, default=150.0,
                     help="plain streaming reads before the warmup steps: the GPU needs ~20 ms of "
                          "memory load to leave its idle clocks")
-    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b", "chain"],
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b", "chain",
+                                                         "ternarize", "ternarize_codec"],
                     help="cfg2-4: decode stacks (tq_gemv_grouped_*); cfg5a/b: prefill stacks (tq_gemm_grouped_*); "
                          "chain: the BitNet b1.58-2B layers as a dependent decode chain (tq_bitnet_chain_*)")
     ap.add_argument("--workgroups", type=int, default=0, help="chain: grid of the persistent launch (0 = default)")
@@ -348,6 +349,7 @@ _FAMILY_SOURCES = {
     "k_gemv": ["tq_gemv_impl.h", "tq_gemv.hip", "tq_entry.hip"],
     "k_gemm": ["tq_gemm_impl.h", "tq_gemm_kernels.h", "tq_gemm.hip"],
     "k_bitnet_chain": ["tq_chain.hip", "tq_gemv_impl.h"],
+    "k_tern": ["tq_ternarize.hip"],
 }
 
 
@@ -468,6 +470,9 @@ def main():
         sys.exit(2)
     if args.config == "chain":
         main_chain(args)
+        return
+    if args.config.startswith("ternarize"):
+        main_ternarize(args)
         return
     import torch
     case = CASES[args.config]
@@ -732,6 +737,82 @@ def main_chain(args):
         "hbm_ceiling": ceiling,
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+# The ternarizer: fit the dense weights of one layer into planes (offline).
+# ---------------------------------------------------------------------------
+def main_ternarize(args):
+    import torch
+    import oracle
+    from ternary_weight_amd import tq
+    from synth.configs import LLAMA_8B
+    codec = args.config == "ternarize_codec"
+    K, g, layout = (3, 16, CODEBOOK) if codec else (3, 256, GROUP_F16)
+    shapes = LLAMA_8B["proj"]
+    cb = torch.from_numpy(gen.codebook_f16(inputs.N_CODEBOOK).view(np.int16)).cuda() if codec else None
+    jobs = []
+    for p, (name, n, kin) in enumerate(shapes):
+        w = torch.empty((n, kin), dtype=torch.float32, device="cuda")
+        device.fill(device.K_NORMAL_F32, gen.tensor_seed(9, 0, p, 7), 0, w)   # N(0, 1) dense weight
+        d = tq.desc(K, g, layout, n, kin, n_codebook=inputs.N_CODEBOOK if codec else 0)
+        trits = torch.empty((K, n, kin), dtype=torch.int8, device="cuda")
+        scales = (torch.empty((n, kin // g), dtype=torch.uint8, device="cuda") if codec
+                  else torch.empty((K, n, kin // g), dtype=torch.int16, device="cuda"))
+        jobs.append((name, d, w, trits, scales))
+    torch.cuda.synchronize()
+    # weights of trained linears are ~N(0, 0.02^2); the fit is scale-equivariant up to the
+    # codebook's range, so the codec is fed 0.02 w
+    if codec:
+        for j in jobs:
+            j[2].mul_(0.02)
+
+    def step():
+        for name, d, w, trits, scales in jobs:
+            tq.ternarize(d, w, trits, scales, cb)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    weights = sum(n * kin for (_, n, kin) in shapes)
+    # algorithmic bytes: the dense weight read once, the trits written once (int8), the scales
+    scale_b = sum(n * (kin // g) * (1 if codec else 2 * K) for (_, n, kin) in shapes)
+    nbytes = 4 * weights + K * weights + scale_b
+    value = nbytes / (ms_step / 1e3) / 1e9
+    check = None
+    if not args.no_check:   # the first projection's first 256 rows against the oracle
+        name, d, w, trits, scales = jobs[1]
+        rows = w[:256].cpu().numpy()
+        t_ref, s_ref = oracle.ternarize(K, g, layout, rows, gen.codebook_f16(inputs.N_CODEBOOK) if codec else None)
+        # the 256-row fit of a row-wise method equals those rows of the full fit
+        t = trits[:, :256].cpu().numpy()
+        s = scales[:256].cpu().numpy() if codec else scales[:, :256].cpu().numpy().view(np.uint16)
+        check = {"projection": name, "rows": 256,
+                 "bit_exact": bool(np.array_equal(t, t_ref) and np.array_equal(s, s_ref))}
+    out = {
+        "metric": "ternarizer effective HBM GB/s (% of peak), Llama-3.1-8B-shaped layer",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic dense weights, seeded N(0,1)" + (" x 0.02" if codec else ""),
+        "config": {"workload": "fit the 7 projections of one Llama-3.1-8B-shaped layer: " +
+                               ("the d=3 codec, groups of 16, 27-entry codebook" if codec else
+                                "K=3 greedy planes, f16 scale per group of 256"),
+                   "weights": weights},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("k_tern_codec" if codec else "k_tern_group"),
+                     "kernel": "k_tern_codec" if codec else "k_tern_group", "bytes_per_launch": nbytes},
+        "parity_spot_check": check,
     }
     print(json.dumps(out))
 

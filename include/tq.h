@@ -282,7 +282,7 @@ tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream);
  *
  *  TQ_SCALE_GROUP_F16, TQ_SCALE_TENSOR -- greedy residual planes.  R = w; for
  *  k = 0 .. K-1, per group (g inputs of a row; the whole tensor for TENSOR):
- *    a = mean |R|;  t = a > 0 ? clamp(rint(fl(R / a)), -1, 1) : 0;
+ *    a = mean |R|;  t = sign(R) where |R| > a / 2, else 0;
  *    s = mean of |R| where t != 0 (the least-squares scale of t; 0 if none);
  *    R = fl(R - s t).
  *  Sums are fp64 in index order (TENSOR: each row, then the row sums in row

@@ -462,7 +462,9 @@ static void balanced_digits(int q, int K, int8_t* dig)
  *   R = w;  for k = 0 .. K-1, per group (g consecutive inputs of a row; the
  *   whole tensor for TENSOR):
  *     a = mean |R| over the group                  (the absmean of BitNet b1.58)
- *     t = a > 0 ? clamp(rint(fl(R / a)), -1, 1) : 0
+ *     t = sign(R) where |R| > a / 2, else 0         (round(R / a) clipped to
+ *                                                    [-1, 1], as an exact
+ *                                                    comparison)
  *     s = mean |R| over the entries with t != 0     (the least-squares scale
  *                                                    of the plane t; 0 if none)
  *     R = fl(R - s t)
@@ -547,11 +549,7 @@ int oracle_ternarize(int K, int g, int layout, int n_cb, int64_t N, int64_t Kin,
                     a = (float)(sum / (double)gs);
                     for (i = grp * gs; i < (grp + 1) * gs; ++i) {
                         float t = 0.0f;
-                        if (a > 0.0f) {
-                            t = rintf(R[n * Kin + i] / a);
-                            if (t > 1.0f) t = 1.0f;
-                            if (t < -1.0f) t = -1.0f;
-                        }
+                        if (a > 0.0f && fabsf(R[n * Kin + i]) > 0.5f * a) t = R[n * Kin + i] > 0.0f ? 1.0f : -1.0f;
                         trits[((int64_t)k * N + n) * Kin + i] = (int8_t)t;
                         if (t != 0.0f) {
                             sum_nz += fabs((double)R[n * Kin + i]);
@@ -583,11 +581,7 @@ int oracle_ternarize(int K, int g, int layout, int n_cb, int64_t N, int64_t Kin,
                     double sr = 0.0;
                     for (i = 0; i < Kin; ++i) {
                         float t = 0.0f;
-                        if (a > 0.0f) {
-                            t = rintf(R[n * Kin + i] / a);
-                            if (t > 1.0f) t = 1.0f;
-                            if (t < -1.0f) t = -1.0f;
-                        }
+                        if (a > 0.0f && fabsf(R[n * Kin + i]) > 0.5f * a) t = R[n * Kin + i] > 0.0f ? 1.0f : -1.0f;
                         trits[((int64_t)k * N + n) * Kin + i] = (int8_t)t;
                         if (t != 0.0f) {
                             sr += fabs((double)R[n * Kin + i]);

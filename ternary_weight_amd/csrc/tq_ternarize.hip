@@ -58,7 +58,11 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f)
     return (uint16_t)(sign | (exp << 10) | (q & 0x3FFu));
 }
 
-__device__ __forceinline__ float clamp_trit(float t) { return fminf(fmaxf(t, -1.0f), 1.0f); }
+// The plane's trit of residual r: sign(r) where |r| > a / 2 (a > 0), else 0.
+__device__ __forceinline__ float trit_of(float r, float a)
+{
+    return (a > 0.0f && fabsf(r) > 0.5f * a) ? (r > 0.0f ? 1.0f : -1.0f) : 0.0f;
+}
 
 // The residual of plane k at input i of a walk: the weight with the planes
 // 0 .. k-1 taken off, fp32, one subtraction per plane in plane order.
@@ -69,7 +73,78 @@ __device__ __forceinline__ float replay(float w, const int8_t* t, int64_t plane_
     return r;
 }
 
-// One thread per (row, group): the K greedy planes of the group.
+// One lane per (row, group), 64 consecutive groups per workgroup (in the
+// flattened (row, group) order they are one contiguous run of the weight):
+// the run is loaded into LDS with 16-byte loads, each lane then walks its
+// group's residual there (row stride g + 1 floats, so the 64 lanes of a
+// read fall in distinct banks), updating it in place plane by plane, and
+// writes its trits four to a dword.
+constexpr int kTernLanes = 64;
+
+__global__ __launch_bounds__(kTernLanes) void k_tern_group_lds(const float* __restrict__ w, int64_t N, int64_t Kin,
+                                                              int g, int K, int8_t* __restrict__ trits,
+                                                              uint16_t* __restrict__ scales)
+{
+    extern __shared__ float R[];                     // [64][g + 1]
+    const int64_t G = Kin / g, total = N * G;
+    const int64_t id0 = (int64_t)blockIdx.x * kTernLanes;
+    const int lane = threadIdx.x;
+    const int ngr = (int)(total - id0 < kTernLanes ? total - id0 : kTernLanes);
+    // load the run: ngr * g floats from w + id0 * g (g is a multiple of 16)
+    const float4* src = (const float4*)(w + id0 * g);
+    const int n4 = ngr * g / 4;
+    for (int v = lane; v < n4; v += kTernLanes) {
+        const float4 x = src[v];
+        const int e = v * 4, grp = e / g, i = e - grp * g;
+        float* row = R + grp * (g + 1) + i;
+        row[0] = x.x;
+        row[1] = x.y;
+        row[2] = x.z;
+        row[3] = x.w;
+    }
+    __syncthreads();
+    if (lane >= ngr) return;
+    const int64_t id = id0 + lane;
+    float* r = R + lane * (g + 1);
+    const int64_t ps = N * Kin;
+    uint32_t* tw = (uint32_t*)(trits + id * g);      // the group's trits of plane 0, 4-byte aligned (g % 16 == 0)
+    double sum = 0.0;                                  // plane 0's sum of |R|
+    for (int i = 0; i < g; ++i) sum += fabs((double)r[i]);
+    for (int k = 0; k < K; ++k) {
+        const float a = (float)(sum / (double)g);
+        double sum_nz = 0.0;
+        int64_t nz = 0;
+        for (int i = 0; i < g; ++i) {
+            if (trit_of(r[i], a) != 0.0f) {
+                sum_nz += fabs((double)r[i]);
+                nz += 1;
+            }
+        }
+        const float sc = nz > 0 ? (float)(sum_nz / (double)nz) : 0.0f;
+        const uint16_t h = f32_to_f16_rne(sc);
+        scales[(int64_t)k * total + id] = h;
+        const float sv = f16_to_f32(h);
+        // write the trits, take the plane off the residual, and sum the next
+        // plane's |R| in the same index order
+        uint32_t* twk = (uint32_t*)((int8_t*)tw + (int64_t)k * ps);
+        sum = 0.0;
+        for (int i = 0; i < g; i += 4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float t = trit_of(r[i + b], a);
+                const float nr = __fsub_rn(r[i + b], __fmul_rn(sv, t));
+                r[i + b] = nr;
+                sum += fabs((double)nr);
+                word |= (uint32_t)(uint8_t)(int8_t)t << (8 * b);
+            }
+            twk[i / 4] = word;
+        }
+    }
+}
+
+// One thread per (row, group): the K greedy planes of the group (groups
+// too long for the LDS walk).
 __global__ void k_tern_group(const float* __restrict__ w, int64_t N, int64_t Kin, int g, int K,
                              int8_t* __restrict__ trits, uint16_t* __restrict__ scales)
 {
@@ -89,7 +164,7 @@ __global__ void k_tern_group(const float* __restrict__ w, int64_t N, int64_t Kin
         int64_t nz = 0;
         for (int i = 0; i < g; ++i) {
             const float r = replay(wr[i], tr + i, ps, s, k);
-            const float t = a > 0.0f ? clamp_trit(rintf(__fdiv_rn(r, a))) : 0.0f;
+            const float t = trit_of(r, a);
             tr[k * ps + i] = (int8_t)t;
             if (t != 0.0f) {
                 sum_nz += fabs((double)r);
@@ -126,7 +201,7 @@ __global__ void k_tern_rows(const float* __restrict__ w, int64_t N, int64_t Kin,
         if (pass == 0) {
             sum += fabs((double)r);
         } else {
-            const float t = a > 0.0f ? clamp_trit(rintf(__fdiv_rn(r, a))) : 0.0f;
+            const float t = trit_of(r, a);
             tr[k * ps + i] = (int8_t)t;
             if (t != 0.0f) {
                 sum += fabs((double)r);
@@ -246,9 +321,21 @@ TQ_EXPORT tq_status tq_ternarize(const tq_weight_desc* desc, const float* w, con
         return tq_check_launch("tq_ternarize") ? TQ_ERR_DEVICE : tq_ok();
     }
     if (L.layout == TQ_SCALE_GROUP_F16) {
-        const int64_t threads = N * (Kin / L.g);
-        hipLaunchKernelGGL(k_tern_group, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, w, N, Kin, L.g,
-                           L.K, trits, (uint16_t*)scales);
+        const int64_t groups = N * (Kin / L.g);
+        const size_t lds = (size_t)kTernLanes * (L.g + 1) * sizeof(float);
+        static bool lds_raised = false;   // the default dynamic-LDS limit is 64 KiB
+        if (!lds_raised) {
+            lds_raised = hipFuncSetAttribute((const void*)k_tern_group_lds,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, TQ_MAX_WG_LDS) == hipSuccess;
+        }
+        if ((lds <= 65536 || lds_raised) && lds <= TQ_MAX_WG_LDS && ((uintptr_t)w & 15) == 0 &&
+            ((uintptr_t)trits & 3) == 0) {
+            hipLaunchKernelGGL(k_tern_group_lds, dim3((unsigned)((groups + kTernLanes - 1) / kTernLanes)),
+                               dim3(kTernLanes), lds, st, w, N, Kin, L.g, L.K, trits, (uint16_t*)scales);
+        } else {
+            hipLaunchKernelGGL(k_tern_group, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, w, N, Kin,
+                               L.g, L.K, trits, (uint16_t*)scales);
+        }
         return tq_check_launch("tq_ternarize") ? TQ_ERR_DEVICE : tq_ok();
     }
     // per-tensor scale: per-row passes and single-thread reductions, plane by plane

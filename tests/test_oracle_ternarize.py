@@ -148,7 +148,8 @@ def test_ternarize_rejects_bad_input():
 TERNARIZE_MUTANTS = [
     ("absmax threshold", "for (i = grp * gs; i < (grp + 1) * gs; ++i) sum += fabs((double)R[n * Kin + i]);",
      "for (i = grp * gs; i < (grp + 1) * gs; ++i) sum = fmax(sum, fabs((double)R[n * Kin + i]) * (double)gs);"),
-    ("truncate", "t = rintf(R[n * Kin + i] / a);", "t = truncf(R[n * Kin + i] / a);"),
+    ("threshold at the absmean", "if (a > 0.0f && fabsf(R[n * Kin + i]) > 0.5f * a) t",
+     "if (a > 0.0f && fabsf(R[n * Kin + i]) > 1.0f * a) t"),
     ("absmean kept as the scale", "sc = nz > 0 ? (float)(sum_nz / (double)nz) : 0.0f;\n                    {",
      "sc = a;\n                    {"),
     ("no residual update", "R[n * Kin + i] = R[n * Kin + i] - sc * (float)trits[((int64_t)k * N + n) * Kin + i];",
