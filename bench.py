@@ -37,6 +37,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "ternary_weight_amd", "csrc")
 METRIC = "ternary GEMV effective HBM GB/s (% of peak) at BitNet-2B/Llama-8B shapes, M=1"
 METRIC_PREFILL = "ternary prefill GEMM effective TOP/s (MFMA utilisation) at BitNet-2B/Llama-8B shapes"
+METRIC_MOE = "MoE expert-grouped ternary GEMV effective HBM GB/s (% of peak), Qwen3-30B-A3B expert shapes"
 METRIC_CHAIN = "BitNet-2B decode chain effective HBM GB/s (% of peak), one token through every layer"
 MFMA_PEAK_I8_TOPS = 5000.0      # dense int8 MFMA, MI355X
 MFMA_PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
@@ -51,10 +52,12 @@ def parse():
                     help="plain streaming reads before the warmup steps: the GPU needs ~20 ms of "
                          "memory load to leave its idle clocks")
     ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5a", "cfg5b", "chain",
-                                                         "ternarize", "ternarize_codec"],
+                                                         "moe", "ternarize", "ternarize_codec"],
                     help="cfg2-4: decode stacks (tq_gemv_grouped_*); cfg5a/b: prefill stacks (tq_gemm_grouped_*); "
                          "chain: the BitNet b1.58-2B layers as a dependent decode chain (tq_bitnet_chain_*)")
     ap.add_argument("--workgroups", type=int, default=0, help="chain: grid of the persistent launch (0 = default)")
+    ap.add_argument("--batch", type=int, default=0, help="moe: tokens decoded together (0 = 64)")
+    ap.add_argument("--moe-int8", action="store_true", help="moe: int8 activations (quantised in the product)")
     ap.add_argument("--M", type=int, default=1, help="tokens per step (cfg4: 1, 4 or 16)")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
@@ -179,6 +182,113 @@ class Stack:
         if self.x_q is None:
             return 0
         return sum(self.M * kin * (4 + 1) + 4 * self.M for (_, _, _, _, kin) in self.projs)
+
+
+class MoeStack:
+    """The routed experts of every MoE layer for one decode batch.
+
+    Every expert's gate, up and down matrices are packed on their own (all
+    experts of all layers stay resident, as in a served model); the batch's
+    tokens are gathered per expert, in expert order, into one buffer per
+    layer and input width; one grouped launch (tq_gemv_grouped_prepare_tokens)
+    computes every (layer, expert, projection) that has tokens, each with its
+    own token count.  An expert with more than 16 tokens is split into
+    problems of at most 16 that share its blob.  int8 activations are
+    quantised per token inside the product (TQ_F32_Q8)."""
+
+    MAX_TOKENS = 16
+
+    def __init__(self, moe):
+        import torch
+        from ternary_weight_amd import tq
+        self.moe = moe
+        K, g, layout = moe.planes, moe.group, moe.layout
+        self.shapes = moe.proj_shapes()
+        self.descs = [tq.desc(K, g, layout, n, kin) for (_, n, kin) in self.shapes]
+        sizes = [tq.packed_size(d) for d in self.descs]
+        self.sizes = sizes
+        aligned = [(s + 255) // 256 * 256 for s in sizes]
+        self.expert_bytes = sum(aligned)
+        self.proj_off = [0, aligned[0], aligned[0] + aligned[1]]
+        E, L = moe.experts, moe.layers
+        self.slab = torch.empty(L * E * self.expert_bytes, dtype=torch.uint8, device="cuda")
+        self.blob_bytes = self.slab.numel()
+        for layer in range(L):
+            for e in range(E):
+                for p in range(3):
+                    d = device.moe_projection(moe, layer, e, p)
+                    tq.pack(self.descs[p], d["trits"], d["scales"], None, self.blob(layer, e, p))
+                    del d
+        torch.cuda.synchronize()
+        self.run_type = {BF16: BF16, F32: F32, I8: tq.F32_Q8}[moe.x_type]
+        self.routes = [inputs.moe_expert_rows(moe, layer) for layer in range(L)]
+        rows = moe.batch * moe.top_k
+        self.xh, self.xi, self.ys = [], [], []
+        items, tokens, self.meta = [], [], []
+        for layer in range(L):
+            r = self.routes[layer]
+            tok = torch.from_numpy(np.concatenate([a for a, _ in r])).cuda()
+            pair = torch.from_numpy(np.concatenate([b for _, b in r])).cuda()
+            self.xh.append(device.moe_hidden(moe, layer).index_select(0, tok).contiguous())
+            self.xi.append(device.moe_inter(moe, layer).index_select(0, pair).contiguous())
+            self.ys.append([torch.empty((rows, n), dtype=torch.float32, device="cuda") for (_, n, _) in self.shapes])
+            off = 0
+            for e in range(E):
+                n_e = len(r[e][0])
+                for c in range(0, n_e, self.MAX_TOKENS):
+                    m = min(self.MAX_TOKENS, n_e - c)
+                    a = off + c
+                    for p in range(3):
+                        x = (self.xh if p < 2 else self.xi)[layer][a:a + m]
+                        items.append((self.descs[p], self.blob(layer, e, p), x, None, self.ys[layer][p][a:a + m], None))
+                        tokens.append(m)
+                        self.meta.append((layer, e, p, a, m))
+                off += n_e
+        torch.cuda.synchronize()
+        self.tokens = tokens
+        self.max_tokens = max(tokens) if tokens else 0
+        self._probs = tq.problems(items)
+        nbytes = tq.gemv_grouped_workspace_size(self._probs, self.max_tokens)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.plan = None
+
+    def blob(self, layer, e, p):
+        o = (layer * self.moe.experts + e) * self.expert_bytes + self.proj_off[p]
+        return self.slab[o:o + self.sizes[p]]
+
+    def prepare(self, waves: int = 0, row_blocks: int = 0):
+        from ternary_weight_amd import tq
+        self.plan = tq.gemv_grouped_prepare_tokens(self._probs, self.tokens, self.run_type, self.ws,
+                                                   self.ws.numel(), waves=waves, row_blocks=row_blocks)
+
+    def gemv(self):
+        from ternary_weight_amd import tq
+        tq.gemv_grouped_run(self.plan)
+
+    def active_experts(self) -> int:
+        return sum(sum(1 for a, _ in r if len(a)) for r in self.routes)
+
+    def gemv_bytes(self) -> int:
+        """Algorithmic bytes of a step: the packed trits and scales of every
+        routed expert once, each routed token's input rows once (the hidden
+        state read by gate and up counts once) and every output written."""
+        moe, K = self.moe, self.moe.planes
+        xsz = {BF16: 2, F32: 4, I8: 4}[moe.x_type]
+        w = 0
+        for (_, n, kin) in self.shapes:
+            w += K * n * kin // 4
+            w += 2 * K * n * (kin // moe.group) if moe.layout == GROUP_F16 else 4 * K
+        pairs = moe.layers * moe.batch * moe.top_k
+        return (self.active_experts() * w + pairs * (moe.hidden + moe.inter) * xsz
+                + pairs * 4 * (2 * moe.inter + moe.hidden))
+
+
+def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
+    """The kernel a grouped decode plan launches (as rocprofv3 names it)."""
+    if plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
+        ks = 32 if layout == TENSOR or group % 32 == 0 else 16
+        return "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (run_type, layout, planes, ks)
+    return "k_gemv_grouped<%d, %d, %d, %d>" % (run_type, layout, planes, 1 if plan.M <= 1 else 4)
 
 
 # ---------------------------------------------------------------------------
@@ -471,6 +581,9 @@ def main():
     if args.config == "chain":
         main_chain(args)
         return
+    if args.config == "moe":
+        main_moe(args)
+        return
     if args.config.startswith("ternarize"):
         main_ternarize(args)
         return
@@ -528,12 +641,7 @@ def main():
         peak = MFMA_PEAK_I8_TOPS if case.x_type == I8 else MFMA_PEAK_BF16_TFLOPS
         unit = "TOP/s" if case.x_type == I8 else "TFLOP/s"
     else:
-        if stack.plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
-            ks = 32 if case.layout == TENSOR or case.group % 32 == 0 else 16
-            kernel_name = "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (stack.run_type, case.layout, case.planes, ks)
-        else:
-            kernel_name = "k_gemv_grouped<%d, %d, %d, %d>" % (stack.run_type, case.layout, case.planes,
-                                                              1 if M == 1 else (4 if M <= 4 else 16))
+        kernel_name = decode_kernel_name(stack.plan, stack.run_type, case.layout, case.planes, case.group)
         value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
         achieved = gbytes / (gemv_avg / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
@@ -735,6 +843,162 @@ def main_chain(args):
         },
         "cpu_baseline": cpu,
         "hbm_ceiling": ceiling,
+        "parity_spot_check": check,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+# MoE experts: the routed experts of every layer for a decode batch.
+# ---------------------------------------------------------------------------
+def moe_reference(moe, layer, e, p, a, m, rows=None):
+    """The oracle's outputs [m][len(rows)] of one problem of a MoeStack, from
+    host-regenerated weights and activations."""
+    import oracle
+    h = inputs.moe_projection(moe, layer, e, p, rows=rows)
+    toks, pairs = inputs.moe_expert_rows(moe, layer)[e]
+    c = a - sum(len(t) for t, _ in inputs.moe_expert_rows(moe, layer)[:e])   # first token of the chunk
+    src = inputs.moe_hidden(moe, layer)[toks[c:c + m]] if p < 2 else inputs.moe_inter(moe, layer)[pairs[c:c + m]]
+    if moe.x_type == I8:
+        q, s = oracle.act_quant_i8(src, F32)
+        return oracle.gemv_i8(moe.planes, moe.group, moe.layout, h["trits"], h["scales"], q, s, None)["y64"]
+    return oracle.gemv_fp(moe.planes, moe.group, moe.layout, h["trits"], h["scales"], src, moe.x_type, None)
+
+
+def moe_spot_check(stack, n_prob=3, rows=64) -> dict:
+    """Rows of a few problems (first, last, one between) against the oracle."""
+    import torch
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(98)
+    picks = sorted({0, len(stack.meta) - 1, int(rng.integers(len(stack.meta)))})[:n_prob]
+    worst = 0.0
+    for i in picks:
+        layer, e, p, a, m = stack.meta[i]
+        n = stack.shapes[p][1]
+        r = np.sort(rng.choice(n, size=min(rows, n), replace=False))
+        y = stack.ys[layer][p][a:a + m].cpu().numpy()[:, r]
+        worst = max(worst, rel_err(y, moe_reference(stack.moe, layer, e, p, a, m, rows=r)))
+    return {"problems": len(picks), "rows_each": rows, "max_rel_err": worst}
+
+
+def moe_cpu_baseline(stack, seconds: float) -> dict:
+    """The oracle on the host cores over the routed experts of layer 0, in order."""
+    import oracle
+    moe = stack.moe
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    orc = oracle.default()
+    hid, inter = inputs.moe_hidden(moe, 0), inputs.moe_inter(moe, 0)
+    route = inputs.moe_expert_rows(moe, 0)
+    xsz = {BF16: 2, F32: 4, I8: 4}[moe.x_type]
+    done, reps, experts, t0 = 0, 0, 0, time.perf_counter()
+    el = 0.0
+    for e in range(moe.experts):
+        toks, pairs = route[e]
+        if not len(toks):
+            continue
+        for p, (_, n, kin) in enumerate(stack.shapes):
+            h = inputs.moe_projection(moe, 0, e, p)
+            x = hid[toks] if p < 2 else inter[pairs]
+            t1 = time.perf_counter()
+            if moe.x_type == I8:
+                q, s = orc.act_quant_i8(x, F32)
+                orc.gemv_i8(moe.planes, moe.group, moe.layout, h["trits"], h["scales"], q, s, None, nthreads=threads)
+            else:
+                orc.gemv_fp(moe.planes, moe.group, moe.layout, h["trits"], h["scales"], x, moe.x_type, None,
+                            nthreads=threads)
+            el += time.perf_counter() - t1
+            done += (moe.planes * n * kin // 4 + 2 * moe.planes * n * (kin // moe.group)
+                     + len(toks) * kin * xsz + 4 * len(toks) * n)
+            reps += 1
+        experts += 1
+        if el >= seconds:
+            break
+    return {"value": round(done / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the first %d routed experts of layer 0 (gate, up, down each, their routed tokens), "
+                      "%.1f s of oracle time (input generation excluded); C oracle, OpenMP over output rows"
+                      % (experts, el)}
+
+
+def main_moe(args):
+    import torch
+    from synth.configs import MOES
+    import dataclasses
+    moe = MOES["moe"]
+    if args.batch:
+        moe = dataclasses.replace(moe, batch=args.batch)
+    if args.moe_int8:
+        moe = dataclasses.replace(moe, x_type=I8)
+    t_build = time.perf_counter()
+    stack = MoeStack(moe)
+    stack.prepare(args.waves, args.row_blocks)
+    print("built moe: %d layers x %d experts, %.1f GB packed, %d problems (%d routed experts), "
+          "plan %d items x %d blocks x %d waves (%.1f s)"
+          % (moe.layers, moe.experts, stack.blob_bytes / 1e9, len(stack.meta), stack.active_experts(),
+             stack.plan.n_items, stack.plan.row_blocks, stack.plan.waves, time.perf_counter() - t_build),
+          file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    spin_up(args.spin_up_ms)
+    for _ in range(args.warmup):
+        stack.gemv()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        stack.gemv()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    gbytes = stack.gemv_bytes()
+    value = gbytes / (ms_step / 1e3) / 1e9
+    kernel_name = decode_kernel_name(stack.plan, stack.run_type, moe.layout, moe.planes, moe.group)
+    check = None if args.no_check else moe_spot_check(stack)
+    cpu = None if args.no_cpu_baseline else moe_cpu_baseline(stack, args.cpu_seconds)
+    out = {
+        "metric": METRIC_MOE,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {I8: "i8", BF16: "bf16", F32: "f32"}[moe.x_type],
+        "data": "synthetic (seeded SplitMix64; trits P(0)=0.4, x ~ N(0,1), uniform top-%d routing)" % moe.top_k,
+        "config": {
+            "workload": moe.name,
+            "layers": moe.layers,
+            "experts": moe.experts,
+            "top_k": moe.top_k,
+            "batch_tokens": moe.batch,
+            "routed_experts": stack.active_experts(),
+            "problems": len(stack.meta),
+            "max_tokens_per_problem": stack.max_tokens,
+            "planes": moe.planes,
+            "group": moe.group,
+            "step": "one grouped launch over every routed (layer, expert, projection) of the batch, each "
+                    "with its own token count" + ("; fp32 inputs quantised per token to int8 inside it"
+                                                  if moe.x_type == I8 else ""),
+            "packed_weight_bytes": stack.blob_bytes,
+            "grouped_waves": stack.plan.waves,
+            "grouped_row_blocks": stack.plan.row_blocks,
+        },
+        "tok_per_s_equiv": round(moe.batch * 1e3 / ms_step, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(value, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(kernel_name),
+            "kernel": kernel_name,
+            "bytes_per_launch": gbytes,
+        },
+        "cpu_baseline": cpu,
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }

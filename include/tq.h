@@ -165,9 +165,10 @@ tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count,
 
 /*
  * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
- * scale per group).  With TQ_BF16 and M >= 8 (and x 16-byte aligned) the
- * product runs on the matrix cores instead, as tq_gemm does; the results meet
- * the same bound.
+ * scale per group; up to 4 tokens per pass over the codes, one launch per
+ * slice of 4 tokens beyond that).  With TQ_BF16 and M >= 8 (and x 16-byte
+ * aligned) the product runs on the matrix cores instead, as tq_gemm does; the
+ * results meet the same bound.
  *   x         device [M][Kin] of x_type
  *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else unused
  *             (TQ_F32_Q8 computes the per-token scales itself)
@@ -244,12 +245,36 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
  * (0 = default: 4 waves, 1 block; with TQ_F32_Q8 1 wave, 4 blocks, so that
  * a workgroup quantises its activations once for four blocks; with TQ_BF16
- * 1 wave, 16 blocks, so that 16 blocks share the workgroup's trit table).  Copies
- * host->device on `stream` and synchronizes it.
+ * 1 wave, 16 blocks, so that 16 blocks share the workgroup's trit table).  The
+ * decode kernels take up to 4 tokens per pass over the codes: with M > 4 each
+ * problem is cut into slices of 4 tokens whose workgroups are placed to run
+ * on one XCD together, so that the later slices read the codes from its L2.
+ * Copies host->device on `stream` and synchronizes it.
  */
 tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
                                   int32_t x_type, void* workspace, size_t workspace_bytes,
                                   tq_grouped_plan* plan, void* stream);
+
+/*
+ * As tq_gemv_grouped_prepare, but problem i has its own token count
+ * tokens[i] (host array of `count`, each 0..16): x is tokens[i] x Kin and y
+ * tokens[i] x N.  This is the expert-grouped decode of a mixture-of-experts
+ * layer: every expert's matrix is fit on its own (sasori page, "How it works
+ * & paper"), so each expert is one problem with its own blob, and the tokens
+ * the router sent to it are gathered into its x.  A problem with no tokens
+ * takes no workgroup (its pointers may then be NULL).  With TQ_BF16, a
+ * largest count above 4 and every x 16-byte aligned the plan is a
+ * matrix-core plan whose tiles cover each problem's own count; otherwise the
+ * vector-ALU kernels take up to 4 tokens per pass and a problem with more is
+ * cut into slices of 4 (as in tq_gemv_grouped_prepare).  The workspace is
+ * tq_gemv_grouped_workspace_size's with M = the largest count.  More than 16 tokens for one expert: split them over
+ * several problems that share the blob.  Errors as tq_gemv_grouped_prepare,
+ * plus TQ_ERR_ARG for a NULL `tokens` with count > 0 or a negative count and
+ * TQ_ERR_UNSUPPORTED for a count above 16.
+ */
+tq_status tq_gemv_grouped_prepare_tokens(const tq_problem* problems, const int32_t* tokens,
+                                         int32_t count, int32_t x_type, void* workspace,
+                                         size_t workspace_bytes, tq_grouped_plan* plan, void* stream);
 
 /* One launch computing every problem of the plan.  Asynchronous. */
 tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream);

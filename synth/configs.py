@@ -9,6 +9,10 @@ Shapes:
   dimensions are the published ones): hidden 4096, 32 layers, 32 query /
   8 KV heads of 128, FFN 14336.
 
+  Qwen3-30B-A3B (the sasori page's "Measured results" runs it as TQ3P, K=3,
+  g=256; the page gives no dimensions, these are the published ones): 48
+  layers, hidden 2048, 128 experts of intermediate 768, 8 routed per token.
+
 Each projection is (name, out_features N, in_features Kin), weight N x Kin.
 """
 from __future__ import annotations
@@ -46,7 +50,7 @@ TENSOR, GROUP_F16, CODEBOOK = 0, 1, 2
 F32, BF16, I8 = 0, 1, 2
 
 # Tensor kinds (low 16 bits of the seed key).
-KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS, KIND_NORM, KIND_DENSE = 1, 2, 3, 4, 5, 6, 7
+KIND_TRITS, KIND_SCALES, KIND_X, KIND_INDEX, KIND_DIGITS, KIND_NORM, KIND_DENSE, KIND_ROUTE = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -130,4 +134,42 @@ CHAINS = {
                    30, 2560, 6912, 20, 5, 128, weights_cfg=2),
     "chain_small": Chain(8, "BitNet-shaped decode chain at small sizes, 6 layers",
                          6, 256, 704, 4, 2, 64, weights_cfg=8),
+}
+
+
+@dataclass(frozen=True)
+class Moe:
+    """The routed experts of mixture-of-experts layers, decoded for a batch of
+    tokens.  Each expert has its own gate, up and down matrices, each fit on
+    its own into K planes (sasori page, "How it works & paper"); a token is
+    sent to ``top_k`` of the ``experts`` experts of every layer."""
+    cfg: int
+    name: str
+    layers: int
+    hidden: int
+    inter: int
+    experts: int
+    top_k: int
+    planes: int
+    group: int
+    layout: int
+    x_type: int
+    batch: int               # tokens decoded together
+
+    def proj_shapes(self):
+        """[(name, N, Kin)] of one expert: gate, up, down."""
+        return [("gate", self.inter, self.hidden), ("up", self.inter, self.hidden),
+                ("down", self.hidden, self.inter)]
+
+    def case(self) -> Case:
+        """The weight recipe of the decode stacks, for the generators."""
+        return Case(self.cfg, self.name, None, self.planes, self.group, self.layout, self.x_type, 0,
+                    single=(self.hidden, self.hidden))
+
+
+MOES = {
+    "moe": Moe(9, "Qwen3-30B-A3B-shaped MoE experts, 48 layers x 128 experts (8 routed per token), "
+                  "K=3, g=256, f16 group scales, bf16 x", 48, 2048, 768, 128, 8, 3, 256, GROUP_F16, BF16, 64),
+    "moe_small": Moe(10, "MoE experts at small sizes, 2 layers x 16 experts (4 routed per token)",
+                     2, 512, 256, 16, 4, 3, 128, GROUP_F16, BF16, 12),
 }

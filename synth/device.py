@@ -93,3 +93,37 @@ def projection(case, layer: int, proj: int, N: int, Kin: int, M=None, device="cu
         fill(K_NORMAL_F32, s["x"], 0, x)
     d["x"] = x
     return d
+
+
+def moe_projection(moe, layer: int, expert: int, proj: int, device="cuda"):
+    """Device tensors with the same values as synth.inputs.moe_projection(...)."""
+    _, N, Kin = moe.proj_shapes()[proj]
+    return projection(moe.case(), layer, expert * 3 + proj, N, Kin, M=0, device=device)
+
+
+def activations(seed: int, M: int, Kin: int, x_type: int, device="cuda"):
+    """Device tensor with the values of synth.inputs.activations(seed, M, Kin, x_type)."""
+    import torch
+    if x_type == BF16:
+        x = torch.empty((M, Kin), dtype=torch.int16, device=device)
+        fill(K_NORMAL_BF16, seed, 0, x)
+    else:
+        x = torch.empty((M, Kin), dtype=torch.float32, device=device)
+        fill(K_NORMAL_F32, seed, 0, x)
+    return x
+
+
+def moe_hidden(moe, layer: int, device="cuda"):
+    """Device copy of synth.inputs.moe_hidden(moe, layer)."""
+    from . import inputs
+    from .configs import KIND_X
+    return activations(gen.tensor_seed(moe.cfg, layer, inputs.MOE_HIDDEN_ID, KIND_X), moe.batch, moe.hidden,
+                       F32 if moe.x_type in (F32, I8) else BF16, device)
+
+
+def moe_inter(moe, layer: int, device="cuda"):
+    """Device copy of synth.inputs.moe_inter(moe, layer)."""
+    from . import inputs
+    from .configs import KIND_X
+    return activations(gen.tensor_seed(moe.cfg, layer, inputs.MOE_INTER_ID, KIND_X), moe.batch * moe.top_k,
+                       moe.inter, F32 if moe.x_type in (F32, I8) else BF16, device)

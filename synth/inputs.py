@@ -24,8 +24,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import gen
-from .configs import (BF16, CODEBOOK, F32, GROUP_F16, I8, KIND_DIGITS,
-                      KIND_DENSE, KIND_INDEX, KIND_NORM, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
+from .configs import (BF16, CODEBOOK, F32, GROUP_F16, I8, KIND_DIGITS, KIND_DENSE, KIND_INDEX,
+                      KIND_NORM, KIND_ROUTE, KIND_SCALES, KIND_TRITS, KIND_X, TENSOR)
 
 N_CODEBOOK = 27
 
@@ -152,6 +152,63 @@ def dense_weight(cfg: int, layer: int, proj: int, N: int, Kin: int, sigma: float
     return (gen.normal(seed, 0, N * Kin) * sigma).astype(np.float32).reshape(N, Kin)
 
 
-__all__ = ["projection", "dense_weight", "chain_projection", "chain_norm", "chain_input", "activations", "plane_values", "plane_values_full", "group_scales",
+# Mixture-of-experts decode: routing, expert weights and the tokens' activations.
+# A layer's routing gives every token top_k distinct experts, uniformly: the
+# experts holding its top_k smallest of one uniform draw per expert (the
+# pages give no router; a trained one is skewed, which only moves tokens
+# between experts).  Expert e's inputs are the rows of its tokens, in token
+# order: the hidden states for gate and up, and for down one row per
+# (token, expert) pair of the intermediate activations.
+MOE_HIDDEN_ID, MOE_INTER_ID = 0xFFFF, 0xFFFE
+
+
+def moe_routing(moe, layer: int) -> np.ndarray:
+    """int64 [batch][top_k]: each token's experts, ascending."""
+    seed = gen.tensor_seed(moe.cfg, layer, 0, KIND_ROUTE)
+    E = moe.experts
+    out = np.empty((moe.batch, moe.top_k), dtype=np.int64)
+    for t in range(moe.batch):
+        keys = gen.uniform(seed, t * E, E)
+        out[t] = np.sort(np.argsort(keys, kind="stable")[:moe.top_k])
+    return out
+
+
+def moe_expert_rows(moe, layer: int):
+    """Per expert: (tokens, pairs), int64 arrays of the batch rows of its
+    tokens and of their rows in the intermediate activations (token * top_k
+    + the expert's place among the token's experts)."""
+    route = moe_routing(moe, layer)
+    toks = [[] for _ in range(moe.experts)]
+    pairs = [[] for _ in range(moe.experts)]
+    for t in range(moe.batch):
+        for j, e in enumerate(route[t]):
+            toks[int(e)].append(t)
+            pairs[int(e)].append(t * moe.top_k + j)
+    return [(np.array(a, dtype=np.int64), np.array(b, dtype=np.int64)) for a, b in zip(toks, pairs)]
+
+
+def moe_hidden(moe, layer: int) -> np.ndarray:
+    """The batch's hidden states entering a layer's experts [batch][hidden]
+    (fp32 values or bf16 bits, as ``activations``)."""
+    return activations(gen.tensor_seed(moe.cfg, layer, MOE_HIDDEN_ID, KIND_X), moe.batch, moe.hidden,
+                       F32 if moe.x_type in (F32, I8) else BF16)
+
+
+def moe_inter(moe, layer: int) -> np.ndarray:
+    """The intermediate activations entering the down matrices, one row per
+    (token, expert) pair [batch * top_k][inter]."""
+    return activations(gen.tensor_seed(moe.cfg, layer, MOE_INTER_ID, KIND_X), moe.batch * moe.top_k,
+                       moe.inter, F32 if moe.x_type in (F32, I8) else BF16)
+
+
+def moe_projection(moe, layer: int, expert: int, proj: int, rows=None) -> dict:
+    """Weights of projection ``proj`` (0 gate, 1 up, 2 down) of one expert, as
+    ``projection`` draws them (no x)."""
+    _, N, Kin = moe.proj_shapes()[proj]
+    return projection(moe.case(), layer, expert * 3 + proj, N, Kin, rows=rows, M=0)
+
+
+__all__ = ["moe_routing", "moe_expert_rows", "moe_hidden", "moe_inter", "moe_projection",
+           "projection", "dense_weight", "chain_projection", "chain_norm", "chain_input", "activations", "plane_values", "plane_values_full", "group_scales",
            "tensor_scales", "codebook_indices", "seeds", "N_CODEBOOK",
            "TENSOR", "GROUP_F16", "CODEBOOK", "F32", "BF16", "I8"]

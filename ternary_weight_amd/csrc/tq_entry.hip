@@ -98,6 +98,12 @@ TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_
     return tq_ok();
 }
 
+namespace {
+
+int64_t pass_slices(int64_t M) { return M <= TQ_PASS_TOKENS ? 1 : (M + TQ_PASS_TOKENS - 1) / TQ_PASS_TOKENS; }
+
+}  // namespace
+
 TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t count,
                                                    int64_t M, size_t* bytes)
 {
@@ -112,15 +118,29 @@ TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, i
         if (s) return tq_fail_problem(s, i);
         items += L.NB;
     }
-    // problems, then one (problem, first row block) item per workgroup (at most one per block)
-    *bytes = (size_t)(tq_ws_items_off(count) + tq_align256(items * 8));
+    // a problem of more than one pass of tokens is cut into slices, each an
+    // entry of the table with its own items; their placement leaves fewer
+    // than 8 (slices + 1) holes in the item list
+    const int64_t slices = pass_slices(M);
+    items = items * slices + (slices > 1 ? 8 * (slices + 1) : 0);
+    // problem entries, then one (entry, first row block) item per workgroup
+    *bytes = (size_t)(tq_ws_items_off(count * slices) + tq_align256(items * 8));
     if (*bytes == 0) *bytes = 256;
     return tq_ok();
 }
 
-TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
-                                            int32_t x_type, void* workspace, size_t workspace_bytes,
-                                            tq_grouped_plan* plan, void* stream)
+namespace {
+
+// The decode plan; tokens (host, may be NULL): each problem's own token
+// count, every one at most M.  The kernels take TQ_PASS_TOKENS tokens per
+// pass over the codes; a problem with more is cut into slices of that many
+// tokens, each an entry of the device table.  Workgroups are dealt to the 8
+// XCDs in turn, so the slices of one row block are placed 8 items apart:
+// they run on one XCD at about the same time and share the codes through
+// its L2 (holes left by this placement are items of entry -1).
+tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int32_t count, int64_t M,
+                          int32_t x_type, void* workspace, size_t workspace_bytes, tq_grouped_plan* plan,
+                          void* stream)
 {
     if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
     const int pow2[] = {1, 2, 4, 8, 16};
@@ -136,22 +156,31 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
     if (s) return s;
     // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte loads
+    const int64_t mfma_min = tokens ? TQ_PASS_TOKENS + 1 : TQ_BF16_MFMA_MIN_M;
     bool mfma = count > 0;
-    for (int32_t i = 0; i < count; ++i) mfma = mfma && tq_gemv_uses_mfma(x_type, M, problems[i].x);
-    if (mfma) return tq_gemm_grouped_prepare(problems, count, M, x_type, workspace, workspace_bytes, plan, stream);
+    for (int32_t i = 0; i < count; ++i)
+        mfma = mfma && x_type == TQ_BF16 && M >= mfma_min && ((uintptr_t)problems[i].x & 15) == 0;
+    if (mfma)
+        return tq_gemm_grouped_prepare_counts(problems, tokens, count, M, x_type, workspace, workspace_bytes, plan,
+                                              stream);
     if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
     if (workspace_bytes < need)
         return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-    std::vector<tq_prob_dev> probs((size_t)count);
-    struct Item { int64_t cost; int32_t prob, rb0; };
-    std::vector<Item> items;
+    std::vector<tq_prob_dev> probs;
+    probs.reserve((size_t)count);
+    struct Unit { int64_t cost; int32_t entry, n, rb0; };   // row blocks of one problem, all its slices
+    std::vector<Unit> units;
+    std::vector<int32_t> first((size_t)count), n_slices((size_t)count);
     int family = -1, K0 = 0, layout0 = -1, g0 = 0;
     size_t x_lds = 0;
     for (int32_t i = 0; i < count; ++i) {
         const tq_problem& pr = problems[i];
         tq_layout L;
         tq_check_desc(pr.desc, &L);
-        if ((s = tq_check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, TQ_MAX_M_GEMV)))
+        const int64_t Mi = tokens ? tokens[i] : M;
+        if (Mi < 0 || Mi > M)
+            return tq_fail(TQ_ERR_ARG, "problem %d: %lld tokens, not in 0..%lld", i, (long long)Mi, (long long)M);
+        if ((s = tq_check_call(L, pr.blob, Mi, x_type, pr.x, pr.x_scale, pr.y, pr.acc, TQ_MAX_M_GEMV)))
             return tq_fail_problem(s, i);
         if (i == 0) {
             K0 = L.K;
@@ -161,11 +190,21 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
             return tq_fail(TQ_ERR_UNSUPPORTED,
                            "problem %d: all problems of a plan must share planes, layout and group", i);
         }
-        probs[(size_t)i] = tq_make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
-        if (x_type == TQ_F32_Q8) x_lds = std::max(x_lds, tq_x_lds_bytes(M, L.Kin));
+        const tq_prob_dev whole = tq_make_prob(L, pr.blob, Mi, pr.x, pr.x_scale, pr.y, pr.acc);
+        first[(size_t)i] = (int32_t)probs.size();
+        if (Mi <= TQ_PASS_TOKENS) {
+            probs.push_back(whole);
+        } else {
+            for (int m0 = 0; m0 < (int)Mi; m0 += TQ_PASS_TOKENS)
+                probs.push_back(tq_prob_slice(whole, x_type, m0, std::min<int>(TQ_PASS_TOKENS, (int)Mi - m0)));
+        }
+        n_slices[(size_t)i] = (int32_t)probs.size() - first[(size_t)i];
+        if (x_type == TQ_F32_Q8)
+            x_lds = std::max(x_lds, tq_x_lds_bytes(std::min<int64_t>(Mi, TQ_PASS_TOKENS), L.Kin));
     }
+    bool sliced = false;
     if (count > 0 && M > 0) {
-        family = tq_gemv_family(x_type, layout0, K0, (int)M);
+        family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, TQ_PASS_TOKENS));
         // a shape whose partial sums overflow the workgroup's LDS: the default
         // one gives up the column split first, a requested one is refused
         auto lds = [&](int w, int rbs) { return tq_gemv_lds_bytes(family, w, w * rbs, x_lds); };
@@ -178,23 +217,42 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
                 return tq_fail(TQ_ERR_UNSUPPORTED, "decode needs more LDS than a workgroup has");
         }
         for (int32_t i = 0; i < count; ++i) {
-            const tq_prob_dev& P = probs[(size_t)i];
+            const tq_prob_dev& P = probs[(size_t)first[(size_t)i]];
+            if (P.M == 0) continue;          // a problem with no tokens has no work
             const int64_t NB = (P.N + 63) / 64;
             for (int64_t rb = 0; rb < NB; rb += row_blocks) {
                 const int64_t nb = std::min<int64_t>(row_blocks, NB - rb);
-                items.push_back({nb * P.NC * (int64_t)K0, i, (int32_t)rb});
+                units.push_back({nb * P.NC * (int64_t)K0, first[(size_t)i], n_slices[(size_t)i], (int32_t)rb});
+                sliced = sliced || n_slices[(size_t)i] > 1;
             }
         }
     }
-    // longest items first, so that the last workgroups to start are short
-    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
-    std::vector<uint8_t> host((size_t)need, 0);
-    if (count > 0) memcpy(host.data(), probs.data(), (size_t)count * sizeof(tq_prob_dev));
-    int32_t* it = (int32_t*)(host.data() + tq_ws_items_off(count));
-    for (size_t j = 0; j < items.size(); ++j) {
-        it[2 * j] = items[j].prob;
-        it[2 * j + 1] = items[j].rb0;
+    // longest units first, so that the last workgroups to start are short
+    std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+    std::vector<int2> items;
+    if (!sliced) {
+        for (const Unit& u : units) items.push_back(make_int2(u.entry, u.rb0));
+    } else {
+        // each unit goes to the XCD whose list is shortest, its slices 8 items apart
+        int64_t next[8];
+        for (int r = 0; r < 8; ++r) next[r] = r;
+        for (const Unit& u : units) {
+            const int r = (int)(std::min_element(next, next + 8) - next);
+            for (int j = 0; j < u.n; ++j) {
+                const size_t pos = (size_t)(next[r] + 8 * j);
+                if (items.size() <= pos) items.resize(pos + 1, make_int2(-1, 0));
+                items[pos] = make_int2(u.entry + j, u.rb0);
+            }
+            next[r] += 8 * (int64_t)u.n;
+        }
     }
+    const int64_t n_entries = (int64_t)probs.size();
+    if ((size_t)(tq_ws_items_off(n_entries) + (int64_t)items.size() * 8) > need)
+        return tq_fail(TQ_ERR_ARG, "internal: plan exceeds its workspace");
+    std::vector<uint8_t> host((size_t)need, 0);
+    if (n_entries > 0) memcpy(host.data(), probs.data(), (size_t)n_entries * sizeof(tq_prob_dev));
+    if (!items.empty())
+        memcpy(host.data() + tq_ws_items_off(n_entries), items.data(), items.size() * sizeof(int2));
     hipStream_t st = (hipStream_t)stream;
     if ((s = tq_check_hip(hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, st),
                           "tq_gemv_grouped_prepare copy")))
@@ -207,10 +265,31 @@ TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t 
     plan->M = (int32_t)M;
     plan->waves = waves;
     plan->row_blocks = row_blocks;
-    plan->n_problems = count;
+    plan->n_problems = (int32_t)n_entries;
     plan->x_lds_bytes = (int32_t)x_lds;
     plan->reserved = 0;
     return tq_ok();
+}
+
+}  // namespace
+
+TQ_EXPORT tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                            int32_t x_type, void* workspace, size_t workspace_bytes,
+                                            tq_grouped_plan* plan, void* stream)
+{
+    return grouped_prepare(problems, nullptr, count, M, x_type, workspace, workspace_bytes, plan, stream);
+}
+
+TQ_EXPORT tq_status tq_gemv_grouped_prepare_tokens(const tq_problem* problems, const int32_t* tokens,
+                                                   int32_t count, int32_t x_type, void* workspace,
+                                                   size_t workspace_bytes, tq_grouped_plan* plan, void* stream)
+{
+    if (count > 0 && !tokens) return tq_fail(TQ_ERR_ARG, "tokens is NULL");
+    int64_t M = 0;
+    for (int32_t i = 0; i < count; ++i) M = std::max<int64_t>(M, tokens[i]);
+    if (M > TQ_MAX_M_GEMV)
+        return tq_fail(TQ_ERR_UNSUPPORTED, "a problem has more than %d tokens", TQ_MAX_M_GEMV);
+    return grouped_prepare(problems, tokens, count, M, x_type, workspace, workspace_bytes, plan, stream);
 }
 
 TQ_EXPORT tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* stream)

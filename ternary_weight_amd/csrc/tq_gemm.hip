@@ -126,9 +126,11 @@ TQ_EXPORT tq_status tq_gemm_grouped_workspace_size(const tq_problem* problems, i
     return tq_ok();
 }
 
-TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
-                                            int32_t x_type, void* workspace, size_t workspace_bytes,
-                                            tq_grouped_plan* plan, void* stream)
+// tokens (host, may be NULL): problem i's own token count, at most M; the
+// kernel is the one of M tokens, each problem's tiles cover its own count.
+tq_status tq_gemm_grouped_prepare_counts(const tq_problem* problems, const int32_t* tokens, int32_t count,
+                                         int64_t M, int32_t x_type, void* workspace, size_t workspace_bytes,
+                                         tq_grouped_plan* plan, void* stream)
 {
     if (!plan) return tq_fail(TQ_ERR_ARG, "plan is NULL");
     size_t need = 0;
@@ -146,7 +148,10 @@ TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t 
         const tq_problem& pr = problems[i];
         tq_layout L;
         tq_check_desc(pr.desc, &L);
-        if ((s = tq_check_call(L, pr.blob, M, x_type, pr.x, pr.x_scale, pr.y, pr.acc, kMaxM, 16)))
+        const int64_t Mi = tokens ? tokens[i] : M;
+        if (Mi < 0 || Mi > M)
+            return tq_fail(TQ_ERR_ARG, "problem %d: %lld tokens, not in 0..%lld", i, (long long)Mi, (long long)M);
+        if ((s = tq_check_call(L, pr.blob, Mi, x_type, pr.x, pr.x_scale, pr.y, pr.acc, kMaxM, 16)))
             return tq_fail_problem(s, i);
         const tq_gemm_kernel* k = gemm_kernel(L, x_type, M);
         if (i == 0) {
@@ -156,9 +161,9 @@ TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t 
             return tq_fail(TQ_ERR_UNSUPPORTED,
                            "problem %d: all problems of a plan must share planes, layout and x_type", i);
         }
-        probs[(size_t)i] = tq_make_prob(L, pr.blob, M, pr.x, pr.x_scale, pr.y, pr.acc);
-        if (M > 0) {
-            const int64_t n = tiles_of(*k, M, L.N, nullptr);
+        probs[(size_t)i] = tq_make_prob(L, pr.blob, Mi, pr.x, pr.x_scale, pr.y, pr.acc);
+        if (Mi > 0) {
+            const int64_t n = tiles_of(*k, Mi, L.N, nullptr);
             for (int64_t t = 0; t < n; ++t) items.push_back({L.Kin * (int64_t)L.K, i, (int32_t)t});
         }
     }
@@ -186,6 +191,14 @@ TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t 
     plan->row_blocks = k0 ? k0->fn * (4 / k0->wm) / 4 : 0;
     plan->n_problems = count;
     return tq_ok();
+}
+
+TQ_EXPORT tq_status tq_gemm_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
+                                            int32_t x_type, void* workspace, size_t workspace_bytes,
+                                            tq_grouped_plan* plan, void* stream)
+{
+    return tq_gemm_grouped_prepare_counts(problems, nullptr, count, M, x_type, workspace, workspace_bytes, plan,
+                                          stream);
 }
 
 TQ_EXPORT tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream)

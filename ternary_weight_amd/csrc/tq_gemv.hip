@@ -5,47 +5,47 @@ namespace {
 
 using namespace tqk;
 
-int mt_index(int M) { return M <= 1 ? 0 : (M <= 4 ? 1 : 2); }
+int mt_index(int M) { return M <= 1 ? 0 : 1; }
 
 // LDS of the partial sums: one area per wave when a row block is split.
 size_t red_bytes(int family, int split_waves, int total_waves)
 {
     if (split_waves <= 1) return 0;
-    const int mti = family % 3, K = (family / 3) % 4 + 1, layout = (family / 12) % 3;
+    const int mti = family % kTiers, K = (family / kTiers) % 4 + 1, layout = (family / (4 * kTiers)) % 3;
     const int R = layout != TQ_SCALE_TENSOR ? kMT[mti] : kMT[mti] * K;
     return (size_t)total_waves * R * 64 * 4;
 }
 
 const single_fn* single_tab(int xt, int mti)
 {
-    static const single_fn* (*const f[kXTypes][3])() = {
-        {single_table_0_0, single_table_0_1, single_table_0_2},
-        {single_table_1_0, single_table_1_1, single_table_1_2},
-        {single_table_2_0, single_table_2_1, single_table_2_2},
-        {single_table_3_0, single_table_3_1, single_table_3_2}};
+    static const single_fn* (*const f[kXTypes][kTiers])() = {
+        {single_table_0_0, single_table_0_1},
+        {single_table_1_0, single_table_1_1},
+        {single_table_2_0, single_table_2_1},
+        {single_table_3_0, single_table_3_1}};
     return f[xt][mti]();
 }
 
 const grouped_fn* grouped_tab(int xt, int mti)
 {
-    static const grouped_fn* (*const f[kXTypes][3])() = {
-        {grouped_table_0_0, grouped_table_0_1, grouped_table_0_2},
-        {grouped_table_1_0, grouped_table_1_1, grouped_table_1_2},
-        {grouped_table_2_0, grouped_table_2_1, grouped_table_2_2},
-        {grouped_table_3_0, grouped_table_3_1, grouped_table_3_2}};
+    static const grouped_fn* (*const f[kXTypes][kTiers])() = {
+        {grouped_table_0_0, grouped_table_0_1},
+        {grouped_table_1_0, grouped_table_1_1},
+        {grouped_table_2_0, grouped_table_2_1},
+        {grouped_table_3_0, grouped_table_3_1}};
     return f[xt][mti]();
 }
 
-// family = ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + M tier
+// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier
 single_fn single_of(int family)
 {
-    const int mti = family % 3, rest = family / 3;
+    const int mti = family % kTiers, rest = family / kTiers;
     return single_tab(rest / 12, mti)[rest % 12];
 }
 
 grouped_fn grouped_of(int family)
 {
-    const int mti = family % 3, rest = family / 3;
+    const int mti = family % kTiers, rest = family / kTiers;
     return grouped_tab(rest / 12, mti)[rest % 12];
 }
 
@@ -53,19 +53,22 @@ grouped_fn grouped_of(int family)
 
 size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_lds_bytes)
 {
-    const int x_type = family / 36;
+    const int x_type = family / kPerXT;
     const size_t fixed = (x_type == TQ_BF16 ? (size_t)kLutBytes : 0) + 1024;
     return fixed + red_bytes(family, split_waves, total_waves) + x_lds_bytes;
 }
 
 int tq_gemv_family(int x_type, int layout, int K, int M)
 {
-    if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 || M > 16)
+    if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 ||
+        M > TQ_PASS_TOKENS)
         return -1;
-    return ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + mt_index(M);
+    return ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + mt_index(M);
 }
 
-tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
+namespace {
+
+tq_status launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
 {
     const int fam = tq_gemv_family(x_type, L.layout, L.K, P.M);
     if (fam < 0) return tq_fail(TQ_ERR_UNSUPPORTED, "no decode kernel for this combination");
@@ -85,10 +88,24 @@ tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_
     return tq_check_launch("tq_gemv");
 }
 
+}  // namespace
+
+// More tokens than one pass takes: one launch per slice of tokens (the
+// codes of the later launches come from the caches when the weight fits).
+tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
+{
+    for (int m0 = 0; m0 < P.M; m0 += TQ_PASS_TOKENS) {
+        const tq_status s =
+            launch_single(L, tq_prob_slice(P, x_type, m0, std::min(TQ_PASS_TOKENS, P.M - m0)), x_type, stream);
+        if (s) return s;
+    }
+    return TQ_OK;
+}
+
 tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const void* workspace,
                                  int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream)
 {
-    if (family < 0 || family >= 3 * 4 * 3 * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
+    if (family < 0 || family >= kPerXT * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
     if (waves < 1 || row_blocks < 1 || waves * row_blocks > 16)
         return tq_fail(TQ_ERR_ARG, "bad plan shape %d x %d", waves, row_blocks);
     if (n_items <= 0) return tq_ok();

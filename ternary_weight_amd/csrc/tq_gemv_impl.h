@@ -815,6 +815,7 @@ __global__ __launch_bounds__(1024) void k_gemv_grouped(const tq_prob_dev* __rest
                                                        const int2* __restrict__ items, int nrb)
 {
     const int2 it = ld_uniform_struct(items + blockIdx.x);
+    if (it.x < 0) return;    // a hole the host left in the item list
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
     gemv_body<XT, LAYOUT, K, MT>(P, it.y, nrb);
 }
@@ -826,9 +827,11 @@ namespace tqk {
 typedef void (*single_fn)(tq_prob_dev);
 typedef void (*grouped_fn)(const tq_prob_dev*, const int2*, int);
 
-constexpr int kMT[3] = {1, 4, 16};
-// family = ((x_type * 3 + layout) * 4 + (K - 1)) * 3 + M-tier; 36 families per x_type
-constexpr int kPerXT = 36;
+// tokens per pass of each M tier (more tokens are taken in slices of the last)
+constexpr int kTiers = 2;
+constexpr int kMT[kTiers] = {1, TQ_PASS_TOKENS};
+// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier; 24 families per x_type
+constexpr int kPerXT = 12 * kTiers;
 constexpr int kXTypes = 4;
 
 // families of one (x_type, M tier): index = layout * 4 + (K - 1)
@@ -855,9 +858,9 @@ const single_fn* single_table(int x_type, int mti);
 const grouped_fn* grouped_table(int x_type, int mti);
 #define TQ_DECLARE_TABLES(xt, mti) \
     const single_fn* single_table_##xt##_##mti(); const grouped_fn* grouped_table_##xt##_##mti();
-TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1) TQ_DECLARE_TABLES(0, 2)
-TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1) TQ_DECLARE_TABLES(1, 2)
-TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1) TQ_DECLARE_TABLES(2, 2)
-TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1) TQ_DECLARE_TABLES(3, 2)
+TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1)
+TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1)
+TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1)
+TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1)
 
 }  // namespace tqk

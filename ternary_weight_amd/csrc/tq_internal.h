@@ -59,6 +59,11 @@ static inline bool tq_gemv_uses_mfma(int x_type, int64_t M, const void* x)
 {
     return x_type == TQ_BF16 && M >= TQ_BF16_MFMA_MIN_M && ((uintptr_t)x & 15) == 0;
 }
+// tq_gemm_grouped_prepare with per-problem token counts (tokens may be NULL:
+// every problem has M); tq_gemm.hip.
+tq_status tq_gemm_grouped_prepare_counts(const tq_problem* problems, const int32_t* tokens, int32_t count,
+                                         int64_t M, int32_t x_type, void* workspace, size_t workspace_bytes,
+                                         tq_grouped_plan* plan, void* stream);
 // Matrix-core launch of one problem (tq_gemm.hip); the arguments are checked.
 tq_status tq_gemm_launch(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream);
 
@@ -67,6 +72,22 @@ tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_
                                 hipStream_t stream);
 tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const void* workspace,
                                  int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream);
+// Bytes of one activation element as the decode kernels read x.
+static inline int64_t tq_x_elem_bytes(int x_type)
+{
+    return x_type == TQ_BF16 ? 2 : (x_type == TQ_I8 ? 1 : 4);
+}
+// Tokens m0 .. m0 + m - 1 of a problem, as a problem of their own.
+static inline tq_prob_dev tq_prob_slice(const tq_prob_dev& P, int x_type, int m0, int m)
+{
+    tq_prob_dev Q = P;
+    Q.x = P.x ? (const uint8_t*)P.x + (int64_t)m0 * P.Kin * tq_x_elem_bytes(x_type) : nullptr;
+    Q.x_scale = P.x_scale ? P.x_scale + m0 : nullptr;
+    Q.y = P.y ? P.y + (int64_t)m0 * P.N : nullptr;
+    Q.acc = P.acc ? P.acc + (int64_t)m0 * P.N : nullptr;
+    Q.M = m;
+    return Q;
+}
 // LDS bytes of M tokens x Kin int8 activations (TQ_F32_Q8), 16-byte rounded.
 static inline size_t tq_x_lds_bytes(int64_t M, int64_t Kin) { return (size_t)((M * Kin + 15) & ~(int64_t)15); }
 // Workspace layout of a grouped plan: problem table, then the items.

@@ -45,6 +45,8 @@
 #define TQ_MAX_KIN 65536
 #define TQ_MAX_N (1 << 24)
 #define TQ_MAX_M_GEMV 16
+// Tokens the multi-token decode kernels take in one pass over the codes.
+#define TQ_PASS_TOKENS 4
 #define TQ_CB_SLOTS 32
 
 // pack status bits

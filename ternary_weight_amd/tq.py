@@ -89,6 +89,8 @@ SIGNATURES = {
                                         ctypes.POINTER(ctypes.c_size_t)], _I32),
     "tq_gemv_grouped_prepare": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32, _VP,
                                  ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
+    "tq_gemv_grouped_prepare_tokens": ([ctypes.POINTER(tq_problem), ctypes.POINTER(_I32), _I32, _I32, _VP,
+                                        ctypes.c_size_t, ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_gemv_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_gemm_grouped_workspace_size": ([ctypes.POINTER(tq_problem), _I32, _I64, _I32,
                                         ctypes.POINTER(ctypes.c_size_t)], _I32),
@@ -228,6 +230,21 @@ def gemv_grouped_prepare(probs, M, x_type, workspace, workspace_bytes, waves=0, 
     _check(lib().tq_gemv_grouped_prepare(probs, len(probs), M, x_type, _ptr(workspace),
                                          workspace_bytes, ctypes.byref(plan), _stream(stream)),
            "tq_gemv_grouped_prepare")
+    return plan
+
+
+def gemv_grouped_prepare_tokens(probs, tokens, x_type, workspace, workspace_bytes, waves=0, row_blocks=0,
+                                stream=None):
+    """Grouped decode plan where problem i has its own token count tokens[i] (0..16)."""
+    if len(tokens) != len(probs):
+        raise ValueError("one token count per problem")
+    counts = (_I32 * max(len(tokens), 1))(*[int(t) for t in tokens])
+    plan = tq_grouped_plan()
+    plan.waves = waves
+    plan.row_blocks = row_blocks
+    _check(lib().tq_gemv_grouped_prepare_tokens(probs, counts, len(probs), x_type, _ptr(workspace),
+                                                workspace_bytes, ctypes.byref(plan), _stream(stream)),
+           "tq_gemv_grouped_prepare_tokens")
     return plan
 
 

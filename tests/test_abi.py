@@ -129,6 +129,29 @@ def test_grouped_validation():
     assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
 
 
+def test_grouped_tokens_validation():
+    """Per-problem token counts: above 16, negative or a NULL list are refused
+    before any device call."""
+    d1 = tq.desc(1, 0, tq.SCALE_TENSOR, 64, 64)
+    good = 0x20000
+    probs = tq.problems([(d1, good, good, good, good, None), (d1, good, good, good, good, None)])
+    n = tq.gemv_grouped_workspace_size(probs, 16)
+    for bad, status in (([17, 1], tq.ERR_UNSUPPORTED), ([1, -1], tq.ERR_ARG)):
+        with pytest.raises(tq.TQError) as e:
+            tq.gemv_grouped_prepare_tokens(probs, bad, tq.I8, good, n, stream=0)
+        assert e.value.status == status
+    with pytest.raises(ValueError):
+        tq.gemv_grouped_prepare_tokens(probs, [1], tq.I8, good, n, stream=0)
+    plan = tq.tq_grouped_plan()
+    assert tq.lib().tq_gemv_grouped_prepare_tokens(probs, None, 2, tq.I8, good, n, ctypes.byref(plan),
+                                                   None) == tq.ERR_ARG
+    d3 = tq.desc(3, 256, tq.SCALE_GROUP_F16, 64, 256)
+    mixed = tq.problems([(d1, good, good, good, good, None), (d3, good, good, good, good, None)])
+    with pytest.raises(tq.TQError) as e:
+        tq.gemv_grouped_prepare_tokens(mixed, [1, 2], tq.I8, good, n, stream=0)
+    assert e.value.status == tq.ERR_UNSUPPORTED
+
+
 def test_gemm_rejects_unsupported_before_device_work():
     L = tq.lib()
     good = 0x30000
@@ -197,22 +220,20 @@ def test_act_quant_batch_validation():
     assert L.tq_act_quant_int8_batch(None, 0, None) == tq.OK
 
 
-def test_grouped_shape_must_fit_the_workgroup_lds():
-    # bf16 decode keeps a 64 KiB trit table in LDS; 16 split waves of a
-    # 4-plane, 16-token per-tensor problem would add 256 KiB of partial sums
-    # (x only 4-byte aligned keeps the vector-ALU kernels, which the shape hints are for)
-    d = tq.desc(4, 0, tq.SCALE_TENSOR, 64, 256)
+def test_grouped_run_rejects_forged_plans():
+    """A plan not written by prepare: a family out of range (there are two
+    token tiers, 1 and 4 tokens per pass), a shape above 16 waves, or more
+    int8 activations than the LDS copy holds."""
     good = 0x60000
-    probs = tq.problems([(d, good, good + 4, None, good, None)])
-    n = tq.gemv_grouped_workspace_size(probs, 16)
-    with pytest.raises(tq.TQError) as e:
-        tq.gemv_grouped_prepare(probs, 16, tq.BF16, good, n, waves=16, row_blocks=1, stream=0)
-    assert e.value.status == tq.ERR_UNSUPPORTED and "LDS" in str(e.value)
-    plan = tq.tq_grouped_plan(workspace=good, n_items=1, family=-1)
-    for fam_x in (tq.BF16, tq.I8):
-        plan.family = ((fam_x * 3 + 0) * 4 + 3) * 3 + 2     # x type, per-tensor, 4 planes, 16 tokens
-        plan.waves, plan.row_blocks, plan.n_problems = 16, 1, 1
-        assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_UNSUPPORTED
+    plan = tq.tq_grouped_plan(workspace=good, n_items=1, family=-1, waves=1, row_blocks=1, n_problems=1)
+    for fam in (-1, 4 * 12 * 2, 4 * 12 * 3 - 1):
+        plan.family = fam
+        assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    plan.family = ((tq.BF16 * 3 + 0) * 4 + 3) * 2 + 1      # bf16, per-tensor, 4 planes, 4 tokens
+    plan.waves, plan.row_blocks = 16, 2
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    plan.waves, plan.row_blocks, plan.x_lds_bytes = 1, 1, 65536 + 16
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
 
 
 def test_chain_workspace_size_validation():

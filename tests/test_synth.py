@@ -82,3 +82,18 @@ def test_case_recipes():
     c2 = inputs.projection(CASES["cfg2"], 3, 6, 64, 256)
     assert c2["scales"].dtype == np.float32 and c2["scales"].shape == (1,)
     assert CASES["cfg3"].layout == GROUP_F16
+
+
+def test_routing_shapes():
+    """Each token has top_k distinct experts; each expert's rows are its tokens."""
+    from synth.configs import MOES
+    moe = MOES["moe_small"]
+    for layer in range(moe.layers):
+        route = inputs.moe_routing(moe, layer)
+        assert route.shape == (moe.batch, moe.top_k)
+        assert all(len(set(r)) == moe.top_k for r in route)
+        rows = inputs.moe_expert_rows(moe, layer)
+        assert sum(len(t) for t, _ in rows) == moe.batch * moe.top_k
+        for e, (toks, pairs) in enumerate(rows):
+            for t, pr in zip(toks, pairs):
+                assert route[t][pr - t * moe.top_k] == e
