@@ -57,7 +57,9 @@ def parse():
                          "chain: the BitNet b1.58-2B layers as a dependent decode chain (tq_bitnet_chain_*)")
     ap.add_argument("--workgroups", type=int, default=0, help="chain: grid of the persistent launch (0 = default)")
     ap.add_argument("--batch", type=int, default=0, help="moe: tokens decoded together (0 = 64)")
-    ap.add_argument("--moe-int8", action="store_true", help="moe: int8 activations (quantised in the product)")
+    ap.add_argument("--moe-x", choices=["i8", "bf16", "f32"], default="i8",
+                    help="moe: activations (i8: fp32 rows quantised per token by the quantiser, or inside "
+                         "the product with --fused)")
     ap.add_argument("--M", type=int, default=1, help="tokens per step (cfg4: 1, 4 or 16)")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
@@ -194,11 +196,13 @@ class MoeStack:
     computes every (layer, expert, projection) that has tokens, each with its
     own token count.  An expert with more than 16 tokens is split into
     problems of at most 16 that share its blob.  int8 activations are
-    quantised per token inside the product (TQ_F32_Q8)."""
+    quantised per token by one tq_act_quant_int8_batch launch over every
+    layer's gathered rows (two segments: hidden and intermediate width)
+    before the product, or, with ``fused``, inside it (TQ_F32_Q8)."""
 
     MAX_TOKENS = 16
 
-    def __init__(self, moe):
+    def __init__(self, moe, fused: bool = False):
         import torch
         from ternary_weight_amd import tq
         self.moe = moe
@@ -220,17 +224,29 @@ class MoeStack:
                     tq.pack(self.descs[p], d["trits"], d["scales"], None, self.blob(layer, e, p))
                     del d
         torch.cuda.synchronize()
-        self.run_type = {BF16: BF16, F32: F32, I8: tq.F32_Q8}[moe.x_type]
+        self.fused = fused and moe.x_type == I8
+        self.run_type = {BF16: BF16, F32: F32, I8: tq.F32_Q8 if self.fused else I8}[moe.x_type]
         self.routes = [inputs.moe_expert_rows(moe, layer) for layer in range(L)]
         rows = moe.batch * moe.top_k
-        self.xh, self.xi, self.ys = [], [], []
+        # every layer's gathered rows in one matrix per width: [layers * rows][width]
+        xh = [device.moe_hidden(moe, layer).index_select(0, torch.from_numpy(
+              np.concatenate([a for a, _ in self.routes[layer]])).cuda()) for layer in range(L)]
+        xi = [device.moe_inter(moe, layer).index_select(0, torch.from_numpy(
+              np.concatenate([b for _, b in self.routes[layer]])).cuda()) for layer in range(L)]
+        self.xh_all, self.xi_all = torch.cat(xh).contiguous(), torch.cat(xi).contiguous()
+        del xh, xi
+        self.quant = moe.x_type == I8 and not self.fused
+        if self.quant:
+            self.qh = torch.empty(self.xh_all.shape, dtype=torch.int8, device="cuda")
+            self.qi = torch.empty(self.xi_all.shape, dtype=torch.int8, device="cuda")
+            self.sh = torch.empty(self.xh_all.shape[0], dtype=torch.float32, device="cuda")
+            self.si = torch.empty(self.xi_all.shape[0], dtype=torch.float32, device="cuda")
+            self._segments = [(self.xh_all.shape[0], moe.hidden, F32, self.xh_all, self.qh, self.sh),
+                              (self.xi_all.shape[0], moe.inter, F32, self.xi_all, self.qi, self.si)]
+        self.ys = []
         items, tokens, self.meta = [], [], []
         for layer in range(L):
             r = self.routes[layer]
-            tok = torch.from_numpy(np.concatenate([a for a, _ in r])).cuda()
-            pair = torch.from_numpy(np.concatenate([b for _, b in r])).cuda()
-            self.xh.append(device.moe_hidden(moe, layer).index_select(0, tok).contiguous())
-            self.xi.append(device.moe_inter(moe, layer).index_select(0, pair).contiguous())
             self.ys.append([torch.empty((rows, n), dtype=torch.float32, device="cuda") for (_, n, _) in self.shapes])
             off = 0
             for e in range(E):
@@ -238,9 +254,14 @@ class MoeStack:
                 for c in range(0, n_e, self.MAX_TOKENS):
                     m = min(self.MAX_TOKENS, n_e - c)
                     a = off + c
+                    g0 = layer * rows + a          # first row in the all-layer matrices
                     for p in range(3):
-                        x = (self.xh if p < 2 else self.xi)[layer][a:a + m]
-                        items.append((self.descs[p], self.blob(layer, e, p), x, None, self.ys[layer][p][a:a + m], None))
+                        if self.quant:
+                            x = (self.qh if p < 2 else self.qi)[g0:g0 + m]
+                            xs = (self.sh if p < 2 else self.si)[g0:g0 + m]
+                        else:
+                            x, xs = (self.xh_all if p < 2 else self.xi_all)[g0:g0 + m], None
+                        items.append((self.descs[p], self.blob(layer, e, p), x, xs, self.ys[layer][p][a:a + m], None))
                         tokens.append(m)
                         self.meta.append((layer, e, p, a, m))
                 off += n_e
@@ -261,6 +282,11 @@ class MoeStack:
         self.plan = tq.gemv_grouped_prepare_tokens(self._probs, self.tokens, self.run_type, self.ws,
                                                    self.ws.numel(), waves=waves, row_blocks=row_blocks)
 
+    def quantize(self):
+        from ternary_weight_amd import tq
+        if self.quant:
+            tq.act_quant_int8_batch(self._segments)
+
     def gemv(self):
         from ternary_weight_amd import tq
         tq.gemv_grouped_run(self.plan)
@@ -279,8 +305,17 @@ class MoeStack:
             w += K * n * kin // 4
             w += 2 * K * n * (kin // moe.group) if moe.layout == GROUP_F16 else 4 * K
         pairs = moe.layers * moe.batch * moe.top_k
+        if self.quant:
+            xsz = 1
         return (self.active_experts() * w + pairs * (moe.hidden + moe.inter) * xsz
-                + pairs * 4 * (2 * moe.inter + moe.hidden))
+                + (pairs * 8 if self.quant else 0) + pairs * 4 * (2 * moe.inter + moe.hidden))
+
+    def quant_bytes(self) -> int:
+        """The quantiser's bytes: fp32 rows in, int8 rows and a scale per row out."""
+        if not self.quant:
+            return 0
+        pairs = self.moe.layers * self.moe.batch * self.moe.top_k
+        return pairs * (self.moe.hidden + self.moe.inter) * 5 + 8 * pairs
 
 
 def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
@@ -288,7 +323,8 @@ def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
     if plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
         ks = 32 if layout == TENSOR or group % 32 == 0 else 16
         return "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (run_type, layout, planes, ks)
-    return "k_gemv_grouped<%d, %d, %d, %d>" % (run_type, layout, planes, 1 if plan.M <= 1 else 4)
+    mt = 1 if plan.M <= 1 else (8 if run_type == 3 and plan.M > 4 else 4)   # 3: TQ_F32_Q8
+    return "k_gemv_grouped<%d, %d, %d, %d>" % (run_type, layout, planes, mt)
 
 
 # ---------------------------------------------------------------------------
@@ -463,8 +499,17 @@ _FAMILY_SOURCES = {
 }
 
 
+def _code_only(text: bytes) -> bytes:
+    """Source text without comments and blank space (edits of comments keep a fingerprint)."""
+    import re
+    t = text.decode("utf-8", "replace")
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split()).encode()
+
+
 def kernel_fingerprint(kernel: str) -> str:
-    """Hash of the sources of the kernel's family (and the header of the ABI)."""
+    """Hash of the code of the kernel's family (and the header of the ABI), comments excluded."""
     fam = next((k for k in _FAMILY_SOURCES if kernel.startswith(k)), None)
     files = _COMMON_SOURCES + (_FAMILY_SOURCES[fam] if fam else [])
     prefix = {"k_gemv": "tq_gemv_", "k_gemm": "tq_gemm_"}.get(fam)
@@ -473,8 +518,8 @@ def kernel_fingerprint(kernel: str) -> str:
     h = hashlib.sha256()
     for f in sorted(set(files)):
         h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "tq.h"), "rb").read())
+        h.update(_code_only(open(os.path.join(CSRC, f), "rb").read()))
+    h.update(_code_only(open(os.path.join(ROOT, "include", "tq.h"), "rb").read()))
     return h.hexdigest()[:16]
 
 
@@ -927,10 +972,11 @@ def main_moe(args):
     moe = MOES["moe"]
     if args.batch:
         moe = dataclasses.replace(moe, batch=args.batch)
-    if args.moe_int8:
-        moe = dataclasses.replace(moe, x_type=I8)
+    moe = dataclasses.replace(moe, x_type={"i8": I8, "bf16": BF16, "f32": F32}[args.moe_x])
+    if moe.x_type != I8:
+        moe = dataclasses.replace(moe, name=moe.name.replace("int8 x (per-token absmax)", args.moe_x + " x"))
     t_build = time.perf_counter()
-    stack = MoeStack(moe)
+    stack = MoeStack(moe, fused=args.fused)
     stack.prepare(args.waves, args.row_blocks)
     print("built moe: %d layers x %d experts, %.1f GB packed, %d problems (%d routed experts), "
           "plan %d items x %d blocks x %d waves (%.1f s)"
@@ -940,20 +986,33 @@ def main_moe(args):
     stream = torch.cuda.current_stream()
     spin_up(args.spin_up_ms)
     for _ in range(args.warmup):
+        stack.quantize()
         stack.gemv()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
+        stack.quantize()
         stack.gemv()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
+    gemv_avg = ms_step
+    if stack.quant:    # the product kernel alone, back to back between one pair of events
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            stack.gemv()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gemv_avg = g0.elapsed_time(g1) / args.steps
     gbytes = stack.gemv_bytes()
-    value = gbytes / (ms_step / 1e3) / 1e9
+    value = (gbytes + stack.quant_bytes()) / (ms_step / 1e3) / 1e9
+    achieved = gbytes / (gemv_avg / 1e3) / 1e9
     kernel_name = decode_kernel_name(stack.plan, stack.run_type, moe.layout, moe.planes, moe.group)
+    ceiling = hbm_ceiling() if args.ceiling else None
     check = None if args.no_check else moe_spot_check(stack)
     cpu = None if args.no_cpu_baseline else moe_cpu_baseline(stack, args.cpu_seconds)
     out = {
@@ -980,25 +1039,28 @@ def main_moe(args):
             "max_tokens_per_problem": stack.max_tokens,
             "planes": moe.planes,
             "group": moe.group,
-            "step": "one grouped launch over every routed (layer, expert, projection) of the batch, each "
+            "step": ("act-quant of every layer's gathered rows (one launch) + " if stack.quant else "") +
+                    "one grouped launch over every routed (layer, expert, projection) of the batch, each "
                     "with its own token count" + ("; fp32 inputs quantised per token to int8 inside it"
-                                                  if moe.x_type == I8 else ""),
+                                                  if stack.fused else ""),
             "packed_weight_bytes": stack.blob_bytes,
             "grouped_waves": stack.plan.waves,
             "grouped_row_blocks": stack.plan.row_blocks,
         },
         "tok_per_s_equiv": round(moe.batch * 1e3 / ms_step, 1),
+        "gemv_us": round(gemv_avg * 1e3, 2),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(value, 1),
+            "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(kernel_name),
             "kernel": kernel_name,
             "bytes_per_launch": gbytes,
         },
         "cpu_baseline": cpu,
+        "hbm_ceiling": ceiling,
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }
@@ -1048,6 +1110,7 @@ def main_ternarize(args):
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
+    ceiling = hbm_ceiling() if args.ceiling else None
     weights = sum(n * kin for (_, n, kin) in shapes)
     # algorithmic bytes: the dense weight read once, the trits written once (int8), the scales
     scale_b = sum(n * (kin // g) * (1 if codec else 2 * K) for (_, n, kin) in shapes)
@@ -1074,8 +1137,10 @@ def main_ternarize(args):
                    "weights": weights},
         "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("k_tern_codec" if codec else "k_tern_group"),
-                     "kernel": "k_tern_codec" if codec else "k_tern_group", "bytes_per_launch": nbytes},
+                     "traffic": None,
+                     "kernel": "k_tern_codec" if codec else "k_tern_group_lds", "bytes_per_step": nbytes,
+                     "launches_per_step": len(jobs)},
+        "hbm_ceiling": ceiling,
         "parity_spot_check": check,
     }
     print(json.dumps(out))

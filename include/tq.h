@@ -243,9 +243,10 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * with one workgroup per item, an item being `row_blocks` consecutive 64-row
  * blocks of one problem, each split over `waves` waves; items are ordered
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
- * (0 = default: 4 waves, 1 block; with TQ_F32_Q8 1 wave, 4 blocks, so that
- * a workgroup quantises its activations once for four blocks; with TQ_BF16
- * 1 wave, 16 blocks, so that 16 blocks share the workgroup's trit table).  The
+ * (0 = default: 4 waves, 1 block; with TQ_F32_Q8, or TQ_I8 and M > 1, 1 wave,
+ * 4 blocks, so that a workgroup quantises its activations once for four
+ * blocks; with TQ_BF16 1 wave, 16 blocks, so that 16 blocks share the
+ * workgroup's trit table).  The
  * decode kernels take up to 4 tokens per pass over the codes: with M > 4 each
  * problem is cut into slices of 4 tokens whose workgroups are placed to run
  * on one XCD together, so that the later slices read the codes from its L2.
@@ -262,11 +263,12 @@ tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int
  * layer: every expert's matrix is fit on its own (sasori page, "How it works
  * & paper"), so each expert is one problem with its own blob, and the tokens
  * the router sent to it are gathered into its x.  A problem with no tokens
- * takes no workgroup (its pointers may then be NULL).  With TQ_BF16, a
- * largest count above 4 and every x 16-byte aligned the plan is a
- * matrix-core plan whose tiles cover each problem's own count; otherwise the
- * vector-ALU kernels take up to 4 tokens per pass and a problem with more is
- * cut into slices of 4 (as in tq_gemv_grouped_prepare).  The workspace is
+ * takes no workgroup (its pointers may then be NULL).  With TQ_BF16, a mean
+ * count of at least 8 over the problems that have tokens, every x 16-byte
+ * aligned and no shape hint in `plan`, the plan is a matrix-core plan whose
+ * tiles cover each problem's own count; otherwise the vector-ALU kernels take
+ * up to 4 tokens per pass and a problem with more is cut into slices of 4 (as
+ * in tq_gemv_grouped_prepare).  The workspace is
  * tq_gemv_grouped_workspace_size's with M = the largest count.  More than 16 tokens for one expert: split them over
  * several problems that share the blob.  Errors as tq_gemv_grouped_prepare,
  * plus TQ_ERR_ARG for a NULL `tokens` with count > 0 or a negative count and

@@ -169,7 +169,8 @@ class Moe:
 
 MOES = {
     "moe": Moe(9, "Qwen3-30B-A3B-shaped MoE experts, 48 layers x 128 experts (8 routed per token), "
-                  "K=3, g=256, f16 group scales, bf16 x", 48, 2048, 768, 128, 8, 3, 256, GROUP_F16, BF16, 64),
+                  "K=3, g=256, f16 group scales, int8 x (per-token absmax)", 48, 2048, 768, 128, 8, 3, 256,
+               GROUP_F16, I8, 64),
     "moe_small": Moe(10, "MoE experts at small sizes, 2 layers x 16 experts (4 routed per token)",
                      2, 512, 256, 16, 4, 3, 128, GROUP_F16, BF16, 12),
 }

@@ -132,9 +132,9 @@ TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, i
 namespace {
 
 // The decode plan; tokens (host, may be NULL): each problem's own token
-// count, every one at most M.  The kernels take TQ_PASS_TOKENS tokens per
-// pass over the codes; a problem with more is cut into slices of that many
-// tokens, each an entry of the device table.  Workgroups are dealt to the 8
+// count, every one at most M.  The kernels take tq_pass_tokens(x_type)
+// tokens per pass over the codes; a problem with more is cut into slices of
+// that many tokens, each an entry of the device table.  Workgroups are dealt to the 8
 // XCDs in turn, so the slices of one row block are placed 8 items apart:
 // they run on one XCD at about the same time and share the codes through
 // its L2 (holes left by this placement are items of entry -1).
@@ -148,24 +148,36 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     int waves = plan->waves, row_blocks = plan->row_blocks;
     const bool hinted = is_shape(waves) && is_shape(row_blocks) && waves * row_blocks <= 16;
     if (!hinted) {
-        // bf16: the trit table fills 64 KiB of LDS, so 16 one-wave row blocks share it
-        waves = (x_type == TQ_F32_Q8 || x_type == TQ_BF16) ? 1 : 4;
-        row_blocks = x_type == TQ_F32_Q8 ? 4 : (x_type == TQ_BF16 ? 16 : 1);
+        // bf16: the trit table fills 64 KiB of LDS, so 16 one-wave row blocks
+        // share it; int8 over several tokens: one wave per row block as well
+        // (measured ahead of 4 waves splitting the columns)
+        const bool one_wave = x_type == TQ_F32_Q8 || x_type == TQ_BF16 || (x_type == TQ_I8 && M > 1);
+        waves = one_wave ? 1 : 4;
+        row_blocks = x_type == TQ_BF16 ? 16 : (one_wave ? 4 : 1);
     }
     size_t need = 0;
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
     if (s) return s;
-    // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte loads
-    const int64_t mfma_min = tokens ? TQ_PASS_TOKENS + 1 : TQ_BF16_MFMA_MIN_M;
-    bool mfma = count > 0;
-    for (int32_t i = 0; i < count; ++i)
-        mfma = mfma && x_type == TQ_BF16 && M >= mfma_min && ((uintptr_t)problems[i].x & 15) == 0;
+    // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte
+    // loads.  With per-problem counts the measure is the mean count of the
+    // problems that have tokens (a 16-token tile costs the same for 1 or 16;
+    // the vector ALUs pay per token), and a shape hint keeps the vector ALUs.
+    int64_t busy = 0, sum = 0;
+    for (int32_t i = 0; tokens && i < count; ++i) {
+        busy += tokens[i] > 0;
+        sum += std::max(tokens[i], 0);
+    }
+    bool mfma = count > 0 && x_type == TQ_BF16 &&
+                (tokens ? !hinted && sum >= TQ_BF16_MFMA_MIN_M * std::max<int64_t>(busy, 1)
+                        : M >= TQ_BF16_MFMA_MIN_M);
+    for (int32_t i = 0; i < count; ++i) mfma = mfma && ((uintptr_t)problems[i].x & 15) == 0;
     if (mfma)
         return tq_gemm_grouped_prepare_counts(problems, tokens, count, M, x_type, workspace, workspace_bytes, plan,
                                               stream);
     if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
     if (workspace_bytes < need)
         return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    const int pass = tq_pass_tokens(x_type);
     std::vector<tq_prob_dev> probs;
     probs.reserve((size_t)count);
     struct Unit { int64_t cost; int32_t entry, n, rb0; };   // row blocks of one problem, all its slices
@@ -192,19 +204,24 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
         }
         const tq_prob_dev whole = tq_make_prob(L, pr.blob, Mi, pr.x, pr.x_scale, pr.y, pr.acc);
         first[(size_t)i] = (int32_t)probs.size();
-        if (Mi <= TQ_PASS_TOKENS) {
+        if (Mi <= pass) {
             probs.push_back(whole);
         } else {
-            for (int m0 = 0; m0 < (int)Mi; m0 += TQ_PASS_TOKENS)
-                probs.push_back(tq_prob_slice(whole, x_type, m0, std::min<int>(TQ_PASS_TOKENS, (int)Mi - m0)));
+            for (int m0 = 0; m0 < (int)Mi; m0 += pass)
+                probs.push_back(tq_prob_slice(whole, x_type, m0, std::min<int>(pass, (int)Mi - m0)));
         }
         n_slices[(size_t)i] = (int32_t)probs.size() - first[(size_t)i];
-        if (x_type == TQ_F32_Q8)
-            x_lds = std::max(x_lds, tq_x_lds_bytes(std::min<int64_t>(Mi, TQ_PASS_TOKENS), L.Kin));
+        if (x_type == TQ_F32_Q8) x_lds = std::max(x_lds, tq_x_lds_bytes(std::min<int64_t>(Mi, pass), L.Kin));
     }
     bool sliced = false;
     if (count > 0 && M > 0) {
-        family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, TQ_PASS_TOKENS));
+        family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, pass));
+        if (std::min<int64_t>(M, pass) > TQ_PASS_TOKENS && waves * row_blocks > 8) {
+            // the 8-token kernels take at most 8 waves per workgroup
+            if (hinted) return tq_fail(TQ_ERR_UNSUPPORTED, "plan shape %d x %d: more than 8 tokens per pass "
+                                       "take at most 8 waves per workgroup", waves, row_blocks);
+            while (waves * row_blocks > 8) (waves > 1 ? waves : row_blocks) /= 2;
+        }
         // a shape whose partial sums overflow the workgroup's LDS: the default
         // one gives up the column split first, a requested one is refused
         auto lds = [&](int w, int rbs) { return tq_gemv_lds_bytes(family, w, w * rbs, x_lds); };

@@ -25,11 +25,12 @@ from tests.gpu_util import TOL, dev, host, pack, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _run(moe, waves=0, row_blocks=0):
+def _run(moe, waves=0, row_blocks=0, fused=False):
     import bench
     import torch
-    st = bench.MoeStack(moe)
+    st = bench.MoeStack(moe, fused=fused)
     st.prepare(waves, row_blocks)
+    st.quantize()
     st.gemv()
     torch.cuda.synchronize()
     return st
@@ -54,16 +55,18 @@ def _check_all(st):
 def test_moe_small_every_output():
     """Small MoE (2 layers x 16 experts, top-4, 12 tokens, K=3, g=128, bf16 x)."""
     st = _run(MOES["moe_small"])
-    assert 4 < st.max_tokens <= 16 and st.plan.family >= 1000     # the matrix-core plan
+    assert 4 < st.max_tokens <= 16 and st.plan.family < 1000     # ~3 tokens each: vector ALUs, slices of 4
     assert len({m for (*_, m) in st.meta}) > 1          # mixed token counts in one launch
     _check_all(st)
     _free(st)
 
 
 def test_moe_small_split_experts():
-    """80 tokens, top-4 of 16: experts hold ~20 tokens and are split into problems of 16."""
+    """80 tokens, top-4 of 16: experts hold ~20 tokens and are split into
+    problems of 16; a mean count of ~10 puts the plan on the matrix cores."""
     moe = dataclasses.replace(MOES["moe_small"], batch=80)
     st = _run(moe)
+    assert st.plan.family >= 1000
     counts = {}
     for (layer, e, p, a, m) in st.meta:
         counts[(layer, e, p)] = counts.get((layer, e, p), 0) + 1
@@ -81,11 +84,13 @@ def test_moe_small_one_token():
     _free(st)
 
 
-@pytest.mark.parametrize("x_type", [F32, I8])
-def test_moe_small_other_activations(x_type):
-    """fp32 x, and fp32 x quantised per token to int8 inside the product."""
+@pytest.mark.parametrize("x_type,fused", [(F32, False), (I8, False), (I8, True)])
+def test_moe_small_other_activations(x_type, fused):
+    """fp32 x; int8 x from the quantiser; fp32 x quantised per token to int8
+    inside the product."""
     moe = dataclasses.replace(MOES["moe_small"], x_type=x_type)
-    st = _run(moe)
+    st = _run(moe, fused=fused)
+    assert st.quant == (x_type == I8 and not fused)
     _check_all(st)
     _free(st)
 
@@ -99,17 +104,18 @@ def test_moe_small_plan_shapes(shape):
     _free(st)
 
 
+@pytest.mark.parametrize("counts", [(3, 0, 1, 16, 5), (9, 0, 16, 8, 12)])
 @pytest.mark.parametrize("x_type", [BF16, F32])
-def test_tokens_zero_and_mixed(x_type):
-    """Problems with 0, 1, 3, 5 and 16 tokens in one plan (the 0-token one has
-    NULL pointers and takes no workgroup); f16 group and per-tensor scales.
-    bf16 runs on the matrix cores, fp32 on the vector ALUs in slices of 4."""
+def test_tokens_zero_and_mixed(x_type, counts):
+    """Problems with mixed token counts in one plan, one of them 0 (NULL
+    pointers, no workgroup); f16 group and per-tensor scales.  A mean count
+    below 8 keeps bf16 on the vector ALUs (slices of 4), 8 or more moves it
+    to the matrix cores."""
     import torch
     from ternary_weight_amd import tq
     rng = np.random.default_rng(5)
     for layout, g in ((GROUP_F16, 64), (0, 0)):
         K, N, Kin = 2, 200, 320
-        counts = [3, 0, 1, 16, 5]
         items, refs, outs, tokens = [], [], [], []
         keep = []
         for i, m in enumerate(counts):
@@ -135,7 +141,8 @@ def test_tokens_zero_and_mixed(x_type):
         probs = tq.problems(items)
         ws = torch.empty(tq.gemv_grouped_workspace_size(probs, 16), dtype=torch.uint8, device="cuda")
         plan = tq.gemv_grouped_prepare_tokens(probs, tokens, x_type, ws, ws.numel())
-        assert (plan.family >= 1000) == (x_type == BF16) and plan.M == 16
+        mfma = x_type == BF16 and sum(counts) >= 8 * sum(c > 0 for c in counts)
+        assert (plan.family >= 1000) == mfma and plan.M == 16
         tq.gemv_grouped_run(plan)
         torch.cuda.synchronize()
         for y, ref in zip(outs, refs):
