@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--secondary", action="store_true",
+                    help="decode and prefill stacks: add secondary timings after the timed region (single passes "
+                         "of the product, cold after a 1 GiB evicting read and warm, the quantiser alone, the "
+                         "projections as single launches in a HIP graph, the one-thread oracle)")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time a plain HBM read (torch sum) and copy of 2 GiB as a practical ceiling")
     return ap.parse_args()
@@ -582,6 +586,16 @@ def summarize(args) -> None:
                   "(factor %.4f)." % (args.read_bytes, read_kib[0], fetch_factor, args.fill_bytes, fill_kib[0], write_factor),
                   "", "Kernel `%s` per launch (%d launches): FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB -> HBM traffic "
                   "%.0f bytes." % (kern, gf[1], gf[0], gw[0], traffic)]
+    for d in args.counters_dir or []:
+        tab = _pmc_means(d)
+        rows = sorted((c, v) for (k, c), v in tab.items() if kern in k)
+        if rows:
+            lines += ["", "Counters per launch of `%s` (mean over %d launches), from `%s`:" % (kern, rows[0][1][1],
+                                                                                            args.counters_cmd or d),
+                      "", "| counter | value |", "|---|---|"]
+            for c, (v, _) in rows:
+                lines.append("| %s | %.6g |" % (c, v))
+                rec.setdefault("counters", {})[c] = v
     lines += ["", "```json", json.dumps(rec), "```", ""]
     open(args.out, "w").write("\n".join(lines))
     print("wrote", args.out)
@@ -601,6 +615,109 @@ def measured_traffic(kernel: str):
 
 
 # ---------------------------------------------------------------------------
+# Secondary timings of a decode stack (reported beside the bench line).
+# ---------------------------------------------------------------------------
+def single_passes(run, reps: int = 20, evict_bytes: int = 0) -> dict:
+    """`run` timed alone (events around it) `reps` times: median, min and max
+    in microseconds.  With `evict_bytes`, each pass follows an untimed read
+    of that many other bytes (more than the 256 MiB MALL; a read, so that no
+    dirty lines are written back during the pass), so that no code comes
+    from a cache."""
+    import torch
+    scratch = torch.ones(max(evict_bytes, 16), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        if evict_bytes:
+            device.stream_read(scratch, sink, 8192)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    times.sort()
+    return {"median_us": round(times[len(times) // 2], 2), "min_us": round(times[0], 2),
+            "max_us": round(times[-1], 2), "reps": reps, "evict_bytes": evict_bytes}
+
+
+def timed_us(run, reps: int = 50) -> float:
+    """Average of `run` back to back between one pair of events (microseconds)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def graph_of_single_launches(stack, replays: int = 20) -> dict:
+    """Every projection of the stack as its own tq_gemv launch, captured in
+    one HIP graph and replayed: the per-launch alternative to the grouped
+    launch (same inputs and outputs)."""
+    import torch
+    from ternary_weight_amd import tq
+    calls = []
+    for i, (layer, p, _, n, kin) in enumerate(stack.projs):
+        w, j = stack.slot[i]
+        M = stack.M
+        if stack.x_q is not None:
+            x, xs = stack.x_q[w][j * M:(j + 1) * M], stack.x_s[w][j * M:(j + 1) * M]
+        else:
+            x, xs = stack.x_raw[w][j * M:(j + 1) * M], None
+        calls.append((stack.descs[i], stack.blobs[i], M, stack.run_type, x, xs, stack.ys[i]))
+
+    def run_all():
+        for (d, blob, M, xt, x, xs, y) in calls:
+            tq.gemv(d, blob, M, xt, x, xs, y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()                                   # warm: the first calls query the device
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    us = timed_us(g.replay, replays)
+    eager = timed_us(run_all, replays)
+    return {"launches": len(calls), "graph_replay_us": round(us, 2), "eager_launches_us": round(eager, 2)}
+
+
+def cpu_one_thread(stack, seconds: float = 2.0) -> dict:
+    """The oracle on one host thread over the first projection of the stack."""
+    import oracle
+    case, M = stack.case, stack.M
+    orc = oracle.default()
+    layer, p, name, n, kin = stack.projs[0]
+    h = inputs.projection(case, layer, p, n, kin, M=M)
+    K, g, layout = case.planes, case.group, case.layout
+    xsz = {I8: 1, BF16: 2, F32: 4}[case.x_type]
+    b = K * n * kin // 4 + M * kin * xsz + 4 * M * n
+    done, t0 = 0, time.perf_counter()
+    while True:
+        if case.x_type == I8:
+            q, sx = orc.act_quant_i8(h["x"], F32)
+            orc.gemv_i8(K, g, layout, h["trits"], h["scales"], q, sx, h["codebook"], nthreads=1)
+        else:
+            orc.gemv_fp(K, g, layout, h["trits"], h["scales"], h["x"], case.x_type, h["codebook"], nthreads=1)
+        done += b
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "projection %s of layer 0 (%d x %d), %.1f s" % (name, n, kin, el)}
+
+
+# ---------------------------------------------------------------------------
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "summarize":
         ap = argparse.ArgumentParser(description="write a profiles/ summary from rocprofv3 output")
@@ -614,6 +731,8 @@ def main():
         ap.add_argument("--fetch-dir")
         ap.add_argument("--write-dir")
         ap.add_argument("--pmc-cmd", default="")
+        ap.add_argument("--counters-dir", action="append", help="rocprofv3 --pmc output of other counters")
+        ap.add_argument("--counters-cmd", default="")
         ap.add_argument("--read-bytes", type=int, default=4 << 30)
         ap.add_argument("--fill-bytes", type=int, default=4 << 30)
         summarize(ap.parse_args())
@@ -694,6 +813,20 @@ def main():
     ceiling = hbm_ceiling() if args.ceiling else None
     check = None if args.no_check else spot_check(stack)
     cpu = None if args.no_cpu_baseline else cpu_baseline(stack, args.cpu_seconds)
+    secondary = None
+    if args.secondary:
+        cold = single_passes(stack.gemv, evict_bytes=1 << 30)
+        warm = single_passes(stack.gemv)
+        for t in (cold, warm):
+            t["frac_of_hbm_peak"] = (None if stack.prefill else
+                                     round(gbytes / (t["median_us"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4))
+        secondary = {"cold_product": cold, "single_pass_product": warm}
+        if stack.x_q is not None:
+            secondary["act_quant_us"] = round(timed_us(stack.quantize), 2)
+        if not stack.prefill:
+            secondary["single_launches"] = graph_of_single_launches(stack)
+        if not args.no_cpu_baseline:
+            secondary["cpu_one_thread"] = cpu_one_thread(stack)
 
     out = {
         "metric": METRIC_PREFILL if stack.prefill else METRIC,
@@ -743,6 +876,7 @@ def main():
         "cpu_baseline": cpu,
         "hbm_ceiling": ceiling,
         "parity_spot_check": check,
+        "secondary": secondary,
         "wall_s_timed": round(wall, 3),
     }
     print(json.dumps(out))

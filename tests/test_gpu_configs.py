@@ -6,8 +6,9 @@ Each stack is generated on the GPU by the device copy of the seeded
 generator; the oracle regenerates the sampled rows (and their activations)
 on the host from the same counters, so no input crosses from the GPU side.
 Samples: the first and last projection of the stack and one in between,
-64 random rows each for every token; for the prefill stacks also every row
-of one projection for 16 random tokens.  Bars: bit-exact for int8
+64 random rows each for every token; for the one-token decode stacks also
+every projection of every layer, 8 random rows each; for the prefill stacks
+also every row of one projection for 16 random tokens.  Bars: bit-exact for int8
 activations with one plane and a per-tensor scale, else the per-token
 relative error 1e-3.
 """
@@ -73,6 +74,24 @@ def _check_rows(st, seed, rows=64):
             assert err <= TOL, (name, layer, err)
 
 
+def _check_every_projection(st, seed, rows=8):
+    """Every projection of every layer: `rows` random rows for every token."""
+    case, M = st.case, st.M
+    rng = np.random.default_rng(seed)
+    exact = case.x_type == I8 and case.layout == TENSOR and case.planes == 1
+    ys = [y.detach().cpu().numpy() for y in st.ys]
+    for i, (layer, p, name, n, kin) in enumerate(st.projs):
+        r = np.sort(rng.choice(n, size=min(rows, n), replace=False))
+        h = inputs.projection(case, layer, p, n, kin, rows=r, M=M)
+        ref = _reference(case, h, case.x_type)
+        y = ys[i][:, r]
+        if exact:
+            assert np.array_equal(y.view(np.uint32), ref["y32"].view(np.uint32)), (name, layer)
+        else:
+            err = rel_err(y, ref["y64"] if case.x_type == I8 else ref)
+            assert err <= TOL, (name, layer, err)
+
+
 def test_tiny_linear_full():
     """256 x 512, one plane, f16 scale per group of 64, fp32 x: every output."""
     from ternary_weight_amd import tq
@@ -95,6 +114,7 @@ def test_tiny_linear_full():
 def test_bitnet_decode_stack():
     st = _stack("cfg2")
     _check_rows(st, 2)
+    _check_every_projection(st, 12)
     # the fused launch (quantisation inside the product) gives the same bits
     import torch
     ys = [y.clone() for y in st.ys]
@@ -108,6 +128,7 @@ def test_bitnet_decode_stack():
 def test_llama_shaped_k3_decode_stack():
     st = _stack("cfg3")
     _check_rows(st, 3)
+    _check_every_projection(st, 13)
     _free(st)
 
 
@@ -115,6 +136,8 @@ def test_llama_shaped_k3_decode_stack():
 def test_codec_d3_decode_stack(M):
     st = _stack("cfg4", M=M)
     _check_rows(st, 40 + M)
+    if M == 1:
+        _check_every_projection(st, 14)
     _free(st)
 
 
