@@ -330,6 +330,54 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
             assert rel_err(host(y), r) <= TOL
 
 
+@pytest.mark.parametrize("M", [5, 9, 16])
+@pytest.mark.parametrize("x_type,shape", [(F32, (0, 0)), (F32, (2, 2)), (I8, (0, 0)), (I8, (4, 1)),
+                                          (F32_Q8, (0, 0)), (F32_Q8, (2, 4)), (BF16, (1, 16))])
+def test_grouped_token_slices(x_type, shape, M):
+    """More tokens than a pass takes (4; 8 for TQ_F32_Q8): each problem is cut
+    into slices placed 8 items apart, with holes in the item list.  bf16 at
+    M = 5 stays on the vector ALUs (the matrix cores take M >= 8)."""
+    from ternary_weight_amd import tq
+    t = torch()
+    K, g, layout = 2, 64, GROUP_F16
+    shapes = [(640, 512), (64, 256), (130, 768), (200, 1024), (96, 64)]
+    keep, items, refs, ys = [], [], [], []
+    for i, (N, Kin) in enumerate(shapes):
+        trits, scales, cb = rand_problem(K, g, layout, N, Kin)
+        d, blob = pack(K, g, layout, trits, scales, cb)
+        if x_type in (I8, F32_Q8):
+            xf = rand_x(M, Kin, F32)
+            q, s = oracle.act_quant_i8(xf)
+            xd, sd = (dev(q), dev(s)) if x_type == I8 else (dev(xf), None)
+            refs.append(oracle.gemv_i8(K, g, layout, trits, scales, q, s, cb)["y64"])
+        else:
+            x = rand_x(M, Kin, x_type)
+            xd, sd = dev(x), None
+            refs.append(oracle.gemv_fp(K, g, layout, trits, scales, x, x_type, cb))
+        y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda")
+        keep += [d, blob, xd, sd]
+        ys.append(y)
+        items.append((d, blob, xd, sd, y, None))
+    probs = tq.problems(items)
+    nbytes = tq.gemv_grouped_workspace_size(probs, M)
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    waves, row_blocks = shape
+    plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
+    if plan.family >= 1000:
+        assert x_type == BF16 and M >= 8
+    else:
+        pass_tokens = 8 if x_type == F32_Q8 else 4
+        slices = (M + pass_tokens - 1) // pass_tokens
+        assert plan.n_problems == len(shapes) * slices
+        R = plan.row_blocks
+        busy = sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes) * slices
+        assert busy <= plan.n_items <= busy + 8 * (slices + 1)
+    tq.gemv_grouped_run(plan)
+    t.cuda.synchronize()
+    for y, r in zip(ys, refs):
+        assert rel_err(host(y), r) <= TOL
+
+
 @pytest.mark.parametrize("N,Kin,M", [(2560, 2560, 1), (640, 2560, 1), (2560, 6912, 1), (130, 80, 3),
                                      (64, 4096, 16), (200, 65536, 1), (64, 16, 1)])
 def test_fused_quantisation_is_bit_identical(N, Kin, M):
