@@ -228,7 +228,9 @@ typedef struct tq_grouped_plan {
                                      per workgroup (waves * row_blocks <= 16)   */
     int32_t n_problems;
     int32_t x_lds_bytes;          /* LDS for in-kernel quantised activations   */
-    int32_t reserved;
+    int32_t mode;                 /* 0: an item per workgroup; 1: an item per
+                                     wave, the token slices of one row block in
+                                     one workgroup (set by prepare, bf16)      */
 } tq_grouped_plan;
 
 /* Device workspace bytes that tq_gemv_grouped_prepare needs for these problems. */
@@ -247,10 +249,13 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * 4 blocks, so that a workgroup quantises its activations once for four
  * blocks; with TQ_BF16 1 wave, 16 blocks, so that 16 blocks share the
  * workgroup's trit table).  The
- * decode kernels take up to 4 tokens per pass over the codes: with M > 4 each
- * problem is cut into slices of 4 tokens whose workgroups are placed to run
- * on one XCD together, so that the later slices read the codes from its L2.
- * Copies host->device on `stream` and synchronizes it.
+ * decode kernels take up to 4 tokens per pass over the codes (8 with
+ * TQ_F32_Q8): with more, each problem is cut into slices of that many tokens.
+ * With TQ_BF16 (per-tensor or f16 group scales) and no shape hint an item is
+ * then one 64-row block of one slice per wave, the slices of a row block in
+ * one workgroup of 16 waves; otherwise the slices' workgroups are placed to
+ * run on one XCD together.  Copies host->device on `stream` and synchronizes
+ * it.
  */
 tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int64_t M,
                                   int32_t x_type, void* workspace, size_t workspace_bytes,

@@ -119,10 +119,11 @@ TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, i
         items += L.NB;
     }
     // a problem of more than one pass of tokens is cut into slices, each an
-    // entry of the table with its own items; their placement leaves fewer
-    // than 8 (slices + 1) holes in the item list
+    // entry of the table with its own items, placed with holes between
     const int64_t slices = pass_slices(M);
-    items = items * slices + (slices > 1 ? 8 * (slices + 1) : 0);
+    // with per-wave items a row block's slices never straddle workgroups,
+    // which leaves fewer holes than items, plus the last workgroup's
+    if (slices > 1) items = 2 * items * slices + 8 * (slices + 1) + 16;
     // problem entries, then one (entry, first row block) item per workgroup
     *bytes = (size_t)(tq_ws_items_off(count * slices) + tq_align256(items * 8));
     if (*bytes == 0) *bytes = 256;
@@ -214,6 +215,12 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
         if (x_type == TQ_F32_Q8) x_lds = std::max(x_lds, tq_x_lds_bytes(std::min<int64_t>(Mi, pass), L.Kin));
     }
     bool sliced = false;
+    for (int32_t i = 0; i < count; ++i) sliced = sliced || n_slices[(size_t)i] > 1;
+    // bf16: per-wave items, the slices of a row block in one workgroup whose
+    // 16 waves share the trit table (measured ahead of workgroup items of 16
+    // row blocks; with int8 activations the two measured alike)
+    const bool wave_mode = sliced && !hinted && x_type == TQ_BF16 && layout0 != TQ_SCALE_CODEBOOK;
+    const int wave_wg = 16;
     if (count > 0 && M > 0) {
         family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, pass));
         if (std::min<int64_t>(M, pass) > TQ_PASS_TOKENS && waves * row_blocks > 8) {
@@ -233,21 +240,31 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
             if (lds(waves, row_blocks) > TQ_MAX_WG_LDS)
                 return tq_fail(TQ_ERR_UNSUPPORTED, "decode needs more LDS than a workgroup has");
         }
+        const int unit_blocks = wave_mode ? 1 : row_blocks;
         for (int32_t i = 0; i < count; ++i) {
             const tq_prob_dev& P = probs[(size_t)first[(size_t)i]];
             if (P.M == 0) continue;          // a problem with no tokens has no work
             const int64_t NB = (P.N + 63) / 64;
-            for (int64_t rb = 0; rb < NB; rb += row_blocks) {
-                const int64_t nb = std::min<int64_t>(row_blocks, NB - rb);
+            for (int64_t rb = 0; rb < NB; rb += unit_blocks) {
+                const int64_t nb = std::min<int64_t>(unit_blocks, NB - rb);
                 units.push_back({nb * P.NC * (int64_t)K0, first[(size_t)i], n_slices[(size_t)i], (int32_t)rb});
-                sliced = sliced || n_slices[(size_t)i] > 1;
             }
         }
     }
     // longest units first, so that the last workgroups to start are short
     std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
     std::vector<int2> items;
-    if (!sliced) {
+    if (wave_mode) {
+        // a row block's slices (at most 4) in consecutive waves of one workgroup
+        for (const Unit& u : units) {
+            const int free = wave_wg - (int)(items.size() % wave_wg);
+            if (u.n > free) items.resize(items.size() + free, make_int2(-1, 0));
+            for (int j = 0; j < u.n; ++j) items.push_back(make_int2(u.entry + j, u.rb0));
+        }
+        items.resize((items.size() + wave_wg - 1) / wave_wg * wave_wg, make_int2(-1, 0));
+        waves = 1;
+        row_blocks = wave_wg;
+    } else if (!sliced) {
         for (const Unit& u : units) items.push_back(make_int2(u.entry, u.rb0));
     } else {
         // each unit goes to the XCD whose list is shortest, its slices 8 items apart
@@ -284,7 +301,7 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     plan->row_blocks = row_blocks;
     plan->n_problems = (int32_t)n_entries;
     plan->x_lds_bytes = (int32_t)x_lds;
-    plan->reserved = 0;
+    plan->mode = wave_mode ? 1 : 0;
     return tq_ok();
 }
 
@@ -318,6 +335,10 @@ TQ_EXPORT tq_status tq_gemv_grouped_run(const tq_grouped_plan* plan, void* strea
     if (plan->n_items < 0 || plan->n_items > (1ll << 31) - 1 || plan->n_problems < 1)
         return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
     if (plan->family >= 1000) return tq_gemm_grouped_run(plan, stream);   // matrix-core plan
+    if (plan->mode == 1)
+        return tq_gemv_launch_wave_items(plan->family, plan->row_blocks, plan->workspace, plan->n_problems,
+                                         plan->n_items, (hipStream_t)stream);
+    if (plan->mode != 0) return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
     if (plan->x_lds_bytes < 0 || plan->x_lds_bytes > TQ_MAX_Q8_LDS)
         return tq_fail(TQ_ERR_ARG, "plan is not filled by tq_gemv_grouped_prepare");
     if ((s = tq_gemv_launch_grouped(plan->family, plan->waves, plan->row_blocks, plan->workspace,

@@ -51,6 +51,13 @@ grouped_fn grouped_of(int family)
     return t ? t[rest % 12] : nullptr;
 }
 
+wave_items_fn wave_items_fn_of(int family)
+{
+    const int mti = family % kTiers, rest = family / kTiers, xt = rest / 12;
+    if (mti != 1 || xt != TQ_BF16) return nullptr;
+    return wave_table_1_1()[rest % 12];
+}
+
 }  // namespace
 
 size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_lds_bytes)
@@ -125,5 +132,21 @@ tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const vo
                        row_blocks);
     const size_t lds = red_bytes(family, waves, total) + (size_t)x_lds_bytes;
     hipLaunchKernelGGL(fn, dim3((unsigned)n_items), dim3(64 * total), lds, stream, probs, items, row_blocks);
+    return tq_check_launch("tq_gemv_grouped_run");
+}
+
+tq_status tq_gemv_launch_wave_items(int family, int waves, const void* workspace, int64_t n_probs,
+                                    int64_t wave_items, hipStream_t stream)
+{
+    if (family < 0 || family >= kPerXT * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
+    if (waves < 1 || waves > max_wg_waves(kMT[family % kTiers]) || wave_items % waves != 0)
+        return tq_fail(TQ_ERR_ARG, "bad per-wave plan: %lld items, %d waves", (long long)wave_items, waves);
+    const wave_items_fn fn = wave_items_fn_of(family);
+    if (!fn) return tq_fail(TQ_ERR_ARG, "no per-wave kernel for plan family %d", family);
+    if (wave_items <= 0) return tq_ok();
+    const uint8_t* ws = (const uint8_t*)workspace;
+    const tq_prob_dev* probs = (const tq_prob_dev*)ws;
+    const int2* items = (const int2*)(ws + tq_ws_items_off(n_probs));
+    hipLaunchKernelGGL(fn, dim3((unsigned)(wave_items / waves)), dim3(64 * waves), 0, stream, probs, items);
     return tq_check_launch("tq_gemv_grouped_run");
 }

@@ -824,12 +824,37 @@ __global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_grouped(const tq
     gemv_body<XT, LAYOUT, K, MT>(P, it.y, nrb);
 }
 
+// One item per wave, for bf16 activations: wave w of workgroup b takes item
+// b * waves + w, one 64-row block of one problem (the host keeps the token
+// slices of one row block in one workgroup).  The workgroup's waves share
+// the trit table, as in the grouped kernel, but each wave has its own
+// problem.  No column split, no codebook: the only workgroup barrier is the
+// table fill.
+template <int XT, int LAYOUT, int K, int MT>
+__global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_wave_items(const tq_prob_dev* __restrict__ probs,
+                                                                           const int2* __restrict__ items)
+{
+    static_assert(XT == TQ_BF16 && LAYOUT != TQ_SCALE_CODEBOOK, "per-wave items: bf16, no codebook");
+    __shared__ float cb_lds[1];
+    __shared__ float sx_lds[1];
+    __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
+    fill_bf16_lut(lut);
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int2 it = ld_uniform_struct(items + (int64_t)blockIdx.x * (blockDim.x >> 6) + wave);
+    if (it.x < 0) return;    // a hole the host left in the item list
+    const tq_prob_dev P = ld_uniform_struct(probs + it.x);
+    rowblock<XT, LAYOUT, K, MT>(P, it.y, 0, 1, nullptr, cb_lds, P.x, sx_lds, it.y * TQ_ROWS < P.N, nullptr,
+                                nullptr, lut);
+}
+
 }  // namespace tqk
 
 namespace tqk {
 
 typedef void (*single_fn)(tq_prob_dev);
 typedef void (*grouped_fn)(const tq_prob_dev*, const int2*, int);
+typedef void (*wave_items_fn)(const tq_prob_dev*, const int2*);
 
 // tokens per pass of each M tier (more tokens are taken in slices of the
 // largest tier of the activation type; the 8-token tier is TQ_F32_Q8 only)
@@ -838,6 +863,15 @@ constexpr int kMT[kTiers] = {1, TQ_PASS_TOKENS, TQ_PASS_TOKENS_Q8};
 // family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier; 36 families per x_type
 constexpr int kPerXT = 12 * kTiers;
 constexpr int kXTypes = 4;
+
+// The per-wave item kernel where the host uses it (bf16, several tokens per
+// pass, no codebook), else none.
+template <int XT, int LAYOUT, int K, int MT>
+constexpr wave_items_fn wave_items_of()
+{
+    if constexpr (MT == 1 || XT != TQ_BF16 || LAYOUT == TQ_SCALE_CODEBOOK) return nullptr;
+    else return &k_gemv_wave_items<XT, LAYOUT, K, MT>;
+}
 
 // families of one (x_type, M tier): index = layout * 4 + (K - 1)
 template <int F>
@@ -850,6 +884,7 @@ template <int XT, int MT, int... Fs>
 struct TablesXT {
     static constexpr single_fn single[] = {&k_gemv_single<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
     static constexpr grouped_fn grouped[] = {&k_gemv_grouped<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
+    static constexpr wave_items_fn wave[] = {wave_items_of<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>()...};
 };
 
 template <int XT, int MT, int... Is>
@@ -867,5 +902,7 @@ TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1)
 TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1)
 TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1)
 TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1) TQ_DECLARE_TABLES(3, 2)
+// per-wave item kernels of the 4-token tier (bf16 activations)
+const wave_items_fn* wave_table_1_1();
 
 }  // namespace tqk

@@ -72,6 +72,10 @@ tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_
                                 hipStream_t stream);
 tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const void* workspace,
                                  int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream);
+// The same with one item per wave: `wave_items` items, `waves` per workgroup
+// (bf16, no column split, no codebook).
+tq_status tq_gemv_launch_wave_items(int family, int waves, const void* workspace, int64_t n_probs,
+                                    int64_t wave_items, hipStream_t stream);
 // Bytes of one activation element as the decode kernels read x.
 static inline int64_t tq_x_elem_bytes(int x_type)
 {

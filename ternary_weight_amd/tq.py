@@ -54,7 +54,7 @@ class tq_grouped_plan(ctypes.Structure):
                 ("family", ctypes.c_int32), ("x_type", ctypes.c_int32), ("M", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
                 ("n_problems", ctypes.c_int32), ("x_lds_bytes", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("mode", ctypes.c_int32)]
 
 
 class tq_bitnet_dims(ctypes.Structure):

@@ -240,6 +240,16 @@ def test_grouped_run_rejects_forged_plans():
     plan.family = fam(tq.BF16, 0, 4, 1)
     plan.waves, plan.row_blocks, plan.x_lds_bytes = 1, 1, 65536 + 16
     assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    # per-wave items: no such mode, no kernel for the family, items not a whole workgroup
+    plan.x_lds_bytes = 0
+    plan.mode = 2
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    plan.mode, plan.row_blocks, plan.n_items = 1, 16, 32
+    for f in (fam(tq.F32_Q8, 1, 3, 1), fam(tq.I8, 1, 3, 1), fam(tq.BF16, 2, 3, 1), fam(tq.BF16, 1, 3, 0)):
+        plan.family = f
+        assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
+    plan.family, plan.n_items = fam(tq.BF16, 1, 3, 1), 24
+    assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
 
 
 def test_chain_workspace_size_validation():

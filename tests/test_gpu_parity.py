@@ -332,11 +332,13 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
 
 @pytest.mark.parametrize("M", [5, 9, 16])
 @pytest.mark.parametrize("x_type,shape", [(F32, (0, 0)), (F32, (2, 2)), (I8, (0, 0)), (I8, (4, 1)),
-                                          (F32_Q8, (0, 0)), (F32_Q8, (2, 4)), (BF16, (1, 16))])
+                                          (F32_Q8, (0, 0)), (F32_Q8, (2, 4)), (BF16, (1, 16)), (BF16, (0, 0))])
 def test_grouped_token_slices(x_type, shape, M):
     """More tokens than a pass takes (4; 8 for TQ_F32_Q8): each problem is cut
-    into slices placed 8 items apart, with holes in the item list.  bf16 at
-    M = 5 stays on the vector ALUs (the matrix cores take M >= 8)."""
+    into slices, with holes in the item list: bf16 without a shape hint an
+    item per wave, a row block's slices in one workgroup; otherwise slices
+    placed 8 workgroups apart.  bf16 at M = 5 stays on the vector ALUs (the
+    matrix cores take M >= 8)."""
     from ternary_weight_amd import tq
     t = torch()
     K, g, layout = 2, 64, GROUP_F16
@@ -370,8 +372,14 @@ def test_grouped_token_slices(x_type, shape, M):
         slices = (M + pass_tokens - 1) // pass_tokens
         assert plan.n_problems == len(shapes) * slices
         R = plan.row_blocks
-        busy = sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes) * slices
-        assert busy <= plan.n_items <= busy + 8 * (slices + 1)
+        if plan.mode == 1:
+            # an item per wave, a row block's slices in one workgroup of R waves
+            assert shape == (0, 0) and x_type == BF16 and R == 16
+            busy = sum((N + 63) // 64 for N, _ in shapes) * slices
+            assert busy <= plan.n_items <= 2 * busy + R and plan.n_items % R == 0
+        else:
+            busy = sum(((N + 63) // 64 + R - 1) // R for N, _ in shapes) * slices
+            assert busy <= plan.n_items <= busy + 8 * (slices + 1)
     tq.gemv_grouped_run(plan)
     t.cuda.synchronize()
     for y, r in zip(ys, refs):
