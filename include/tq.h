@@ -247,8 +247,8 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
  * (0 = default: 4 waves, 1 block; with TQ_F32_Q8, or TQ_I8 and M > 1, 1 wave,
  * 4 blocks, so that a workgroup quantises its activations once for four
- * blocks; with TQ_BF16 1 wave, 16 blocks, so that 16 blocks share the
- * workgroup's trit table).  The
+ * blocks; with TQ_BF16 1 wave, 16 blocks, or 2 waves, 4 blocks for M > 1,
+ * so that the blocks share the workgroup's trit table).  The
  * decode kernels take up to 4 tokens per pass over the codes (8 with
  * TQ_F32_Q8): with more, each problem is cut into slices of that many tokens.
  * With TQ_BF16 (per-tensor or f16 group scales) and no shape hint an item is

@@ -98,6 +98,12 @@ TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_
     return tq_ok();
 }
 
+// Waves per workgroup of a bf16 plan with an item per wave (they share the
+// 64 KiB trit table).
+#ifndef TQ_BF16_WAVE_WG
+#define TQ_BF16_WAVE_WG 16
+#endif
+
 namespace {
 
 int64_t pass_slices(int64_t M) { return M <= TQ_PASS_TOKENS ? 1 : (M + TQ_PASS_TOKENS - 1) / TQ_PASS_TOKENS; }
@@ -135,10 +141,11 @@ namespace {
 // The decode plan; tokens (host, may be NULL): each problem's own token
 // count, every one at most M.  The kernels take tq_pass_tokens(x_type)
 // tokens per pass over the codes; a problem with more is cut into slices of
-// that many tokens, each an entry of the device table.  Workgroups are dealt to the 8
-// XCDs in turn, so the slices of one row block are placed 8 items apart:
-// they run on one XCD at about the same time and share the codes through
-// its L2 (holes left by this placement are items of entry -1).
+// that many tokens, each an entry of the device table.  The slices of one
+// row block are placed 8 workgroup items apart (workgroups are dealt to the
+// 8 XCDs in turn, so they run on one XCD at about the same time), or, for
+// bf16, in consecutive waves of one workgroup (an item per wave).  Holes
+// left by either placement are items of entry -1.
 tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int32_t count, int64_t M,
                           int32_t x_type, void* workspace, size_t workspace_bytes, tq_grouped_plan* plan,
                           void* stream)
@@ -149,12 +156,18 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     int waves = plan->waves, row_blocks = plan->row_blocks;
     const bool hinted = is_shape(waves) && is_shape(row_blocks) && waves * row_blocks <= 16;
     if (!hinted) {
-        // bf16: the trit table fills 64 KiB of LDS, so 16 one-wave row blocks
-        // share it; int8 over several tokens: one wave per row block as well
-        // (measured ahead of 4 waves splitting the columns)
-        const bool one_wave = x_type == TQ_F32_Q8 || x_type == TQ_BF16 || (x_type == TQ_I8 && M > 1);
-        waves = one_wave ? 1 : 4;
-        row_blocks = x_type == TQ_BF16 ? 16 : (one_wave ? 4 : 1);
+        // bf16: the trit table fills 64 KiB of LDS, so 16 waves share it: 16
+        // one-wave row blocks for one token, 4 two-wave row blocks for
+        // several; int8 over several tokens: one wave per row block (each
+        // measured ahead of the other shapes)
+        if (x_type == TQ_BF16) {
+            waves = M > 1 ? 2 : 1;
+            row_blocks = M > 1 ? 4 : 16;
+        } else {
+            const bool one_wave = x_type == TQ_F32_Q8 || (x_type == TQ_I8 && M > 1);
+            waves = one_wave ? 1 : 4;
+            row_blocks = one_wave ? 4 : 1;
+        }
     }
     size_t need = 0;
     tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
@@ -220,7 +233,7 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     // 16 waves share the trit table (measured ahead of workgroup items of 16
     // row blocks; with int8 activations the two measured alike)
     const bool wave_mode = sliced && !hinted && x_type == TQ_BF16 && layout0 != TQ_SCALE_CODEBOOK;
-    const int wave_wg = 16;
+    const int wave_wg = TQ_BF16_WAVE_WG;
     if (count > 0 && M > 0) {
         family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, pass));
         if (std::min<int64_t>(M, pass) > TQ_PASS_TOKENS && waves * row_blocks > 8) {
