@@ -245,9 +245,10 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * with one workgroup per item, an item being `row_blocks` consecutive 64-row
  * blocks of one problem, each split over `waves` waves; items are ordered
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
- * (0 = default: 4 waves, 1 block; with TQ_F32_Q8, or TQ_I8 and M > 1, 1 wave,
- * 4 blocks, so that a workgroup quantises its activations once for four
- * blocks; with TQ_BF16 1 wave, 16 blocks, or 2 waves, 4 blocks for M > 1,
+ * (0 = default: 4 waves, 1 block; with TQ_F32_Q8 1 wave, 4 blocks, so that a
+ * workgroup quantises its activations once for four blocks; with TQ_I8 and
+ * M > 1 2 waves, 2 blocks for one plane and a per-tensor scale, else 1 wave,
+ * 4 blocks; with TQ_BF16 1 wave, 16 blocks, or 2 waves, 4 blocks for M > 1,
  * so that the blocks share the workgroup's trit table).  The
  * decode kernels take up to 4 tokens per pass over the codes (8 with
  * TQ_F32_Q8): with more, each problem is cut into slices of that many tokens.

@@ -155,23 +155,28 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     auto is_shape = [&](int v) { for (int p : pow2) if (v == p) return true; return false; };
     int waves = plan->waves, row_blocks = plan->row_blocks;
     const bool hinted = is_shape(waves) && is_shape(row_blocks) && waves * row_blocks <= 16;
+    size_t need = 0;
+    tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);   // validates the descs
+    if (s) return s;
     if (!hinted) {
         // bf16: the trit table fills 64 KiB of LDS, so 16 waves share it: 16
         // one-wave row blocks for one token, 4 two-wave row blocks for
-        // several; int8 over several tokens: one wave per row block (each
-        // measured ahead of the other shapes)
+        // several.  int8 over several tokens: 2 x 2 for one plane and a
+        // per-tensor scale, one wave per row block otherwise.  Each was
+        // measured ahead of the other shapes.
+        const bool k1 = count > 0 && problems[0].desc->planes == 1 &&
+                        problems[0].desc->scale_layout == TQ_SCALE_TENSOR;
         if (x_type == TQ_BF16) {
             waves = M > 1 ? 2 : 1;
             row_blocks = M > 1 ? 4 : 16;
+        } else if (x_type == TQ_I8 && M > 1) {
+            waves = k1 ? 2 : 1;
+            row_blocks = k1 ? 2 : 4;
         } else {
-            const bool one_wave = x_type == TQ_F32_Q8 || (x_type == TQ_I8 && M > 1);
-            waves = one_wave ? 1 : 4;
-            row_blocks = one_wave ? 4 : 1;
+            waves = x_type == TQ_F32_Q8 ? 1 : 4;
+            row_blocks = x_type == TQ_F32_Q8 ? 4 : 1;
         }
     }
-    size_t need = 0;
-    tq_status s = tq_gemv_grouped_workspace_size(problems, count, M, &need);
-    if (s) return s;
     // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte
     // loads.  With per-problem counts the measure is the mean count of the
     // problems that have tokens (a 16-token tile costs the same for 1 or 16;
