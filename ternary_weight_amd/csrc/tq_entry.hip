@@ -90,7 +90,7 @@ TQ_EXPORT tq_status tq_gemv(const tq_weight_desc* desc, const void* blob, int64_
     if ((s = tq_check_call(L, blob, M, x_type, x, x_scale, y, acc, TQ_MAX_M_GEMV))) return s;
     if (M == 0 || L.N == 0) return tq_ok();
     const tq_prob_dev P = tq_make_prob(L, blob, M, x, x_scale, y, acc);
-    if (tq_gemv_uses_mfma(x_type, M, x))
+    if (tq_gemv_uses_mfma(x_type, L.layout, M, x))
         s = tq_gemm_launch(L, P, x_type, (hipStream_t)stream);
     else
         s = tq_gemv_launch_single(L, P, x_type, (hipStream_t)stream);
@@ -186,9 +186,9 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
         busy += tokens[i] > 0;
         sum += std::max(tokens[i], 0);
     }
+    const int64_t mfma_min = count > 0 ? tq_bf16_mfma_min_m(problems[0].desc->scale_layout) : TQ_BF16_MFMA_MIN_M;
     bool mfma = count > 0 && x_type == TQ_BF16 &&
-                (tokens ? !hinted && sum >= TQ_BF16_MFMA_MIN_M * std::max<int64_t>(busy, 1)
-                        : M >= TQ_BF16_MFMA_MIN_M);
+                (tokens ? !hinted && sum >= mfma_min * std::max<int64_t>(busy, 1) : M >= mfma_min);
     for (int32_t i = 0; i < count; ++i) mfma = mfma && ((uintptr_t)problems[i].x & 15) == 0;
     if (mfma)
         return tq_gemm_grouped_prepare_counts(problems, tokens, count, M, x_type, workspace, workspace_bytes, plan,

@@ -51,13 +51,22 @@ tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const 
 tq_status tq_fail_problem(tq_status s, int32_t i);
 
 // bf16 decode with at least this many tokens runs on the matrix cores (the
-// prefill kernels' one-tile variant) when x is 16-byte aligned.
+// prefill kernels' one-tile variant) when x is 16-byte aligned: 8, or 13 for
+// the codec, whose matrix-core kernel applies a scale after every 16
+// columns (measured crossovers).
 #ifndef TQ_BF16_MFMA_MIN_M
 #define TQ_BF16_MFMA_MIN_M 8
 #endif
-static inline bool tq_gemv_uses_mfma(int x_type, int64_t M, const void* x)
+#ifndef TQ_BF16_MFMA_MIN_M_CODEC
+#define TQ_BF16_MFMA_MIN_M_CODEC 13
+#endif
+static inline int64_t tq_bf16_mfma_min_m(int layout)
 {
-    return x_type == TQ_BF16 && M >= TQ_BF16_MFMA_MIN_M && ((uintptr_t)x & 15) == 0;
+    return layout == TQ_SCALE_CODEBOOK ? TQ_BF16_MFMA_MIN_M_CODEC : TQ_BF16_MFMA_MIN_M;
+}
+static inline bool tq_gemv_uses_mfma(int x_type, int layout, int64_t M, const void* x)
+{
+    return x_type == TQ_BF16 && M >= tq_bf16_mfma_min_m(layout) && ((uintptr_t)x & 15) == 0;
 }
 // tq_gemm_grouped_prepare with per-problem token counts (tokens may be NULL:
 // every problem has M); tq_gemm.hip.

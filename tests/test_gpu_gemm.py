@@ -203,11 +203,12 @@ def test_gemm_grouped_equals_single(xt, K, g, layout):
 
 
 @pytest.mark.parametrize("layout,K,g", [(CODEBOOK, 3, 16), (GROUP_F16, 3, 256), (GROUP_F16, 2, 16)])
-@pytest.mark.parametrize("M", [8, 9, 16])
+@pytest.mark.parametrize("M", [8, 9, 12, 13, 16])
 def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
-    """tq_gemv and the grouped decode plan route bf16 with several tokens to the
-    one-tile matrix-core kernels; both agree with the oracle, the grouped plan
-    bit for bit with the single call."""
+    """tq_gemv and the grouped decode plan route bf16 with 8 or more tokens (13
+    or more for the codec) to the one-tile matrix-core kernels, fewer to the
+    vector ALUs in slices of 4; both agree with the oracle, and on the matrix
+    cores the grouped plan bit for bit with the single call."""
     from ternary_weight_amd import tq
     t = torch()
     rng = np.random.default_rng(M * 10 + g + K)
@@ -228,8 +229,12 @@ def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
     n = tq.gemv_grouped_workspace_size(probs, M)
     ws = t.empty(n, dtype=t.uint8, device="cuda")
     plan = tq.gemv_grouped_prepare(probs, M, BF16, ws, n)
-    assert plan.family >= 1000                       # a matrix-core plan
+    on_mfma = M >= (13 if layout == CODEBOOK else 8)
+    assert (plan.family >= 1000) == on_mfma          # a matrix-core plan, or the vector ALUs
     tq.gemv_grouped_run(plan)
     t.cuda.synchronize()
     for (d, blob, xd, y), w in zip(keep, want):
-        assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
+        if on_mfma:
+            assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
+        else:
+            assert rel_err(host(y), w) <= TOL
