@@ -327,7 +327,7 @@ def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
     if plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
         ks = 32 if layout == TENSOR or group % 32 == 0 else 16
         return "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (run_type, layout, planes, ks)
-    mt = 1 if plan.M <= 1 else (8 if run_type == 3 and plan.M > 4 else 4)   # 3: TQ_F32_Q8
+    mt = 1 if plan.M <= 1 else 4
     kind = "k_gemv_wave_items" if plan.mode == 1 else "k_gemv_grouped"   # an item per wave, or per workgroup
     return "%s<%d, %d, %d, %d>" % (kind, run_type, layout, planes, mt)
 

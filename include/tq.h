@@ -251,8 +251,8 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
  * M > 1 2 waves, 2 blocks for one plane and a per-tensor scale, else 1 wave,
  * 4 blocks; with TQ_BF16 1 wave, 16 blocks, or 2 waves, 4 blocks for M > 1,
  * so that the blocks share the workgroup's trit table).  The
- * decode kernels take up to 4 tokens per pass over the codes (8 with
- * TQ_F32_Q8): with more, each problem is cut into slices of that many tokens.
+ * decode kernels take up to 4 tokens per pass over the codes: with more, each
+ * problem is cut into slices of 4 tokens.
  * With TQ_BF16 (per-tensor or f16 group scales) and no shape hint an item is
  * then one 64-row block of one slice per wave, the slices of a row block in
  * one workgroup of 16 waves; otherwise the slices' workgroups are placed to

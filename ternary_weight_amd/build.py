@@ -32,8 +32,7 @@ COMMON = [
 
 TQ_SOURCES = ["tq_api.hip", "tq_pack.hip", "tq_act.hip", "tq_gemv.hip", "tq_entry.hip", "tq_gemm.hip",
                "tq_gemm_i8.hip", "tq_gemm_bf16.hip", "tq_gemm_bf16_skinny.hip", "tq_chain.hip", "tq_ternarize.hip"] + [
-    "tq_gemv_%s_m%d.hip" % (x, m) for x in ("f32", "bf16", "i8", "f32q8") for m in (1, 4)] + [
-    "tq_gemv_f32q8_m8.hip"]
+    "tq_gemv_%s_m%d.hip" % (x, m) for x in ("f32", "bf16", "i8", "f32q8") for m in (1, 4)]
 
 
 def _deps_mtime() -> float:

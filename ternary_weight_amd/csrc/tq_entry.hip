@@ -139,9 +139,9 @@ TQ_EXPORT tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, i
 namespace {
 
 // The decode plan; tokens (host, may be NULL): each problem's own token
-// count, every one at most M.  The kernels take tq_pass_tokens(x_type)
-// tokens per pass over the codes; a problem with more is cut into slices of
-// that many tokens, each an entry of the device table.  The slices of one
+// count, every one at most M.  The kernels take TQ_PASS_TOKENS tokens per
+// pass over the codes; a problem with more is cut into slices of that many
+// tokens, each an entry of the device table.  The slices of one
 // row block are placed 8 workgroup items apart (workgroups are dealt to the
 // 8 XCDs in turn, so they run on one XCD at about the same time), or, for
 // bf16, in consecutive waves of one workgroup (an item per wave).  Holes
@@ -196,7 +196,7 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     if ((s = tq_check_ptr(workspace, "workspace", false))) return s;
     if (workspace_bytes < need)
         return tq_fail(TQ_ERR_ARG, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-    const int pass = tq_pass_tokens(x_type);
+    const int pass = TQ_PASS_TOKENS;
     std::vector<tq_prob_dev> probs;
     probs.reserve((size_t)count);
     struct Unit { int64_t cost; int32_t entry, n, rb0; };   // row blocks of one problem, all its slices
@@ -241,12 +241,6 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     const int wave_wg = TQ_BF16_WAVE_WG;
     if (count > 0 && M > 0) {
         family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, pass));
-        if (std::min<int64_t>(M, pass) > TQ_PASS_TOKENS && waves * row_blocks > 8) {
-            // the 8-token kernels take at most 8 waves per workgroup
-            if (hinted) return tq_fail(TQ_ERR_UNSUPPORTED, "plan shape %d x %d: more than 8 tokens per pass "
-                                       "take at most 8 waves per workgroup", waves, row_blocks);
-            while (waves * row_blocks > 8) (waves > 1 ? waves : row_blocks) /= 2;
-        }
         // a shape whose partial sums overflow the workgroup's LDS: the default
         // one gives up the column split first, a requested one is refused
         auto lds = [&](int w, int rbs) { return tq_gemv_lds_bytes(family, w, w * rbs, x_lds); };

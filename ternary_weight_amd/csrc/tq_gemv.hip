@@ -5,7 +5,7 @@ namespace {
 
 using namespace tqk;
 
-int mt_index(int M) { return M <= 1 ? 0 : (M <= TQ_PASS_TOKENS ? 1 : 2); }
+int mt_index(int M) { return M <= 1 ? 0 : 1; }
 
 // LDS of the partial sums: one area per wave when a row block is split.
 size_t red_bytes(int family, int split_waves, int total_waves)
@@ -19,21 +19,21 @@ size_t red_bytes(int family, int split_waves, int total_waves)
 const single_fn* single_tab(int xt, int mti)
 {
     static const single_fn* (*const f[kXTypes][kTiers])() = {
-        {single_table_0_0, single_table_0_1, nullptr},
-        {single_table_1_0, single_table_1_1, nullptr},
-        {single_table_2_0, single_table_2_1, nullptr},
-        {single_table_3_0, single_table_3_1, single_table_3_2}};
-    return f[xt][mti] ? f[xt][mti]() : nullptr;
+        {single_table_0_0, single_table_0_1},
+        {single_table_1_0, single_table_1_1},
+        {single_table_2_0, single_table_2_1},
+        {single_table_3_0, single_table_3_1}};
+    return f[xt][mti]();
 }
 
 const grouped_fn* grouped_tab(int xt, int mti)
 {
     static const grouped_fn* (*const f[kXTypes][kTiers])() = {
-        {grouped_table_0_0, grouped_table_0_1, nullptr},
-        {grouped_table_1_0, grouped_table_1_1, nullptr},
-        {grouped_table_2_0, grouped_table_2_1, nullptr},
-        {grouped_table_3_0, grouped_table_3_1, grouped_table_3_2}};
-    return f[xt][mti] ? f[xt][mti]() : nullptr;
+        {grouped_table_0_0, grouped_table_0_1},
+        {grouped_table_1_0, grouped_table_1_1},
+        {grouped_table_2_0, grouped_table_2_1},
+        {grouped_table_3_0, grouped_table_3_1}};
+    return f[xt][mti]();
 }
 
 // family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier
@@ -70,7 +70,7 @@ size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_
 int tq_gemv_family(int x_type, int layout, int K, int M)
 {
     if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 ||
-        M > tq_pass_tokens(x_type))
+        M > TQ_PASS_TOKENS)
         return -1;
     return ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + mt_index(M);
 }
@@ -86,9 +86,8 @@ tq_status launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hi
     const int64_t nunits = (L.NC + cpu - 1) / cpu;
     int waves = 1;
     const int64_t target = 4 * (int64_t)tq_device_cus();
-    const int wmax = max_wg_waves(kMT[fam % kTiers]);
-    while (waves < wmax && L.NB * waves < target && nunits >= 4 * waves * 2) waves *= 2;
-    if (x_type == TQ_BF16) waves = wmax;   // the 64 KiB trit table is shared by up to 16 waves
+    while (waves < 16 && L.NB * waves < target && nunits >= 4 * waves * 2) waves *= 2;
+    if (x_type == TQ_BF16) waves = 16;   // the 64 KiB trit table is shared by up to 16 waves
     const size_t x_lds = x_type == TQ_F32_Q8 ? tq_x_lds_bytes(P.M, L.Kin) : 0;
     while (waves > 1 && tq_gemv_lds_bytes(fam, waves, waves, x_lds) > TQ_MAX_WG_LDS) waves /= 2;
     if (tq_gemv_lds_bytes(fam, waves, waves, x_lds) > TQ_MAX_WG_LDS)
@@ -106,9 +105,9 @@ tq_status launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hi
 // codes of the later launches come from the caches when the weight fits).
 tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
 {
-    const int pass = tq_pass_tokens(x_type);
-    for (int m0 = 0; m0 < P.M; m0 += pass) {
-        const tq_status s = launch_single(L, tq_prob_slice(P, x_type, m0, std::min(pass, P.M - m0)), x_type, stream);
+    for (int m0 = 0; m0 < P.M; m0 += TQ_PASS_TOKENS) {
+        const tq_status s =
+            launch_single(L, tq_prob_slice(P, x_type, m0, std::min(TQ_PASS_TOKENS, P.M - m0)), x_type, stream);
         if (s) return s;
     }
     return TQ_OK;
@@ -118,7 +117,7 @@ tq_status tq_gemv_launch_grouped(int family, int waves, int row_blocks, const vo
                                  int64_t n_probs, int64_t n_items, int x_lds_bytes, hipStream_t stream)
 {
     if (family < 0 || family >= kPerXT * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
-    if (waves < 1 || row_blocks < 1 || waves * row_blocks > max_wg_waves(kMT[family % kTiers]))
+    if (waves < 1 || row_blocks < 1 || waves * row_blocks > 16)
         return tq_fail(TQ_ERR_ARG, "bad plan shape %d x %d", waves, row_blocks);
     const grouped_fn fn = grouped_of(family);
     if (!fn) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
@@ -139,7 +138,7 @@ tq_status tq_gemv_launch_wave_items(int family, int waves, const void* workspace
                                     int64_t wave_items, hipStream_t stream)
 {
     if (family < 0 || family >= kPerXT * kXTypes) return tq_fail(TQ_ERR_ARG, "bad plan family %d", family);
-    if (waves < 1 || waves > max_wg_waves(kMT[family % kTiers]) || wave_items % waves != 0)
+    if (waves < 1 || waves > 16 || wave_items % waves != 0)
         return tq_fail(TQ_ERR_ARG, "bad per-wave plan: %lld items, %d waves", (long long)wave_items, waves);
     const wave_items_fn fn = wave_items_fn_of(family);
     if (!fn) return tq_fail(TQ_ERR_ARG, "no per-wave kernel for plan family %d", family);

@@ -770,10 +770,6 @@ __device__ __forceinline__ void rowblock(const tq_prob_dev& P, const int rb, con
     }
 }
 
-// Waves per workgroup: the 8-token kernels keep more partial sums and
-// activations in registers, so they take at most 512 threads (256 VGPRs).
-__host__ __device__ constexpr int max_wg_waves(int MT) { return MT > TQ_PASS_TOKENS ? 8 : 16; }
-
 // One workgroup: `nrb` row blocks starting at rb0, each split over
 // blockDim / (64 * nrb) waves.
 template <int XT, int LAYOUT, int K, int MT>
@@ -807,7 +803,7 @@ __device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb
 }
 
 template <int XT, int LAYOUT, int K, int MT>
-__global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_single(tq_prob_dev P)
+__global__ __launch_bounds__(1024) void k_gemv_single(tq_prob_dev P)
 {
     gemv_body<XT, LAYOUT, K, MT>(P, (int)blockIdx.x, 1);
 }
@@ -815,7 +811,7 @@ __global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_single(tq_prob_d
 // A whole stack in one launch: workgroup i takes item i, `nrb` row blocks of
 // one problem (items are ordered longest first by the host).
 template <int XT, int LAYOUT, int K, int MT>
-__global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_grouped(const tq_prob_dev* __restrict__ probs,
+__global__ __launch_bounds__(1024) void k_gemv_grouped(const tq_prob_dev* __restrict__ probs,
                                                        const int2* __restrict__ items, int nrb)
 {
     const int2 it = ld_uniform_struct(items + blockIdx.x);
@@ -831,7 +827,7 @@ __global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_grouped(const tq
 // problem.  No column split, no codebook: the only workgroup barrier is the
 // table fill.
 template <int XT, int LAYOUT, int K, int MT>
-__global__ __launch_bounds__(64 * max_wg_waves(MT)) void k_gemv_wave_items(const tq_prob_dev* __restrict__ probs,
+__global__ __launch_bounds__(1024) void k_gemv_wave_items(const tq_prob_dev* __restrict__ probs,
                                                                            const int2* __restrict__ items)
 {
     static_assert(XT == TQ_BF16 && LAYOUT != TQ_SCALE_CODEBOOK, "per-wave items: bf16, no codebook");
@@ -856,11 +852,10 @@ typedef void (*single_fn)(tq_prob_dev);
 typedef void (*grouped_fn)(const tq_prob_dev*, const int2*, int);
 typedef void (*wave_items_fn)(const tq_prob_dev*, const int2*);
 
-// tokens per pass of each M tier (more tokens are taken in slices of the
-// largest tier of the activation type; the 8-token tier is TQ_F32_Q8 only)
-constexpr int kTiers = 3;
-constexpr int kMT[kTiers] = {1, TQ_PASS_TOKENS, TQ_PASS_TOKENS_Q8};
-// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier; 36 families per x_type
+// tokens per pass of each M tier (more tokens are taken in slices of the last)
+constexpr int kTiers = 2;
+constexpr int kMT[kTiers] = {1, TQ_PASS_TOKENS};
+// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier; 24 families per x_type
 constexpr int kPerXT = 12 * kTiers;
 constexpr int kXTypes = 4;
 
@@ -901,7 +896,7 @@ const grouped_fn* grouped_table(int x_type, int mti);
 TQ_DECLARE_TABLES(0, 0) TQ_DECLARE_TABLES(0, 1)
 TQ_DECLARE_TABLES(1, 0) TQ_DECLARE_TABLES(1, 1)
 TQ_DECLARE_TABLES(2, 0) TQ_DECLARE_TABLES(2, 1)
-TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1) TQ_DECLARE_TABLES(3, 2)
+TQ_DECLARE_TABLES(3, 0) TQ_DECLARE_TABLES(3, 1)
 // per-wave item kernels of the 4-token tier (bf16 activations)
 const wave_items_fn* wave_table_1_1();
 

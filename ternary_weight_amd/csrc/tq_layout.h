@@ -45,13 +45,9 @@
 #define TQ_MAX_KIN 65536
 #define TQ_MAX_N (1 << 24)
 #define TQ_MAX_M_GEMV 16
-// Tokens the multi-token decode kernels take in one pass over the codes:
-// 8 when the kernel quantises fp32 activations into LDS (TQ_F32_Q8), 4
-// otherwise (activations read through the scalar cache: 8 tokens of them
-// and their sums cost more occupancy than the second pass over the codes).
+// Tokens the multi-token decode kernels take in one pass over the codes
+// (more are taken in slices of this many).
 #define TQ_PASS_TOKENS 4
-#define TQ_PASS_TOKENS_Q8 8
-static inline int tq_pass_tokens(int x_type) { return x_type == 3 ? TQ_PASS_TOKENS_Q8 : TQ_PASS_TOKENS; }
 #define TQ_CB_SLOTS 32
 
 // pack status bits

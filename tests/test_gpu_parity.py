@@ -334,7 +334,7 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
 @pytest.mark.parametrize("x_type,shape", [(F32, (0, 0)), (F32, (2, 2)), (I8, (0, 0)), (I8, (4, 1)),
                                           (F32_Q8, (0, 0)), (F32_Q8, (2, 4)), (BF16, (1, 16)), (BF16, (0, 0))])
 def test_grouped_token_slices(x_type, shape, M):
-    """More tokens than a pass takes (4; 8 for TQ_F32_Q8): each problem is cut
+    """More tokens than a pass takes (4): each problem is cut
     into slices, with holes in the item list: bf16 without a shape hint an
     item per wave, a row block's slices in one workgroup; otherwise slices
     placed 8 workgroups apart.  bf16 at M = 5 stays on the vector ALUs (the
@@ -368,8 +368,7 @@ def test_grouped_token_slices(x_type, shape, M):
     if plan.family >= 1000:
         assert x_type == BF16 and M >= 8
     else:
-        pass_tokens = 8 if x_type == F32_Q8 else 4
-        slices = (M + pass_tokens - 1) // pass_tokens
+        slices = (M + 3) // 4
         assert plan.n_problems == len(shapes) * slices
         R = plan.row_blocks
         if plan.mode == 1:
