@@ -312,6 +312,7 @@ struct RowBlock {
     const tq_prob_dev& P;
     const int rb, lane;
     const void* xsrc;     // activations: global x, or the LDS copy quantised to int8
+    const void* xrow[MT];  // each token's row of them (the loads then add only the column)
     const LDS_AS uint8_t* lut;   // bf16 trit table (TQ_BF16)
     uint32_t copyoff;
     A p[MT][K];
@@ -323,11 +324,13 @@ struct RowBlock {
         : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_), lut((const LDS_AS uint8_t*)lut_),
           copyoff((uint32_t)(threadIdx.x & 31) * 8u)
     {
+        constexpr int64_t kXBytes = XT == TQ_F32 ? 4 : (XT == TQ_BF16 ? 2 : 1);   // TQ_F32_Q8: the int8 copy
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             out[m] = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) p[m][k] = 0;
+            xrow[m] = (const uint8_t*)xsrc + (int64_t)m * P.Kin * kXBytes;
         }
         cbase = (const uint8_t*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS * 16;
         sbase = (const uint8_t*)P.scales +
@@ -487,7 +490,7 @@ struct RowBlock {
                 if (MT > 1 && m >= P.M) break;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
-                else xu.load(xsrc, (int64_t)m * P.Kin + (int64_t)u * 16);
+                else xu.load(xrow[m], (int64_t)u * 16);
                 if constexpr (XT == TQ_BF16) {
                     const BfPairs xp = bf_pairs(xu);
 #pragma unroll
