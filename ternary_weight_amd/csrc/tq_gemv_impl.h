@@ -330,7 +330,9 @@ struct RowBlock {
             out[m] = 0.0f;
 #pragma unroll
             for (int k = 0; k < K; ++k) p[m][k] = 0;
-            xrow[m] = (const uint8_t*)xsrc + (int64_t)m * P.Kin * kXBytes;
+            // a token past the problem's count reads its last token's row
+            // (the token loop stops before it)
+            xrow[m] = (const uint8_t*)xsrc + (int64_t)std::min(m, P.M - 1) * P.Kin * kXBytes;
         }
         cbase = (const uint8_t*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS * 16;
         sbase = (const uint8_t*)P.scales +
@@ -454,8 +456,10 @@ struct RowBlock {
 
     // Columns of chunk c: `nu` 16-column units (4 for a full chunk).
     // kG16: the group size is 16, so each unit is one group and its sums
-    // start from zero in fresh registers.
-    template <bool kFull, bool kG16>
+    // start from zero in fresh registers.  kAll: the problem has all MT
+    // tokens, so the token loop has no branch (with fewer, each token past
+    // the count ends it).
+    template <bool kFull, bool kG16, bool kAll>
     __device__ __forceinline__ void compute(int c_, int nu, const Slot<K, LAYOUT>& s, const XChunk<XT>* xc,
                                             const float* cb_lds)
     {
@@ -487,7 +491,7 @@ struct RowBlock {
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                if (MT > 1 && m >= P.M) break;
+                if (!kAll && MT > 1 && m >= P.M) break;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
                 else xu.load(xrow[m], (int64_t)u * 16);
@@ -545,14 +549,21 @@ struct RowBlock {
 
     __device__ __forceinline__ void finish(const float* cb_lds)
     {
-        if (kGroup && P.g == 16) run_chunks<true>(cb_lds);
-        else run_chunks<false>(cb_lds);
+        // one copy of the loop per case, chosen once per row block
+        const bool all = MT == 1 || P.M == MT;
+        if (kGroup && P.g == 16) {
+            if (all) run_chunks<true, true>(cb_lds);
+            else run_chunks<true, MT == 1>(cb_lds);
+        } else {
+            if (all) run_chunks<false, true>(cb_lds);
+            else run_chunks<false, MT == 1>(cb_lds);
+        }
     }
 
     // The full chunks c0 .. cf - 1, D at a time, the next D loading while
     // one set computes (two register sets in turn, so no copies), then the
     // ragged last chunk of the row (Kin % 64 != 0).
-    template <bool kG16>
+    template <bool kG16, bool kAll>
     __device__ __forceinline__ void run_chunks(const float* cb_lds)
     {
         const int c0 = c0_, c1 = c1_, cf = cf_;
@@ -567,7 +578,7 @@ struct RowBlock {
                     if (c + j < cf) {
                         XChunk<XT> xn;
                         if (kXPre && c + j + 1 < cf) xn.load(xsrc, (int64_t)(c + j + 1) * TQ_CHUNK);
-                        compute<true, kG16>(c + j, 4, set[j], &xc, cb_lds);
+                        compute<true, kG16, kAll>(c + j, 4, set[j], &xc, cb_lds);
                         if (kXPre) xc = xn;
                     }
                 }
@@ -586,7 +597,7 @@ struct RowBlock {
         if (cf < c1) {
             Slot<K, LAYOUT> s;
             load_slot(cf, s);
-            compute<false, kG16>(cf, n16 - 4 * cf, s, nullptr, cb_lds);
+            compute<false, kG16, kAll>(cf, n16 - 4 * cf, s, nullptr, cb_lds);
         }
     }
 };
