@@ -332,7 +332,7 @@ struct RowBlock {
             for (int k = 0; k < K; ++k) p[m][k] = 0;
             // a token past the problem's count reads its last token's row
             // (the token loop stops before it)
-            xrow[m] = (const uint8_t*)xsrc + (int64_t)std::min(m, P.M - 1) * P.Kin * kXBytes;
+            if (MT > 1) xrow[m] = (const uint8_t*)xsrc + (int64_t)std::min(m, P.M - 1) * P.Kin * kXBytes;
         }
         cbase = (const uint8_t*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS * 16;
         sbase = (const uint8_t*)P.scales +
@@ -494,6 +494,7 @@ struct RowBlock {
                 if (!kAll && MT > 1 && m >= P.M) break;
                 XUnit<XT> xu;
                 if (kXPre && kFull) xu = xc->unit(d);
+                else if (MT == 1) xu.load(xsrc, (int64_t)u * 16);
                 else xu.load(xrow[m], (int64_t)u * 16);
                 if constexpr (XT == TQ_BF16) {
                     const BfPairs xp = bf_pairs(xu);
