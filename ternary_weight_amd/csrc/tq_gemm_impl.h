@@ -318,11 +318,22 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     };
     auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&sw)[FN]) {
         static_assert(sizeof(a) == FM * sizeof(Frag), "fragments");
+        // the first step of a group starts its sums from zero in the MFMA
+        // itself (no registers to clear when the previous group ends)
+        if (!kDirect && c.j == 0) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const Frag b = MF::decode(w[fn], q);
+            for (int fn = 0; fn < FN; ++fn) {
+                const Frag b = MF::decode(w[fn], q);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, part[fm][fn]);
+                for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, Part{0, 0, 0, 0});
+            }
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const Frag b = MF::decode(w[fn], q);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, part[fm][fn]);
+            }
         }
         if (kDirect || c.j != seg_steps - 1) return;
         // the block's scale for the lane's weight rows, applied once
@@ -351,7 +362,6 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
                 for (int e = 0; e < 4; ++e)
                     acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e] =
                         fmaf(sc[fn], (float)part[fm][fn][e], acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e]);
-                part[fm][fn] = Part{0, 0, 0, 0};
             }
     };
 
