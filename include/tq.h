@@ -166,7 +166,7 @@ tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count,
 /*
  * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
  * scale per group; up to 4 tokens per pass over the codes, one launch per
- * slice of 4 tokens beyond that).  With TQ_BF16 and M >= 8 (13 for
+ * slice of 4 tokens beyond that).  With TQ_BF16 and M >= 3 (5 for
  * TQ_SCALE_CODEBOOK; x 16-byte aligned) the product runs on the matrix cores
  * instead, as tq_gemm does; the results meet the same bound.
  *   x         device [M][Kin] of x_type
@@ -239,8 +239,8 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
 
 /*
  * Validate the problems, write their descriptor table and the work list into
- * `workspace` (device, caller-owned) and fill `plan`.  With TQ_BF16, M >= 8
- * (13 for TQ_SCALE_CODEBOOK) and every x 16-byte aligned the plan is a
+ * `workspace` (device, caller-owned) and fill `plan`.  With TQ_BF16, M >= 3
+ * (5 for TQ_SCALE_CODEBOOK) and every x 16-byte aligned the plan is a
  * matrix-core plan (as from tq_gemm_grouped_prepare; the shape hints are
  * then unused).  The run is one launch
  * with one workgroup per item, an item being `row_blocks` consecutive 64-row
@@ -271,7 +271,7 @@ tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int
  * & paper"), so each expert is one problem with its own blob, and the tokens
  * the router sent to it are gathered into its x.  A problem with no tokens
  * takes no workgroup (its pointers may then be NULL).  With TQ_BF16, a mean
- * count of at least 8 (13 for TQ_SCALE_CODEBOOK) over the problems that have
+ * count of at least 3 (5 for TQ_SCALE_CODEBOOK) over the problems that have
  * tokens, every x 16-byte
  * aligned and no shape hint in `plan`, the plan is a matrix-core plan whose
  * tiles cover each problem's own count; otherwise the vector-ALU kernels take

@@ -198,6 +198,15 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int CW = kLds ? (XT == TQ_I8 ? 4 : 2) : 1;
     constexpr int CPT = kLds ? TN * CW / kThreads : 1;
     static_assert(!kLds || (CPT >= 1 && CW % CPT == 0), "code dwords per thread");
+    // Codes through a stage of the wave's own: the bf16 one-tile kernels,
+    // whose wave owns one whole 64-row block.  Lane l loads row l's code
+    // dwords of the step (and its scale word), so a load covers the block's
+    // 1 KiB slot in order, and the MFMA fragments are read back from LDS.
+    // Only the wave touches its stage, and a wave's LDS accesses complete in
+    // order, so no barrier is needed.
+    constexpr bool kWave = !kLds && XT == TQ_BF16 && FN == 4 && WM == 1;
+    constexpr int CWW = KS / 16;                          // code dwords of a row per step
+    constexpr int WST = 64 * CWW + (kWord ? 64 : 0);      // dwords per wave and stage
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -211,7 +220,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, (int64_t)NB * NC * K * 1024);
     const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)NB * P.NID * 256
                                                                                  : (int64_t)NB * P.NGD * K * 256);
-    uint32_t xoff[FM], coff[FN], soff[FN];
+    uint32_t xoff[FM], coff[FN], soff[FN], cwoff = 0, swoff = 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) xoff[fm] = ((uint32_t)(m0 + 16 * fm + r) * Kin + q * QCOLS) * ESZ;
     // LDS staging: chunk id = thread + 256 i holds row id / 4, 16-byte column
@@ -257,6 +266,15 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         soff[fn] = LAYOUT == TQ_SCALE_CODEBOOK ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4
                                                : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
     }
+    if constexpr (kWave) {
+        const uint32_t n = n0 + lane;                      // n0 is a multiple of 64
+        cwoff = ((n >> 6) * NC * K * 64 + (n & 63)) * 16;
+        swoff = LAYOUT == TQ_SCALE_CODEBOOK ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4
+                                            : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
+    }
+    __shared__ __attribute__((aligned(16))) uint32_t wlds[kWave ? 2 : 1][kWave ? 4 * WST : 4];
+    LDS_AS uint32_t* const wst0 = (LDS_AS uint32_t*)wlds[0] + (kWave ? wave * WST : 0);
+    LDS_AS uint32_t* const wst1 = (LDS_AS uint32_t*)wlds[kWave ? 1 : 0] + (kWave ? wave * WST : 0);
 
     const int nks = (Kin + KS - 1) / KS;                       // MFMA steps per row
     const int seg_steps = LAYOUT == TQ_SCALE_TENSOR ? nks : P.g / KS;
@@ -276,10 +294,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // Columns of x past Kin in a ragged last step read the next row (or zero
     // past the end); the codes there are padding (zero trits), so they add 0.
     constexpr int AREG = kLds ? XCH : FM;                  // x registers per step buffer
-    constexpr int WREG = kLds ? CPT : FN;                  // code registers per step buffer
+    constexpr int WREG = kLds ? CPT : kWave ? CWW : FN;    // code registers per step buffer
+    constexpr int SREG = kWave ? 1 : FN;                   // scale words per step buffer
     Frag abuf[NBUF][AREG];
-    uint32_t wbuf[NBUF][WREG], swbuf[NBUF][FN];
-    auto load = [&](const Cursor& cur, Frag (&a)[AREG], uint32_t (&w)[WREG], uint32_t (&sw)[FN]) {
+    uint32_t wbuf[NBUF][WREG], swbuf[NBUF][SREG];
+    auto load = [&](const Cursor& cur, Frag (&a)[AREG], uint32_t (&w)[WREG], uint32_t (&sw)[SREG]) {
         // a cursor past the last step (the prefetch runs ahead of the end)
         // loads the last step again: the data is in cache and never used
         const bool past = cur.seg >= nseg;
@@ -305,6 +324,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             } else {
                 w[0] = buffer_load<uint32_t>(rc, ccoff, cs);
             }
+        } else if constexpr (kWave) {
+            if constexpr (CWW == 2) {
+                const u32x2 v = buffer_load<u32x2>(rc, cwoff, cs);
+                w[0] = v[0];
+                w[CWW - 1] = v[1];
+            } else {
+                w[0] = buffer_load<uint32_t>(rc, cwoff, cs);
+            }
         } else {
 #pragma unroll
             for (int fn = 0; fn < WREG; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
@@ -312,11 +339,16 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         if (kWord) {   // the block's word, with every step (no branch around a load)
             const uint32_t ss = LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(c.seg / 6) * 256
                                                             : ((uint32_t)(c.seg >> 1) * K + c.k) * 256;
+            if constexpr (kWave) {
+                sw[0] = buffer_load<uint32_t>(rs, swoff, ss);
+            } else {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) sw[fn] = buffer_load<uint32_t>(rs, soff[fn], ss);
+                for (int fn = 0; fn < FN; ++fn) sw[fn] = buffer_load<uint32_t>(rs, soff[fn], ss);
+            }
         }
     };
-    auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&sw)[FN]) {
+    auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&swr)[SREG],
+                       const LDS_AS uint32_t* wst) {
         static_assert(sizeof(a) == FM * sizeof(Frag), "fragments");
         // the first step of a group starts its sums from zero in the MFMA
         // itself (no registers to clear when the previous group ends)
@@ -337,6 +369,9 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         }
         if (kDirect || c.j != seg_steps - 1) return;
         // the block's scale for the lane's weight rows, applied once
+        uint32_t sw[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) sw[fn] = kWave ? (kWord ? wst[64 * CWW + 16 * fn + r] : 0u) : swr[kWave ? 0 : fn];
         float sc[FN];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -389,6 +424,27 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         for (int fn = 0; fn < FN; ++fn) w[fn] = ((const LDS_AS uint32_t*)clds[stage])[clds_r[fn]];
     };
     auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // the wave's own stage (double buffered like the workgroup one): lane l
+    // writes row l's code dwords and scale word; the fragments are read back
+    // in the MFMA layout, row 16 fn + r, the lane group's dword
+    auto wave_write = [&](int stage, const uint32_t (&w)[WREG], const uint32_t (&sw)[SREG]) {
+        if constexpr (kWave) {
+            LDS_AS uint32_t* st = stage ? wst1 : wst0;
+            if constexpr (CWW == 2) {
+                *(LDS_AS u32x2*)(st + 2 * lane) = u32x2{w[0], w[CWW - 1]};
+            } else {
+                st[lane] = w[0];
+            }
+            if constexpr (kWord) st[64 * CWW + lane] = sw[0];
+        }
+    };
+    auto wave_read = [&](int stage, uint32_t (&w)[FN]) {
+        if constexpr (kWave) {
+            const LDS_AS uint32_t* st = stage ? wst1 : wst0;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) w[fn] = st[(16 * fn + r) * CWW + MF::dword_lane(q)];
+        }
+    };
     // one step: the loads of step t + NBUF - 1, then (LDS path) the staging of
     // step t + 1, then the MFMAs of step t
     auto step = [&](int u, Cursor& ld, Cursor& cp, bool issue) {
@@ -405,9 +461,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             barrier();
             lds_write((u + 1) & 1, abuf[(u + 1) % NBUF], wbuf[(u + 1) % NBUF]);
             lds_read(u & 1, a, w);
-            compute(cp, a, w, swbuf[u]);
+            compute(cp, a, w, swbuf[u], wst0);
+        } else if constexpr (kWave) {
+            uint32_t w[FN];
+            wave_write((u + 1) & 1, wbuf[(u + 1) % NBUF], swbuf[(u + 1) % NBUF]);
+            wave_read(u & 1, w);
+            compute(cp, abuf[u], w, swbuf[u], (u & 1) ? wst1 : wst0);
         } else {
-            compute(cp, abuf[u], wbuf[u], swbuf[u]);
+            compute(cp, abuf[u], wbuf[u], swbuf[u], wst0);
         }
         cp.advance(seg_steps, K);
     };
@@ -419,7 +480,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         ld.advance(seg_steps, K);
     }
     if constexpr (kLds) lds_write(0, abuf[0], wbuf[0]);
-    static_assert(!kLds || NBUF % 2 == 0, "stage parity follows the buffer index");
+    if constexpr (kWave) wave_write(0, wbuf[0], swbuf[0]);
+    static_assert(!(kLds || kWave) || NBUF % 2 == 0, "stage parity follows the buffer index");
     int t = 0;
     for (; t + NBUF <= total; t += NBUF) {
 #pragma unroll

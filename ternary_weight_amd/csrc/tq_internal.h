@@ -51,14 +51,14 @@ tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const 
 tq_status tq_fail_problem(tq_status s, int32_t i);
 
 // bf16 decode with at least this many tokens runs on the matrix cores (the
-// prefill kernels' one-tile variant) when x is 16-byte aligned: 8, or 13 for
+// prefill kernels' one-tile variant) when x is 16-byte aligned: 3, or 5 for
 // the codec, whose matrix-core kernel applies a scale after every 16
 // columns (measured crossovers).
 #ifndef TQ_BF16_MFMA_MIN_M
-#define TQ_BF16_MFMA_MIN_M 8
+#define TQ_BF16_MFMA_MIN_M 3
 #endif
 #ifndef TQ_BF16_MFMA_MIN_M_CODEC
-#define TQ_BF16_MFMA_MIN_M_CODEC 13
+#define TQ_BF16_MFMA_MIN_M_CODEC 5
 #endif
 static inline int64_t tq_bf16_mfma_min_m(int layout)
 {

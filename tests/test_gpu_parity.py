@@ -337,8 +337,9 @@ def test_grouped_token_slices(x_type, shape, M):
     """More tokens than a pass takes (4): each problem is cut
     into slices, with holes in the item list: bf16 without a shape hint an
     item per wave, a row block's slices in one workgroup; otherwise slices
-    placed 8 workgroups apart.  bf16 at M = 5 stays on the vector ALUs (the
-    matrix cores take M >= 8)."""
+    placed 8 workgroups apart.  bf16 goes to the matrix cores (M >= 3); with
+    a shape hint, through the per-token plan (every problem M tokens), it
+    stays on the vector ALUs."""
     from ternary_weight_amd import tq
     t = torch()
     K, g, layout = 2, 64, GROUP_F16
@@ -364,9 +365,14 @@ def test_grouped_token_slices(x_type, shape, M):
     nbytes = tq.gemv_grouped_workspace_size(probs, M)
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     waves, row_blocks = shape
-    plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
+    if x_type == BF16 and shape != (0, 0):
+        plan = tq.gemv_grouped_prepare_tokens(probs, [M] * len(shapes), x_type, ws, nbytes, waves=waves,
+                                              row_blocks=row_blocks)
+        assert plan.family < 1000 and plan.mode == 0
+    else:
+        plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
     if plan.family >= 1000:
-        assert x_type == BF16 and M >= 8
+        assert x_type == BF16 and M >= 3 and shape == (0, 0)
     else:
         slices = (M + 3) // 4
         assert plan.n_problems == len(shapes) * slices
