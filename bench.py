@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--moe-x", choices=["i8", "bf16", "f32"], default="i8",
                     help="moe: activations (i8: fp32 rows quantised per token by the quantiser, or inside "
                          "the product with --fused)")
-    ap.add_argument("--M", type=int, default=1, help="decode stacks (cfg2-4): tokens per step (cfg4: 1, 4 or 16)")
+    ap.add_argument("--M", type=int, default=1, help="decode stacks (cfg2-4): tokens per step, 1 to 16")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
     ap.add_argument("--fused", action="store_true",
