@@ -200,9 +200,10 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     static_assert(!kLds || (CPT >= 1 && CW % CPT == 0), "code dwords per thread");
     // Codes through a stage of the wave's own: the bf16 kernels without the
     // workgroup stage (the one-tile kernels, and 16-column steps), whose wave
-    // owns one whole 64-row block.  Lane l loads row l's code
-    // dwords of the step (and its scale word), so a load covers the block's
-    // 1 KiB slot in order, and the MFMA fragments are read back from LDS.
+    // owns one whole 64-row block.  Lane l loads row l's code dwords of the
+    // step (half or a quarter of the row's 16 bytes) and its scale word, so
+    // one load walks the block's 1 KiB slot in row order; the MFMA fragments
+    // are read back from LDS.
     // Only the wave touches its stage, and a wave's LDS accesses complete in
     // order, so no barrier is needed.
     constexpr bool kWave = !kLds && XT == TQ_BF16 && FN == 4;
