@@ -134,6 +134,10 @@ CHAINS = {
                    30, 2560, 6912, 20, 5, 128, weights_cfg=2),
     "chain_small": Chain(8, "BitNet-shaped decode chain at small sizes, 6 layers",
                          6, 256, 704, 4, 2, 64, weights_cfg=8),
+    # widths that are not multiples of the 64-row block (240, 48 and 720):
+    # the last block of every projection is partly padding
+    "chain_ragged": Chain(9, "decode chain with ragged widths, 3 layers",
+                          3, 240, 720, 5, 1, 48, weights_cfg=9),
 }
 
 

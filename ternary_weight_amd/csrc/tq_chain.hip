@@ -65,6 +65,8 @@ struct PhaseDev {
     int32_t splits;     // column splits per block
     int32_t items;      // groups * splits
     int32_t width;      // input length
+    int32_t acc_base;   // first accumulator row of the phase's blocks
+    int32_t cnt_base;   // first arrival counter of the phase's blocks
 };
 
 struct ChainDev {
@@ -76,8 +78,8 @@ struct ChainDev {
     float* qkv;         // [nq + 2 nkv]
     float* x1;          // [hidden]
     float* act;         // [inter]
-    int32_t* acc;       // [max(nq + 2 nkv, hidden, 2 inter)] split partial sums, kept zero
-    uint32_t* cnt;      // [max groups] arrivals per block, kept zero
+    int32_t* acc;       // split partial sums, 64 rows per block, kept zero (sizes_of)
+    uint32_t* cnt;      // arrivals per block, kept zero
     uint32_t* done;     // [n_layers][5] blocks written: QKV, v, O, GU, DOWN
     int32_t* err;       // set when a wait gives up
 };
@@ -108,7 +110,9 @@ struct Item {
     int rb;             // 64-row block within the projection
     int split;
     int group;
-    int off;            // first accumulator row of the block (of gate for GU)
+    int off;            // first output row of the block (in q|k|v for QKV)
+    int arow;           // first accumulator row of the block (of gate for GU): 64 rows
+                        // of its own, apart from every other block that can be in flight
 };
 
 __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, int ph, int item)
@@ -130,6 +134,9 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, in
         it.rb = it.group;
         it.off = it.group * 64;
     }
+    // O runs while q and k are still being summed, so its rows and counters
+    // lie past those of the QKV blocks (acc_base, cnt_base)
+    it.arow = P.acc_base + it.group * 64;
     return it;
 }
 
@@ -324,8 +331,8 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     for (int k = 0; k < nw; ++k) sa += red[k][lane];
                     if (ph == PH_GU)
                         for (int k = nw; k < kWaves; ++k) sb += red[k][lane];
-                    const int ra = it.off + lane;                   // accumulator rows
-                    const int rbw = C.inter + it.off + lane;
+                    const int ra = it.arow + lane;                  // accumulator rows
+                    const int rbw = ra + C.ph[PH_GU].groups * 64;   // GU: up's rows past gate's
                     bool last = true;
                     if (P.splits > 1) {
                         __hip_atomic_fetch_add(C.acc + ra, sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -333,13 +340,13 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                         wait_stores();     // the partial sums are in before the count says so
                         uint32_t old = 0;
                         if (lane == 0)
-                            old = __hip_atomic_fetch_add(C.cnt + it.group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            old = __hip_atomic_fetch_add(C.cnt + P.cnt_base + it.group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         old = __shfl(old, 0, 64);
                         last = old == (uint32_t)P.splits - 1;
                         if (last) {
                             sa = __hip_atomic_exchange(C.acc + ra, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             if (ph == PH_GU) sb = __hip_atomic_exchange(C.acc + rbw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (lane == 0) __hip_atomic_store(C.cnt + it.group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (lane == 0) __hip_atomic_store(C.cnt + P.cnt_base + it.group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         }
                     }
                     const tq_prob_dev& Pa = Ld.p[it.proj];
@@ -419,9 +426,12 @@ Sizes sizes_of(const tq_bitnet_dims* d, int32_t n_layers)
     Sizes s;
     s.nq = (int64_t)d->n_heads * d->head_dim;
     s.nkv = (int64_t)d->n_kv_heads * d->head_dim;
-    s.acc_n = std::max({s.nq + 2 * s.nkv, (int64_t)d->hidden, 2 * (int64_t)d->intermediate}) + 64;
-    s.cnt_n = std::max({(s.nq + 2 * s.nkv + 63) / 64 + 2, ((int64_t)d->hidden + 63) / 64,
-                        ((int64_t)d->intermediate + 63) / 64});
+    // blocks: QKV (q, k, v), then O's own range after them; GU (gate, then up);
+    // DOWN -- 64 accumulator rows and one counter per block
+    const int64_t nb_qkv = (s.nq + 63) / 64 + 2 * ((s.nkv + 63) / 64);
+    const int64_t nb_h = ((int64_t)d->hidden + 63) / 64, nb_i = ((int64_t)d->intermediate + 63) / 64;
+    s.acc_n = 64 * std::max({nb_qkv + nb_h, 2 * nb_i, nb_h});
+    s.cnt_n = std::max({nb_qkv + nb_h, nb_i, nb_h});
     int64_t o = tq_align256(sizeof(ChainDev));
     s.off_layers = o;
     o = tq_align256(o + (int64_t)n_layers * sizeof(LayerDev));
@@ -549,6 +559,8 @@ TQ_EXPORT tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq
         c.ph[ph].splits = (int32_t)S;
         c.ph[ph].items = (int32_t)(groups[ph] * S);
         c.ph[ph].width = (int32_t)width[ph];
+        c.ph[ph].acc_base = ph == PH_O ? (int32_t)(64 * groups[PH_QKV]) : 0;
+        c.ph[ph].cnt_base = ph == PH_O ? (int32_t)groups[PH_QKV] : 0;
     }
     c.layers = (const LayerDev*)(ws + z.off_layers);
     c.qkv = (float*)(ws + z.off_qkv);

@@ -1,12 +1,15 @@
 """The decode chain (tq_bitnet_chain_*) against the CPU oracle, bit for bit.
 
-Each layer's q, k, v and the hidden state after every layer are compared
-with oracle.bitnet_layer on the same seeded inputs: the small BitNet-shaped
-chain over all its layers and several grid sizes (items per workgroup and
-column splits change with the grid), and the BitNet b1.58-2B shapes over two
-layers.  The only rounding that the two sides take in a different order is
-the fp64 sum of squares inside RMSNorm (see tq.h); a mismatch there would
-show as a difference in the last bits of one layer.
+Each layer's q, k, v and the hidden state after the last layer are compared
+with oracle.bitnet_layer on the same seeded inputs (layer l's q, k and v
+are a function of the state entering it, so every layer's state is pinned):
+the small BitNet-shaped chain over all its layers and several grid sizes
+(items per workgroup and column splits change with the grid), a chain whose
+widths are not multiples of the 64-row block, and the BitNet b1.58-2B shapes
+over all 30 layers at the default grid and another, each run repeated on
+the same plan.  The only rounding that the two sides take in a different
+order is the fp64 sum of squares inside RMSNorm (see tq.h); a mismatch
+there would show as a difference in the last bits of one layer.
 """
 from __future__ import annotations
 
@@ -43,6 +46,35 @@ def _device_layers(chain, n_layers):
         host.append((trits, np.array(s_w, dtype=np.float32), norms_h))
     torch.cuda.synchronize()
     return layers, host, keep
+
+
+def _device_layers_generated(chain, n_layers):
+    """As _device_layers, with the weights drawn by the device copy of the
+    seeded generator (equal to the host one, test_gpu_synth) and copied back
+    for the oracle: the host generator is too slow for 30 full-size layers."""
+    import torch
+    from synth import device
+    from synth.configs import CASES
+    from ternary_weight_amd import tq
+    wcase = CASES["cfg2"]
+    assert chain.weights_cfg == wcase.cfg
+    layers, host = [], []
+    for layer in range(n_layers):
+        blobs, trits, s_w = [], [], []
+        for p, (_, N, Kin) in enumerate(chain.proj_shapes()):
+            d = device.projection(wcase, layer, p, N, Kin, M=1)
+            desc = tq.desc(1, 0, tq.SCALE_TENSOR, N, Kin)
+            blob = torch.empty(tq.packed_size(desc), dtype=torch.uint8, device="cuda")
+            tq.pack(desc, d["trits"], d["scales"], None, blob)
+            blobs.append(blob)
+            trits.append(d["trits"][0].cpu().numpy())
+            s_w.append(float(d["scales"][0].cpu().numpy()))
+            del d
+        norms_h = [inputs.chain_norm(chain, layer, j) for j in range(4)]
+        layers.append((blobs, [torch.from_numpy(n).cuda() for n in norms_h]))
+        host.append((trits, np.array(s_w, dtype=np.float32), norms_h))
+    torch.cuda.synchronize()
+    return layers, host
 
 
 def _oracle_chain(chain, host):
@@ -106,16 +138,51 @@ def test_small_chain_prefixes_and_repeats(small):
     assert np.array_equal(x2.cpu().numpy().view(np.uint32), xs[1].view(np.uint32))
 
 
-def test_bitnet_shapes_two_layers():
-    chain = CHAINS["chain"]
-    print("chain BitNet-2B layers=2", flush=True)
-    layers, host, keep = _device_layers(chain, 2)
+def _check_runs(chain, layers, xs, qkvs, n_layers, workgroups, repeats):
+    import torch
+    from ternary_weight_amd import tq
+    plan, ws, x, qkv = _run(chain, layers, n_layers, workgroups)
+    for r in range(repeats):
+        if r:
+            xd = torch.from_numpy(inputs.chain_input(chain)).cuda()
+            qd = torch.zeros_like(torch.from_numpy(qkv)).cuda()
+            tq.bitnet_chain_run(plan, xd, qd)
+            tq.bitnet_chain_status(plan)
+            x, qkv = xd.cpu().numpy(), qd.cpu().numpy()
+        for layer in range(n_layers):
+            assert np.array_equal(qkv[layer].view(np.uint32), qkvs[layer].view(np.uint32)), \
+                (workgroups, r, layer)
+        assert np.array_equal(x.view(np.uint32), xs[n_layers - 1].view(np.uint32)), (workgroups, r)
+    del plan, ws
+
+
+@pytest.mark.parametrize("workgroups", [0, 3, 16, 97])
+def test_ragged_widths_chain(workgroups):
+    """hidden 240, 48-wide KV heads, FFN 720: every projection ends in a
+    partly padded 64-row block, whose accumulator rows must not reach the
+    next block's."""
+    chain = CHAINS["chain_ragged"]
+    print("chain_ragged layers=%d workgroups=%d" % (chain.layers, workgroups), flush=True)
+    layers, host, keep = _device_layers(chain, chain.layers)
     xs, qkvs = _oracle_chain(chain, host)
-    for wg in (0, 97):
-        _, _, x, qkv = _run(chain, layers, 2, wg)
-        for layer in range(2):
-            assert np.array_equal(qkv[layer].view(np.uint32), qkvs[layer].view(np.uint32)), (wg, layer)
-        assert np.array_equal(x.view(np.uint32), xs[-1].view(np.uint32)), wg
+    _check_runs(chain, layers, xs, qkvs, chain.layers, workgroups, repeats=3)
+
+
+@pytest.fixture(scope="module")
+def bitnet30():
+    chain = CHAINS["chain"]
+    print("chain BitNet-2B: generating %d layers" % chain.layers, flush=True)
+    layers, host = _device_layers_generated(chain, chain.layers)
+    xs, qkvs = _oracle_chain(chain, host)
+    return chain, layers, xs, qkvs
+
+
+@pytest.mark.parametrize("workgroups", [0, 97, 256])
+def test_bitnet_shapes_all_layers(bitnet30, workgroups):
+    """Every one of the 30 BitNet b1.58-2B layers, bit for bit, three runs on one plan."""
+    chain, layers, xs, qkvs = bitnet30
+    print("chain BitNet-2B layers=%d workgroups=%d" % (chain.layers, workgroups), flush=True)
+    _check_runs(chain, layers, xs, qkvs, chain.layers, workgroups, repeats=3)
 
 
 def test_prepare_rejects_mismatched_blobs(small):
