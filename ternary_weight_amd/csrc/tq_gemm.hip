@@ -79,6 +79,8 @@ int64_t tiles_of(const tq_gemm_kernel& k, int64_t M, int64_t N, int64_t* tiles_m
 
 }  // namespace
 
+bool tq_gemm_supports(const tq_layout& L, int x_type, int64_t M) { return gemm_kernel(L, x_type, M) != nullptr; }
+
 tq_status tq_gemm_launch(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream)
 {
     const tq_gemm_kernel* k = gemm_kernel(L, x_type, P.M);

@@ -75,6 +75,10 @@ tq_status tq_gemm_grouped_prepare_counts(const tq_problem* problems, const int32
                                          tq_grouped_plan* plan, void* stream);
 // Matrix-core launch of one problem (tq_gemm.hip); the arguments are checked.
 tq_status tq_gemm_launch(const tq_layout& L, const tq_prob_dev& P, int x_type, hipStream_t stream);
+// Whether a matrix-core kernel takes this shape (every operand below the
+// 4 GiB its 32-bit offsets reach); the decode entry points send a bf16 call
+// that it does not take to the vector-ALU kernels instead.
+bool tq_gemm_supports(const tq_layout& L, int x_type, int64_t M);
 
 // Decode launch shared by tq_gemv and tq_gemv_grouped_run (tq_gemv.hip).
 tq_status tq_gemv_launch_single(const tq_layout& L, const tq_prob_dev& P, int x_type,

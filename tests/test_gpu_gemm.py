@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from oracle import BF16, CODEBOOK, F32, GROUP_F16, I8, TENSOR
+from synth import gen
 from tests.gpu_util import TOL, dev, gemv, host, pack, rel_err, torch
 from tests.test_gpu_parity import rand_problem, rand_x
 
@@ -238,3 +239,50 @@ def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
             assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
         else:
             assert rel_err(host(y), w) <= TOL
+
+
+def test_bf16_several_tokens_weight_over_4gib_runs_on_vector_alus():
+    """A bf16 call with several tokens whose codes exceed the 4 GiB that the
+    matrix-core kernels address goes to the vector-ALU kernels (tq_gemv and
+    the grouped plan) instead of failing: K = 3, g = 256, 1,400,017 x 4096
+    (4.3 GB of codes), 3 tokens, 64 sampled rows against the oracle."""
+    import torch
+    from synth import device
+    from ternary_weight_amd import tq
+    K, g, N, Kin, M = 3, 256, 1_400_017, 4096, 3
+    print("bf16 K=3 %d x %d M=%d (codes over 4 GiB)" % (N, Kin, M), flush=True)
+    seed = 0x5EED4
+    trits = torch.empty((K, N, Kin), dtype=torch.int8, device="cuda")
+    device.fill(device.K_TRITS, seed, 0, trits)
+    lo, span = gen.log_uniform_params(1e-3, 1e-1)
+    sc = torch.empty((K, N, Kin // g), dtype=torch.int16, device="cuda")
+    device.fill(device.K_LOGU_F16, seed + 1, 0, sc, a=lo, b=span)
+    x = torch.empty((M, Kin), dtype=torch.int16, device="cuda")
+    device.fill(device.K_NORMAL_BF16, seed + 2, 0, x)
+    d = tq.desc(K, g, GROUP_F16, N, Kin)
+    blob = torch.empty(tq.packed_size(d), dtype=torch.uint8, device="cuda")
+    assert tq.packed_size(d) > (1 << 32)
+    tq.pack(d, trits, sc, None, blob)
+    rows = np.sort(np.random.default_rng(3).choice(N, size=64, replace=False))
+    rows[-1] = N - 1
+    ridx = torch.from_numpy(rows).cuda()
+    t_h = trits.index_select(1, ridx).cpu().numpy()
+    s_h = sc.index_select(1, ridx).cpu().numpy().view(np.uint16)
+    x_h = x.cpu().numpy().view(np.uint16)
+    del trits
+    torch.cuda.empty_cache()
+    ref = oracle.gemv_fp(K, g, GROUP_F16, t_h, s_h, x_h, BF16)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    tq.gemv(d, blob, M, BF16, x, None, y)
+    torch.cuda.synchronize()
+    assert rel_err(y[:, ridx].cpu().numpy(), ref) <= TOL
+    y2 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    probs = tq.problems([(d, blob, x, None, y2, None)])
+    ws = torch.empty(tq.gemv_grouped_workspace_size(probs, M), dtype=torch.uint8, device="cuda")
+    plan = tq.gemv_grouped_prepare(probs, M, BF16, ws, ws.numel())
+    assert plan.family < 1000            # a vector-ALU plan
+    tq.gemv_grouped_run(plan)
+    torch.cuda.synchronize()
+    assert rel_err(y2[:, ridx].cpu().numpy(), ref) <= TOL
+    del blob, y, y2, ws
+    torch.cuda.empty_cache()
