@@ -443,6 +443,16 @@ def cpu_baseline(stack, seconds: float) -> dict:
                       "OpenMP over output rows" % (per_layer, reps, el)}
 
 
+def release_device():
+    """Wait for all queued work and return the freed buffers to the device."""
+    import gc
+    import torch
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+
+
 def spin_up(ms: float, nbytes: int = 1 << 30):
     """Keep HBM busy for about `ms` with the harness read kernel (not timed, not a step)."""
     import torch
@@ -880,7 +890,8 @@ def main():
         "secondary": secondary,
         "wall_s_timed": round(wall, 3),
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    release_device()
 
 
 # ---------------------------------------------------------------------------
@@ -918,6 +929,8 @@ def chain_spot_check(chain, blobs, norms_dev, dims) -> dict:
                                  np.array([w["scales"][0] for w in ws_], dtype=np.float32), norms,
                                  inputs.chain_input(chain))
     got = x.cpu().numpy()
+    del plan, ws, x
+    release_device()
     return {"layers": 1, "bit_exact": bool(np.array_equal(got.view(np.uint32), ref.view(np.uint32)))}
 
 
@@ -1026,7 +1039,12 @@ def main_chain(args):
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    # every launch complete and every buffer the plan points at released
+    # before the interpreter exits
+    tq.bitnet_chain_status(plan)
+    del plan, ws, x, x0, layers, norms_dev, stack
+    release_device()
 
 
 # ---------------------------------------------------------------------------
@@ -1199,7 +1217,8 @@ def main_moe(args):
         "parity_spot_check": check,
         "wall_s_timed": round(wall, 3),
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    release_device()
 
 
 # ---------------------------------------------------------------------------
@@ -1278,7 +1297,8 @@ def main_ternarize(args):
         "hbm_ceiling": ceiling,
         "parity_spot_check": check,
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    release_device()
 
 
 if __name__ == "__main__":
