@@ -33,7 +33,8 @@
  *    weight; x is [M][Kin] row-major and y is [M][N] row-major fp32.
  *  - Pointers marked "device" are HIP device pointers owned by the caller;
  *    the library keeps no reference after the call's work has run and
- *    allocates no device memory.
+ *    allocates no device memory (tq_ternarize_noalloc's fixed scratch array
+ *    aside, see there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    their kernels on it and return without waiting, except tq_pack (see
  *    there) and tq_gemv_grouped_prepare.
@@ -340,6 +341,23 @@ tq_status tq_gemm_grouped_run(const tq_grouped_plan* plan, void* stream);
 tq_status tq_ternarize_workspace_size(const tq_weight_desc* desc, size_t* bytes);
 tq_status tq_ternarize(const tq_weight_desc* desc, const float* w, const uint16_t* codebook, int8_t* trits,
                        void* scales, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tq_ternarize for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * same fit and the same results, bit for bit, with no workspace argument.
+ * TQ_SCALE_TENSOR keeps its per-row partial sums in a scratch array that
+ * the library holds in device memory, one copy per GPU for the life of the
+ * process (4 MiB): at most 262144 rows (TQ_ERR_UNSUPPORTED beyond, before
+ * anything is enqueued).  Every row the fit reads is written first in the
+ * same call, so nothing in the scratch has to start at zero; it keeps the
+ * last call's contents.  All calls on one GPU share that array: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.  The other layouts use no scratch.  No call here
+ * allocates; the rest is as tq_ternarize.
+ */
+tq_status tq_ternarize_noalloc(const tq_weight_desc* desc, const float* w, const uint16_t* codebook,
+                               int8_t* trits, void* scales, void* stream);
 
 /*
  * Decode chain: BitNet b1.58 layers run back to back for one token in one

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "tq_internal.h"
@@ -273,6 +274,38 @@ __global__ void k_tern_codec(const float* __restrict__ w, int64_t N, int64_t Kin
 
 size_t tensor_ws_bytes(int64_t N) { return (size_t)(N * 16 + 256); }
 
+// Scratch of tq_ternarize_noalloc: the per-row sums, counts and the absmean
+// of the per-tensor fit, for up to kNoallocRows rows.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// is only a stand-in; the device address comes from hipGetSymbolAddress.
+constexpr int64_t kNoallocRows = 1 << 18;
+constexpr size_t kScratchBytes = (size_t)kNoallocRows * 16 + 256;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call
+// on that device (with it current) and kept.
+tq_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    tq_status s;
+    if ((s = tq_check_hip(hipGetDevice(&dev), "tq_ternarize_noalloc device"))) return s;
+    if (dev < 0 || dev >= kMaxDevices) return tq_fail(TQ_ERR_DEVICE, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((s = tq_check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "tq_ternarize_noalloc scratch address")))
+            return s;
+        if (!p) return tq_fail(TQ_ERR_DEVICE, "tq_ternarize_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TQ_OK;
+}
+
 }  // namespace
 
 TQ_EXPORT tq_status tq_ternarize_workspace_size(const tq_weight_desc* desc, size_t* bytes)
@@ -354,4 +387,20 @@ TQ_EXPORT tq_status tq_ternarize(const tq_weight_desc* desc, const float* w, con
         hipLaunchKernelGGL(k_tern_reduce, dim3(1), dim3(64), 0, st, N, Kin, k, 1, rowsum, rownz, absmean, ps);
     }
     return tq_check_launch("tq_ternarize") ? TQ_ERR_DEVICE : tq_ok();
+}
+
+TQ_EXPORT tq_status tq_ternarize_noalloc(const tq_weight_desc* desc, const float* w, const uint16_t* codebook,
+                                         int8_t* trits, void* scales, void* stream)
+{
+    tq_layout L;
+    tq_status s = tq_check_desc(desc, &L);
+    if (s) return s;
+    if (L.layout != TQ_SCALE_TENSOR)   // these fits use no scratch
+        return tq_ternarize(desc, w, codebook, trits, scales, nullptr, 0, stream);
+    if (L.N > kNoallocRows)
+        return tq_fail(TQ_ERR_UNSUPPORTED, "tq_ternarize_noalloc: %lld rows exceed the %lld its scratch holds",
+                       (long long)L.N, (long long)kNoallocRows);
+    void* ws = nullptr;
+    if ((s = scratch_of_current_device(&ws))) return s;
+    return tq_ternarize(desc, w, codebook, trits, scales, ws, kScratchBytes, stream);
 }

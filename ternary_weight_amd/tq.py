@@ -99,6 +99,7 @@ SIGNATURES = {
     "tq_gemm_grouped_run": ([ctypes.POINTER(tq_grouped_plan), _VP], _I32),
     "tq_ternarize_workspace_size": ([_DESC, ctypes.POINTER(ctypes.c_size_t)], _I32),
     "tq_ternarize": ([_DESC, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP], _I32),
+    "tq_ternarize_noalloc": ([_DESC, _VP, _VP, _VP, _VP, _VP], _I32),
     "tq_bitnet_chain_workspace_size": ([ctypes.POINTER(tq_bitnet_dims), _I32, ctypes.POINTER(ctypes.c_size_t)],
                                        _I32),
     "tq_bitnet_chain_prepare": ([ctypes.POINTER(tq_bitnet_dims), ctypes.POINTER(tq_bitnet_layer), _I32, _VP,
@@ -315,3 +316,9 @@ def ternarize_workspace_size(d: tq_weight_desc) -> int:
 def ternarize(d: tq_weight_desc, w, trits, scales, codebook=None, workspace=None, workspace_bytes=0, stream=None):
     _check(lib().tq_ternarize(ctypes.byref(d), _ptr(w), _ptr(codebook), _ptr(trits), _ptr(scales), _ptr(workspace),
                               workspace_bytes, _stream(stream)), "tq_ternarize")
+
+
+def ternarize_noalloc(d: tq_weight_desc, w, trits, scales, codebook=None, stream=None):
+    """tq_ternarize without a workspace: the library's own scratch array (no allocation)."""
+    _check(lib().tq_ternarize_noalloc(ctypes.byref(d), _ptr(w), _ptr(codebook), _ptr(trits), _ptr(scales),
+                                      _stream(stream)), "tq_ternarize_noalloc")
