@@ -67,8 +67,12 @@ def parse():
                     help="int8 path as one call: fp32 activations quantised inside the grouped product "
                          "(TQ_F32_Q8); default is two launches, the batched quantiser then the product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="cfg2 at one token: leave out the Llama-8B-shaped one-token stacks (cfg3, cfg4) that the "
+                         "line otherwise carries under 'legs'")
     ap.add_argument("--no-check", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=3.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds of oracle work per CPU baseline (a bounded sample of the workload)")
     ap.add_argument("--secondary", action="store_true",
                     help="decode and prefill stacks: add secondary timings after the timed region (single passes "
                          "of the product, cold after a 1 GiB evicting read and warm, the quantiser alone, the "
@@ -373,12 +377,22 @@ def spot_check(stack, n_proj=3, rows=64) -> dict:
             "bit_exact" if case.x_type == I8 else "max_rel_err": exact if case.x_type == I8 else worst}
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle baseline: the process's CPU share as the
+    job sets it (OMP_NUM_THREADS), else every core the process may run on."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    return n if n > 0 else len(os.sched_getaffinity(0))
+
+
 def cpu_baseline_prefill(stack, seconds: float, tokens: int = 32) -> dict:
     """The oracle on the host cores: the first projection of the stack for its first `tokens` tokens,
     repeated for about `seconds`, as operations per second."""
     import oracle
     case = stack.case
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads = oracle_threads()
     orc = oracle.default()
     layer, p, name, n, kin = stack.projs[0]
     h = inputs.projection(case, layer, p, n, kin, M=tokens)
@@ -401,20 +415,33 @@ def cpu_baseline_prefill(stack, seconds: float, tokens: int = 32) -> dict:
                       "%.1f s; C oracle, OpenMP over output rows" % (name, n, kin, K, tokens, reps, el)}
 
 
+def canonical_inputs(case, layer, p, n, kin, M) -> dict:
+    """Host copies of the canonical arrays of one projection, drawn by the
+    device copy of the seeded generator (bit-identical to the host one, which
+    is too slow for whole layers of the 8B-shaped stacks)."""
+    d = device.projection(case, layer, p, n, kin, M=M)
+    h = {"trits": d["trits"].cpu().numpy()}
+    sc = d["scales"].cpu().numpy()
+    h["scales"] = sc.view(np.uint16) if case.layout == GROUP_F16 else sc
+    h["codebook"] = None if d["codebook"] is None else d["codebook"].cpu().numpy().view(np.uint16)
+    x = d["x"].cpu().numpy()
+    h["x"] = x.view(np.uint16) if case.x_type == BF16 else x
+    return h
+
+
 def cpu_baseline(stack, seconds: float) -> dict:
     """The oracle on the host cores, over whole layers of the same stack."""
     import oracle
     case, M = stack.case, stack.M
     if stack.prefill:
         return cpu_baseline_prefill(stack, seconds)
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads = oracle_threads()
     orc = oracle.default()
-    # layer 0 of the stack (its first four projections for the 8B-shaped stacks, to keep the
-    # host-side input generation short)
-    per_layer = len(case.model["proj"]) if case.planes == 1 else 4
+    # layer 0 of the stack, every projection
+    per_layer = len(case.model["proj"])
     layer_inputs = []
     for (layer, p, _, n, kin) in stack.projs[:per_layer]:
-        layer_inputs.append((n, kin, inputs.projection(case, layer, p, n, kin, M=M)))
+        layer_inputs.append((n, kin, canonical_inputs(case, layer, p, n, kin, M)))
     done_bytes, t0, reps = 0, time.perf_counter(), 0
     layer_bytes = 0
     K, g, layout = case.planes, case.group, case.layout
@@ -762,19 +789,39 @@ def main():
     if args.config.startswith("ternarize"):
         main_ternarize(args)
         return
+    M = args.M if args.config in ("cfg2", "cfg3", "cfg4") else CASES[args.config].M
+    out = measure_stack(args, args.config, M, fused=args.fused, waves=args.waves, row_blocks=args.row_blocks,
+                        spin_up_ms=args.spin_up_ms, secondary=args.secondary, ceiling=args.ceiling)
+    if args.config == "cfg2" and M == 1 and not args.no_legs:
+        # the metric names both shapes: the Llama-8B-shaped one-token stacks
+        # are measured the same way, after the BitNet line's own timed region
+        out["legs"] = {}
+        for name in ("cfg3", "cfg4"):
+            leg = measure_stack(args, name, 1, fused=False, waves=0, row_blocks=0, spin_up_ms=args.spin_up_ms,
+                                secondary=False, ceiling=False)
+            out["legs"][name] = {k: leg[k] for k in ("value", "unit", "ms_per_step", "dtype", "tok_per_s_equiv",
+                                                     "gemv_us", "roofline", "cold_pass", "cpu_baseline",
+                                                     "parity_spot_check", "steps", "warmup")}
+            out["legs"][name]["workload"] = leg["config"]["workload"]
+            out["legs"][name]["M"] = 1
+    print(json.dumps(out), flush=True)
+    release_device()
+
+
+def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, secondary, ceiling) -> dict:
+    """Build one stack, time args.steps steps after args.warmup, and return its bench line."""
     import torch
-    case = CASES[args.config]
-    M = args.M if args.config in ("cfg2", "cfg3", "cfg4") else case.M
+    case = CASES[config]
     t_build = time.perf_counter()
-    stack = Stack(case, M, fused=args.fused)
-    stack.prepare(args.waves, args.row_blocks)
+    stack = Stack(case, M, fused=fused)
+    stack.prepare(waves, row_blocks)
     build_s = time.perf_counter() - t_build
     print("built %s: %d projections, %.1f MB packed, plan %d items x %d blocks x %d waves (%.1f s)"
-          % (args.config, len(stack.projs), stack.blob_bytes / 1e6, stack.plan.n_items,
+          % (config, len(stack.projs), stack.blob_bytes / 1e6, stack.plan.n_items,
              stack.plan.row_blocks, stack.plan.waves, build_s), file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    spin_up(args.spin_up_ms)
+    spin_up(spin_up_ms)
     for _ in range(args.warmup):
         stack.quantize()
         stack.gemv()
@@ -821,23 +868,27 @@ def main():
         achieved = gbytes / (gemv_avg / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
 
-    ceiling = hbm_ceiling() if args.ceiling else None
+    ceil = hbm_ceiling() if ceiling else None
     check = None if args.no_check else spot_check(stack)
     cpu = None if args.no_cpu_baseline else cpu_baseline(stack, args.cpu_seconds)
-    secondary = None
-    if args.secondary:
-        cold = single_passes(stack.gemv, evict_bytes=1 << 30)
+    # the product alone, one pass at a time, each after an untimed 1 GiB read
+    # of other memory (more than the 256 MiB MALL), so that no code comes from
+    # a cache: the cold figure beside the back-to-back one
+    cold = single_passes(stack.gemv, evict_bytes=1 << 30)
+    cold["frac_of_hbm_peak"] = (None if stack.prefill else
+                                round(gbytes / (cold["median_us"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4))
+    sec = None
+    if secondary:
         warm = single_passes(stack.gemv)
-        for t in (cold, warm):
-            t["frac_of_hbm_peak"] = (None if stack.prefill else
-                                     round(gbytes / (t["median_us"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4))
-        secondary = {"cold_product": cold, "single_pass_product": warm}
+        warm["frac_of_hbm_peak"] = (None if stack.prefill else
+                                    round(gbytes / (warm["median_us"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4))
+        sec = {"single_pass_product": warm}
         if stack.x_q is not None:
-            secondary["act_quant_us"] = round(timed_us(stack.quantize), 2)
+            sec["act_quant_us"] = round(timed_us(stack.quantize), 2)
         if not stack.prefill:
-            secondary["single_launches"] = graph_of_single_launches(stack)
+            sec["single_launches"] = graph_of_single_launches(stack)
         if not args.no_cpu_baseline:
-            secondary["cpu_one_thread"] = cpu_one_thread(stack)
+            sec["cpu_one_thread"] = cpu_one_thread(stack)
 
     out = {
         "metric": METRIC_PREFILL if stack.prefill else METRIC,
@@ -885,11 +936,15 @@ def main():
                 "effective_hbm_GBs": round(gbytes / (gemv_avg / 1e3) / 1e9, 1)} if stack.prefill else {}),
         },
         "cpu_baseline": cpu,
-        "hbm_ceiling": ceiling,
+        "hbm_ceiling": ceil,
         "parity_spot_check": check,
-        "secondary": secondary,
+        "cold_pass": cold,
+        "secondary": sec,
         "wall_s_timed": round(wall, 3),
     }
+    del stack
+    release_device()
+    return out
     print(json.dumps(out), flush=True)
     release_device()
 
@@ -1084,7 +1139,7 @@ def moe_cpu_baseline(stack, seconds: float) -> dict:
     """The oracle on the host cores over the routed experts of layer 0, in order."""
     import oracle
     moe = stack.moe
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    threads = oracle_threads()
     orc = oracle.default()
     hid, inter = inputs.moe_hidden(moe, 0), inputs.moe_inter(moe, 0)
     route = inputs.moe_expert_rows(moe, 0)
