@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 from synth import device, gen, inputs  # noqa: E402
 from synth.configs import BF16, CASES, CHAINS, CODEBOOK, F32, GROUP_F16, I8, TENSOR  # noqa: E402
 
+CODEBOOK_B3 = 3   # the codec with compact base-3 codes (tq.h)
+
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "ternary_weight_amd", "csrc")
@@ -60,7 +62,11 @@ def parse():
     ap.add_argument("--moe-x", choices=["i8", "bf16", "f32"], default="i8",
                     help="moe: activations (i8: fp32 rows quantised per token by the quantiser, or inside "
                          "the product with --fused)")
-    ap.add_argument("--M", type=int, default=1, help="decode stacks (cfg2-4): tokens per step, 1 to 16")
+    ap.add_argument("--M", type=int, default=1, help="decode stacks (cfg2-4): tokens per step, 1 to 16 (more: "
+                                                     "the prefill kernels)")
+    ap.add_argument("--b3", action="store_true",
+                    help="cfg4: pack the codec with compact base-3 codes (TQ_SCALE_CODEBOOK_B3) instead of two-bit "
+                         "digit planes")
     ap.add_argument("--waves", type=int, default=0, help="waves per 64-row block in the grouped launch")
     ap.add_argument("--row-blocks", type=int, default=0, help="64-row blocks per workgroup")
     ap.add_argument("--fused", action="store_true",
@@ -88,17 +94,20 @@ def parse():
 class Stack:
     """Every projection of a case packed in one slab, with its activations and outputs."""
 
-    def __init__(self, case, M: int, fused: bool = True):
+    def __init__(self, case, M: int, fused: bool = True, b3: bool = False):
         import torch
         from ternary_weight_amd import tq
         self.case, self.M = case, M
+        # the codec's weights packed with compact base-3 codes (same canonical arrays)
+        self.b3 = b3 and case.layout == CODEBOOK
+        self.pack_layout = CODEBOOK_B3 if self.b3 else case.layout
         self.prefill = M > 16          # matrix-core product (tq_gemm) instead of the decode kernels
         # int8 activations: quantise inside the product (one launch per step) or as a separate call
         self.fused = fused and case.x_type == I8 and not self.prefill
         self.run_type = tq.F32_Q8 if self.fused else case.x_type
         self.projs = case.projections()
-        K, g, layout = case.planes, case.group, case.layout
-        ncb = inputs.N_CODEBOOK if layout == CODEBOOK else 0
+        K, g, layout = case.planes, case.group, self.pack_layout
+        ncb = inputs.N_CODEBOOK if case.layout == CODEBOOK else 0
         self.descs = [tq.desc(K, g, layout, n, kin, n_codebook=ncb) for (_, _, _, n, kin) in self.projs]
         sizes = [tq.packed_size(d) for d in self.descs]
         offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])])
@@ -176,7 +185,8 @@ class Stack:
         xsz = 4 if self.fused else {I8: 1, BF16: 2, F32: 4}[self.case.x_type]
         total = 0
         for (_, _, _, n, kin) in self.projs:
-            b = K * n * kin // 4                               # packed trits, 2 bits each
+            # packed trits, 2 bits each; compact base-3 codec: 10 bits per two weights
+            b = 5 * n * kin // 8 if self.b3 else K * n * kin // 4
             if layout == TENSOR:
                 b += 4 * K
             elif layout == GROUP_F16:
@@ -328,6 +338,8 @@ class MoeStack:
 
 def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
     """The kernel a grouped decode plan launches (as rocprofv3 names it)."""
+    if layout == CODEBOOK_B3:
+        planes = 1              # the compact codec's kernels take one combined value per weight
     if plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
         ks = 32 if layout == TENSOR or group % 32 == 0 else 16
         return "k_gemm_grouped<%d, %d, %d, 1, 4, %d, 1>" % (run_type, layout, planes, ks)
@@ -791,7 +803,7 @@ def main():
         return
     M = args.M if args.config in ("cfg2", "cfg3", "cfg4") else CASES[args.config].M
     out = measure_stack(args, args.config, M, fused=args.fused, waves=args.waves, row_blocks=args.row_blocks,
-                        spin_up_ms=args.spin_up_ms, secondary=args.secondary, ceiling=args.ceiling)
+                        spin_up_ms=args.spin_up_ms, secondary=args.secondary, ceiling=args.ceiling, b3=args.b3)
     if args.config == "cfg2" and M == 1 and not args.no_legs:
         # the metric names both shapes: the Llama-8B-shaped one-token stacks
         # are measured the same way, after the BitNet line's own timed region
@@ -808,12 +820,12 @@ def main():
     release_device()
 
 
-def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, secondary, ceiling) -> dict:
+def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, secondary, ceiling, b3=False) -> dict:
     """Build one stack, time args.steps steps after args.warmup, and return its bench line."""
     import torch
     case = CASES[config]
     t_build = time.perf_counter()
-    stack = Stack(case, M, fused=fused)
+    stack = Stack(case, M, fused=fused, b3=b3)
     stack.prepare(waves, row_blocks)
     build_s = time.perf_counter() - t_build
     print("built %s: %d projections, %.1f MB packed, plan %d items x %d blocks x %d waves (%.1f s)"
@@ -856,14 +868,15 @@ def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, seconda
     gbytes, qbytes = stack.gemv_bytes(), stack.quant_bytes()
     if stack.prefill:
         step = 64 if case.x_type == I8 else (32 if case.layout == TENSOR or case.group % 32 == 0 else 16)
-        kernel_name = "k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, case.layout, case.planes, step)
+        kernel_name = ("k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, CODEBOOK_B3, 1, 16) if stack.b3 else
+                       "k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, case.layout, case.planes, step))
         ops = stack.ops()
         value = ops / (ms_step / 1e3) / 1e12
         achieved = ops / (gemv_avg / 1e3) / 1e12
         peak = MFMA_PEAK_I8_TOPS if case.x_type == I8 else MFMA_PEAK_BF16_TFLOPS
         unit = "TOP/s" if case.x_type == I8 else "TFLOP/s"
     else:
-        kernel_name = decode_kernel_name(stack.plan, stack.run_type, case.layout, case.planes, case.group)
+        kernel_name = decode_kernel_name(stack.plan, stack.run_type, stack.pack_layout, case.planes, case.group)
         value = (gbytes + qbytes) / (ms_step / 1e3) / 1e9
         achieved = gbytes / (gemv_avg / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
@@ -910,7 +923,8 @@ def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, seconda
             "M": M,
             "planes": case.planes,
             "group": case.group,
-            "scale_layout": {TENSOR: "tensor", GROUP_F16: "group_f16", CODEBOOK: "codebook"}[case.layout],
+            "scale_layout": {TENSOR: "tensor", GROUP_F16: "group_f16", CODEBOOK: "codebook",
+                             CODEBOOK_B3: "codebook_b3"}[stack.pack_layout],
             "step": ("act-quant of every projection input + one grouped MFMA GEMM launch over the stack"
                      if case.x_type == I8 else "one grouped MFMA GEMM launch over the stack") if stack.prefill else
                     ("one grouped launch over the stack; fp32 inputs quantised per token to int8 "

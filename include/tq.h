@@ -73,7 +73,16 @@ typedef enum tq_status {
 typedef enum tq_scale_layout {
     TQ_SCALE_TENSOR = 0,     /* canonical scales: fp32 s[K]                           */
     TQ_SCALE_GROUP_F16 = 1,  /* canonical scales: f16 bits s[K][N][Kin/g]             */
-    TQ_SCALE_CODEBOOK = 2    /* canonical scales: uint8 idx[N][Kin/g] into f16 cb[]   */
+    TQ_SCALE_CODEBOOK = 2,   /* canonical scales: uint8 idx[N][Kin/g] into f16 cb[]   */
+    TQ_SCALE_CODEBOOK_B3 = 3 /* the codec of TQ_SCALE_CODEBOOK (same canonical arrays,
+                                same results) with its codes packed compactly in base 3:
+                                the K = 3 digits of a weight are one base-27 value v in
+                                [-13, 13], and two neighbouring weights one 10-bit code
+                                (v0 mod 27) + 27 (v1 mod 27) < 729, so 5 bits per weight
+                                where the two-bit planes take 6 (the Tritium page's
+                                feature list names "compact B3 packing"; this is our
+                                reading of it for the codec).  planes must be 3.
+                                Decode and prefill take bf16 activations only.         */
 } tq_scale_layout;
 
 typedef enum tq_dtype {

@@ -49,7 +49,7 @@ tq_status tq_check_desc(const tq_weight_desc* d, tq_layout* L)
     if (!d) return tq_fail(TQ_ERR_ARG, "desc is NULL");
     if (d->planes < 1 || d->planes > 4)
         return tq_fail(TQ_ERR_ARG, "planes = %d, must be 1..4", d->planes);
-    if (d->scale_layout < TQ_SCALE_TENSOR || d->scale_layout > TQ_SCALE_CODEBOOK)
+    if (d->scale_layout < TQ_SCALE_TENSOR || d->scale_layout > TQ_SCALE_CODEBOOK_B3)
         return tq_fail(TQ_ERR_ARG, "scale_layout = %d is not a tq_scale_layout", d->scale_layout);
     if (d->out_features < 0 || d->in_features < 0)
         return tq_fail(TQ_ERR_ARG, "negative shape %lld x %lld", (long long)d->out_features,
@@ -67,8 +67,11 @@ tq_status tq_check_desc(const tq_weight_desc* d, tq_layout* L)
             return tq_fail(TQ_ERR_SHAPE, "in_features = %lld is not a multiple of group %d",
                            (long long)d->in_features, d->group);
     }
-    if (d->scale_layout == TQ_SCALE_CODEBOOK && (d->n_codebook < 1 || d->n_codebook > TQ_CB_SLOTS))
+    if (tq_is_codebook(d->scale_layout) && (d->n_codebook < 1 || d->n_codebook > TQ_CB_SLOTS))
         return tq_fail(TQ_ERR_ARG, "n_codebook = %d, must be 1..%d", d->n_codebook, TQ_CB_SLOTS);
+    if (d->scale_layout == TQ_SCALE_CODEBOOK_B3 && d->planes != 3)
+        return tq_fail(TQ_ERR_UNSUPPORTED, "TQ_SCALE_CODEBOOK_B3 packs three digits per weight (planes = %d)",
+                       d->planes);
     if (L) tq_layout_make(d, L);
     return TQ_OK;
 }

@@ -82,9 +82,34 @@ __device__ __forceinline__ u32x2 buffer_load<u32x2, 0>(__amdgpu_buffer_rsrc_t r,
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 template <>
+__device__ __forceinline__ u32x2 buffer_load<u32x2, kCacheNT>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCacheNT));
+}
+template <>
 __device__ __forceinline__ uint32_t buffer_load<uint32_t, 0>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// The pair-code table of the compact base-3 codec: entry e (10-bit code),
+// copy c at byte offset e * 64 + c * 4 holds bf16(v0) | bf16(v1) << 16 for
+// e = (v0 mod 27) + 27 (v1 mod 27) < 729, and zero for the codes never
+// written.  Lane l reads copy l % 16.
+constexpr int kB3Copies = 16;
+__device__ __forceinline__ void fill_b3_lut(uint8_t* lut)
+{
+    for (int i = threadIdx.x; i < 1024 * kB3Copies; i += blockDim.x) {
+        const uint32_t e = (uint32_t)i / kB3Copies, c = (uint32_t)i % kB3Copies;
+        uint32_t v = 0;
+        if (e < (uint32_t)TQ_B3_CODES) {
+            const int a = (int)(e % 27u), b = (int)(e / 27u);
+            // small integers: the fp32 value's upper half is the exact bf16
+            v = (__float_as_uint((float)(a > 13 ? a - 27 : a)) >> 16) |
+                (__float_as_uint((float)(b > 13 ? b - 27 : b)) & 0xFFFF0000u);
+        }
+        *(LDS_AS uint32_t*)((LDS_AS uint8_t*)lut + e * (4 * kB3Copies) + c * 4) = v;
+    }
 }
 
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }

@@ -64,7 +64,7 @@ tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const 
     const uint8_t* b = (const uint8_t*)blob;
     P.codes = b + L.codes_off;
     P.scales = b + L.scales_off;
-    P.cb = L.layout == TQ_SCALE_CODEBOOK ? (const uint16_t*)(b + L.cb_off) : nullptr;
+    P.cb = tq_is_codebook(L.layout) ? (const uint16_t*)(b + L.cb_off) : nullptr;
     P.x = x;
     P.x_scale = x_scale;
     P.y = y;
@@ -243,7 +243,7 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
     // bf16: per-wave items, the slices of a row block in one workgroup whose
     // 16 waves share the trit table (measured ahead of workgroup items of 16
     // row blocks; with int8 activations the two measured alike)
-    const bool wave_mode = sliced && !hinted && x_type == TQ_BF16 && layout0 != TQ_SCALE_CODEBOOK;
+    const bool wave_mode = sliced && !hinted && x_type == TQ_BF16 && !tq_is_codebook(layout0);
     const int wave_wg = TQ_BF16_WAVE_WG;
     if (count > 0 && M > 0) {
         family = tq_gemv_family(x_type, layout0, K0, (int)std::min<int64_t>(M, pass));

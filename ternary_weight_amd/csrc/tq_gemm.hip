@@ -16,6 +16,7 @@ int gemm_row(const tq_layout& L, int x_type)
 {
     if (L.layout == TQ_SCALE_TENSOR) return TQ_GEMM_ROW_TENSOR;
     if (L.layout == TQ_SCALE_CODEBOOK) return TQ_GEMM_ROW_CODEBOOK;
+    if (L.layout == TQ_SCALE_CODEBOOK_B3) return TQ_GEMM_ROW_CODEBOOK_B3;
     if (x_type == TQ_BF16 && L.g % 32 != 0) return TQ_GEMM_ROW_GROUP16;
     return TQ_GEMM_ROW_GROUP;
 }
@@ -45,8 +46,8 @@ const tq_gemm_kernel* gemm_kernel(const tq_layout& L, int x_type, int64_t M)
     // including the rows a partial tile reads past M and N
     const int64_t lim = (int64_t)UINT32_MAX;
     const int64_t xb = (M + 16 * k->fm * k->wm) * L.Kin * (x_type == TQ_I8 ? 1 : 2);
-    const int64_t cb = (L.NB + 4 * k->fn) * L.NC * L.K * 1024;
-    const int64_t sb = (L.NB + 4 * k->fn) * (L.layout == TQ_SCALE_CODEBOOK ? L.NID : L.NGD * L.K) * 256;
+    const int64_t cb = (L.NB + 4 * k->fn) * L.NC * (L.layout == TQ_SCALE_CODEBOOK_B3 ? TQ_B3_CHUNK_BYTES : L.K * 1024);
+    const int64_t sb = (L.NB + 4 * k->fn) * (tq_is_codebook(L.layout) ? L.NID : L.NGD * L.K) * 256;
     if (xb > lim || cb > lim || sb > lim) {
         tq_fail(TQ_ERR_UNSUPPORTED, "tq_gemm: an operand exceeds 4 GiB (x %lld, codes %lld bytes)", (long long)xb,
                 (long long)cb);

@@ -11,6 +11,7 @@ const tq_gemm_kernel (*tq_gemm_table_bf16())[4]
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 4, 4, 4, 4, 32, 2),
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 4, 4, 4, 4, 16, 2),
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_CODEBOOK, 4, 4, 4, 4, 16, 2),
+        TQ_GEMM_ROW_B3(4, 4, 2),
     };
     return t;
 }

@@ -10,6 +10,7 @@ const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4]
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 1, 4, 1, 4, 32, 1),
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 1, 4, 1, 4, 16, 1),
         TQ_GEMM_ROW(TQ_BF16, TQ_SCALE_CODEBOOK, 1, 4, 1, 4, 16, 1),
+        TQ_GEMM_ROW_B3(1, 4, 1),
     };
     return t;
 }

@@ -12,6 +12,7 @@ const tq_gemm_kernel (*tq_gemm_table_i8())[4]
         TQ_GEMM_ROW(TQ_I8, TQ_SCALE_GROUP_F16, 4, 4, 4, 4, 64, 2),
         TQ_GEMM_NONE,    // groups of 16 are below the 64-column int8 step
         TQ_GEMM_NONE,
+        TQ_GEMM_NONE,    // the compact base-3 codec takes bf16 activations
     };
     return t;
 }

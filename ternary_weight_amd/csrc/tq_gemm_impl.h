@@ -170,7 +170,8 @@ struct Cursor {
 };
 
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
-__device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, const LDS_AS float* cb_lds)
+__device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, const LDS_AS float* cb_lds,
+                                          const LDS_AS uint8_t* b3_lut)
 {
     using MF = Mfma<XT, KS>;
     using Part = typename MF::Part;
@@ -207,8 +208,17 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // Only the wave touches its stage, and a wave's LDS accesses complete in
     // order, so no barrier is needed.
     constexpr bool kWave = !kLds && XT == TQ_BF16 && FN == 4;
-    constexpr int CWW = KS / 16;                          // code dwords of a row per step
-    constexpr int WST = 64 * CWW + (kWord ? 64 : 0);      // dwords per wave and stage
+    // The codec's compact base-3 codes (CODEBOOK_B3): one combined value per
+    // weight (K = 1 here), 16-column steps of 80 bits per row -- dwords
+    // (5 d) / 2 .. + 2 of the 64-column chunk's ten, d = step % 4 -- staged
+    // per wave, and decoded through the pair-code table: one MFMA and one
+    // codebook scale per 16-column group, in place of one per digit plane.
+    constexpr bool kB3 = LAYOUT == TQ_SCALE_CODEBOOK_B3;
+    constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || kB3;
+    static_assert(!kB3 || (kWave && K == 1 && KS == 16), "compact base-3 codes: the per-wave stage, 16-column steps");
+    constexpr int CWW = kB3 ? 3 : KS / 16;                // code dwords of a row per step
+    constexpr int WST = 64 * CWW + (kWord ? 64 : 0) + (kB3 ? 4 : 0);   // dwords per wave and stage (B3: a
+                                                                      // pad dword read past the last row)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -219,9 +229,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     const int n0 = tn * (16 * FN * (4 / WM)) + (wave / WM) * (16 * FN);
 
     const int64_t xbytes = (int64_t)M * Kin * ESZ;
-    const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, (int64_t)NB * NC * K * 1024);
-    const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)NB * P.NID * 256
-                                                                                 : (int64_t)NB * P.NGD * K * 256);
+    const __amdgpu_buffer_rsrc_t rc = rsrc(P.codes, kB3 ? (int64_t)NB * NC * TQ_B3_CHUNK_BYTES : (int64_t)NB * NC * K * 1024);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, kCb ? (int64_t)NB * P.NID * 256 : (int64_t)NB * P.NGD * K * 256);
     uint32_t xoff[FM], coff[FN], soff[FN], cwoff = 0, swoff = 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) xoff[fm] = ((uint32_t)(m0 + 16 * fm + r) * Kin + q * QCOLS) * ESZ;
@@ -265,15 +274,33 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     for (int fn = 0; fn < FN; ++fn) {
         const uint32_t n = n0 + 16 * fn + r;
         coff[fn] = ((n >> 6) * NC * K * 64 + (n & 63)) * 16 + MF::dword_lane(q) * 4;
-        soff[fn] = LAYOUT == TQ_SCALE_CODEBOOK ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4
-                                               : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
+        soff[fn] = kCb ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4 : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
     }
+    uint32_t cwoff2 = 0;   // B3: the lane's offset in its block's third part (dwords 8, 9)
     if constexpr (kWave) {
         const uint32_t n = n0 + lane;                      // n0 is a multiple of 64
-        cwoff = ((n >> 6) * NC * K * 64 + (n & 63)) * 16;
-        swoff = LAYOUT == TQ_SCALE_CODEBOOK ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4
-                                            : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
+        if constexpr (kB3) {
+            // the block offset goes in the lane's offset, so that a block past
+            // N is past the resource's size and reads zeros
+            cwoff = (n >> 6) * NC * TQ_B3_CHUNK_BYTES + (n & 63) * 16;
+            cwoff2 = (n >> 6) * NC * TQ_B3_CHUNK_BYTES + 2048 + (n & 63) * 8;
+        } else {
+            cwoff = ((n >> 6) * NC * K * 64 + (n & 63)) * 16;
+        }
+        swoff = kCb ? ((n >> 6) * P.NID * 64 + (n & 63)) * 4 : ((n >> 6) * P.NGD * K * 64 + (n & 63)) * 4;
     }
+    // B3: where lane (r, q)'s 20 bits (columns 4q .. 4q + 3 of the step) sit
+    // in its row's three staged dwords -- bit 16 (d % 2) + 20 q
+    uint32_t b3_lo[2] = {0, 0}, b3_sh[2] = {0, 0};
+    if constexpr (kB3) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const uint32_t o = 16u * par + 20u * (uint32_t)q;
+            b3_lo[par] = o >> 5;
+            b3_sh[par] = o & 31u;
+        }
+    }
+    const uint32_t b3_copy = kB3 ? (uint32_t)(lane % 16) * 4u : 0u;
     __shared__ __attribute__((aligned(16))) uint32_t wlds[kWave ? 2 : 1][kWave ? 4 * WST : 4];
     LDS_AS uint32_t* const wst0 = (LDS_AS uint32_t*)wlds[0] + (kWave ? wave * WST : 0);
     LDS_AS uint32_t* const wst1 = (LDS_AS uint32_t*)wlds[kWave ? 1 : 0] + (kWave ? wave * WST : 0);
@@ -326,6 +353,17 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             } else {
                 w[0] = buffer_load<uint32_t>(rc, ccoff, cs);
             }
+        } else if constexpr (kB3) {
+            // dwords D0 .. D0 + 2 of the step's chunk: 0..7 in the two 16-byte
+            // parts (lane * 16), 8..9 in the third (lane * 8)
+            const uint32_t chunk = (uint32_t)ks >> 2, d = (uint32_t)ks & 3u, D0 = (5u * d) >> 1;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const uint32_t D = D0 + i;
+                const bool third = D >= 8;
+                const uint32_t so = chunk * TQ_B3_CHUNK_BYTES + (third ? (D - 8) * 4 : (D >> 2) * 1024 + (D & 3) * 4);
+                w[i] = buffer_load<uint32_t>(rc, third ? cwoff2 : cwoff, so);
+            }
         } else if constexpr (kWave) {
             if constexpr (CWW == 2) {
                 const u32x2 v = buffer_load<u32x2>(rc, cwoff, cs);
@@ -339,7 +377,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             for (int fn = 0; fn < WREG; ++fn) w[fn] = buffer_load<uint32_t>(rc, coff[fn], cs);
         }
         if (kWord) {   // the block's word, with every step (no branch around a load)
-            const uint32_t ss = LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(c.seg / 6) * 256
+            const uint32_t ss = kCb ? (uint32_t)(c.seg / 6) * 256
                                                             : ((uint32_t)(c.seg >> 1) * K + c.k) * 256;
             if constexpr (kWave) {
                 sw[0] = buffer_load<uint32_t>(rs, swoff, ss);
@@ -347,6 +385,20 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) sw[fn] = buffer_load<uint32_t>(rs, soff[fn], ss);
             }
+        }
+    };
+    // the weight operand of one fragment: the codes' decode, or (B3) two
+    // pair-code table reads for the lane's 20 bits -- columns 4q, 4q + 1 and
+    // 4q + 2, 4q + 3, each a bf16 pair in column order
+    auto decode = [&](uint32_t wv) -> Frag {
+        if constexpr (kB3) {
+            const uint32_t a0 = ((wv & 0x3FFu) << 6) | b3_copy, a1 = (((wv >> 10) & 0x3FFu) << 6) | b3_copy;
+            Frag f;
+            f[0] = *(const LDS_AS uint32_t*)(b3_lut + a0);
+            f[1] = *(const LDS_AS uint32_t*)(b3_lut + a1);
+            return f;
+        } else {
+            return MF::decode(wv, q);
         }
     };
     auto compute = [&](const Cursor& c, const Frag (&a)[FM], const uint32_t (&w)[FN], const uint32_t (&swr)[SREG],
@@ -357,14 +409,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         if (!kDirect && c.j == 0) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const Frag b = MF::decode(w[fn], q);
+                const Frag b = decode(w[fn]);
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, Part{0, 0, 0, 0});
             }
         } else {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const Frag b = MF::decode(w[fn], q);
+                const Frag b = decode(w[fn]);
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm) part[fm][fn] = MF::run(a[fm], b, part[fm][fn]);
             }
@@ -379,6 +431,9 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         for (int fn = 0; fn < FN; ++fn) {
             if (LAYOUT == TQ_SCALE_TENSOR) {
                 sc[fn] = ld_uniform(((const float*)P.scales) + c.k) * MF::kScale;
+            } else if (kB3) {
+                // the table holds the combined values exactly: the group's scale alone
+                sc[fn] = cb_lds[(sw[fn] >> (5 * (c.seg % 6))) & 31u];
             } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
                 // digit plane k weighs 3^(K-1-k); the group's scale is cb[idx[n][group]]
                 const uint32_t idx = (sw[fn] >> (5 * (c.seg % 6))) & 31u;
@@ -430,7 +485,12 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // writes row l's code dwords and scale word; the fragments are read back
     // in the MFMA layout, row 16 fn + r, the lane group's dword
     auto wave_write = [&](int stage, const uint32_t (&w)[WREG], const uint32_t (&sw)[SREG]) {
-        if constexpr (kWave) {
+        if constexpr (kB3) {
+            LDS_AS uint32_t* st = stage ? wst1 : wst0;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) st[3 * lane + i] = w[i];   // stride 3: no bank conflicts
+            st[64 * CWW + lane] = sw[0];
+        } else if constexpr (kWave) {
             LDS_AS uint32_t* st = stage ? wst1 : wst0;
             if constexpr (CWW == 2) {
                 *(LDS_AS u32x2*)(st + 2 * lane) = u32x2{w[0], w[CWW - 1]};
@@ -441,7 +501,17 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         }
     };
     auto wave_read = [&](int stage, uint32_t (&w)[FN]) {
-        if constexpr (kWave) {
+        if constexpr (kB3) {
+            // the stage of step s is s % 2, and the step's 80 bits start at
+            // bit 16 (s % 2) of its first staged dword: the lane's 20 bits
+            const LDS_AS uint32_t* st = stage ? wst1 : wst0;
+            const uint32_t lo = b3_lo[stage], sh = b3_sh[stage];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint32_t base = (16 * fn + r) * 3 + lo;
+                w[fn] = __builtin_amdgcn_alignbit(st[base + 1], st[base], sh);
+            }
+        } else if constexpr (kWave) {
             const LDS_AS uint32_t* st = stage ? wst1 : wst0;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) w[fn] = st[(16 * fn + r) * CWW + MF::dword_lane(q)];
@@ -524,22 +594,29 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     }
 }
 
-// The codebook as fp32 in LDS (codec layout only).
+// The codebook as fp32 in LDS (codec layouts only), and the pair-code table
+// of the compact base-3 codes.
 template <int LAYOUT>
-__device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_lds)
+__device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_lds, uint8_t* b3_lut)
 {
-    if (LAYOUT != TQ_SCALE_CODEBOOK) return;
+    if (LAYOUT != TQ_SCALE_CODEBOOK && LAYOUT != TQ_SCALE_CODEBOOK_B3) return;
     if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+    if (LAYOUT == TQ_SCALE_CODEBOOK_B3) fill_b3_lut(b3_lut);
     __syncthreads();
 }
+
+template <int LAYOUT>
+constexpr int b3_lut_bytes() { return LAYOUT == TQ_SCALE_CODEBOOK_B3 ? 1024 * 4 * kB3Copies : 16; }
 
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
 __global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_single(tq_prob_dev P, int tiles_m)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    stage_codebook<LAYOUT>(P, cb_lds);
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
+    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
     const int tile = blockIdx.x;
-    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, tile % tiles_m, tile / tiles_m, (const LDS_AS float*)cb_lds);
+    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, tile % tiles_m, tile / tiles_m, (const LDS_AS float*)cb_lds,
+                                             (const LDS_AS uint8_t*)b3_lut);
 }
 
 // Grouped: item i = (problem, tile); tiles of a problem run token-tile fastest.
@@ -549,9 +626,11 @@ __global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_group
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    stage_codebook<LAYOUT>(P, cb_lds);
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
+    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
     const int tiles_m = (P.M + 16 * FM * WM - 1) / (16 * FM * WM);
-    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, it.y % tiles_m, it.y / tiles_m, (const LDS_AS float*)cb_lds);
+    gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, it.y % tiles_m, it.y / tiles_m, (const LDS_AS float*)cb_lds,
+                                             (const LDS_AS uint8_t*)b3_lut);
 }
 
 }  // namespace tqm

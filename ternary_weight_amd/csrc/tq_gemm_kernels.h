@@ -15,7 +15,7 @@ struct tq_gemm_kernel {
 
 // Rows of a kernel table: the scale layout and, for bf16, the MFMA step.
 enum { TQ_GEMM_ROW_TENSOR = 0, TQ_GEMM_ROW_GROUP = 1, TQ_GEMM_ROW_GROUP16 = 2, TQ_GEMM_ROW_CODEBOOK = 3,
-       TQ_GEMM_ROWS = 4 };
+       TQ_GEMM_ROW_CODEBOOK_B3 = 4, TQ_GEMM_ROWS = 5 };
 
 // Kernels of one activation type, indexed [row][K - 1]; null where unsupported.
 const tq_gemm_kernel (*tq_gemm_table_i8())[4];
@@ -29,5 +29,10 @@ const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4];
 #define TQ_GEMM_ROW(XT, LAYOUT, FM1, FN1, FM, FN, KS, WM)                                           \
     {TQ_GEMM_ENTRY(XT, LAYOUT, 1, FM1, FN1, KS, WM), TQ_GEMM_ENTRY(XT, LAYOUT, 2, FM, FN, KS, WM),   \
      TQ_GEMM_ENTRY(XT, LAYOUT, 3, FM, FN, KS, WM), TQ_GEMM_ENTRY(XT, LAYOUT, 4, FM, FN, KS, WM)}
-#define TQ_GEMM_NONE {{nullptr, nullptr, 0, 0, 0, 0}, {nullptr, nullptr, 0, 0, 0, 0}, \
-                      {nullptr, nullptr, 0, 0, 0, 0}, {nullptr, nullptr, 0, 0, 0, 0}}
+#define TQ_GEMM_NONE_ENTRY {nullptr, nullptr, 0, 0, 0, 0}
+#define TQ_GEMM_NONE {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY}
+// The compact base-3 codec: planes = 3 (the table's index), one combined
+// value per weight in the kernel (its K = 1), 16-column steps.
+#define TQ_GEMM_ROW_B3(FM, FN, WM) \
+    {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_GEMM_ENTRY(TQ_BF16, TQ_SCALE_CODEBOOK_B3, 1, FM, FN, 16, WM), \
+     TQ_GEMM_NONE_ENTRY}

@@ -11,7 +11,7 @@ int mt_index(int M) { return M <= 1 ? 0 : 1; }
 size_t red_bytes(int family, int split_waves, int total_waves)
 {
     if (split_waves <= 1) return 0;
-    const int mti = family % kTiers, K = (family / kTiers) % 4 + 1, layout = (family / (4 * kTiers)) % 3;
+    const int mti = family % kTiers, K = (family / kTiers) % 4 + 1, layout = (family / (4 * kTiers)) % kLayouts;
     const int R = layout != TQ_SCALE_TENSOR ? kMT[mti] : kMT[mti] * K;
     return (size_t)total_waves * R * 64 * 4;
 }
@@ -36,26 +36,28 @@ const grouped_fn* grouped_tab(int xt, int mti)
     return f[xt][mti]();
 }
 
-// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier
+// family = ((x_type * kLayouts + layout) * 4 + (K - 1)) * kTiers + M tier
+constexpr int kPerTable = 4 * kLayouts;
+
 single_fn single_of(int family)
 {
     const int mti = family % kTiers, rest = family / kTiers;
-    const single_fn* t = single_tab(rest / 12, mti);
-    return t ? t[rest % 12] : nullptr;
+    const single_fn* t = single_tab(rest / kPerTable, mti);
+    return t ? t[rest % kPerTable] : nullptr;
 }
 
 grouped_fn grouped_of(int family)
 {
     const int mti = family % kTiers, rest = family / kTiers;
-    const grouped_fn* t = grouped_tab(rest / 12, mti);
-    return t ? t[rest % 12] : nullptr;
+    const grouped_fn* t = grouped_tab(rest / kPerTable, mti);
+    return t ? t[rest % kPerTable] : nullptr;
 }
 
 wave_items_fn wave_items_fn_of(int family)
 {
-    const int mti = family % kTiers, rest = family / kTiers, xt = rest / 12;
+    const int mti = family % kTiers, rest = family / kTiers, xt = rest / kPerTable;
     if (mti != 1 || xt != TQ_BF16) return nullptr;
-    return wave_table_1_1()[rest % 12];
+    return wave_table_1_1()[rest % kPerTable];
 }
 
 }  // namespace
@@ -69,10 +71,15 @@ size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_
 
 int tq_gemv_family(int x_type, int layout, int K, int M)
 {
-    if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout > 2 || K < 1 || K > 4 || M < 1 ||
+    if (x_type < 0 || x_type >= kXTypes || layout < 0 || layout >= kLayouts || K < 1 || K > 4 || M < 1 ||
         M > TQ_PASS_TOKENS)
         return -1;
-    return ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + mt_index(M);
+    if (layout == TQ_SCALE_CODEBOOK_B3) {
+        // the three digits decode to one combined value: kernel K = 1, bf16 only
+        if (x_type != TQ_BF16 || K != 3) return -1;
+        K = 1;
+    }
+    return ((x_type * kLayouts + layout) * 4 + (K - 1)) * kTiers + mt_index(M);
 }
 
 namespace {

@@ -32,6 +32,14 @@
 //         32 different copies, so a wave's read has no bank conflicts.
 //  fp32   int8 decode as above, converted per trit and accumulated with fma
 //         (t in {-1, 0, 1}, so each fma is an exact add, subtract or no-op).
+//  codec, compact base-3 codes (CODEBOOK_B3, bf16 activations): a table in
+//         LDS maps each 10-bit pair code to the two weights' values as a
+//         bf16 pair (exact: integers in [-13, 13]); one field extract, one
+//         address op and one 4-byte LDS read per two columns, then one
+//         v_dot2_f32_bf16 against the activation pair of the same two
+//         columns (consecutive, so x needs no rearranging).  The digits'
+//         weights 9, 3, 1 are in the table values, so a group's sum is scaled
+//         once by its codebook entry.  1024 entries x 16 copies (64 KiB).
 #include "tq_internal.h"
 #include "tq_decode.h"
 
@@ -228,6 +236,22 @@ __device__ __forceinline__ void fill_bf16_lut(uint8_t* lut)
     }
 }
 
+// Field i (columns 2i, 2i + 1) of 16-column unit d of a CODEBOOK_B3 chunk
+// stream (ten dwords w), as its table address.
+template <int d, int i>
+__device__ __forceinline__ uint32_t b3_addr(const u32x4 (&w)[3], uint32_t copyoff)
+{
+    constexpr int bit = 80 * d + 10 * i, D = bit >> 5, S = bit & 31;
+    uint32_t f;
+    if constexpr (S <= 22) {
+        f = __builtin_amdgcn_ubfe(w[D >> 2][D & 3], S, 10);
+    } else {
+        constexpr int D1 = D + 1;
+        f = __builtin_amdgcn_alignbit(w[D1 >> 2][D1 & 3], w[D >> 2][D & 3], S) & 0x3FFu;
+    }
+    return (f << 6) | copyoff;
+}
+
 __device__ __forceinline__ void accum(const Trits<TQ_F32>& t, const XUnit<TQ_F32>& x, float& acc)
 {
 #pragma unroll
@@ -265,7 +289,8 @@ __device__ __forceinline__ float codec_combine(const float (&p)[K])
 // Code (and scale) registers of one 64-column chunk.
 template <int K, int LAYOUT>
 struct Slot {
-    u32x4 w[K];
+    // CODEBOOK_B3: the chunk's 320-bit stream in w[0], w[1] and w[2].xy
+    u32x4 w[LAYOUT == TQ_SCALE_CODEBOOK_B3 ? 3 : K];
     uint32_t sw[LAYOUT == TQ_SCALE_TENSOR ? 1 : K][2];
 };
 
@@ -301,6 +326,11 @@ template <int XT, int LAYOUT, int K, int MT, int kDepth = 0>
 struct RowBlock {
     using A = typename AccT<XT>::type;
     static constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
+    // the codec's compact base-3 codes: one combined value per weight (K = 1
+    // here), decoded through the pair-code table (bf16 activations only)
+    static constexpr bool kB3 = LAYOUT == TQ_SCALE_CODEBOOK_B3;
+    static constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || kB3;
+    static_assert(!kB3 || (K == 1 && XT == TQ_BF16), "compact base-3 codes: one combined plane, bf16 activations");
     // chunks in flight per wave (codes of K planes each)
     static constexpr int D = kDepth > 0 ? kDepth
                            : (MT > 1 ? 1 : (XT == TQ_BF16 ? TQ_DEPTH_BF16 : (K == 1 ? TQ_DEPTH_K1 : TQ_DEPTH_KN)));
@@ -322,7 +352,7 @@ struct RowBlock {
 
     __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_, const uint8_t* lut_)
         : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_), lut((const LDS_AS uint8_t*)lut_),
-          copyoff((uint32_t)(threadIdx.x & 31) * 8u)
+          copyoff(kB3 ? (uint32_t)(threadIdx.x % kB3Copies) * 4u : (uint32_t)(threadIdx.x & 31) * 8u)
     {
         constexpr int64_t kXBytes = XT == TQ_F32 ? 4 : (XT == TQ_BF16 ? 2 : 1);   // TQ_F32_Q8: the int8 copy
 #pragma unroll
@@ -334,9 +364,9 @@ struct RowBlock {
             // (the token loop stops before it)
             if (MT > 1) xrow[m] = (const uint8_t*)xsrc + (int64_t)std::min(m, P.M - 1) * P.Kin * kXBytes;
         }
-        cbase = (const uint8_t*)P.codes + (int64_t)rb * P.NC * K * TQ_ROWS * 16;
-        sbase = (const uint8_t*)P.scales +
-                (LAYOUT == TQ_SCALE_CODEBOOK ? (int64_t)rb * P.NID : (int64_t)rb * P.NGD * K) * TQ_ROWS * 4;
+        cbase = (const uint8_t*)P.codes +
+                (kB3 ? (int64_t)rb * P.NC * TQ_B3_CHUNK_BYTES : (int64_t)rb * P.NC * K * TQ_ROWS * 16);
+        sbase = (const uint8_t*)P.scales + (kCb ? (int64_t)rb * P.NID : (int64_t)rb * P.NGD * K) * TQ_ROWS * 4;
     }
 
     // A buffer resource over `bytes` bytes at `base + off` (no bytes when the
@@ -355,9 +385,17 @@ struct RowBlock {
     {
         const int c = __builtin_amdgcn_readfirstlane(c_);   // wave-uniform: keep its arithmetic scalar
         const bool valid = c < c1_;
-        const __amdgpu_buffer_rsrc_t rc = window(cbase, (int64_t)c * K * TQ_ROWS * 16, valid, K * TQ_ROWS * 16);
+        if constexpr (kB3) {
+            const __amdgpu_buffer_rsrc_t rc = window(cbase, (int64_t)c * TQ_B3_CHUNK_BYTES, valid, TQ_B3_CHUNK_BYTES);
+            s.w[0] = buffer_load<u32x4, kCacheNT>(rc, lane * 16, 0);
+            s.w[1] = buffer_load<u32x4, kCacheNT>(rc, lane * 16, 1024);
+            const u32x2 t = buffer_load<u32x2, kCacheNT>(rc, lane * 8, 2048);
+            s.w[2] = u32x4{t[0], t[1], 0u, 0u};
+        } else {
+            const __amdgpu_buffer_rsrc_t rc = window(cbase, (int64_t)c * K * TQ_ROWS * 16, valid, K * TQ_ROWS * 16);
 #pragma unroll
-        for (int k = 0; k < K; ++k) s.w[k] = buffer_load<u32x4, kCacheNT>(rc, lane * 16, k * TQ_ROWS * 16);
+            for (int k = 0; k < K; ++k) s.w[k] = buffer_load<u32x4, kCacheNT>(rc, lane * 16, k * TQ_ROWS * 16);
+        }
         constexpr int kWordRow = TQ_ROWS * 4;   // one scale word per row of the block
         if (LAYOUT == TQ_SCALE_GROUP_F16) {
             const int g = P.g;
@@ -380,7 +418,7 @@ struct RowBlock {
 #pragma unroll
                 for (int k = 0; k < K; ++k) s.sw[k][0] = buffer_load<uint32_t>(r0, lane * 4, k * kWordRow);
             }
-        } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
+        } else if (kCb) {
             const int end = std::min((c + 1) * TQ_CHUNK, P.Kin);
             const int first_id = ((c * TQ_CHUNK) >> P.log2g) / 6;
             const int last_id = ((end >> P.log2g) - 1) / 6;
@@ -464,7 +502,7 @@ struct RowBlock {
                                             const float* cb_lds)
     {
         const int c = __builtin_amdgcn_readfirstlane(c_);   // wave-uniform: keep its arithmetic scalar
-        const uint32_t pos0 = kG16 && LAYOUT == TQ_SCALE_CODEBOOK ? (uint32_t)(4 * c) % 6u : 0u;
+        const uint32_t pos0 = kG16 && kCb ? (uint32_t)(4 * c) % 6u : 0u;
         const auto unit = [&](auto dc) {
             constexpr int d = decltype(dc)::value;
             if (!kFull && d >= nu) return;
@@ -482,6 +520,35 @@ struct RowBlock {
 #pragma unroll
                 for (int k = 0; k < K; ++k) q[m][k] = kG16 ? (A)0 : p[m][k];
             }
+            if constexpr (kB3) {
+                // the unit's eight pair codes through the table, once for every token
+                uint32_t e[8];
+                const auto look = [&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    e[i] = *(const LDS_AS uint32_t*)(lut + b3_addr<d, i>(s.w, copyoff));
+                };
+                look(std::integral_constant<int, 0>{});
+                look(std::integral_constant<int, 1>{});
+                look(std::integral_constant<int, 2>{});
+                look(std::integral_constant<int, 3>{});
+                look(std::integral_constant<int, 4>{});
+                look(std::integral_constant<int, 5>{});
+                look(std::integral_constant<int, 6>{});
+                look(std::integral_constant<int, 7>{});
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (!kAll && MT > 1 && m >= P.M) break;
+                    XUnit<XT> xu;
+                    if (MT == 1) xu.load(xsrc, (int64_t)u * 16);
+                    else xu.load(xrow[m], (int64_t)u * 16);
+                    // x dword i holds columns 2i (low half) and 2i + 1: the pair of entry i
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        q[m][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e[i]),
+                                                                  __builtin_bit_cast(bf16x2_t, xu.v[i]), q[m][0],
+                                                                  false);
+                }
+            } else {
             // one token: each plane decoded right before its sums; several:
             // the unit's trits decoded once, then every token's sums
             TX t[MT > 1 ? K : 1];
@@ -508,6 +575,7 @@ struct RowBlock {
                     for (int k = 0; k < K; ++k) accum(MT > 1 ? t[k] : decode(k), xu, q[m][k]);
                 }
             }
+            }   // not kB3
             if constexpr (kG16) {
                 float sc[K];
                 scales_g16<d>(s, pos0, cb_lds, sc);
@@ -797,9 +865,11 @@ __device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb
     __shared__ __attribute__((aligned(16))) uint8_t lut[XT == TQ_BF16 ? kLutBytes : 16];
     constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     constexpr int Rw = kGroup ? MT : MT * K;          // partial sums per lane
-    if (LAYOUT == TQ_SCALE_CODEBOOK && threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
-    if (XT == TQ_BF16) fill_bf16_lut(lut);
-    if (LAYOUT == TQ_SCALE_CODEBOOK || XT == TQ_BF16) __syncthreads();
+    constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || LAYOUT == TQ_SCALE_CODEBOOK_B3;
+    if (kCb && threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+    if constexpr (LAYOUT == TQ_SCALE_CODEBOOK_B3) fill_b3_lut(lut);
+    else if constexpr (XT == TQ_BF16) fill_bf16_lut(lut);
+    if (kCb || XT == TQ_BF16) __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwaves = (int)(blockDim.x >> 6);
     const int S = nwaves / nrb;                       // waves per row block
@@ -845,7 +915,8 @@ template <int XT, int LAYOUT, int K, int MT>
 __global__ __launch_bounds__(1024) void k_gemv_wave_items(const tq_prob_dev* __restrict__ probs,
                                                                            const int2* __restrict__ items)
 {
-    static_assert(XT == TQ_BF16 && LAYOUT != TQ_SCALE_CODEBOOK, "per-wave items: bf16, no codebook");
+    static_assert(XT == TQ_BF16 && LAYOUT != TQ_SCALE_CODEBOOK && LAYOUT != TQ_SCALE_CODEBOOK_B3,
+                  "per-wave items: bf16, no codebook");
     __shared__ float cb_lds[1];
     __shared__ float sx_lds[1];
     __shared__ __attribute__((aligned(16))) uint8_t lut[kLutBytes];
@@ -870,17 +941,35 @@ typedef void (*wave_items_fn)(const tq_prob_dev*, const int2*);
 // tokens per pass of each M tier (more tokens are taken in slices of the last)
 constexpr int kTiers = 2;
 constexpr int kMT[kTiers] = {1, TQ_PASS_TOKENS};
-// family = ((x_type * 3 + layout) * 4 + (K - 1)) * kTiers + M tier; 24 families per x_type
-constexpr int kPerXT = 12 * kTiers;
+// family = ((x_type * 4 + layout) * 4 + (K - 1)) * kTiers + M tier; 32 families per x_type.
+// CODEBOOK_B3 (three digits combined into one value) is kernel K = 1, bf16 only.
+constexpr int kLayouts = 4;
+constexpr int kPerXT = 4 * kLayouts * kTiers;
 constexpr int kXTypes = 4;
+
+template <int XT, int LAYOUT, int K>
+constexpr bool decode_exists() { return LAYOUT != TQ_SCALE_CODEBOOK_B3 || (XT == TQ_BF16 && K == 1); }
 
 // The per-wave item kernel where the host uses it (bf16, several tokens per
 // pass, no codebook), else none.
 template <int XT, int LAYOUT, int K, int MT>
 constexpr wave_items_fn wave_items_of()
 {
-    if constexpr (MT == 1 || XT != TQ_BF16 || LAYOUT == TQ_SCALE_CODEBOOK) return nullptr;
+    if constexpr (MT == 1 || XT != TQ_BF16 || LAYOUT == TQ_SCALE_CODEBOOK || LAYOUT == TQ_SCALE_CODEBOOK_B3)
+        return nullptr;
     else return &k_gemv_wave_items<XT, LAYOUT, K, MT>;
+}
+template <int XT, int LAYOUT, int K, int MT>
+constexpr single_fn single_of_t()
+{
+    if constexpr (!decode_exists<XT, LAYOUT, K>()) return nullptr;
+    else return &k_gemv_single<XT, LAYOUT, K, MT>;
+}
+template <int XT, int LAYOUT, int K, int MT>
+constexpr grouped_fn grouped_of_t()
+{
+    if constexpr (!decode_exists<XT, LAYOUT, K>()) return nullptr;
+    else return &k_gemv_grouped<XT, LAYOUT, K, MT>;
 }
 
 // families of one (x_type, M tier): index = layout * 4 + (K - 1)
@@ -892,8 +981,8 @@ struct FamOf {
 
 template <int XT, int MT, int... Fs>
 struct TablesXT {
-    static constexpr single_fn single[] = {&k_gemv_single<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
-    static constexpr grouped_fn grouped[] = {&k_gemv_grouped<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>...};
+    static constexpr single_fn single[] = {single_of_t<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>()...};
+    static constexpr grouped_fn grouped[] = {grouped_of_t<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>()...};
     static constexpr wave_items_fn wave[] = {wave_items_of<XT, FamOf<Fs>::layout, FamOf<Fs>::K, MT>()...};
 };
 
@@ -901,7 +990,7 @@ template <int XT, int MT, int... Is>
 constexpr auto make_tables(std::integer_sequence<int, Is...>) { return TablesXT<XT, MT, Is...>{}; }
 
 template <int XT, int MT>
-using TablesFor = decltype(make_tables<XT, MT>(std::make_integer_sequence<int, 12>{}));
+using TablesFor = decltype(make_tables<XT, MT>(std::make_integer_sequence<int, 4 * kLayouts>{}));
 
 // one translation unit per (x_type, M tier) defines its pair of tables
 const single_fn* single_table(int x_type, int mti);

@@ -60,9 +60,13 @@ tq_status tq_fail_problem(tq_status s, int32_t i);
 #ifndef TQ_BF16_MFMA_MIN_M_CODEC
 #define TQ_BF16_MFMA_MIN_M_CODEC 5
 #endif
+#ifndef TQ_BF16_MFMA_MIN_M_B3
+#define TQ_BF16_MFMA_MIN_M_B3 5
+#endif
 static inline int64_t tq_bf16_mfma_min_m(int layout)
 {
-    return layout == TQ_SCALE_CODEBOOK ? TQ_BF16_MFMA_MIN_M_CODEC : TQ_BF16_MFMA_MIN_M;
+    return layout == TQ_SCALE_CODEBOOK ? TQ_BF16_MFMA_MIN_M_CODEC
+                                       : (layout == TQ_SCALE_CODEBOOK_B3 ? TQ_BF16_MFMA_MIN_M_B3 : TQ_BF16_MFMA_MIN_M);
 }
 static inline bool tq_gemv_uses_mfma(int x_type, int layout, int64_t M, const void* x)
 {

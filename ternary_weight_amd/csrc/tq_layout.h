@@ -30,6 +30,21 @@
 // holding the 5-bit index of group 6id + j in bits 5j .. 5j+4 (j = 0..5).
 //
 // TENSOR: K fp32 scales at scales_off.
+//
+// CODEBOOK_B3 (the codec with compact base-3 codes; K = 3 digits): the
+// codebook and the 5-bit group indices as CODEBOOK, and in place of the K
+// two-bit planes one 320-bit stream per (row, 64-column chunk): the weights'
+// base-27 values v = 9 t0 + 3 t1 + t2 (digit planes 0, 1, 2), two columns per
+// 10-bit code
+//     code(j) = (v[2j] mod 27) + 27 (v[2j+1] mod 27)       j = 0 .. 31
+// at bits 10j .. 10j+9 of the stream (little-endian dwords 0..9, so the
+// 16-column unit d is bits 80d .. 80d+79).  Code 0 is two zero weights;
+// codes 729 .. 1023 are never written and read as zeros.  For row block rb
+// and chunk c the 64 lanes' streams are stored in three parts, 2560 bytes:
+//     dwords 0..3: codes + (rb * NC + c) * 2560 +        lane * 16
+//     dwords 4..7: codes + (rb * NC + c) * 2560 + 1024 + lane * 16
+//     dwords 8..9: codes + (rb * NC + c) * 2560 + 2048 + lane * 8
+// so a wave reads its chunk with two 1 KiB and one 512-byte coalesced load.
 #pragma once
 
 #include <stdint.h>
@@ -49,6 +64,14 @@
 // (more are taken in slices of this many).
 #define TQ_PASS_TOKENS 4
 #define TQ_CB_SLOTS 32
+#define TQ_B3_CHUNK_BYTES 2560      // CODEBOOK_B3: bytes of one (row block, 64-column chunk)
+#define TQ_B3_CODES 729             // CODEBOOK_B3: valid 10-bit pair codes (27 * 27)
+
+// CODEBOOK and CODEBOOK_B3 share the codebook and the group indices.
+#if defined(__HIP__)
+__host__ __device__
+#endif
+static inline bool tq_is_codebook(int layout) { return layout == TQ_SCALE_CODEBOOK || layout == TQ_SCALE_CODEBOOK_B3; }
 
 // pack status bits
 #define TQ_PACK_BAD_TRIT 1u
@@ -94,14 +117,15 @@ static inline void tq_layout_make(const tq_weight_desc* d, tq_layout* L)
     L->K = d->planes;
     L->layout = d->scale_layout;
     L->g = (d->scale_layout == TQ_SCALE_TENSOR) ? 0 : d->group;
-    L->ncb = (d->scale_layout == TQ_SCALE_CODEBOOK) ? d->n_codebook : 0;
+    L->ncb = tq_is_codebook(d->scale_layout) ? d->n_codebook : 0;
     L->NB = (L->N + TQ_ROWS - 1) / TQ_ROWS;
     L->NC = (L->Kin + TQ_CHUNK - 1) / TQ_CHUNK;
     L->G = (L->layout == TQ_SCALE_TENSOR) ? 1 : (L->g > 0 ? L->Kin / L->g : 0);
     L->NGD = (L->G + 1) / 2;
     L->NID = (L->G + 5) / 6;
     L->codes_off = TQ_HEADER_BYTES;
-    L->codes_bytes = L->NB * L->NC * (int64_t)L->K * TQ_ROWS * 16;
+    L->codes_bytes = L->layout == TQ_SCALE_CODEBOOK_B3 ? L->NB * L->NC * TQ_B3_CHUNK_BYTES
+                                                       : L->NB * L->NC * (int64_t)L->K * TQ_ROWS * 16;
     int64_t end = tq_align256(L->codes_off + L->codes_bytes);
     L->cb_off = 0;
     if (L->layout == TQ_SCALE_TENSOR) {

@@ -18,7 +18,7 @@ __global__ void k_write_header(tq_blob_header* h, tq_weight_desc d)
         v.planes = d.planes;
         v.group = d.scale_layout == TQ_SCALE_TENSOR ? 0 : d.group;
         v.scale_layout = d.scale_layout;
-        v.n_codebook = d.scale_layout == TQ_SCALE_CODEBOOK ? d.n_codebook : 0;
+        v.n_codebook = tq_is_codebook(d.scale_layout) ? d.n_codebook : 0;
         v.out_features = d.out_features;
         v.in_features = d.in_features;
         v.pack_status = 0;
@@ -131,6 +131,92 @@ __global__ void k_pack_group_scales(const uint16_t* __restrict__ s, uint32_t* __
     if (bad) atomicOr(status, bad);
 }
 
+// CODEBOOK_B3: one thread per (row block, chunk, lane) -- the 64 columns of
+// one row in one chunk, three digit planes -> 32 ten-bit pair codes (the
+// 320-bit stream of tq_layout.h, in its three parts).
+__global__ void k_pack_b3(const int8_t* __restrict__ trits, uint8_t* __restrict__ codes, uint32_t* status,
+                          int64_t total, int64_t N, int64_t Kin, int64_t NC)
+{
+    uint32_t bad = 0;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(t & 63);
+        const int64_t rest = t >> 6;
+        const int64_t c = rest % NC, rb = rest / NC;
+        const int64_t n = rb * TQ_ROWS + lane;
+        uint32_t w[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        if (n < N) {
+            for (int q = 0; q < 4; ++q) {            // 16 columns at a time (Kin is a multiple of 16)
+                const int64_t col0 = c * TQ_CHUNK + 16 * q;
+                if (col0 >= Kin) break;
+                int v[16];
+                for (int i = 0; i < 16; ++i) v[i] = 0;
+                for (int k = 0; k < 3; ++k) {       // digit plane k weighs 3^(2-k)
+                    const int4 d = *reinterpret_cast<const int4*>(trits + ((int64_t)k * N + n) * Kin + col0);
+                    const uint32_t b[4] = {(uint32_t)d.x, (uint32_t)d.y, (uint32_t)d.z, (uint32_t)d.w};
+                    for (int i = 0; i < 16; ++i) {
+                        const int tv = (int8_t)((b[i >> 2] >> (8 * (i & 3))) & 0xFF);
+                        if (tv < -1 || tv > 1) bad |= TQ_PACK_BAD_TRIT;
+                        v[i] = 3 * v[i] + tv;
+                    }
+                }
+                for (int i = 0; i < 8; ++i) {       // pair j = 8q + i: columns 2j, 2j + 1
+                    const uint32_t a = (uint32_t)((v[2 * i] % 27 + 27) % 27);
+                    const uint32_t b = (uint32_t)((v[2 * i + 1] % 27 + 27) % 27);
+                    const uint32_t code = (a + 27u * b) & 0x3FFu;
+                    const int bit = 10 * (8 * q + i), dw = bit >> 5, sh = bit & 31;
+                    w[dw] |= code << sh;
+                    if (sh > 22) w[dw + 1] |= code >> (32 - sh);
+                }
+            }
+        }
+        uint8_t* blk = codes + (rb * NC + c) * TQ_B3_CHUNK_BYTES;
+        *reinterpret_cast<uint4*>(blk + lane * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(blk + 1024 + lane * 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        *reinterpret_cast<uint2*>(blk + 2048 + lane * 8) = make_uint2(w[8], w[9]);
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+// Inverse of k_pack_b3: pair codes -> the three digit planes (codes >= 729,
+// never written, read as zero weights).
+__global__ void k_unpack_b3(const uint8_t* __restrict__ codes, int8_t* __restrict__ trits, int64_t total, int64_t N,
+                            int64_t Kin, int64_t NC)
+{
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(t & 63);
+        const int64_t rest = t >> 6;
+        const int64_t c = rest % NC, rb = rest / NC;
+        const int64_t n = rb * TQ_ROWS + lane;
+        if (n >= N) continue;
+        const uint8_t* blk = codes + (rb * NC + c) * TQ_B3_CHUNK_BYTES;
+        const uint4 p0 = *reinterpret_cast<const uint4*>(blk + lane * 16);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(blk + 1024 + lane * 16);
+        const uint2 p2 = *reinterpret_cast<const uint2*>(blk + 2048 + lane * 8);
+        const uint32_t w[11] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w, p2.x, p2.y, 0u};
+        for (int j = 0; j < 32; ++j) {
+            const int bit = 10 * j, dw = bit >> 5, sh = bit & 31;
+            uint32_t code = w[dw] >> sh;
+            if (sh > 22) code |= w[dw + 1] << (32 - sh);
+            code &= 0x3FFu;
+            if (code >= (uint32_t)TQ_B3_CODES) code = 0;
+            for (int h = 0; h < 2; ++h) {
+                const int64_t col = c * TQ_CHUNK + 2 * j + h;
+                if (col >= Kin) continue;
+                const int u = (int)(h ? code / 27u : code % 27u);
+                int v = u > 13 ? u - 27 : u;
+                for (int k = 2; k >= 0; --k) {      // least significant digit first: plane 2
+                    const int r = ((v % 3) + 3) % 3;
+                    const int tv = r == 2 ? -1 : r;
+                    trits[((int64_t)k * N + n) * Kin + col] = (int8_t)tv;
+                    v = (v - tv) / 3;
+                }
+            }
+        }
+    }
+}
+
 // CODEBOOK: one thread per index dword (six groups of one row).
 __global__ void k_pack_indices(const uint8_t* __restrict__ idx, uint32_t* __restrict__ out,
                                uint32_t* status, int64_t total, int64_t N, int64_t G, int64_t NID,
@@ -215,7 +301,7 @@ TQ_EXPORT tq_status tq_pack(const tq_weight_desc* desc, const int8_t* trits, con
     if ((s = tq_check_ptr(trits, "trits", !need_trits))) return s;
     if ((s = tq_check_ptr(scales, "scales", L.layout != TQ_SCALE_TENSOR && !need_trits, 4))) return s;
     if ((s = tq_check_ptr(blob, "blob", false))) return s;
-    if (L.layout == TQ_SCALE_CODEBOOK) {
+    if (tq_is_codebook(L.layout)) {
         if ((s = tq_check_ptr(codebook, "codebook", false, 2))) return s;
     }
     hipStream_t stream = (hipStream_t)stream_;
@@ -227,7 +313,12 @@ TQ_EXPORT tq_status tq_pack(const tq_weight_desc* desc, const int8_t* trits, con
     hipLaunchKernelGGL(k_write_header, dim3(1), dim3(64), 0, stream, (tq_blob_header*)b, *desc);
     if ((s = tq_check_launch("tq_pack header"))) return s;
     const int64_t ncodes = L.codes_bytes / 4;
-    if (ncodes > 0) {
+    if (ncodes > 0 && L.layout == TQ_SCALE_CODEBOOK_B3) {
+        const int64_t n = L.NB * L.NC * TQ_ROWS;
+        hipLaunchKernelGGL(k_pack_b3, dim3(grid_for(n)), dim3(kBlock), 0, stream, trits, b + L.codes_off, status, n,
+                           L.N, L.Kin, L.NC);
+        if ((s = tq_check_launch("tq_pack codes"))) return s;
+    } else if (ncodes > 0) {
         hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(ncodes)), dim3(kBlock), 0, stream, trits,
                            (uint32_t*)(b + L.codes_off), status, ncodes, L.K, L.N, L.Kin, L.NC);
         if ((s = tq_check_launch("tq_pack codes"))) return s;
@@ -278,7 +369,12 @@ TQ_EXPORT tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8
     hipStream_t stream = (hipStream_t)stream_;
     const uint8_t* b = (const uint8_t*)blob;
     const int64_t ncodes = L.codes_bytes / 4;
-    if (ncodes > 0 && trits) {
+    if (ncodes > 0 && trits && L.layout == TQ_SCALE_CODEBOOK_B3) {
+        const int64_t n = L.NB * L.NC * TQ_ROWS;
+        hipLaunchKernelGGL(k_unpack_b3, dim3(grid_for(n)), dim3(kBlock), 0, stream, b + L.codes_off, trits, n, L.N,
+                           L.Kin, L.NC);
+        if ((s = tq_check_launch("tq_unpack codes"))) return s;
+    } else if (ncodes > 0 && trits) {
         hipLaunchKernelGGL(k_unpack_codes, dim3(grid_for(ncodes)), dim3(kBlock), 0, stream,
                            (const uint32_t*)(b + L.codes_off), trits, ncodes, L.K, L.N, L.Kin, L.NC);
         if ((s = tq_check_launch("tq_unpack codes"))) return s;
@@ -303,7 +399,7 @@ TQ_EXPORT tq_status tq_unpack(const tq_weight_desc* desc, const void* blob, int8
         }
         if ((s = tq_check_launch("tq_unpack scales"))) return s;
     }
-    if (codebook && L.layout == TQ_SCALE_CODEBOOK) {
+    if (codebook && tq_is_codebook(L.layout)) {
         hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(64), 0, stream, (const void*)(b + L.cb_off),
                            (void*)codebook, (uint32_t*)nullptr, L.ncb, L.ncb, 1, 1);
         if ((s = tq_check_launch("tq_unpack codebook"))) return s;

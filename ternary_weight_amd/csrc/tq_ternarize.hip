@@ -332,7 +332,7 @@ TQ_EXPORT tq_status tq_ternarize(const tq_weight_desc* desc, const float* w, con
     hipStream_t st = (hipStream_t)stream;
     const int64_t N = L.N, Kin = L.Kin;
     if (N == 0 || Kin == 0) return tq_ok();
-    if (L.layout == TQ_SCALE_CODEBOOK) {
+    if (tq_is_codebook(L.layout)) {   // the canonical arrays of both codec layouts are alike
         if ((s = tq_check_ptr(codebook, "codebook", false, 2))) return s;
         // the codebook must ascend, from a positive entry: read it back (an offline call)
         uint16_t cb[32];

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libtq.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_UNSUPPORTED, ERR_DEVICE = range(7)
-SCALE_TENSOR, SCALE_GROUP_F16, SCALE_CODEBOOK = 0, 1, 2
+SCALE_TENSOR, SCALE_GROUP_F16, SCALE_CODEBOOK, SCALE_CODEBOOK_B3 = 0, 1, 2, 3
 F32, BF16, I8, F32_Q8 = 0, 1, 2, 3
 
 

@@ -74,10 +74,41 @@ def _align256(v):
     return (v + 255) & ~255
 
 
+def b3_stream_codes(words):
+    """The 32 ten-bit codes of 320-bit streams: words uint32 [..., 10] -> [..., 32]."""
+    w = np.asarray(words, dtype=np.uint64)
+    out = np.zeros(w.shape[:-1] + (32,), dtype=np.int64)
+    for j in range(32):
+        bit = 10 * j
+        d, sh = bit // 32, bit % 32
+        v = w[..., d] >> np.uint64(sh)
+        if sh > 22:
+            v = v | (w[..., d + 1] << np.uint64(32 - sh))
+        out[..., j] = (v & np.uint64(0x3FF)).astype(np.int64)
+    return out
+
+
+def b3_digits(codes):
+    """Pair codes -> the three digit planes of the two columns: int8 [3][..., 2]
+    (codes >= 729 read as zero weights)."""
+    codes = np.where(codes < 729, codes, 0)
+    vals = np.stack([codes % 27, codes // 27], axis=-1)
+    vals = np.where(vals > 13, vals - 27, vals)              # v in [-13, 13]
+    digits = []
+    for _ in range(3):                                        # least significant first
+        r = np.mod(vals, 3)
+        t = np.where(r == 2, -1, r)
+        digits.append(t.astype(np.int8))
+        vals = (vals - t) // 3
+    return np.stack(digits[::-1], axis=0)                     # plane 0 = the most significant
+
+
 def read_blob(blob, K, N, Kin, layout, g=0):
     """(trits int8 [K][N][Kin], raw 2-bit codes [K][NBr][NCc], scales, codebook)."""
     b = np.asarray(blob, dtype=np.uint8)
     NB, NC = (N + 63) // 64, (Kin + 63) // 64
+    if layout == 3:
+        return _read_b3(b, N, Kin, g, NB, NC)
     nwords = NB * NC * K * 64 * 4
     words = b[256:256 + 4 * nwords].view(np.uint32).reshape(NB, NC, K, 64, 4)
     d = np.arange(4).reshape(4, 1, 1)
@@ -108,4 +139,31 @@ def read_blob(blob, K, N, Kin, layout, g=0):
         j = np.arange(6, dtype=np.uint32)
         idx = ((iw[..., None] >> (5 * j)) & np.uint32(31)).astype(np.uint8)      # [NB,NID,64,6]
         out["scales"] = idx.transpose(0, 2, 1, 3).reshape(NB * 64, NID * 6)[:N, :G]
+    return out
+
+
+def _read_b3(b, N, Kin, g, NB, NC):
+    """The compact base-3 codec blob: per (row block, chunk) 2560 bytes -- the
+    64 lanes' dwords 0..3, then 4..7 (16 bytes a lane), then 8..9 (8 bytes a
+    lane) of each row's 320-bit stream; then the codebook and indices as for
+    the codebook layout."""
+    nbytes = NB * NC * 2560
+    blk = b[256:256 + nbytes].reshape(NB, NC, 2560)
+    p0 = blk[:, :, :1024].view(np.uint32).reshape(NB, NC, 64, 4)
+    p1 = blk[:, :, 1024:2048].view(np.uint32).reshape(NB, NC, 64, 4)
+    p2 = blk[:, :, 2048:].view(np.uint32).reshape(NB, NC, 64, 2)
+    words = np.concatenate([p0, p1, p2], axis=-1)                     # [NB, NC, 64 lanes, 10]
+    codes = b3_stream_codes(words)                                    # [NB, NC, 64, 32]
+    digits = b3_digits(codes)                                         # [3, NB, NC, 64, 32, 2]
+    trits = digits.reshape(3, NB, NC, 64, 64).transpose(0, 1, 3, 2, 4).reshape(3, NB * 64, NC * 64)
+    codes_rc = codes.transpose(0, 2, 1, 3).reshape(NB * 64, NC * 32)
+    out = {"codes": codes_rc, "trits": trits[:, :N, :Kin]}
+    end = _align256(256 + nbytes)
+    G = Kin // g
+    NID = (G + 5) // 6
+    out["codebook"] = b[end:end + 64].view(np.uint16).copy()
+    iw = b[end + 256:end + 256 + NB * NID * 64 * 4].view(np.uint32).reshape(NB, NID, 64)
+    j = np.arange(6, dtype=np.uint32)
+    idx = ((iw[..., None] >> (5 * j)) & np.uint32(31)).astype(np.uint8)
+    out["scales"] = idx.transpose(0, 2, 1, 3).reshape(NB * 64, NID * 6)[:N, :G]
     return out

@@ -185,7 +185,7 @@ def test_gemm_grouped_validation():
     assert e.value.status == tq.ERR_UNSUPPORTED
     plan = tq.tq_grouped_plan(workspace=good, n_items=3, family=5, n_problems=1)
     assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a decode family
-    plan.family = 1000 + 3 * 4 * 4                                                 # past the last family
+    plan.family = 1000 + 3 * 5 * 4                                                 # past the last family
     assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     plan.family = 1000 + 2 * 4 + 0                                                 # int8 with groups of 16: none
@@ -226,8 +226,8 @@ def test_grouped_run_rejects_forged_plans():
     than the LDS copy holds, or a per-wave plan that is not one."""
     good = 0x60000
     plan = tq.tq_grouped_plan(workspace=good, n_items=1, family=-1, waves=1, row_blocks=1, n_problems=1)
-    fam = lambda xt, layout, K, tier: ((xt * 3 + layout) * 4 + K - 1) * 2 + tier
-    for f in (-1, 4 * 12 * 2):
+    fam = lambda xt, layout, K, tier: ((xt * 4 + layout) * 4 + K - 1) * 2 + tier
+    for f in (-1, 4 * 16 * 2):
         plan.family = f
         assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     plan.family = fam(tq.BF16, 0, 4, 1)      # bf16, per-tensor, 4 planes, 4 tokens
@@ -240,7 +240,8 @@ def test_grouped_run_rejects_forged_plans():
     plan.mode = 2
     assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     plan.mode, plan.row_blocks, plan.n_items = 1, 16, 32
-    for f in (fam(tq.F32_Q8, 1, 3, 1), fam(tq.I8, 1, 3, 1), fam(tq.BF16, 2, 3, 1), fam(tq.BF16, 1, 3, 0)):
+    for f in (fam(tq.F32_Q8, 1, 3, 1), fam(tq.I8, 1, 3, 1), fam(tq.BF16, 2, 3, 1), fam(tq.BF16, 1, 3, 0),
+              fam(tq.BF16, 3, 1, 1)):
         plan.family = f
         assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     plan.family, plan.n_items = fam(tq.BF16, 1, 3, 1), 24
