@@ -93,24 +93,33 @@ __device__ __forceinline__ uint32_t buffer_load<uint32_t, 0>(__amdgpu_buffer_rsr
 }
 
 // The pair-code table of the compact base-3 codec: entry e (10-bit code),
-// copy c at byte offset e * 64 + c * 4 holds bf16(v0) | bf16(v1) << 16 for
+// copy c at byte offset e * 4 C + c * 4 holds bf16(v0) | bf16(v1) << 16 for
 // e = (v0 mod 27) + 27 (v1 mod 27) < 729, and zero for the codes never
-// written.  Lane l reads copy l % 16.
-constexpr int kB3Copies = 16;
-__device__ __forceinline__ void fill_b3_lut(uint8_t* lut)
-{
-    for (int i = threadIdx.x; i < 1024 * kB3Copies; i += blockDim.x) {
-        const uint32_t e = (uint32_t)i / kB3Copies, c = (uint32_t)i % kB3Copies;
-        uint32_t v = 0;
-        if (e < (uint32_t)TQ_B3_CODES) {
-            const int a = (int)(e % 27u), b = (int)(e / 27u);
-            // small integers: the fp32 value's upper half is the exact bf16
-            v = (__float_as_uint((float)(a > 13 ? a - 27 : a)) >> 16) |
-                (__float_as_uint((float)(b > 13 ? b - 27 : b)) & 0xFFFF0000u);
+// written.  Lane l reads copy l % C.  C copies spread the lanes' reads over
+// the banks (C = 16, 64 KiB, for one-token decode; 8, 32 KiB, where a
+// smaller table lets more waves share a compute unit -- measured).
+template <int C>
+struct B3Table {
+    static_assert(C == 8 || C == 16 || C == 32, "8, 16 or 32 copies");
+    static constexpr int kCopies = C;
+    static constexpr int kShift = C == 32 ? 7 : (C == 16 ? 6 : 5);   // log2(4 C)
+    static constexpr int kBytes = 1024 * 4 * C;
+    static __device__ __forceinline__ void fill(uint8_t* lut)
+    {
+        for (int i = threadIdx.x; i < 1024 * C; i += blockDim.x) {
+            const uint32_t e = (uint32_t)i / C, c = (uint32_t)i % C;
+            uint32_t v = 0;
+            if (e < (uint32_t)TQ_B3_CODES) {
+                const int a = (int)(e % 27u), b = (int)(e / 27u);
+                // small integers: the fp32 value's upper half is the exact bf16
+                v = (__float_as_uint((float)(a > 13 ? a - 27 : a)) >> 16) |
+                    (__float_as_uint((float)(b > 13 ? b - 27 : b)) & 0xFFFF0000u);
+            }
+            *(LDS_AS uint32_t*)((LDS_AS uint8_t*)lut + e * (4 * C) + c * 4) = v;
         }
-        *(LDS_AS uint32_t*)((LDS_AS uint8_t*)lut + e * (4 * kB3Copies) + c * 4) = v;
     }
-}
+    static __device__ __forceinline__ uint32_t copy_offset() { return (uint32_t)(threadIdx.x % C) * 4u; }
+};
 
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 

@@ -41,6 +41,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;   // 4 waves
+#ifndef TQ_GEMM_B3_NBUF
+#define TQ_GEMM_B3_NBUF 4          // steps in flight of the compact codec's kernels
+#endif
 #ifndef TQ_GEMM_WAVES_PER_SIMD
 #define TQ_GEMM_WAVES_PER_SIMD 2   // register budget: two waves per SIMD, so that one
                                    // wave's trit decode overlaps the other's MFMAs
@@ -178,7 +181,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     using Frag = typename MF::Frag;
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
-    constexpr int NBUF = 4;                               // steps in flight (loads issued 3 steps ahead)
+    // steps in flight (loads issued NBUF - 1 steps ahead)
+    constexpr int NBUF = LAYOUT == TQ_SCALE_CODEBOOK_B3 ? TQ_GEMM_B3_NBUF : 4;
     // int8, one plane, per-tensor scale: the int32 sum is the result
     constexpr bool kDirect = XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1;
     // the scale word of a (segment, plane) block: two f16 group scales, or six 5-bit codebook indices
@@ -300,7 +304,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             b3_sh[par] = o & 31u;
         }
     }
-    const uint32_t b3_copy = kB3 ? (uint32_t)(lane % 16) * 4u : 0u;
+    using B3T = B3Table<8>;   // pair-code table, 8 copies (32 KiB: more workgroups per unit, measured)
+    const uint32_t b3_copy = kB3 ? B3T::copy_offset() : 0u;
     __shared__ __attribute__((aligned(16))) uint32_t wlds[kWave ? 2 : 1][kWave ? 4 * WST : 4];
     LDS_AS uint32_t* const wst0 = (LDS_AS uint32_t*)wlds[0] + (kWave ? wave * WST : 0);
     LDS_AS uint32_t* const wst1 = (LDS_AS uint32_t*)wlds[kWave ? 1 : 0] + (kWave ? wave * WST : 0);
@@ -392,7 +397,8 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // 4q + 2, 4q + 3, each a bf16 pair in column order
     auto decode = [&](uint32_t wv) -> Frag {
         if constexpr (kB3) {
-            const uint32_t a0 = ((wv & 0x3FFu) << 6) | b3_copy, a1 = (((wv >> 10) & 0x3FFu) << 6) | b3_copy;
+            const uint32_t a0 = ((wv & 0x3FFu) << B3T::kShift) | b3_copy;
+            const uint32_t a1 = (((wv >> 10) & 0x3FFu) << B3T::kShift) | b3_copy;
             Frag f;
             f[0] = *(const LDS_AS uint32_t*)(b3_lut + a0);
             f[1] = *(const LDS_AS uint32_t*)(b3_lut + a1);
@@ -601,15 +607,20 @@ __device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_l
 {
     if (LAYOUT != TQ_SCALE_CODEBOOK && LAYOUT != TQ_SCALE_CODEBOOK_B3) return;
     if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
-    if (LAYOUT == TQ_SCALE_CODEBOOK_B3) fill_b3_lut(b3_lut);
+    if (LAYOUT == TQ_SCALE_CODEBOOK_B3) B3Table<8>::fill(b3_lut);
     __syncthreads();
 }
 
 template <int LAYOUT>
-constexpr int b3_lut_bytes() { return LAYOUT == TQ_SCALE_CODEBOOK_B3 ? 1024 * 4 * kB3Copies : 16; }
+constexpr int b3_lut_bytes() { return LAYOUT == TQ_SCALE_CODEBOOK_B3 ? B3Table<8>::kBytes : 16; }
+
+// Waves per SIMD the register budget is sized for: the compact codec's
+// few-token kernel (98 VGPRs) takes four, as its table leaves room for them.
+template <int LAYOUT, int FM>
+constexpr int waves_per_simd() { return LAYOUT == TQ_SCALE_CODEBOOK_B3 && FM == 1 ? 4 : TQ_GEMM_WAVES_PER_SIMD; }
 
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
-__global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_single(tq_prob_dev P, int tiles_m)
+__global__ __launch_bounds__(kThreads, (waves_per_simd<LAYOUT, FM>())) void k_gemm_single(tq_prob_dev P, int tiles_m)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
     __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
@@ -621,7 +632,7 @@ __global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_singl
 
 // Grouped: item i = (problem, tile); tiles of a problem run token-tile fastest.
 template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
-__global__ __launch_bounds__(kThreads, TQ_GEMM_WAVES_PER_SIMD) void k_gemm_grouped(const tq_prob_dev* probs, const int2* items)
+__global__ __launch_bounds__(kThreads, (waves_per_simd<LAYOUT, FM>())) void k_gemm_grouped(const tq_prob_dev* probs, const int2* items)
 {
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);

@@ -64,8 +64,10 @@ wave_items_fn wave_items_fn_of(int family)
 
 size_t tq_gemv_lds_bytes(int family, int split_waves, int total_waves, size_t x_lds_bytes)
 {
-    const int x_type = family / kPerXT;
-    const size_t fixed = (x_type == TQ_BF16 ? (size_t)kLutBytes : 0) + 1024;
+    const int x_type = family / kPerXT, layout = (family / (4 * kTiers)) % kLayouts, mti = family % kTiers;
+    const size_t lut = layout == TQ_SCALE_CODEBOOK_B3 ? (size_t)(mti == 0 ? B3Table<16>::kBytes : B3Table<8>::kBytes)
+                                                      : (size_t)kLutBytes;
+    const size_t fixed = (x_type == TQ_BF16 ? lut : 0) + 1024;
     return fixed + red_bytes(family, split_waves, total_waves) + x_lds_bytes;
 }
 

@@ -39,7 +39,8 @@
 //         v_dot2_f32_bf16 against the activation pair of the same two
 //         columns (consecutive, so x needs no rearranging).  The digits'
 //         weights 9, 3, 1 are in the table values, so a group's sum is scaled
-//         once by its codebook entry.  1024 entries x 16 copies (64 KiB).
+//         once by its codebook entry.  1024 entries x 16 copies (64 KiB)
+//         for one token, 8 (32 KiB) for several.
 #include "tq_internal.h"
 #include "tq_decode.h"
 
@@ -238,7 +239,7 @@ __device__ __forceinline__ void fill_bf16_lut(uint8_t* lut)
 
 // Field i (columns 2i, 2i + 1) of 16-column unit d of a CODEBOOK_B3 chunk
 // stream (ten dwords w), as its table address.
-template <int d, int i>
+template <int d, int i, int SHIFT>
 __device__ __forceinline__ uint32_t b3_addr(const u32x4 (&w)[3], uint32_t copyoff)
 {
     constexpr int bit = 80 * d + 10 * i, D = bit >> 5, S = bit & 31;
@@ -249,7 +250,7 @@ __device__ __forceinline__ uint32_t b3_addr(const u32x4 (&w)[3], uint32_t copyof
         constexpr int D1 = D + 1;
         f = __builtin_amdgcn_alignbit(w[D1 >> 2][D1 & 3], w[D >> 2][D & 3], S) & 0x3FFu;
     }
-    return (f << 6) | copyoff;
+    return (f << SHIFT) | copyoff;
 }
 
 __device__ __forceinline__ void accum(const Trits<TQ_F32>& t, const XUnit<TQ_F32>& x, float& acc)
@@ -330,6 +331,7 @@ struct RowBlock {
     // here), decoded through the pair-code table (bf16 activations only)
     static constexpr bool kB3 = LAYOUT == TQ_SCALE_CODEBOOK_B3;
     static constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || kB3;
+    using B3T = B3Table<MT == 1 ? 16 : 8>;   // pair-code table (one token: more copies, fewer conflicts)
     static_assert(!kB3 || (K == 1 && XT == TQ_BF16), "compact base-3 codes: one combined plane, bf16 activations");
     // chunks in flight per wave (codes of K planes each)
     static constexpr int D = kDepth > 0 ? kDepth
@@ -352,7 +354,7 @@ struct RowBlock {
 
     __device__ __forceinline__ RowBlock(const tq_prob_dev& P_, int rb_, const void* xsrc_, const uint8_t* lut_)
         : P(P_), rb(rb_), lane(threadIdx.x & 63), xsrc(xsrc_), lut((const LDS_AS uint8_t*)lut_),
-          copyoff(kB3 ? (uint32_t)(threadIdx.x % kB3Copies) * 4u : (uint32_t)(threadIdx.x & 31) * 8u)
+          copyoff(kB3 ? B3T::copy_offset() : (uint32_t)(threadIdx.x & 31) * 8u)
     {
         constexpr int64_t kXBytes = XT == TQ_F32 ? 4 : (XT == TQ_BF16 ? 2 : 1);   // TQ_F32_Q8: the int8 copy
 #pragma unroll
@@ -525,7 +527,7 @@ struct RowBlock {
                 uint32_t e[8];
                 const auto look = [&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    e[i] = *(const LDS_AS uint32_t*)(lut + b3_addr<d, i>(s.w, copyoff));
+                    e[i] = *(const LDS_AS uint32_t*)(lut + b3_addr<d, i, B3T::kShift>(s.w, copyoff));
                 };
                 look(std::integral_constant<int, 0>{});
                 look(std::integral_constant<int, 1>{});
@@ -862,12 +864,14 @@ __device__ __forceinline__ void gemv_body(const tq_prob_dev& P, int rb0, int nrb
     __shared__ float cb_lds[TQ_CB_SLOTS];
     __shared__ float sx_lds[TQ_MAX_M_GEMV];
     __shared__ float wmax[16];
-    __shared__ __attribute__((aligned(16))) uint8_t lut[XT == TQ_BF16 ? kLutBytes : 16];
+    using B3T = B3Table<MT == 1 ? 16 : 8>;
+    __shared__ __attribute__((aligned(16))) uint8_t lut[LAYOUT == TQ_SCALE_CODEBOOK_B3 ? B3T::kBytes
+                                                        : (XT == TQ_BF16 ? kLutBytes : 16)];
     constexpr bool kGroup = LAYOUT != TQ_SCALE_TENSOR;
     constexpr int Rw = kGroup ? MT : MT * K;          // partial sums per lane
     constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || LAYOUT == TQ_SCALE_CODEBOOK_B3;
     if (kCb && threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
-    if constexpr (LAYOUT == TQ_SCALE_CODEBOOK_B3) fill_b3_lut(lut);
+    if constexpr (LAYOUT == TQ_SCALE_CODEBOOK_B3) B3T::fill(lut);
     else if constexpr (XT == TQ_BF16) fill_bf16_lut(lut);
     if (kCb || XT == TQ_BF16) __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
