@@ -807,15 +807,17 @@ def main():
     if args.config == "cfg2" and M == 1 and not args.no_legs:
         # the metric names both shapes: the Llama-8B-shaped one-token stacks
         # are measured the same way, after the BitNet line's own timed region
+        # (and the codec once more with its compact base-3 codes)
         out["legs"] = {}
-        for name in ("cfg3", "cfg4"):
+        for key, name, b3 in (("cfg3", "cfg3", False), ("cfg4", "cfg4", False), ("cfg4_b3", "cfg4", True)):
             leg = measure_stack(args, name, 1, fused=False, waves=0, row_blocks=0, spin_up_ms=args.spin_up_ms,
-                                secondary=False, ceiling=False)
-            out["legs"][name] = {k: leg[k] for k in ("value", "unit", "ms_per_step", "dtype", "tok_per_s_equiv",
-                                                     "gemv_us", "roofline", "cold_pass", "cpu_baseline",
-                                                     "parity_spot_check", "steps", "warmup")}
-            out["legs"][name]["workload"] = leg["config"]["workload"]
-            out["legs"][name]["M"] = 1
+                                secondary=False, ceiling=False, b3=b3)
+            out["legs"][key] = {k: leg[k] for k in ("value", "unit", "ms_per_step", "dtype", "tok_per_s_equiv",
+                                                    "gemv_us", "roofline", "cold_pass", "cpu_baseline",
+                                                    "parity_spot_check", "steps", "warmup")}
+            out["legs"][key]["workload"] = leg["config"]["workload"] + (
+                ", compact base-3 codes (5 bits per weight)" if b3 else "")
+            out["legs"][key]["M"] = 1
     print(json.dumps(out), flush=True)
     release_device()
 

@@ -7,6 +7,8 @@ Coverage:
     the d=3 codec): every output of every projection of every layer;
   - the codec at 4 and 16 tokens: every output of the first and the last
     layer for every token, and 64 random rows of a few other projections;
+  - the codec packed with compact base-3 codes: the same, every output at
+    one token;
   - the BitNet-2B prefill stack (2048 tokens, int8): every output of the
     first and the last layer; every other layer sampled (16 random tokens x
     every row, and every token x 16 random rows, for every projection);
@@ -40,11 +42,11 @@ from tests.gpu_util import TOL, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def _stack(name, M=None, fused=False):
+def _stack(name, M=None, fused=False, b3=False):
     import bench
     import torch
     case = CASES[name]
-    st = bench.Stack(case, case.M if M is None else M, fused=fused)
+    st = bench.Stack(case, case.M if M is None else M, fused=fused, b3=b3)
     st.prepare()
     st.quantize()
     st.gemv()
@@ -211,6 +213,21 @@ def test_codec_several_tokens(M):
     last = st.case.model["layers"] - 1
     worst = _check_every_output(st, _layer_projs(st, 0) + _layer_projs(st, last))
     print("cfg4 M=%d worst per-token relative error %.3g" % (M, worst), flush=True)
+    _free(st)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_codec_compact_codes(M):
+    """The codec stack packed with compact base-3 codes (same canonical arrays,
+    the same oracle): every output at one token, the first and last layer in
+    full at 4 and 16 tokens."""
+    print("cfg4 compact codes M=%d" % M, flush=True)
+    st = _stack("cfg4", M=M, b3=True)
+    _check_sampled_rows(st, 80 + M)
+    last = st.case.model["layers"] - 1
+    idxs = range(len(st.projs)) if M == 1 else _layer_projs(st, 0) + _layer_projs(st, last)
+    worst = _check_every_output(st, idxs)
+    print("cfg4 compact codes M=%d worst per-token relative error %.3g" % (M, worst), flush=True)
     _free(st)
 
 
