@@ -23,10 +23,10 @@
 //   1. issues the code loads of its first item -- weights do not depend on
 //      the activations, so they stream in while the workgroup waits;
 //   2. waits for the blocks it reads;
-//   3. reads the phase's input vector (a few KiB, from L2/HBM), takes its
-//      RMSNorm and int8 quantisation into LDS -- every workgroup does this
-//      itself, in the same order, so all hold the same bytes and no extra
-//      barrier is needed;
+//   3. reads the phase's input vector (a few KiB, from L2/HBM, all loads in
+//      flight together), takes its RMSNorm and int8 quantisation into LDS --
+//      every workgroup does this itself, in the same order, so all hold the
+//      same bytes and no extra barrier is needed;
 //   4. runs its items: a 64-row block of one projection (GU: the same block
 //      of gate and of up, half the waves each), restricted to one of S
 //      column splits, the waves splitting that range further (the decode
@@ -47,7 +47,10 @@ namespace {
 
 using namespace tqk;
 
-constexpr int kThreads = 512;            // 8 waves
+#ifndef TQ_CHAIN_THREADS
+#define TQ_CHAIN_THREADS 512
+#endif
+constexpr int kThreads = TQ_CHAIN_THREADS;   // 8 waves (measured against 16)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxWidth = 8192;          // longest phase input (held in registers, 16 per thread)
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls of one wait before giving up (~seconds)
@@ -150,8 +153,12 @@ __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t targ
     if (threadIdx.x == 0) {
         uint32_t spins = 0;
         int ok = 1;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (__hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        for (;;) {
+            // both loads in flight together: one memory round trip per poll
+            const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int e = __hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (c >= target) break;
+            if (e) {
                 ok = 0;
                 break;
             }
@@ -175,44 +182,55 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return v;
 }
 
-// Input element i of a phase (global memory written by the previous phase).
-__device__ __forceinline__ float phase_input(const ChainDev& C, int ph, const float* x, int i)
+// The element of the phase input that position i reads (global memory
+// written by the previous phase): x, x1, act, or for O repeat(v) -- query
+// head h reads KV head h / (n_heads / n_kv).  `src` is the phase's base.
+__device__ __forceinline__ const float* phase_source(const ChainDev& C, int ph, const float* x)
 {
-    if (ph == PH_QKV) return ld_shared(x + i);
-    if (ph == PH_GU) return ld_shared(C.x1 + i);
-    if (ph == PH_DOWN) return ld_shared(C.act + i);
-    // O: repeat(v): query head h reads KV head h / (n_heads / n_kv)
-    const int head = i / C.head_dim, d = i - head * C.head_dim;
-    const int kvh = head / (C.n_heads / C.n_kv);
-    return ld_shared(C.qkv + C.nq + C.nkv + kvh * C.head_dim + d);
+    return ph == PH_QKV ? x : (ph == PH_GU ? C.x1 : (ph == PH_DOWN ? C.act : C.qkv + C.nq + C.nkv));
 }
 
 // RMSNorm of the phase input with weight w, then the per-token absmax int8
 // quantisation, into LDS (xq, zero-padded to whole 64-column chunks) and
 // *sx.  The steps are tq.h's; every workgroup computes the same bytes.  A
-// thread holds its kPer inputs and weights in registers, all loads issued
-// before the first use.
+// thread holds its kPer inputs and weights in registers.  Every load is
+// issued before the first use and none sits under a branch (positions past
+// n read element n - 1 and are zeroed afterwards): behind branches each
+// load waited for the one before, one memory round trip per element.
 constexpr int kPer = kMaxWidth / kThreads;
 
-__device__ __forceinline__ void load_norm_weight(const float* w, int n, float (&wt)[kPer])
+// The O phase's element positions (repeat(v)) of this thread, computed once
+// per launch: the integer divisions would otherwise recur in every layer.
+__device__ __forceinline__ void o_positions(const ChainDev& C, int (&o_at)[kPer])
 {
+    const int group = C.n_heads / C.n_kv, n = C.nq;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int i = threadIdx.x + j * kThreads;
-        wt[j] = i < n ? w[i] : 0.0f;
+        const int i = min((int)threadIdx.x + j * kThreads, n - 1);
+        const int head = i / C.head_dim, d = i - head * C.head_dim;
+        o_at[j] = (head / group) * C.head_dim + d;
     }
 }
 
 __device__ void norm_quant(const ChainDev& C, int ph, const float* x, const float* w, int n, int8_t* xq,
-                           float* sx, double* red_d, float* red_f)
+                           float* sx, double* red_d, float* red_f, const int (&o_at)[kPer])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* src = phase_source(C, ph, x);
+    int at[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) at[j] = ph == PH_O ? o_at[j] : min(tid + j * kThreads, n - 1);
     float v[kPer], wt[kPer];
-    load_norm_weight(w, n, wt);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * kThreads;
-        v[j] = i < n ? phase_input(C, ph, x, i) : 0.0f;
+        v[j] = ld_shared(src + at[j]);
+        wt[j] = w[min(tid + j * kThreads, n - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const bool in = tid + j * kThreads < n;
+        v[j] = in ? v[j] : 0.0f;
+        wt[j] = in ? wt[j] : 0.0f;
     }
     double ss = 0.0;
 #pragma unroll
@@ -276,12 +294,14 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
+    int o_at[kPer];
+    o_positions(C, o_at);
 
     for (int l = 0; l < C.n_layers; ++l) {
         const LayerDev& Ld = C.layers[l];
         for (int ph = 0; ph < 4; ++ph) {
             const PhaseDev P = ld_uniform_struct(&Cp->ph[ph]);
-            // GU: waves 0..3 run gate, 4..7 up; else all waves one projection
+            // GU: waves 0..kWaves/2-1 run gate, the others up; else all waves one projection
             const int nw = ph == PH_GU ? kWaves / 2 : kWaves;
             const int wp = ph == PH_GU ? wave / nw : 0;
             const int ws = wave - wp * nw;
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                 ok = wait_count(C, dl + DONE_GU, (uint32_t)C.ph[PH_GU].groups, &flag);
             }
             if (!ok) return;
-            norm_quant(C, ph, x, Ld.norm[ph], P.width, xq, &sx_lds, red_d, (float*)red_f);
+            norm_quant(C, ph, x, Ld.norm[ph], P.width, xq, &sx_lds, red_d, (float*)red_f, o_at);
             const float sx = sx_lds;
             for (int item = first; item < P.items; item += C.G) {
                 int part;
