@@ -27,8 +27,15 @@ _CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-
            "-std=c99", "-Wall", "-Wextra"]
 
 
-def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc (plain C, OpenMP over output rows)."""
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = False, sanitize: bool = False, out: str = "") -> str:
+    """Compile liboracle.so with gcc (plain C, OpenMP over output rows).
+    sanitize: AddressSanitizer and UndefinedBehaviorSanitizer, into `out`."""
+    if sanitize:
+        subprocess.check_call(["gcc", *_CFLAGS, *_SAN_FLAGS, SRC, "-o", out, "-lm"])
+        return out
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *_CFLAGS, SRC, "-o", tmp, "-lm"])
@@ -208,9 +215,11 @@ _default = None
 
 
 def default() -> Oracle:
+    """The oracle build the tests use (TQ_ORACLE_LIB names another build, e.g.
+    a sanitizer one)."""
     global _default
     if _default is None:
-        _default = Oracle(build())
+        _default = Oracle(os.environ.get("TQ_ORACLE_LIB") or build())
     return _default
 
 

@@ -42,6 +42,12 @@ def _deps_mtime() -> float:
 
 
 INCREMENTAL = False
+# --sanitize: the host code of every translation unit built with AddressSanitizer
+# and UndefinedBehaviorSanitizer (device code unchanged) into _build/asan/libtq.so,
+# for running the CPU tests of the ABI's validation paths under the sanitizers.
+SANITIZE = False
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _compile(src: str, obj: str, extra=()) -> str:
@@ -49,7 +55,7 @@ def _compile(src: str, obj: str, extra=()) -> str:
     if INCREMENTAL and os.path.exists(obj) and \
             os.path.getmtime(obj) > max(os.path.getmtime(src), _deps_mtime()):
         return obj
-    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *(SAN_FLAGS if SANITIZE else []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
@@ -58,7 +64,7 @@ def _compile(src: str, obj: str, extra=()) -> str:
 
 def _link(objs, out):
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SAN_FLAGS if SANITIZE else []), *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed for %s:\n%s" % (out, r.stderr[-4000:]))
@@ -68,13 +74,15 @@ def _link(objs, out):
 def build_libtq(jobs: int = 0) -> str:
     jobs = jobs or min(8, os.cpu_count() or 4)
     objs = []
+    sub = "asan" if SANITIZE else "tq"
+    out = os.path.join(BUILD_DIR, "asan", "libtq.so") if SANITIZE else LIBTQ
     with cf.ThreadPoolExecutor(jobs) as ex:
-        futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(BUILD_DIR, "tq", s + ".o"))
+        futs = [ex.submit(_compile, os.path.join(CSRC, s), os.path.join(BUILD_DIR, sub, s + ".o"))
                 for s in TQ_SOURCES]
         for f in futs:
             objs.append(f.result())
-    _link(objs, LIBTQ)
-    return LIBTQ
+    _link(objs, out)
+    return out
 
 
 def build_synth() -> str:
@@ -91,5 +99,9 @@ def build_all() -> None:
 
 if __name__ == "__main__":
     INCREMENTAL = "--incremental" in sys.argv
-    build_all()
-    print("built", LIBTQ, file=sys.stderr)
+    SANITIZE = "--sanitize" in sys.argv
+    if SANITIZE:
+        print("built", build_libtq(), file=sys.stderr)
+    else:
+        build_all()
+        print("built", LIBTQ, file=sys.stderr)

@@ -13,7 +13,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libtq.so")
+# TQ_LIB names another build of the library (e.g. the sanitizer build of its host code)
+LIB_PATH = os.environ.get("TQ_LIB") or os.path.join(PKG, "libtq.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_VALUE, ERR_UNSUPPORTED, ERR_DEVICE = range(7)
 SCALE_TENSOR, SCALE_GROUP_F16, SCALE_CODEBOOK, SCALE_CODEBOOK_B3 = 0, 1, 2, 3
