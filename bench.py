@@ -582,12 +582,16 @@ def _trace_rows(d):
     return list(csv.DictReader(open(f[0]))) if f else []
 
 
-def _pmc_means(d):
+def _pmc_values(d):
     out = {}
     for f in glob.glob(os.path.join(d, "*_counter_collection.csv")):
         for r in csv.DictReader(open(f)):
             out.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+    return out
+
+
+def _pmc_means(d):
+    return {k: (sum(v) / len(v), len(v)) for k, v in _pmc_values(d).items()}
 
 
 def summarize(args) -> None:
@@ -600,20 +604,27 @@ def summarize(args) -> None:
         lines += ["Command: `%s`" % args.trace_cmd, "", "rocprofv3 --kernel-trace --stats, top kernels by total time:", "",
                   "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
         rows = list(csv.DictReader(open(stats[0])))
-        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        ranked = sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))
+        shown = ranked[:8] + [r for r in ranked[8:] if kern in r["Name"]]
+        for r in shown:
             lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3,
                                                                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        for r in rows:
             if kern in r["Name"]:
                 rec["avg_us"] = round(float(r["AverageNs"]) / 1e3, 3)
                 rec["calls"] = int(r["Calls"])
         tr = [r for r in _trace_rows(args.trace_dir) if kern in r["Kernel_Name"]]
         if tr:
             tr.sort(key=lambda r: int(r["Start_Timestamp"]))
-            last = tr[-args.timed_launches:] if args.timed_launches else tr
-            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+            if args.timed_launches:
+                sel = tr[args.first_launch:args.first_launch + args.timed_launches]
+                what = "launches %d .. %d (the timed region)" % (args.first_launch, args.first_launch + len(sel) - 1)
+            else:
+                sel, what = tr, "all launches"
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
             rec["timed_avg_us"] = round(sum(d) / len(d), 3)
-            lines += ["", "Kernel `%s`: average of all %d launches %.2f us; of the last %d (the timed region) %.2f us."
-                      % (kern, len(tr), rec.get("avg_us", float("nan")), len(last), rec["timed_avg_us"])]
+            lines += ["", "Kernel `%s`: average of all %d launches %.2f us; of %s %.2f us."
+                      % (kern, len(tr), rec.get("avg_us", float("nan")), what, rec["timed_avg_us"])]
     if args.fetch_dir and args.write_dir:
         f, w = _pmc_means(args.fetch_dir), _pmc_means(args.write_dir)
 
@@ -622,8 +633,16 @@ def summarize(args) -> None:
                 if name in k and c == counter:
                     return v
             return None
-        read_kib = find(f, "k_stream_read", "FETCH_SIZE")
-        fill_kib = find(w, "vectorized_elementwise_kernel<16", "WRITE_SIZE")
+        # calibration: the largest dispatch of the harness read and of torch's
+        # fill is the one of known size (the smaller ones warm the GPU up or
+        # evict the caches)
+        def largest(d, name, counter):
+            for (k, c), v in _pmc_values(d).items():
+                if name in k and c == counter:
+                    return (max(v), len(v))
+            return None
+        read_kib = largest(args.fetch_dir, "k_stream_read", "FETCH_SIZE")
+        fill_kib = largest(args.write_dir, "vectorized_elementwise_kernel<16", "WRITE_SIZE")
         gf, gw = find(f, kern, "FETCH_SIZE"), find(w, kern, "WRITE_SIZE")
         fetch_factor = (args.read_bytes / 1024) / read_kib[0]
         write_factor = (args.fill_bytes / 1024) / fill_kib[0]
@@ -778,6 +797,7 @@ def main():
         ap.add_argument("--trace-dir")
         ap.add_argument("--trace-cmd", default="")
         ap.add_argument("--timed-launches", type=int, default=0)
+        ap.add_argument("--first-launch", type=int, default=0, help="index of the first timed launch of the kernel")
         ap.add_argument("--fetch-dir")
         ap.add_argument("--write-dir")
         ap.add_argument("--pmc-cmd", default="")
