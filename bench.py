@@ -340,9 +340,12 @@ def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
     """The kernel a grouped decode plan launches (as rocprofv3 names it)."""
     if layout == CODEBOOK_B3:
         planes = 1              # the compact codec's kernels take one combined value per weight
-    if plan.family >= 1000:     # several bf16 tokens: the matrix-core decode kernel
-        ks = 32 if layout in (TENSOR, GROUP_F16) and (layout == TENSOR or group % 32 == 0) else 16
-        return "k_gemm_skinny_grouped<%d, %d, %d>" % (layout, planes, ks)
+    if plan.family >= 1000:     # several tokens: the matrix-core decode kernel
+        if run_type == I8:
+            ks = 64
+        else:
+            ks = 32 if layout in (TENSOR, GROUP_F16) and (layout == TENSOR or group % 32 == 0) else 16
+        return "k_gemm_skinny_grouped<%d, %d, %d, %d>" % (run_type, layout, planes, ks)
     mt = 1 if plan.M <= 1 else 4
     kind = "k_gemv_wave_items" if plan.mode == 1 else "k_gemv_grouped"   # an item per wave, or per workgroup
     return "%s<%d, %d, %d, %d>" % (kind, run_type, layout, planes, mt)

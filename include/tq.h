@@ -177,8 +177,11 @@ tq_status tq_act_quant_int8_batch(const tq_act_segment* segments, int32_t count,
  * Decode product for M <= 16 tokens (vector-ALU kernels: unpack, add/subtract,
  * scale per group; up to 4 tokens per pass over the codes, one launch per
  * slice of 4 tokens beyond that).  With TQ_BF16 and M >= 3 (5 for the two
- * codebook layouts; x 16-byte aligned) the product runs on the matrix cores
- * instead, as tq_gemm does; the results meet the same bound.
+ * codebook layouts), or TQ_I8, M >= 2 and groups of 64 or more columns (or
+ * a per-tensor scale), and x 16-byte aligned, the product runs on the
+ * matrix cores instead, as tq_gemm does, one pass over the codes for all M
+ * tokens; the results meet the same bound (TQ_I8 with one plane and a
+ * per-tensor scale: the same bits).
  *   x         device [M][Kin] of x_type
  *   x_scale   device fp32 [M], TQ_I8 only (from tq_act_quant_int8), else unused
  *             (TQ_F32_Q8 computes the per-token scales itself)
@@ -250,9 +253,10 @@ tq_status tq_gemv_grouped_workspace_size(const tq_problem* problems, int32_t cou
 /*
  * Validate the problems, write their descriptor table and the work list into
  * `workspace` (device, caller-owned) and fill `plan`.  With TQ_BF16, M >= 3
- * (5 for the codebook layouts) and every x 16-byte aligned the plan is a
- * matrix-core plan (as from tq_gemm_grouped_prepare; the shape hints are
- * then unused).  The run is one launch
+ * (5 for the codebook layouts), or TQ_I8, M >= 2 and every problem's groups
+ * of 64 columns or more (or a per-tensor scale), every x 16-byte aligned and
+ * no shape hint in `plan`, the plan is a matrix-core plan (as from
+ * tq_gemm_grouped_prepare).  Otherwise the run is one launch
  * with one workgroup per item, an item being `row_blocks` consecutive 64-row
  * blocks of one problem, each split over `waves` waves; items are ordered
  * longest first.  On entry plan->waves and plan->row_blocks choose the shape
@@ -280,9 +284,10 @@ tq_status tq_gemv_grouped_prepare(const tq_problem* problems, int32_t count, int
  * layer: every expert's matrix is fit on its own (sasori page, "How it works
  * & paper"), so each expert is one problem with its own blob, and the tokens
  * the router sent to it are gathered into its x.  A problem with no tokens
- * takes no workgroup (its pointers may then be NULL).  With TQ_BF16, a mean
- * count of at least 3 (5 for the codebook layouts) over the problems that have
- * tokens, every x 16-byte
+ * takes no workgroup (its pointers may then be NULL).  With TQ_BF16 and a
+ * mean count of at least 3 (5 for the codebook layouts) over the problems
+ * that have tokens, or TQ_I8 and a mean count of at least 2 (groups of 64
+ * columns or more), every x 16-byte
  * aligned and no shape hint in `plan`, the plan is a matrix-core plan whose
  * tiles cover each problem's own count; otherwise the vector-ALU kernels take
  * up to 4 tokens per pass and a problem with more is cut into slices of 4 (as

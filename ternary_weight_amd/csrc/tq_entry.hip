@@ -177,18 +177,19 @@ tq_status grouped_prepare(const tq_problem* problems, const int32_t* tokens, int
             row_blocks = x_type == TQ_F32_Q8 ? 4 : 1;
         }
     }
-    // several bf16 tokens: the matrix-core kernels, if every x allows 16-byte
-    // loads.  With per-problem counts the measure is the mean count of the
-    // problems that have tokens (a 16-token tile costs the same for 1 or 16;
-    // the vector ALUs pay per token), and a shape hint keeps the vector ALUs.
+    // several bf16 or int8 tokens: the matrix-core kernels, if every x allows
+    // 16-byte loads and no shape hint asks for the vector ALUs.  With
+    // per-problem counts the measure is the mean count of the problems that
+    // have tokens (a 16-token tile costs the same for 1 or 16; the vector
+    // ALUs pay per pass of 4 tokens).
     int64_t busy = 0, sum = 0;
     for (int32_t i = 0; tokens && i < count; ++i) {
         busy += tokens[i] > 0;
         sum += std::max(tokens[i], 0);
     }
-    const int64_t mfma_min = count > 0 ? tq_bf16_mfma_min_m(problems[0].desc->scale_layout) : TQ_BF16_MFMA_MIN_M;
-    bool mfma = count > 0 && x_type == TQ_BF16 &&
-                (tokens ? !hinted && sum >= mfma_min * std::max<int64_t>(busy, 1) : M >= mfma_min);
+    const int64_t mfma_min = count > 0 ? tq_mfma_min_m(x_type, problems[0].desc->scale_layout) : INT64_MAX;
+    bool mfma = count > 0 && !hinted && (x_type == TQ_BF16 || x_type == TQ_I8) &&
+                (tokens ? sum >= mfma_min * std::max<int64_t>(busy, 1) : M >= mfma_min);
     for (int32_t i = 0; i < count && mfma; ++i) {
         mfma = ((uintptr_t)problems[i].x & 15) == 0;
         // a shape the matrix-core kernels do not take sends the plan to the vector ALUs

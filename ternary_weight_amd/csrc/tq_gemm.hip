@@ -21,12 +21,23 @@ int gemm_row(const tq_layout& L, int x_type)
     return TQ_GEMM_ROW_GROUP;
 }
 
-// Kernel tables: 0 int8, 1 bf16, 2 bf16 with at most 16 tokens.
-int table_index(int x_type, int64_t M) { return x_type == TQ_I8 ? 0 : (M <= TQ_MAX_M_GEMV ? 2 : 1); }
+// Kernel tables: 0 int8, 1 bf16, 2 bf16 with at most 16 tokens, 3 int8 with
+// at most 16 tokens.
+constexpr int kTables = 4;
+int table_index(int x_type, int64_t M)
+{
+    const bool few = M <= TQ_MAX_M_GEMV;
+    return x_type == TQ_I8 ? (few ? 3 : 0) : (few ? 2 : 1);
+}
 
 const tq_gemm_kernel (*gemm_table(int index))[4]
 {
-    return index == 0 ? tq_gemm_table_i8() : (index == 1 ? tq_gemm_table_bf16() : tq_gemm_table_bf16_skinny());
+    switch (index) {
+    case 0: return tq_gemm_table_i8();
+    case 1: return tq_gemm_table_bf16();
+    case 2: return tq_gemm_table_bf16_skinny();
+    default: return tq_gemm_table_i8_skinny();
+    }
 }
 
 // Kernel for (x_type, layout, K, g, M), or null with the reason recorded.
@@ -64,7 +75,7 @@ int gemm_family(const tq_layout& L, int x_type, int64_t M)
 const tq_gemm_kernel* kernel_of_family(int family)
 {
     const int f = family - kFamilyBase;
-    if (f < 0 || f >= 3 * TQ_GEMM_ROWS * 4) return nullptr;
+    if (f < 0 || f >= kTables * TQ_GEMM_ROWS * 4) return nullptr;
     const tq_gemm_kernel* k = &gemm_table(f / (TQ_GEMM_ROWS * 4))[(f / 4) % TQ_GEMM_ROWS][f % 4];
     return k->single ? k : nullptr;
 }

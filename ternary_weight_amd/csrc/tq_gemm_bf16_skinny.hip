@@ -7,10 +7,10 @@
 const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4]
 {
     static const tq_gemm_kernel t[TQ_GEMM_ROWS][4] = {
-        TQ_SKINNY_ROW(TQ_SCALE_TENSOR, 32),
-        TQ_SKINNY_ROW(TQ_SCALE_GROUP_F16, 32),
-        TQ_SKINNY_ROW(TQ_SCALE_GROUP_F16, 16),
-        TQ_SKINNY_ROW(TQ_SCALE_CODEBOOK, 16),
+        TQ_SKINNY_ROW(TQ_BF16, TQ_SCALE_TENSOR, 32),
+        TQ_SKINNY_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 32),
+        TQ_SKINNY_ROW(TQ_BF16, TQ_SCALE_GROUP_F16, 16),
+        TQ_SKINNY_ROW(TQ_BF16, TQ_SCALE_CODEBOOK, 16),
         TQ_SKINNY_ROW_B3,
     };
     return t;

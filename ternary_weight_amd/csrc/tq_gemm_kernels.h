@@ -20,8 +20,9 @@ enum { TQ_GEMM_ROW_TENSOR = 0, TQ_GEMM_ROW_GROUP = 1, TQ_GEMM_ROW_GROUP16 = 2, T
 // Kernels of one activation type, indexed [row][K - 1]; null where unsupported.
 const tq_gemm_kernel (*tq_gemm_table_i8())[4];
 const tq_gemm_kernel (*tq_gemm_table_bf16())[4];
-// bf16 kernels for a few tokens (M <= 16): one 16-token tile, 4 waves along the rows.
+// Kernels for a few tokens (M <= 16): one 16-token tile, 4 waves along the rows.
 const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4];
+const tq_gemm_kernel (*tq_gemm_table_i8_skinny())[4];
 
 #define TQ_GEMM_ENTRY(XT, LAYOUT, K, FM, FN, KS, WM)                                               \
     {tqm::k_gemm_single<XT, LAYOUT, K, FM, FN, KS, WM>, tqm::k_gemm_grouped<XT, LAYOUT, K, FM, FN, KS, WM>, \
@@ -36,12 +37,12 @@ const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4];
 #define TQ_GEMM_ROW_B3(FM, FN, WM) \
     {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_GEMM_ENTRY(TQ_BF16, TQ_SCALE_CODEBOOK_B3, 1, FM, FN, 16, WM), \
      TQ_GEMM_NONE_ENTRY}
-// The few-token bf16 kernels (tq_gemm_skinny.h): one 16-token tile, 4 waves
-// of 64 rows each, a 64-column chunk of every plane per step.
-#define TQ_SKINNY_ENTRY(LAYOUT, K, KS) \
-    {tqm::k_gemm_skinny<LAYOUT, K, KS>, tqm::k_gemm_skinny_grouped<LAYOUT, K, KS>, 1, 4, KS, 1}
-#define TQ_SKINNY_ROW(LAYOUT, KS)                                                               \
-    {TQ_SKINNY_ENTRY(LAYOUT, 1, KS), TQ_SKINNY_ENTRY(LAYOUT, 2, KS), TQ_SKINNY_ENTRY(LAYOUT, 3, KS), \
-     TQ_SKINNY_ENTRY(LAYOUT, 4, KS)}
+// The few-token kernels (tq_gemm_skinny.h): one 16-token tile, 4 waves of
+// 64 rows each, a 64-column chunk of every plane per step.
+#define TQ_SKINNY_ENTRY(XT, LAYOUT, K, KS) \
+    {tqm::k_gemm_skinny<XT, LAYOUT, K, KS>, tqm::k_gemm_skinny_grouped<XT, LAYOUT, K, KS>, 1, 4, KS, 1}
+#define TQ_SKINNY_ROW(XT, LAYOUT, KS)                                                                     \
+    {TQ_SKINNY_ENTRY(XT, LAYOUT, 1, KS), TQ_SKINNY_ENTRY(XT, LAYOUT, 2, KS), TQ_SKINNY_ENTRY(XT, LAYOUT, 3, KS), \
+     TQ_SKINNY_ENTRY(XT, LAYOUT, 4, KS)}
 #define TQ_SKINNY_ROW_B3 \
-    {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_SKINNY_ENTRY(TQ_SCALE_CODEBOOK_B3, 1, 16), TQ_GEMM_NONE_ENTRY}
+    {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_SKINNY_ENTRY(TQ_BF16, TQ_SCALE_CODEBOOK_B3, 1, 16), TQ_GEMM_NONE_ENTRY}

@@ -104,18 +104,22 @@ struct SkinnyStage {
     static constexpr int WST = 64 * (CDS + SWN);   // dwords per wave and stage
 };
 
-template <int LAYOUT, int K, int KS, int GM>
+template <int XT, int LAYOUT, int K, int KS, int GM>
 __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const LDS_AS float* cb_lds,
                                             const LDS_AS uint8_t* b3_lut, LDS_AS uint32_t* wlds)
 {
-    using MF = Mfma<TQ_BF16, KS>;
+    using MF = Mfma<XT, KS>;
     using Frag = typename MF::Frag;
-    using Part = f32x4;
+    using Part = typename MF::Part;
+    constexpr bool kI8 = XT == TQ_I8;
+    constexpr int ESZ = kI8 ? 1 : 2;             // bytes per activation
     constexpr bool kB3 = LAYOUT == TQ_SCALE_CODEBOOK_B3;
     constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || kB3;
     constexpr bool kTensor = LAYOUT == TQ_SCALE_TENSOR;
-    static_assert(!kB3 || (K == 1 && KS == 16), "compact base-3 codes: one stream, 16-column steps");
-    static_assert(KS == 32 || KS == 16, "MFMA step");
+    // int8, one plane, per-tensor scale: the int32 sum is the result (exact)
+    constexpr bool kDirect = kI8 && kTensor && K == 1;
+    static_assert(!kB3 || (!kI8 && K == 1 && KS == 16), "compact base-3 codes: one stream, 16-column steps");
+    static_assert(kI8 ? (KS == 64 && !kCb) : (KS == 32 || KS == 16), "MFMA step");
     static_assert((GM == kGroupNone) == kTensor, "group mode");
     constexpr int KP = K;                        // code streams per chunk: planes, or the one B3 stream
     constexpr int KPC = 64 / KS;                 // MFMA steps per chunk
@@ -126,8 +130,8 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     // where four would not fit the registers of two waves per SIMD
     constexpr int NBUF = K == 4 ? 2 : TQ_SKINNY_NBUF;
     static_assert(NBUF % 2 == 0 && NBUF >= 2, "chunks in flight");
-    constexpr int XL = KS == 32 ? 2 : 4;         // x loads per chunk (16 or 8 bytes each)
-    using XF = typename std::conditional<KS == 32, u32x4, u32x2>::type;
+    constexpr int XL = 64 / KS;                  // x loads per chunk (one MFMA step's fragment each)
+    using XF = typename std::conditional<KS * ESZ == 64, u32x4, u32x2>::type;
     static_assert(sizeof(XF) == sizeof(Frag), "an x load is one MFMA step's fragment");
     constexpr int CL = kB3 ? 3 : KP;             // code loads per chunk
     using B3T = B3Table<8>;
@@ -142,13 +146,13 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     // Buffer resources (tq_decode.h): a lane whose VGPR offset is at or past
     // the size reads zeros, so token rows past M and row blocks past N read
     // zeros; the per-chunk SGPR offsets stay inside the data.
-    const __amdgpu_buffer_rsrc_t rx = rsrc(P.x, (int64_t)M * Kin * 2);
+    const __amdgpu_buffer_rsrc_t rx = rsrc(P.x, (int64_t)M * Kin * ESZ);
     const __amdgpu_buffer_rsrc_t rc =
         rsrc(P.codes, kB3 ? (int64_t)NB * NC * TQ_B3_CHUNK_BYTES : (int64_t)NB * NC * K * 1024);
     const __amdgpu_buffer_rsrc_t rs = rsrc(P.scales, kTensor ? 256 : (kCb ? (int64_t)NB * P.NID * 256
                                                                           : (int64_t)NB * P.NGD * K * 256));
     // x: lane (r, q) takes token r, in step s columns s KS + q KS / 4 .. + KS / 4 - 1
-    const uint32_t xv0 = (uint32_t)r * (uint32_t)Kin * 2u + (uint32_t)q * (KS / 2);
+    const uint32_t xv0 = ((uint32_t)r * (uint32_t)Kin + (uint32_t)q * (KS / 4)) * ESZ;
     // codes: lane l loads row n0 + l; the block's offset is in the VGPR offset
     const uint32_t cv = kB3 ? (uint32_t)rb * (uint32_t)NC * TQ_B3_CHUNK_BYTES + (uint32_t)lane * 16u
                             : ((uint32_t)rb * (uint32_t)NC * K * 64u + (uint32_t)lane) * 16u;
@@ -192,9 +196,9 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     };
     auto load = [&](int c, u32x4 (&cb)[CL], uint32_t (&sw)[SWN > 0 ? SWN : 1], XF (&xa)[XL]) {
         c = c < NC ? c : NC - 1;   // a prefetch past the last chunk loads the last again (never used)
-        const uint32_t xv = xv0 + (uint32_t)c * 128u;
+        const uint32_t xv = xv0 + (uint32_t)c * (64u * ESZ);
 #pragma unroll
-        for (int i = 0; i < XL; ++i) xa[i] = buffer_load<XF>(rx, xv + (uint32_t)i * (KS == 32 ? 64u : 32u), 0);
+        for (int i = 0; i < XL; ++i) xa[i] = buffer_load<XF>(rx, xv + (uint32_t)i * (KS * ESZ), 0);
         if constexpr (kB3) {
             const uint32_t so = (uint32_t)c * TQ_B3_CHUNK_BYTES;
             cb[0] = buffer_load<u32x4, kCacheNT>(rc, cv, so);
@@ -232,13 +236,16 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     for (int fn = 0; fn < 4; ++fn) {
         acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KP; ++k) part[k][fn] = Part{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < KP; ++k) part[k][fn] = Part{0, 0, 0, 0};
     }
 
     // the weight fragment of plane k, tile fn, step s from the stage
     auto frag = [&](const LDS_AS uint32_t* st, int k, int fn, int s) -> Frag {
         const LDS_AS uint32_t* row = st + (16 * fn + r) * CDS;
-        if constexpr (kB3) {
+        if constexpr (kI8) {
+            // the one step: dword q of the plane's slot, int8 trits of its 16 columns in order
+            return MF::decode(row[4 * k + q], q);
+        } else if constexpr (kB3) {
             const uint32_t i = b3_i[s];
             const uint32_t wv = __builtin_amdgcn_alignbit(row[i + 1], row[i], b3_h[s]);
             const uint32_t a0 = ((wv & 0x3FFu) << B3T::kShift) | b3_copy;
@@ -288,12 +295,13 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             for (int k = 0; k < KP; ++k) {
                 const float sc = group_scale(st, c, grp, k, fn);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[fn][e] = fmaf(sc, part[k][fn][e], acc[fn][e]);
+                for (int e = 0; e < 4; ++e) acc[fn][e] = fmaf(sc, (float)part[k][fn][e], acc[fn][e]);
             }
     };
     // x columns past Kin (a ragged last step of a per-tensor scale): zero,
     // so that whatever the next token's row holds there adds nothing
     auto mask_x = [&](int c, XF (&xa)[XL]) {
+        if constexpr (kI8) return;   // integer products: zero trits add exactly zero
 #pragma unroll
         for (int i = 0; i < XL; ++i)
 #pragma unroll
@@ -313,13 +321,13 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         auto one_step = [&](int s, bool zero) {
             // x in the weight fragments' column order (the compact codes'
             // table gives consecutive columns)
-            const Frag a = __builtin_bit_cast(Frag, kB3 ? xa[s] : xodd_even(xa[s]));
+            const Frag a = __builtin_bit_cast(Frag, kB3 || kI8 ? xa[s] : xodd_even(xa[s]));
 #pragma unroll
             for (int k = 0; k < KP; ++k)
 #pragma unroll
                 for (int fn = 0; fn < 4; ++fn) {
                     const Frag b = frag(st, k, fn, s);
-                    part[k][fn] = MF::run(a, b, zero ? Part{0.f, 0.f, 0.f, 0.f} : part[k][fn]);
+                    part[k][fn] = MF::run(a, b, zero ? Part{0, 0, 0, 0} : part[k][fn]);
                 }
             if constexpr (GM == kGroupStep) apply(st, c, c * KPC + s);
         };
@@ -338,7 +346,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 #pragma unroll
                     for (int k = 0; k < KP; ++k)
 #pragma unroll
-                        for (int fn = 0; fn < 4; ++fn) part[k][fn] = Part{0.f, 0.f, 0.f, 0.f};
+                        for (int fn = 0; fn < 4; ++fn) part[k][fn] = Part{0, 0, 0, 0};
                 }
             }
         }
@@ -366,7 +374,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     for (int u = 0; u + 1 < NBUF; ++u) {   // the last NC % NBUF chunks, already loaded
         if (t + u < NC) step(u, t + u);
     }
-    if constexpr (GM == kGroupNone) {
+    if constexpr (GM == kGroupNone && !kDirect) {
         // per-tensor scale: one fp32 per plane, after the whole row
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
@@ -374,19 +382,32 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 #pragma unroll
             for (int fn = 0; fn < 4; ++fn)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[fn][e] = fmaf(sc, part[k][fn][e], acc[fn][e]);
+                for (int e = 0; e < 4; ++e) acc[fn][e] = fmaf(sc, (float)part[k][fn][e], acc[fn][e]);
         }
     }
 
-    // lane (r, q) holds weight row n0 + 16 fn + r of tokens 4 q + e
+    // lane (r, q) holds weight row n0 + 16 fn + r of tokens 4 q + e; int8
+    // activations take their token's scale (one plane with a per-tensor
+    // scale: y = fl32(float(acc) * fl32(s_w * x_scale[m])), tq.h)
+    const float s_w = kDirect ? ld_uniform((const float*)P.scales) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int m = 4 * q + e;
         if (m >= M) continue;
+        const float xs = kI8 ? P.x_scale[m] : 1.0f;
+        const float cm = kDirect ? s_w * xs : xs;
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn) {
             const int n = n0 + 16 * fn + r;
-            if (n < N) P.y[(int64_t)m * N + n] = acc[fn][e];
+            if (n >= N) continue;
+            const int64_t o = (int64_t)m * N + n;
+            if constexpr (kDirect) {
+                const int v = part[0][fn][e];
+                P.y[o] = (float)v * cm;
+                if (P.acc) P.acc[o] = v;
+            } else {
+                P.y[o] = kI8 ? acc[fn][e] * cm : acc[fn][e];
+            }
         }
     }
 }
@@ -394,31 +415,31 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 // The group mode of a launch: groups of the step's width end with every
 // step, larger ones after g / KS steps (one kernel takes both; the branch is
 // uniform).
-template <int LAYOUT, int K, int KS>
+template <int XT, int LAYOUT, int K, int KS>
 __device__ __forceinline__ void skinny_dispatch(const tq_prob_dev& P, int tn, const LDS_AS float* cb_lds,
                                                 const LDS_AS uint8_t* b3_lut, LDS_AS uint32_t* wlds)
 {
     if constexpr (LAYOUT == TQ_SCALE_TENSOR) {
-        skinny_tile<LAYOUT, K, KS, kGroupNone>(P, tn, cb_lds, b3_lut, wlds);
+        skinny_tile<XT, LAYOUT, K, KS, kGroupNone>(P, tn, cb_lds, b3_lut, wlds);
     } else {
-        if (P.g == KS) skinny_tile<LAYOUT, K, KS, kGroupStep>(P, tn, cb_lds, b3_lut, wlds);
-        else skinny_tile<LAYOUT, K, KS, kGroupSteps>(P, tn, cb_lds, b3_lut, wlds);
+        if (P.g == KS) skinny_tile<XT, LAYOUT, K, KS, kGroupStep>(P, tn, cb_lds, b3_lut, wlds);
+        else skinny_tile<XT, LAYOUT, K, KS, kGroupSteps>(P, tn, cb_lds, b3_lut, wlds);
     }
 }
 
-template <int LAYOUT, int K, int KS>
+template <int XT, int LAYOUT, int K, int KS>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny(tq_prob_dev P, int /*tiles_m*/)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
     __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
     __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
     stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
-    skinny_dispatch<LAYOUT, K, KS>(P, blockIdx.x, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
+    skinny_dispatch<XT, LAYOUT, K, KS>(P, blockIdx.x, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
                                    (LDS_AS uint32_t*)wlds);
 }
 
 // Grouped: item i = (problem, tile); one token tile per problem.
-template <int LAYOUT, int K, int KS>
+template <int XT, int LAYOUT, int K, int KS>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny_grouped(const tq_prob_dev* probs, const int2* items)
 {
     const int2 it = items[blockIdx.x];
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny_grouped(const tq_pr
     __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
     __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
     stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
-    skinny_dispatch<LAYOUT, K, KS>(P, it.y, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
+    skinny_dispatch<XT, LAYOUT, K, KS>(P, it.y, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
                                    (LDS_AS uint32_t*)wlds);
 }
 

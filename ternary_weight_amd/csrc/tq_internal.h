@@ -64,14 +64,27 @@ tq_status tq_fail_problem(tq_status s, int32_t i);
 #ifndef TQ_BF16_MFMA_MIN_M_B3
 #define TQ_BF16_MFMA_MIN_M_B3 5
 #endif
+// int8 decode with at least this many tokens runs on the matrix cores (one
+// pass over the codes for up to 16 tokens, where the vector ALUs take them
+// 4 at a time), when the groups are whole 64-column steps and x is 16-byte
+// aligned.
+#ifndef TQ_I8_MFMA_MIN_M
+#define TQ_I8_MFMA_MIN_M 2
+#endif
 static inline int64_t tq_bf16_mfma_min_m(int layout)
 {
     return layout == TQ_SCALE_CODEBOOK ? TQ_BF16_MFMA_MIN_M_CODEC
                                        : (layout == TQ_SCALE_CODEBOOK_B3 ? TQ_BF16_MFMA_MIN_M_B3 : TQ_BF16_MFMA_MIN_M);
 }
+// The fewest tokens of a decode call that go to the matrix cores (x_type
+// TQ_BF16 or TQ_I8; never for the others).
+static inline int64_t tq_mfma_min_m(int x_type, int layout)
+{
+    return x_type == TQ_BF16 ? tq_bf16_mfma_min_m(layout) : (x_type == TQ_I8 ? TQ_I8_MFMA_MIN_M : INT64_MAX);
+}
 static inline bool tq_gemv_uses_mfma(int x_type, int layout, int64_t M, const void* x)
 {
-    return x_type == TQ_BF16 && M >= tq_bf16_mfma_min_m(layout) && ((uintptr_t)x & 15) == 0;
+    return M >= tq_mfma_min_m(x_type, layout) && ((uintptr_t)x & 15) == 0;
 }
 // tq_gemm_grouped_prepare with per-problem token counts (tokens may be NULL:
 // every problem has M); tq_gemm.hip.

@@ -313,8 +313,8 @@ def test_grouped_matches_oracle(x_type, K, g, layout, M, waves, row_blocks):
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
     if plan.family >= 1000:
-        # a matrix-core plan (bf16 with several tokens): one item per 16-token x 256-row tile
-        assert x_type == BF16 and M > 1
+        # a matrix-core plan (bf16 or int8 with several tokens): one item per 16-token x 256-row tile
+        assert x_type in (BF16, I8) and M > 1
         assert plan.n_items == sum((N + 255) // 256 for N, _ in shapes)
     else:
         R = plan.row_blocks
@@ -337,9 +337,9 @@ def test_grouped_token_slices(x_type, shape, M):
     """More tokens than a pass takes (4): each problem is cut
     into slices, with holes in the item list: bf16 without a shape hint an
     item per wave, a row block's slices in one workgroup; otherwise slices
-    placed 8 workgroups apart.  bf16 goes to the matrix cores (M >= 3); with
-    a shape hint, through the per-token plan (every problem M tokens), it
-    stays on the vector ALUs."""
+    placed 8 workgroups apart.  bf16 (M >= 3) and int8 (M >= 2, groups of 64)
+    without a shape hint go to the matrix cores; with one they stay on the
+    vector ALUs."""
     from ternary_weight_amd import tq
     t = torch()
     K, g, layout = 2, 64, GROUP_F16
@@ -372,7 +372,7 @@ def test_grouped_token_slices(x_type, shape, M):
     else:
         plan = tq.gemv_grouped_prepare(probs, M, x_type, ws, nbytes, waves=waves, row_blocks=row_blocks)
     if plan.family >= 1000:
-        assert x_type == BF16 and M >= 3 and shape == (0, 0)
+        assert x_type in (BF16, I8) and shape == (0, 0)
     else:
         slices = (M + 3) // 4
         assert plan.n_problems == len(shapes) * slices
