@@ -134,7 +134,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     using XF = typename std::conditional<KS * ESZ == 64, u32x4, u32x2>::type;
     static_assert(sizeof(XF) == sizeof(Frag), "an x load is one MFMA step's fragment");
     constexpr int CL = kB3 ? 3 : KP;             // code loads per chunk
-    using B3T = B3Table<8>;
+    using B3T = B3Table<8>;   // pair-code table, 8 copies (32 KiB)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, q = lane >> 4;
@@ -262,13 +262,28 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             return decode_oe16(row[4 * k + s], q);
         }
     };
+    // the codec: the chunk's two index words of tile fn's row, read once per
+    // chunk (idxw), and the index of the chunk's first group in the first
+    uint32_t idxw[kCb ? 4 : 1][2];
+    int idx0 = 0;
+    auto read_idx = [&](const LDS_AS uint32_t* st, int c) {
+        if constexpr (kCb) {
+            const int g0 = (c << 6) >> lg;                        // the chunk's first group
+            idx0 = g0 - 6 * (g0 / 6);
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn) {
+                idxw[fn][0] = st[64 * CDS + 16 * fn + r];
+                idxw[fn][1] = st[64 * CDS + 64 + 16 * fn + r];
+            }
+        }
+    };
     // the scale of plane k of group `grp` (a global group index), for tile
     // fn's row, from the stage's scale words of the chunk
     auto group_scale = [&](const LDS_AS uint32_t* st, int c, int grp, int k, int fn) -> float {
         const LDS_AS uint32_t* sw = st + 64 * CDS + 16 * fn + r;
         if constexpr (kCb) {
-            const int j = grp - 6 * (((c << 6) >> lg) / 6);     // 0 .. 7: word j / 6, field j % 6
-            const uint32_t w = sw[j >= 6 ? 64 : 0];
+            const int j = idx0 + grp - ((c << 6) >> lg);         // 0 .. 7: word j / 6, field j % 6
+            const uint32_t w = j >= 6 ? idxw[fn][1] : idxw[fn][0];
             const float cb = cb_lds[(w >> (5 * (j >= 6 ? j - 6 : j))) & 31u];
             if constexpr (kB3) {
                 return cb;                                         // the table holds the combined values
@@ -318,6 +333,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     auto compute = [&](int c, const LDS_AS uint32_t* st, XF (&xa)[XL]) {
         const int nv = nks - c * KPC;              // valid steps of the chunk (>= 1; more than KPC: all)
         if (kTensor && c == NC - 1 && Kin % KS != 0) mask_x(c, xa);
+        read_idx(st, c);
         auto one_step = [&](int s, bool zero) {
             // x in the weight fragments' column order (the compact codes'
             // table gives consecutive columns)
