@@ -54,6 +54,9 @@ constexpr int kThreads = TQ_CHAIN_THREADS;   // 8 waves (measured against 16)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxWidth = 8192;          // longest phase input (held in registers, 16 per thread)
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls of one wait before giving up (~seconds)
+#ifndef TQ_CHAIN_SLEEP
+#define TQ_CHAIN_SLEEP 16                    // s_sleep between two polls of a wait (units of 64 cycles)
+#endif
 
 enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3 };
 enum { W_Q = 0, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN };
@@ -162,7 +165,7 @@ __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t targ
                 ok = 0;
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(TQ_CHAIN_SLEEP);
             if (++spins >= kSpinLimit) {
                 __hip_atomic_store(C.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;

@@ -539,6 +539,18 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             barrier();
             lds_write((u + 1) & 1, abuf[(u + 1) % NBUF], wbuf[(u + 1) % NBUF]);
             lds_read(u & 1, a, w);
+            // bf16 with a per-tensor scale and a ragged last step: x columns
+            // past Kin (the next token's first ones) are zeroed, so that an
+            // infinity there adds nothing to this token
+            if (XT == TQ_BF16 && LAYOUT == TQ_SCALE_TENSOR && Kin % KS != 0 && cp.j == seg_steps - 1) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int d = 0; d < (int)(sizeof(Frag) / 4); ++d) {
+                        const int col = cp.j * KS + q * QCOLS + 2 * d;
+                        a[fm][d] &= col + 1 < Kin ? 0xFFFFFFFFu : (col < Kin ? 0x0000FFFFu : 0u);
+                    }
+            }
             compute(cp, a, w, swbuf[u], wst0);
         } else if constexpr (kWave) {
             uint32_t w[FN];

@@ -104,6 +104,32 @@ def test_gemm_ragged_kin_tail():
             assert rel_err(gemv(d, blob, BF16, x, gemm=True), oracle.gemv_fp(1, 0, TENSOR, trits, scales, x, BF16)) <= TOL
 
 
+@pytest.mark.parametrize("M", [3, 16, 40])
+@pytest.mark.parametrize("Kin,K", [(48, 1), (80, 3), (1008, 2)])
+def test_ragged_kin_ignores_the_next_tokens_infinity(M, Kin, K):
+    """bf16 x, per-tensor scale, Kin not a multiple of the 32-column MFMA
+    step: the last step's columns past Kin lie in the next token's row.  An
+    infinity at the start of token 1 must leave every other token finite and
+    equal to the oracle (which takes finite inputs only: its reference has
+    token 1 zeroed, which no other token depends on).  M = 3 and 16 run the
+    few-token kernels (tq_gemv and tq_gemm), M = 40 the prefill kernels."""
+    rng = np.random.default_rng(Kin + M + K)
+    N = 70
+    trits, scales, _ = rand_problem(K, 0, TENSOR, N, Kin, rng)
+    d, blob = pack(K, 0, TENSOR, trits, scales)
+    v = rng.standard_normal((M, Kin))
+    v[1] = 0.0
+    ref = oracle.gemv_fp(K, 0, TENSOR, trits, scales, gen.bf16_bits(v), BF16)
+    v[1, :3] = [np.inf, -np.inf, np.inf]
+    x = gen.bf16_bits(v)
+    keep = [m for m in range(M) if m != 1]
+    for y in (gemv(d, blob, BF16, x, gemm=True), gemv(d, blob, BF16, x) if M <= 16 else None):
+        if y is None:
+            continue
+        assert np.all(np.isfinite(y[keep]))
+        assert rel_err(y[keep], ref[keep]) <= TOL
+
+
 def test_gemm_one_hot_indexing():
     # x = e_j picks column j: y[j][n] = s[n][j / g] * t[n][j] exactly, for every
     # j of a row of two groups and every n of two weight tiles
