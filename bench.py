@@ -550,7 +550,7 @@ def hbm_ceiling(nbytes: int = 4 << 30, reps: int = 5) -> dict:
 _COMMON_SOURCES = ["tq_decode.h", "tq_internal.h", "tq_layout.h"]
 _FAMILY_SOURCES = {
     "k_gemv": ["tq_gemv_impl.h", "tq_gemv.hip", "tq_entry.hip"],
-    "k_gemm": ["tq_gemm_impl.h", "tq_gemm_kernels.h", "tq_gemm.hip"],
+    "k_gemm": ["tq_gemm_impl.h", "tq_gemm_kernels.h", "tq_gemm_skinny.h", "tq_gemm.hip"],
     "k_bitnet_chain": ["tq_chain.hip", "tq_gemv_impl.h"],
     "k_tern": ["tq_ternarize.hip"],
 }

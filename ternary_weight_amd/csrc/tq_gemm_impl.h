@@ -41,6 +41,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;   // 4 waves
+#ifndef TQ_GEMM_NBUF
+#define TQ_GEMM_NBUF 4             // steps in flight of the prefill kernels
+#endif
 #ifndef TQ_GEMM_B3_NBUF
 #define TQ_GEMM_B3_NBUF 4          // steps in flight of the compact codec's kernels
 #endif
@@ -182,7 +185,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
     // steps in flight (loads issued NBUF - 1 steps ahead)
-    constexpr int NBUF = LAYOUT == TQ_SCALE_CODEBOOK_B3 ? TQ_GEMM_B3_NBUF : 4;
+    constexpr int NBUF = LAYOUT == TQ_SCALE_CODEBOOK_B3 ? TQ_GEMM_B3_NBUF : TQ_GEMM_NBUF;
     // int8, one plane, per-tensor scale: the int32 sum is the result
     constexpr bool kDirect = XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1;
     // the scale word of a (segment, plane) block: two f16 group scales, or six 5-bit codebook indices
