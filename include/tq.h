@@ -440,7 +440,7 @@ tq_status tq_bitnet_chain_workspace_size(const tq_bitnet_dims* dims, int32_t n_l
  * n_layers; each blob's header is read back to check its shape and format),
  * write the layer table into `workspace` (device, caller-owned, kept for the
  * plan's lifetime) and clear the chain state.  Widths up to 8192, each a
- * multiple of 16.  plan->workgroups on entry: 0 for one workgroup per two
+ * multiple of 16; head_dim a multiple of 4.  plan->workgroups on entry: 0 for one workgroup per two
  * compute units, else the grid to use (at most what fits the GPU at once).
  * Copies host->device on `stream` and synchronizes it.
  */

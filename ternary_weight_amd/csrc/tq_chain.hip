@@ -31,10 +31,20 @@
 //      of gate and of up, half the waves each), restricted to one of S
 //      column splits, the waves splitting that range further (the decode
 //      kernels' row-block loop, one row per lane).  The waves' partial sums
-//      meet in LDS; with S > 1 the splits of a block meet in an int32
-//      accumulator in global memory (exact, any order) and the last split
-//      to arrive, counted with an atomic per block, applies the epilogue,
-//      clears the accumulator and the count, and counts the block done.
+//      meet in LDS; the item stores its block's int32 partial sums to a slot
+//      of its own (split, row) and counts the item done.
+// Nobody adds the splits of a block or applies its epilogue at the end of a
+// phase: the next phase's workgroups read every split's slot along with the
+// rest of their input, add them (int32, exact in any order) and apply the
+// epilogue themselves (fl(float(sum) * fl(s_w * s_x)), the residual add or
+// relu2(gate) * up), the same operations in the same order, so the bits are
+// those of a single writer.  A phase's critical path is then the slot
+// stores and the count, the consumer's poll and one read of its input:
+// three memory round trips, where a last-split reduction (atomic adds, an
+// arrival count that returns, an exchange, the output stores) took six or
+// seven.  The residual vectors that later phases need whole (x, x1) are
+// stored by designated workgroups, and workgroup 0 publishes each phase's
+// input scale s_x.
 #include <string.h>
 
 #include <algorithm>
@@ -66,13 +76,22 @@ struct LayerDev {
     const float* norm[4];
 };
 
+#ifndef TQ_CHAIN_SPLITS
+#define TQ_CHAIN_SPLITS 3
+#endif
+#ifndef TQ_CHAIN_SPLITS_GU
+#define TQ_CHAIN_SPLITS_GU 2
+#endif
+constexpr int kMaxSplits = TQ_CHAIN_SPLITS;      // column splits of a block (the consumers add this many slots at most)
+constexpr int kMaxSplitsGU = TQ_CHAIN_SPLITS_GU; // GU's: DOWN's input reads two slot vectors (gate, up), so half as many
+
 struct PhaseDev {
     int32_t groups;     // output blocks: 64-row blocks (QKV over q|k|v; GU: gate/up pairs)
-    int32_t splits;     // column splits per block
+    int32_t splits;     // column splits per block, 1 .. kMaxSplits
     int32_t items;      // groups * splits
     int32_t width;      // input length
-    int32_t acc_base;   // first accumulator row of the phase's blocks
-    int32_t cnt_base;   // first arrival counter of the phase's blocks
+    int32_t prow;       // rows of one split's partial sums (QKV: q|k|v; GU: gate|up)
+    int32_t pbase;      // the phase's first slot: split s, row r at part[pbase + s prow + r]
 };
 
 struct ChainDev {
@@ -81,12 +100,10 @@ struct ChainDev {
     int32_t nq, nkv, nb_q, nb_kv, G;
     float eps;
     const LayerDev* layers;
-    float* qkv;         // [nq + 2 nkv]
-    float* x1;          // [hidden]
-    float* act;         // [inter]
-    int32_t* acc;       // split partial sums, 64 rows per block, kept zero (sizes_of)
-    uint32_t* cnt;      // arrivals per block, kept zero
-    uint32_t* done;     // [n_layers][5] blocks written: QKV, v, O, GU, DOWN
+    float* x1;          // [hidden] x + o of the current layer (the residual of DOWN)
+    int32_t* part;      // the phases' int32 partial sums per split and row
+    float* sxs;         // [n_layers][4] the int8 scale of each phase's input
+    uint32_t* done;     // [n_layers][5] items written: QKV, v, O, GU, DOWN
     int32_t* err;       // set when a wait gives up
 };
 
@@ -108,6 +125,38 @@ __device__ __forceinline__ void st_shared(float* p, float v)
 {
     __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int32_t ld_shared_i32(const int32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_shared_i32(int32_t* p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same accesses through a buffer resource: the byte offset within the
+// buffer is one 32-bit VGPR where a global access takes a 64-bit address in
+// two, and a uniform offset rides in an SGPR.  The phase inputs keep dozens
+// of loads in flight per thread, so this halves their address registers.
+// Cache policy sc1 is the agent scope of the accesses above.  They are
+// ordered after a wait by the barrier that ends it, as any memory access.
+constexpr int kAgent = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p)
+{
+    // every buffer here is far below 4 GiB; dword 3 is gfx9's raw-dword format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ int32_t ld_buf_i32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kAgent);
+}
+__device__ __forceinline__ float ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __int_as_float(ld_buf_i32(r, voff, soff));
+}
+__device__ __forceinline__ void st_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, (int)voff, 0, kAgent);
+}
 // Wait until this wave's stores and atomics have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -116,9 +165,7 @@ struct Item {
     int rb;             // 64-row block within the projection
     int split;
     int group;
-    int off;            // first output row of the block (in q|k|v for QKV)
-    int arow;           // first accumulator row of the block (of gate for GU): 64 rows
-                        // of its own, apart from every other block that can be in flight
+    int off;            // first output row of the block (in q|k|v for QKV; of gate for GU)
 };
 
 __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, int ph, int item)
@@ -140,9 +187,6 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, in
         it.rb = it.group;
         it.off = it.group * 64;
     }
-    // O runs while q and k are still being summed, so its rows and counters
-    // lie past those of the QKV blocks (acc_base, cnt_base)
-    it.arow = P.acc_base + it.group * 64;
     return it;
 }
 
@@ -185,55 +229,192 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return v;
 }
 
-// The element of the phase input that position i reads (global memory
-// written by the previous phase): x, x1, act, or for O repeat(v) -- query
-// head h reads KV head h / (n_heads / n_kv).  `src` is the phase's base.
-__device__ __forceinline__ const float* phase_source(const ChainDev& C, int ph, const float* x)
-{
-    return ph == PH_QKV ? x : (ph == PH_GU ? C.x1 : (ph == PH_DOWN ? C.act : C.qkv + C.nq + C.nkv));
-}
-
 // RMSNorm of the phase input with weight w, then the per-token absmax int8
 // quantisation, into LDS (xq, zero-padded to whole 64-column chunks) and
 // *sx.  The steps are tq.h's; every workgroup computes the same bytes.  A
-// thread holds its kPer inputs and weights in registers.  Every load is
-// issued before the first use and none sits under a branch (positions past
-// n read element n - 1 and are zeroed afterwards): behind branches each
-// load waited for the one before, one memory round trip per element.
+// thread holds kPer inputs and weights in registers, as kRuns runs of four
+// consecutive elements (from 4 (tid + j kThreads)), each read with one
+// 16-byte load: a vector is 4 loads per thread, and a phase's loads stay
+// within the 63 a wave can have outstanding.  Every load is issued before
+// the first use and none sits under a branch (runs past n read the last
+// run and are zeroed afterwards): behind branches each load waited for the
+// one before.
 constexpr int kPer = kMaxWidth / kThreads;
+constexpr int kRuns = kPer / 4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The O phase's element positions (repeat(v)) of this thread, computed once
-// per launch: the integer divisions would otherwise recur in every layer.
-__device__ __forceinline__ void o_positions(const ChainDev& C, int (&o_at)[kPer])
+template <int AUX = kAgent>
+__device__ __forceinline__ u32x4 ld_buf4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    const int group = C.n_heads / C.n_kv, n = C.nq;
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
+}
+__device__ __forceinline__ int run_start(int j, int n)
+{
+    return min(4 * ((int)threadIdx.x + j * kThreads), n - 4);
+}
+
+// The O phase's input runs (repeat(v)) of this thread as byte offsets into
+// v, computed once per launch: the integer divisions would otherwise recur
+// in every layer.  A run stays within one head (head_dim is a multiple of 4).
+__device__ __forceinline__ void o_positions(const ChainDev& C, uint32_t (&o_at)[kRuns])
+{
+    const int group = C.n_heads / C.n_kv;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = min((int)threadIdx.x + j * kThreads, n - 1);
+    for (int j = 0; j < kRuns; ++j) {
+        const int i = run_start(j, C.nq);
         const int head = i / C.head_dim, d = i - head * C.head_dim;
-        o_at[j] = (head / group) * C.head_dim + d;
+        o_at[j] = 4u * (uint32_t)((head / group) * C.head_dim + d);
     }
 }
 
-__device__ void norm_quant(const ChainDev& C, int ph, const float* x, const float* w, int n, int8_t* xq,
-                           float* sx, double* red_d, float* red_f, const int (&o_at)[kPer])
+// The sum of a phase's S split slots at the runs of byte offsets off[j]
+// (slot s at sbase + s sstep bytes): every load is issued before the first
+// add (S fixed at compile time).
+template <int S>
+__device__ __forceinline__ void slot_sums(__amdgpu_buffer_rsrc_t r, uint32_t sbase, uint32_t sstep,
+                                          const uint32_t (&off)[kRuns], int32_t (&sum)[kPer])
+{
+    u32x4 t[S][kRuns];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int j = 0; j < kRuns; ++j) t[s][j] = ld_buf4(r, off[j], sbase + s * sstep);
+#pragma unroll
+    for (int j = 0; j < kRuns; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t a = t[0][j][k];
+#pragma unroll
+            for (int s = 1; s < S; ++s) a += t[s][j][k];
+            sum[4 * j + k] = (int32_t)a;
+        }
+}
+template <int MAXS>
+__device__ __forceinline__ void slot_sum(const ChainDev& C, int ph, int row0, const uint32_t (&off)[kRuns],
+                                         int32_t (&sum)[kPer])
+{
+    const PhaseDev& P = C.ph[ph];
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(C.part);
+    const uint32_t sbase = 4u * (uint32_t)(P.pbase + row0), sstep = 4u * (uint32_t)P.prow;
+    if (P.splits == 1 || MAXS == 1) slot_sums<1>(r, sbase, sstep, off, sum);
+    else if (P.splits == 2 || MAXS == 2) slot_sums<2>(r, sbase, sstep, off, sum);
+    else if (P.splits == 3 || MAXS == 3) slot_sums<3>(r, sbase, sstep, off, sum);
+    else slot_sums<MAXS>(r, sbase, sstep, off, sum);
+}
+// A vector's runs at byte offsets off[j], agent scope.
+__device__ __forceinline__ void load_runs(const float* p, const uint32_t (&off)[kRuns], float (&v)[kPer])
+{
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(p);
+    u32x4 t[kRuns];
+#pragma unroll
+    for (int j = 0; j < kRuns; ++j) t[j] = ld_buf4(r, off[j], 0);
+#pragma unroll
+    for (int j = 0; j < kRuns; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[4 * j + k] = __uint_as_float(t[j][k]);
+}
+// fl(s_w * s_x): the epilogue factor of a product of phase ph in layer l
+// (the weight's per-tensor scale times the phase input's int8 scale, which
+// workgroup 0 published)
+__device__ __forceinline__ float epi_scale(const ChainDev& C, const LayerDev& L, int proj, int l, int ph)
+{
+    return __fmul_rn(ld_uniform((const float*)L.p[proj].scales), ld_shared(C.sxs + l * 4 + ph));
+}
+
+// The elements of this thread's runs (byte offsets off[j]) of phase ph's
+// input in layer l, from what the earlier phases left in memory:
+//   QKV   x (layer 0: the input; then x1 + down of the layer before)
+//   O     repeat(v): v from the QKV slots
+//   GU    x1 = x + o
+//   DOWN  relu2(gate) * up
+// each product fl(float(sum of the splits) * fl(s_w * s_x)).
+__device__ __forceinline__ void phase_input(const ChainDev& C, int l, int ph, const float* x,
+                                            const uint32_t (&off)[kRuns], float (&v)[kPer])
+{
+    int32_t a[kPer];
+    if (ph == PH_QKV && l == 0) {
+        load_runs(x, off, v);
+    } else if (ph == PH_QKV) {
+        float r[kPer];
+        load_runs(C.x1, off, r);
+        slot_sum<kMaxSplits>(C, PH_DOWN, 0, off, a);
+        const float ca = epi_scale(C, C.layers[l - 1], W_DOWN, l - 1, PH_DOWN);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
+    } else if (ph == PH_O) {
+        slot_sum<kMaxSplits>(C, PH_QKV, C.nq + C.nkv, off, a);
+        const float ca = epi_scale(C, C.layers[l], W_V, l, PH_QKV);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) v[j] = __fmul_rn((float)a[j], ca);
+    } else if (ph == PH_GU) {
+        float r[kPer];
+        load_runs(x, off, r);
+        slot_sum<kMaxSplits>(C, PH_O, 0, off, a);
+        const float ca = epi_scale(C, C.layers[l], W_O, l, PH_O);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
+    } else {
+        int32_t b[kPer];
+        slot_sum<kMaxSplitsGU>(C, PH_GU, 0, off, a);
+        slot_sum<kMaxSplitsGU>(C, PH_GU, C.inter, off, b);
+        const float cg = epi_scale(C, C.layers[l], W_GATE, l, PH_GU);
+        const float cu = epi_scale(C, C.layers[l], W_UP, l, PH_GU);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const float g = fmaxf(__fmul_rn((float)a[j], cg), 0.0f);
+            const float u = __fmul_rn((float)b[j], cu);
+            v[j] = __fmul_rn(__fmul_rn(g, g), u);
+        }
+    }
+}
+
+// The phase input (phase_input), then its RMSNorm with weight w and the
+// per-token absmax int8 quantisation, into LDS (xq, zero-padded to whole
+// 64-column chunks) and *sx.  The steps are tq.h's; every workgroup computes
+// the same bytes.  On the way the workgroup stores the rows of the residual
+// vectors it is designated for (QKV: x; GU: x1; block b by the workgroup
+// b mod npart, npart the phase's participants) and workgroup 0 publishes
+// s_x; the stores are complete when it returns.
+__device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const float* w, int n, int npart, int8_t* xq,
+                           float* sx, double* red_d, float* red_f, const uint32_t (&o_at)[kRuns])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* src = phase_source(C, ph, x);
-    int at[kPer];
+    uint32_t off[kRuns];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) at[j] = ph == PH_O ? o_at[j] : min(tid + j * kThreads, n - 1);
+    for (int j = 0; j < kRuns; ++j) off[j] = ph == PH_O ? o_at[j] : 4u * (uint32_t)run_start(j, n);
     float v[kPer], wt[kPer];
+    {
+        const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
+        u32x4 t[kRuns];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        v[j] = ld_shared(src + at[j]);
-        wt[j] = w[min(tid + j * kThreads, n - 1)];
+        for (int j = 0; j < kRuns; ++j) t[j] = ld_buf4<0>(rw, 4u * (uint32_t)run_start(j, n), 0);
+#pragma unroll
+        for (int j = 0; j < kRuns; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wt[4 * j + k] = __uint_as_float(t[j][k]);
     }
+    phase_input(C, l, ph, x, off, v);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const bool in = tid + j * kThreads < n;
-        v[j] = in ? v[j] : 0.0f;
-        wt[j] = in ? wt[j] : 0.0f;
+    for (int j = 0; j < kRuns; ++j) {
+        const bool in = 4 * (tid + j * kThreads) < n;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[4 * j + k] = in ? v[4 * j + k] : 0.0f;
+            wt[4 * j + k] = in ? wt[4 * j + k] : 0.0f;
+        }
+    }
+    if ((ph == PH_QKV && l > 0) || ph == PH_GU) {
+        const __amdgpu_buffer_rsrc_t rd = rsrc_of(ph == PH_QKV ? x : C.x1);
+#pragma unroll
+        for (int j = 0; j < kRuns; ++j) {
+            const int e = 4 * (tid + j * kThreads);
+            if (e < n && (e >> 6) % npart == (int)blockIdx.x) {
+                u32x4 q;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) q[k] = __float_as_uint(v[4 * j + k]);
+                __builtin_amdgcn_raw_buffer_store_b128(q, rd, (int)(4u * (uint32_t)e), 0, kAgent);
+            }
+        }
     }
     double ss = 0.0;
 #pragma unroll
@@ -259,15 +440,25 @@ __device__ void norm_quant(const ChainDev& C, int ph, const float* x, const floa
     const float inv = a > 0.0f ? 127.0f / a : 0.0f;
     const int npad = (n + TQ_CHUNK - 1) / TQ_CHUNK * TQ_CHUNK;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * kThreads;
-        if (i < npad) {
-            float t = rintf(__fmul_rn(v[j], inv));
-            t = fminf(fmaxf(t, -127.0f), 127.0f);
-            xq[i] = (int8_t)(int)t;
+    for (int j = 0; j < kRuns; ++j) {
+        const int e = 4 * (tid + j * kThreads);
+        if (e < npad) {   // npad is a multiple of 4: a run is wholly in or out
+            uint32_t q = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float t = rintf(__fmul_rn(v[4 * j + k], inv));
+                t = fminf(fmaxf(t, -127.0f), 127.0f);
+                q |= ((uint32_t)(int)t & 0xffu) << (8 * k);
+            }
+            *(uint32_t*)(xq + e) = q;
         }
     }
-    if (tid == 0) *sx = a > 0.0f ? a / 127.0f : 0.0f;
+    const float sxv = a > 0.0f ? a / 127.0f : 0.0f;
+    if (tid == 0) {
+        *sx = sxv;
+        if (blockIdx.x == 0) st_shared(C.sxs + l * 4 + ph, sxv);
+    }
+    wait_stores();   // the designated rows and s_x are out before any item is counted
     __syncthreads();
 }
 
@@ -286,6 +477,35 @@ __device__ __forceinline__ void wave_range(int NC, int splits, int s, int nw, in
     *c1 = a + (int)((int64_t)(b - a) * (w + 1) / nw);
 }
 
+// The layer's q | k | v for the caller, from the QKV slots: wave w of the
+// workgroup takes the 64-row blocks blockIdx + npart (w + kWaves i).  The
+// designated workgroups (npart: those with both a GU and a DOWN item) call
+// it in the DOWN phase before its wait, while they would idle: they waited
+// for every QKV item in the GU phase, and the next layer's QKV items, which
+// rewrite the slots, wait for their DOWN items.
+__device__ void qkv_rows(const ChainDev& C, const LayerDev& Ld, int l, float* qkv_out)
+{
+    const int npart = min(min(C.ph[PH_GU].items, C.ph[PH_DOWN].items), C.G);
+    if ((int)blockIdx.x >= npart) return;
+    const int R = C.nq + 2 * C.nkv, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float cq = epi_scale(C, Ld, W_Q, l, PH_QKV), ck = epi_scale(C, Ld, W_K, l, PH_QKV),
+                cv = epi_scale(C, Ld, W_V, l, PH_QKV);
+    const PhaseDev& Q = C.ph[PH_QKV];
+    for (int blk = blockIdx.x + npart * wave; blk * 64 < R; blk += npart * kWaves) {
+        const int i = blk * 64 + lane;
+        if (i >= R) break;
+        int32_t t[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            t[sp] = sp < Q.splits ? ld_shared_i32(C.part + Q.pbase + sp * Q.prow + i) : 0;
+        int32_t sum = 0;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) sum += t[sp];
+        const float ca = i < C.nq ? cq : (i < C.nq + C.nkv ? ck : cv);
+        qkv_out[(int64_t)l * R + i] = __fmul_rn((float)sum, ca);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __restrict__ Cp, float* x, float* qkv_out)
 {
     const ChainDev C = ld_uniform_struct(Cp);
@@ -297,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
     __shared__ int flag;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    int o_at[kPer];
+    uint32_t o_at[kRuns];
     o_positions(C, o_at);
 
     for (int l = 0; l < C.n_layers; ++l) {
@@ -319,20 +539,20 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
             uint32_t* dl = C.done + l * DONE_N;
             bool ok = true;
             if (ph == PH_QKV) {
-                if (l > 0) ok = wait_count(C, dl - DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].groups, &flag);
+                if (l > 0) ok = wait_count(C, dl - DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].items, &flag);
             } else if (ph == PH_O) {
-                ok = wait_count(C, dl + DONE_V, (uint32_t)C.nb_kv, &flag);
+                ok = wait_count(C, dl + DONE_V, (uint32_t)(C.nb_kv * C.ph[PH_QKV].splits), &flag);
             } else if (ph == PH_GU) {
-                // x1 complete; and every QKV block, so that no workgroup still
-                // reads x when DOWN rewrites it
-                ok = wait_count(C, dl + DONE_O, (uint32_t)C.ph[PH_O].groups, &flag) &&
-                     wait_count(C, dl + DONE_QKV, (uint32_t)C.ph[PH_QKV].groups, &flag);
+                // x1 = x + o needs every O item, and x the rows the QKV
+                // workgroups store
+                ok = wait_count(C, dl + DONE_O, (uint32_t)C.ph[PH_O].items, &flag) &&
+                     wait_count(C, dl + DONE_QKV, (uint32_t)C.ph[PH_QKV].items, &flag);
             } else {
-                ok = wait_count(C, dl + DONE_GU, (uint32_t)C.ph[PH_GU].groups, &flag);
+                if (qkv_out) qkv_rows(C, Ld, l, qkv_out);
+                ok = wait_count(C, dl + DONE_GU, (uint32_t)C.ph[PH_GU].items, &flag);
             }
             if (!ok) return;
-            norm_quant(C, ph, x, Ld.norm[ph], P.width, xq, &sx_lds, red_d, (float*)red_f, o_at);
-            const float sx = sx_lds;
+            norm_quant(C, l, ph, x, Ld.norm[ph], P.width, min(P.items, C.G), xq, &sx_lds, red_d, (float*)red_f, o_at);
             for (int item = first; item < P.items; item += C.G) {
                 int part;
                 if (item == first) {
@@ -354,65 +574,48 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     for (int k = 0; k < nw; ++k) sa += red[k][lane];
                     if (ph == PH_GU)
                         for (int k = nw; k < kWaves; ++k) sb += red[k][lane];
-                    const int ra = it.arow + lane;                  // accumulator rows
-                    const int rbw = ra + C.ph[PH_GU].groups * 64;   // GU: up's rows past gate's
-                    bool last = true;
-                    if (P.splits > 1) {
-                        __hip_atomic_fetch_add(C.acc + ra, sa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (ph == PH_GU) __hip_atomic_fetch_add(C.acc + rbw, sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        wait_stores();     // the partial sums are in before the count says so
-                        uint32_t old = 0;
-                        if (lane == 0)
-                            old = __hip_atomic_fetch_add(C.cnt + P.cnt_base + it.group, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        old = __shfl(old, 0, 64);
-                        last = old == (uint32_t)P.splits - 1;
-                        if (last) {
-                            sa = __hip_atomic_exchange(C.acc + ra, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (ph == PH_GU) sb = __hip_atomic_exchange(C.acc + rbw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (lane == 0) __hip_atomic_store(C.cnt + P.cnt_base + it.group, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                    }
+                    // the item's slot: its split's partial sums of the block's rows
                     const tq_prob_dev& Pa = Ld.p[it.proj];
-                    const int n = it.rb * 64 + lane;
-                    if (last && n < Pa.N) {
-                        const float ca = __fmul_rn(ld_uniform((const float*)Pa.scales), sx);
-                        const float ya = __fmul_rn((float)sa, ca);
-                        if (ph == PH_QKV) {
-                            st_shared(C.qkv + it.off + lane, ya);
-                            if (qkv_out) qkv_out[(int64_t)l * (C.nq + 2 * C.nkv) + it.off + lane] = ya;
-                        } else if (ph == PH_O) {
-                            st_shared(C.x1 + n, __fadd_rn(ld_shared(x + n), ya));
-                        } else if (ph == PH_GU) {
-                            const tq_prob_dev& Pb = Ld.p[W_UP];
-                            const float cb = __fmul_rn(ld_uniform((const float*)Pb.scales), sx);
-                            const float u = __fmul_rn((float)sb, cb);
-                            const float g = fmaxf(ya, 0.0f);
-                            st_shared(C.act + n, __fmul_rn(__fmul_rn(g, g), u));
-                        } else {
-                            st_shared(x + n, __fadd_rn(ld_shared(C.x1 + n), ya));
-                        }
+                    int32_t* slot = C.part + P.pbase + it.split * P.prow + it.off;
+                    if (it.rb * 64 + lane < Pa.N) {
+                        st_shared_i32(slot + lane, sa);
+                        if (ph == PH_GU) st_shared_i32(slot + C.inter + lane, sb);
                     }
-                    if (last) {   // the block is written: count it once its stores are complete
-                        wait_stores();
-                        if (lane == 0) {
-                            const int c = ph == PH_QKV ? DONE_QKV : (ph == PH_O ? DONE_O : (ph == PH_GU ? DONE_GU : DONE_DOWN));
-                            __hip_atomic_fetch_add(dl + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (ph == PH_QKV && it.proj == W_V)
-                                __hip_atomic_fetch_add(dl + DONE_V, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
+                    wait_stores();   // the slot is written before the count says so
+                    if (lane == 0) {
+                        const int c = ph == PH_QKV ? DONE_QKV : (ph == PH_O ? DONE_O : (ph == PH_GU ? DONE_GU : DONE_DOWN));
+                        __hip_atomic_fetch_add(dl + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (ph == PH_QKV && it.proj == W_V)
+                            __hip_atomic_fetch_add(dl + DONE_V, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
                 __syncthreads();
             }
         }
     }
+    // the hidden state after the last layer, x = x1 + down: wave w of every
+    // workgroup takes the 64-row blocks b with b = blockIdx + G (w + kWaves i)
+    const int L = C.n_layers - 1;
+    if (!wait_count(C, C.done + L * DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].items, &flag)) return;
+    const float cd = epi_scale(C, C.layers[L], W_DOWN, L, PH_DOWN);
+    const PhaseDev& D = C.ph[PH_DOWN];
+    for (int blk = blockIdx.x + C.G * wave; blk * 64 < C.hidden; blk += C.G * kWaves) {
+        const int i = blk * 64 + lane;
+        if (i >= C.hidden) break;
+        int32_t t[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            t[sp] = sp < D.splits ? ld_shared_i32(C.part + D.pbase + sp * D.prow + i) : 0;
+        int32_t sum = 0;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) sum += t[sp];
+        st_shared(x + i, __fadd_rn(ld_shared(C.x1 + i), __fmul_rn((float)sum, cd)));
+    }
 }
 
-__global__ void k_chain_reset(ChainDev* C, int acc_n, int cnt_n)
+__global__ void k_chain_reset(ChainDev* C)
 {
     const ChainDev c = *C;
-    for (int i = threadIdx.x; i < acc_n; i += blockDim.x) c.acc[i] = 0;
-    for (int i = threadIdx.x; i < cnt_n; i += blockDim.x) c.cnt[i] = 0;
     for (int i = threadIdx.x; i < c.n_layers * DONE_N; i += blockDim.x) c.done[i] = 0;
     if (threadIdx.x == 0) *c.err = 0;
 }
@@ -421,8 +624,9 @@ __global__ void k_chain_reset(ChainDev* C, int acc_n, int cnt_n)
 // Host side.
 // ---------------------------------------------------------------------------
 struct Sizes {
-    int64_t nq, nkv, acc_n, cnt_n;
-    int64_t off_layers, off_qkv, off_x1, off_act, off_acc, off_cnt, off_done, off_err, total;
+    int64_t nq, nkv;
+    int64_t prow[4], pbase[4], part_n;   // each phase's slot rows and first slot; every slot
+    int64_t off_layers, off_x1, off_part, off_sxs, off_done, off_err, total;
 };
 
 tq_status check_dims(const tq_bitnet_dims* d, int32_t n_layers)
@@ -438,6 +642,7 @@ tq_status check_dims(const tq_bitnet_dims* d, int32_t n_layers)
                        (long long)d->n_heads * d->head_dim, d->hidden);
     if (d->hidden % 16 || d->intermediate % 16 || ((int64_t)d->n_kv_heads * d->head_dim) % 16)
         return tq_fail(TQ_ERR_SHAPE, "widths must be multiples of 16");
+    if (d->head_dim % 4) return tq_fail(TQ_ERR_SHAPE, "head_dim %d not a multiple of 4", d->head_dim);
     if (d->hidden > kMaxWidth || d->intermediate > kMaxWidth)
         return tq_fail(TQ_ERR_UNSUPPORTED, "widths above %d", kMaxWidth);
     if (!(d->eps >= 0.0f) || !std::isfinite(d->eps)) return tq_fail(TQ_ERR_VALUE, "eps must be finite and >= 0");
@@ -449,25 +654,24 @@ Sizes sizes_of(const tq_bitnet_dims* d, int32_t n_layers)
     Sizes s;
     s.nq = (int64_t)d->n_heads * d->head_dim;
     s.nkv = (int64_t)d->n_kv_heads * d->head_dim;
-    // blocks: QKV (q, k, v), then O's own range after them; GU (gate, then up);
-    // DOWN -- 64 accumulator rows and one counter per block
-    const int64_t nb_qkv = (s.nq + 63) / 64 + 2 * ((s.nkv + 63) / 64);
-    const int64_t nb_h = ((int64_t)d->hidden + 63) / 64, nb_i = ((int64_t)d->intermediate + 63) / 64;
-    s.acc_n = 64 * std::max({nb_qkv + nb_h, 2 * nb_i, nb_h});
-    s.cnt_n = std::max({nb_qkv + nb_h, nb_i, nb_h});
+    // the slots of every phase, kMaxSplits per row: QKV (q|k|v), O, GU
+    // (gate|up), DOWN, one after the other (no two phases share a slot)
+    const int64_t prow[4] = {s.nq + 2 * s.nkv, d->hidden, 2 * (int64_t)d->intermediate, d->hidden};
+    s.part_n = 0;
+    for (int ph = 0; ph < 4; ++ph) {
+        s.prow[ph] = prow[ph];
+        s.pbase[ph] = s.part_n;
+        s.part_n += kMaxSplits * prow[ph];
+    }
     int64_t o = tq_align256(sizeof(ChainDev));
     s.off_layers = o;
     o = tq_align256(o + (int64_t)n_layers * sizeof(LayerDev));
-    s.off_qkv = o;
-    o = tq_align256(o + 4 * (s.nq + 2 * s.nkv));
     s.off_x1 = o;
     o = tq_align256(o + 4 * (int64_t)d->hidden);
-    s.off_act = o;
-    o = tq_align256(o + 4 * (int64_t)d->intermediate);
-    s.off_acc = o;
-    o = tq_align256(o + 4 * s.acc_n);
-    s.off_cnt = o;
-    o = tq_align256(o + 4 * s.cnt_n);
+    s.off_part = o;
+    o = tq_align256(o + 4 * s.part_n);
+    s.off_sxs = o;
+    o = tq_align256(o + 4 * 4 * (int64_t)n_layers);
     s.off_done = o;
     o = tq_align256(o + 4 * (int64_t)n_layers * DONE_N);
     s.off_err = o;
@@ -578,25 +782,24 @@ TQ_EXPORT tq_status tq_bitnet_chain_prepare(const tq_bitnet_dims* dims, const tq
         const int nw = ph == PH_GU ? kWaves / 2 : kWaves;
         int64_t S = std::max<int64_t>(1, G / groups[ph]);
         S = std::min<int64_t>(S, std::max<int64_t>(1, chunks[ph] / nw));
+        S = std::min<int64_t>(S, ph == PH_GU ? kMaxSplitsGU : kMaxSplits);
         c.ph[ph].groups = (int32_t)groups[ph];
         c.ph[ph].splits = (int32_t)S;
         c.ph[ph].items = (int32_t)(groups[ph] * S);
         c.ph[ph].width = (int32_t)width[ph];
-        c.ph[ph].acc_base = ph == PH_O ? (int32_t)(64 * groups[PH_QKV]) : 0;
-        c.ph[ph].cnt_base = ph == PH_O ? (int32_t)groups[PH_QKV] : 0;
+        c.ph[ph].prow = (int32_t)z.prow[ph];
+        c.ph[ph].pbase = (int32_t)z.pbase[ph];
     }
     c.layers = (const LayerDev*)(ws + z.off_layers);
-    c.qkv = (float*)(ws + z.off_qkv);
     c.x1 = (float*)(ws + z.off_x1);
-    c.act = (float*)(ws + z.off_act);
-    c.acc = (int32_t*)(ws + z.off_acc);
-    c.cnt = (uint32_t*)(ws + z.off_cnt);
+    c.part = (int32_t*)(ws + z.off_part);
+    c.sxs = (float*)(ws + z.off_sxs);
     c.done = (uint32_t*)(ws + z.off_done);
     c.err = (int32_t*)(ws + z.off_err);
-    std::vector<uint8_t> host((size_t)z.off_qkv, 0);
+    std::vector<uint8_t> host((size_t)z.off_x1, 0);
     memcpy(host.data(), &c, sizeof c);
     memcpy(host.data() + z.off_layers, ld.data(), ld.size() * sizeof(LayerDev));
-    if ((s = tq_check_hip(hipMemsetAsync(ws + z.off_qkv, 0, (size_t)(z.total - z.off_qkv), st), "tq_bitnet_chain_prepare clear")))
+    if ((s = tq_check_hip(hipMemsetAsync(ws + z.off_x1, 0, (size_t)(z.total - z.off_x1), st), "tq_bitnet_chain_prepare clear")))
         return s;
     if ((s = tq_check_hip(hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, st),
                           "tq_bitnet_chain_prepare copy")))
@@ -617,10 +820,9 @@ TQ_EXPORT tq_status tq_bitnet_chain_run(const tq_chain_plan* plan, float* x, flo
     tq_status s;
     if ((s = tq_check_ptr(x, "x", false, 4))) return s;
     if ((s = tq_check_ptr(qkv, "qkv", true, 4))) return s;
-    const Sizes z = sizes_of(&plan->dims, plan->n_layers);
     hipStream_t st = (hipStream_t)stream;
     ChainDev* c = (ChainDev*)plan->workspace;
-    hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(256), 0, st, c, (int)z.acc_n, (int)z.cnt_n);
+    hipLaunchKernelGGL(k_chain_reset, dim3(1), dim3(256), 0, st, c);
     if ((s = tq_check_launch("tq_bitnet_chain_run reset"))) return s;
     const ChainDev* cp = c;
     void* args[] = {(void*)&cp, (void*)&x, (void*)&qkv};

@@ -257,6 +257,7 @@ def test_chain_workspace_size_validation():
         (tq.bitnet_dims(2560, 6912, 20, 6, 128, 1e-5), tq.ERR_SHAPE),      # 20 % 6
         (tq.bitnet_dims(2560, 6912, 16, 4, 128, 1e-5), tq.ERR_SHAPE),      # heads * dim != hidden
         (tq.bitnet_dims(2560, 6900, 20, 5, 128, 1e-5), tq.ERR_SHAPE),      # width % 16
+        (tq.bitnet_dims(96, 256, 16, 8, 6, 1e-5), tq.ERR_SHAPE),           # head_dim % 4
         (tq.bitnet_dims(20480, 6912, 160, 5, 128, 1e-5), tq.ERR_UNSUPPORTED),   # wider than LDS holds
         (tq.bitnet_dims(2560, 6912, 20, 5, 128, float("nan")), tq.ERR_VALUE),
     ]
