@@ -191,6 +191,20 @@ __device__ __forceinline__ Item item_of(const ChainDev& C, const PhaseDev& P, in
 }
 
 enum { DONE_QKV = 0, DONE_V = 1, DONE_O = 2, DONE_GU = 3, DONE_DOWN = 4, DONE_N = 5 };
+#ifndef TQ_CHAIN_CTR_STRIDE
+#define TQ_CHAIN_CTR_STRIDE 64
+#endif
+// Counter c of layer l, each in a 256-byte line of its own: the polls of one
+// counter then do not queue behind the increments of another.
+constexpr int kCtrStride = TQ_CHAIN_CTR_STRIDE;   // dwords
+#ifndef TQ_CHAIN_ERR_EVERY
+#define TQ_CHAIN_ERR_EVERY 16
+#endif
+constexpr uint32_t kErrEvery = TQ_CHAIN_ERR_EVERY;   // a power of two
+__device__ __forceinline__ uint32_t* counter(const ChainDev& C, int l, int c)
+{
+    return C.done + (l * DONE_N + c) * kCtrStride;
+}
 
 // Wait until counter ctr reaches target.  Returns false when the wait gave
 // up, or another workgroup's did (every wait is bounded).
@@ -201,11 +215,12 @@ __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t targ
         uint32_t spins = 0;
         int ok = 1;
         for (;;) {
-            // both loads in flight together: one memory round trip per poll
             const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int e = __hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (c >= target) break;
-            if (e) {
+            // the error flag, which every waiting workgroup would otherwise
+            // poll on one line, only every kErrEvery polls
+            if ((spins & (kErrEvery - 1)) == kErrEvery - 1 &&
+                __hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
                 ok = 0;
                 break;
             }
@@ -222,20 +237,58 @@ __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t targ
     return *flag_lds != 0;
 }
 
+// Wave reductions with DPP moves inside each 16-lane row (pairs, quads,
+// halves, rows) and four lane reads across the rows: no LDS round trip,
+// where a shuffle per step (ds_bpermute) costs one in a dependent chain.
+// Every lane returns the same value, in a fixed order of operations.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = dpp<CTRL>((uint32_t)u), hi = dpp<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+enum { kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f64<kDppSwap1>(v);        // quad_perm [1,0,3,2]
+    v += dpp_f64<kDppSwap2>(v);        // quad_perm [2,3,0,1]: the quad's sum
+    v += dpp_f64<kDppHalfMirror>(v);   // lane i <- 7 - i: the 8 lanes' sum
+    v += dpp_f64<kDppMirror>(v);       // lane i <- 15 - i: the row's sum
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, __uint_as_float(dpp<kDppSwap1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp<kDppSwap2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
+    const float a = fmaxf(__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0)),
+                          __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 16)));
+    const float b = fmaxf(__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32)),
+                          __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 48)));
+    return fmaxf(a, b);
 }
 
 // RMSNorm of the phase input with weight w, then the per-token absmax int8
 // quantisation, into LDS (xq, zero-padded to whole 64-column chunks) and
 // *sx.  The steps are tq.h's; every workgroup computes the same bytes.  A
-// thread holds kPer inputs and weights in registers, as kRuns runs of four
+// thread holds 4 R inputs and weights in registers, as R runs of four
 // consecutive elements (from 4 (tid + j kThreads)), each read with one
-// 16-byte load: a vector is 4 loads per thread, and a phase's loads stay
-// within the 63 a wave can have outstanding.  Every load is issued before
+// 16-byte load: a vector is R loads per thread (R = 2 up to 4096 wide, else
+// 4), and a phase's loads stay within the 63 a wave can have outstanding.  Every load is issued before
 // the first use and none sits under a branch (runs past n read the last
 // run and are zeroed afterwards): behind branches each load waited for the
 // one before.
@@ -270,7 +323,7 @@ __device__ __forceinline__ void o_positions(const ChainDev& C, uint32_t (&o_at)[
 // The sum of a phase's S split slots at the runs of byte offsets off[j]
 // (slot s at sbase + s sstep bytes): every load is issued before the first
 // add (S fixed at compile time).
-template <int S>
+template <int S, int R>
 __device__ __forceinline__ void slot_sums(__amdgpu_buffer_rsrc_t r, uint32_t sbase, uint32_t sstep,
                                           const uint32_t (&off)[kRuns], int32_t (&sum)[kPer])
 {
@@ -278,9 +331,9 @@ __device__ __forceinline__ void slot_sums(__amdgpu_buffer_rsrc_t r, uint32_t sba
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int j = 0; j < kRuns; ++j) t[s][j] = ld_buf4(r, off[j], sbase + s * sstep);
+        for (int j = 0; j < R; ++j) t[s][j] = ld_buf4(r, off[j], sbase + s * sstep);
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j)
+    for (int j = 0; j < R; ++j)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t a = t[0][j][k];
@@ -289,27 +342,28 @@ __device__ __forceinline__ void slot_sums(__amdgpu_buffer_rsrc_t r, uint32_t sba
             sum[4 * j + k] = (int32_t)a;
         }
 }
-template <int MAXS>
+template <int MAXS, int R>
 __device__ __forceinline__ void slot_sum(const ChainDev& C, int ph, int row0, const uint32_t (&off)[kRuns],
                                          int32_t (&sum)[kPer])
 {
     const PhaseDev& P = C.ph[ph];
     const __amdgpu_buffer_rsrc_t r = rsrc_of(C.part);
     const uint32_t sbase = 4u * (uint32_t)(P.pbase + row0), sstep = 4u * (uint32_t)P.prow;
-    if (P.splits == 1 || MAXS == 1) slot_sums<1>(r, sbase, sstep, off, sum);
-    else if (P.splits == 2 || MAXS == 2) slot_sums<2>(r, sbase, sstep, off, sum);
-    else if (P.splits == 3 || MAXS == 3) slot_sums<3>(r, sbase, sstep, off, sum);
-    else slot_sums<MAXS>(r, sbase, sstep, off, sum);
+    if (P.splits == 1 || MAXS == 1) slot_sums<1, R>(r, sbase, sstep, off, sum);
+    else if (P.splits == 2 || MAXS == 2) slot_sums<2, R>(r, sbase, sstep, off, sum);
+    else if (P.splits == 3 || MAXS == 3) slot_sums<3, R>(r, sbase, sstep, off, sum);
+    else slot_sums<MAXS, R>(r, sbase, sstep, off, sum);
 }
 // A vector's runs at byte offsets off[j], agent scope.
+template <int R>
 __device__ __forceinline__ void load_runs(const float* p, const uint32_t (&off)[kRuns], float (&v)[kPer])
 {
     const __amdgpu_buffer_rsrc_t r = rsrc_of(p);
     u32x4 t[kRuns];
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j) t[j] = ld_buf4(r, off[j], 0);
+    for (int j = 0; j < R; ++j) t[j] = ld_buf4(r, off[j], 0);
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j)
+    for (int j = 0; j < R; ++j)
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[4 * j + k] = __uint_as_float(t[j][k]);
 }
@@ -328,39 +382,40 @@ __device__ __forceinline__ float epi_scale(const ChainDev& C, const LayerDev& L,
 //   GU    x1 = x + o
 //   DOWN  relu2(gate) * up
 // each product fl(float(sum of the splits) * fl(s_w * s_x)).
+template <int R>
 __device__ __forceinline__ void phase_input(const ChainDev& C, int l, int ph, const float* x,
                                             const uint32_t (&off)[kRuns], float (&v)[kPer])
 {
     int32_t a[kPer];
     if (ph == PH_QKV && l == 0) {
-        load_runs(x, off, v);
+        load_runs<R>(x, off, v);
     } else if (ph == PH_QKV) {
         float r[kPer];
-        load_runs(C.x1, off, r);
-        slot_sum<kMaxSplits>(C, PH_DOWN, 0, off, a);
+        load_runs<R>(C.x1, off, r);
+        slot_sum<kMaxSplits, R>(C, PH_DOWN, 0, off, a);
         const float ca = epi_scale(C, C.layers[l - 1], W_DOWN, l - 1, PH_DOWN);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
+        for (int j = 0; j < 4 * R; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
     } else if (ph == PH_O) {
-        slot_sum<kMaxSplits>(C, PH_QKV, C.nq + C.nkv, off, a);
+        slot_sum<kMaxSplits, R>(C, PH_QKV, C.nq + C.nkv, off, a);
         const float ca = epi_scale(C, C.layers[l], W_V, l, PH_QKV);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) v[j] = __fmul_rn((float)a[j], ca);
+        for (int j = 0; j < 4 * R; ++j) v[j] = __fmul_rn((float)a[j], ca);
     } else if (ph == PH_GU) {
         float r[kPer];
-        load_runs(x, off, r);
-        slot_sum<kMaxSplits>(C, PH_O, 0, off, a);
+        load_runs<R>(x, off, r);
+        slot_sum<kMaxSplits, R>(C, PH_O, 0, off, a);
         const float ca = epi_scale(C, C.layers[l], W_O, l, PH_O);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
+        for (int j = 0; j < 4 * R; ++j) v[j] = __fadd_rn(r[j], __fmul_rn((float)a[j], ca));
     } else {
         int32_t b[kPer];
-        slot_sum<kMaxSplitsGU>(C, PH_GU, 0, off, a);
-        slot_sum<kMaxSplitsGU>(C, PH_GU, C.inter, off, b);
+        slot_sum<kMaxSplitsGU, R>(C, PH_GU, 0, off, a);
+        slot_sum<kMaxSplitsGU, R>(C, PH_GU, C.inter, off, b);
         const float cg = epi_scale(C, C.layers[l], W_GATE, l, PH_GU);
         const float cu = epi_scale(C, C.layers[l], W_UP, l, PH_GU);
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
+        for (int j = 0; j < 4 * R; ++j) {
             const float g = fmaxf(__fmul_rn((float)a[j], cg), 0.0f);
             const float u = __fmul_rn((float)b[j], cu);
             v[j] = __fmul_rn(__fmul_rn(g, g), u);
@@ -374,28 +429,29 @@ __device__ __forceinline__ void phase_input(const ChainDev& C, int l, int ph, co
 // the same bytes.  On the way the workgroup stores the rows of the residual
 // vectors it is designated for (QKV: x; GU: x1; block b by the workgroup
 // b mod npart, npart the phase's participants) and workgroup 0 publishes
-// s_x; the stores are complete when it returns.
+// s_x; each wave waits for these stores before the item is counted.
+template <int R>
 __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const float* w, int n, int npart, int8_t* xq,
                            float* sx, double* red_d, float* red_f, const uint32_t (&o_at)[kRuns])
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t off[kRuns];
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j) off[j] = ph == PH_O ? o_at[j] : 4u * (uint32_t)run_start(j, n);
+    for (int j = 0; j < R; ++j) off[j] = ph == PH_O ? o_at[j] : 4u * (uint32_t)run_start(j, n);
     float v[kPer], wt[kPer];
     {
         const __amdgpu_buffer_rsrc_t rw = rsrc_of(w);
         u32x4 t[kRuns];
 #pragma unroll
-        for (int j = 0; j < kRuns; ++j) t[j] = ld_buf4<0>(rw, 4u * (uint32_t)run_start(j, n), 0);
+        for (int j = 0; j < R; ++j) t[j] = ld_buf4<0>(rw, 4u * (uint32_t)run_start(j, n), 0);
 #pragma unroll
-        for (int j = 0; j < kRuns; ++j)
+        for (int j = 0; j < R; ++j)
 #pragma unroll
             for (int k = 0; k < 4; ++k) wt[4 * j + k] = __uint_as_float(t[j][k]);
     }
-    phase_input(C, l, ph, x, off, v);
+    phase_input<R>(C, l, ph, x, off, v);
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j) {
+    for (int j = 0; j < R; ++j) {
         const bool in = 4 * (tid + j * kThreads) < n;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -406,7 +462,7 @@ __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const flo
     if ((ph == PH_QKV && l > 0) || ph == PH_GU) {
         const __amdgpu_buffer_rsrc_t rd = rsrc_of(ph == PH_QKV ? x : C.x1);
 #pragma unroll
-        for (int j = 0; j < kRuns; ++j) {
+        for (int j = 0; j < R; ++j) {
             const int e = 4 * (tid + j * kThreads);
             if (e < n && (e >> 6) % npart == (int)blockIdx.x) {
                 u32x4 q;
@@ -418,7 +474,7 @@ __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const flo
     }
     double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) ss += (double)v[j] * (double)v[j];
+    for (int j = 0; j < 4 * R; ++j) ss += (double)v[j] * (double)v[j];
     ss = wave_sum_f64(ss);
     if (lane == 0) red_d[wave] = ss;
     __syncthreads();
@@ -428,11 +484,11 @@ __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const flo
     const float r = 1.0f / sqrtf(ms + C.eps);
     float a = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < 4 * R; ++j) {
         v[j] = __fmul_rn(__fmul_rn(v[j], r), wt[j]);   // zero past n
         a = fmaxf(a, fabsf(v[j]));
     }
-    a = wave_max(a);
+    a = wave_max_dpp(a);
     if (lane == 0) red_f[wave] = a;
     __syncthreads();
     a = red_f[0];
@@ -440,7 +496,7 @@ __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const flo
     const float inv = a > 0.0f ? 127.0f / a : 0.0f;
     const int npad = (n + TQ_CHUNK - 1) / TQ_CHUNK * TQ_CHUNK;
 #pragma unroll
-    for (int j = 0; j < kRuns; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int e = 4 * (tid + j * kThreads);
         if (e < npad) {   // npad is a multiple of 4: a run is wholly in or out
             uint32_t q = 0;
@@ -458,13 +514,11 @@ __device__ void norm_quant(const ChainDev& C, int l, int ph, float* x, const flo
         *sx = sxv;
         if (blockIdx.x == 0) st_shared(C.sxs + l * 4 + ph, sxv);
     }
-    wait_stores();   // the designated rows and s_x are out before any item is counted
     __syncthreads();
 }
 
 #ifndef TQ_CHAIN_DEPTH
-#define TQ_CHAIN_DEPTH 2     // chunks in flight per wave (measured: 4, 6 and 8 were no faster; the
-                             // phase time is in the barrier, the input's round trip and the stores)
+#define TQ_CHAIN_DEPTH 6     // chunks in flight per wave (measured: 2, 4, 6 and 8 within 1.3%; 6 best)
 #endif
 using RB = RowBlock<TQ_F32_Q8, TQ_SCALE_TENSOR, 1, 1, TQ_CHAIN_DEPTH>;
 
@@ -531,28 +585,35 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
             const int first = blockIdx.x;
             if (first >= P.items) continue;      // no item in this phase
             Item it = item_of(C, P, ph, first);
-            const tq_prob_dev& Pp = Ld.p[it.proj + wp];
+            // the projection's descriptor in SGPRs: a descriptor loaded
+            // into VGPRs makes every code load a waterfall loop that waits
+            // for all loads in flight (one round trip per chunk)
+            const tq_prob_dev Pp = ld_uniform_struct(&Ld.p[it.proj + wp]);
             int c0 = 0, c1 = 0;
             wave_range(Pp.NC, P.splits, it.split, nw, ws, &c0, &c1);
+            int n_out = (int)ld_uniform_u32(&Ld.p[it.proj], offsetof(tq_prob_dev, N) / 4);   // output rows
             RB blk(Pp, it.rb, xq, nullptr);
             blk.begin(c0, c1);     // the codes stream in during the wait
-            uint32_t* dl = C.done + l * DONE_N;
             bool ok = true;
             if (ph == PH_QKV) {
-                if (l > 0) ok = wait_count(C, dl - DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].items, &flag);
+                if (l > 0) ok = wait_count(C, counter(C, l - 1, DONE_DOWN), (uint32_t)C.ph[PH_DOWN].items, &flag);
             } else if (ph == PH_O) {
-                ok = wait_count(C, dl + DONE_V, (uint32_t)(C.nb_kv * C.ph[PH_QKV].splits), &flag);
+                ok = wait_count(C, counter(C, l, DONE_V), (uint32_t)(C.nb_kv * C.ph[PH_QKV].splits), &flag);
             } else if (ph == PH_GU) {
                 // x1 = x + o needs every O item, and x the rows the QKV
                 // workgroups store
-                ok = wait_count(C, dl + DONE_O, (uint32_t)C.ph[PH_O].items, &flag) &&
-                     wait_count(C, dl + DONE_QKV, (uint32_t)C.ph[PH_QKV].items, &flag);
+                ok = wait_count(C, counter(C, l, DONE_O), (uint32_t)C.ph[PH_O].items, &flag) &&
+                     wait_count(C, counter(C, l, DONE_QKV), (uint32_t)C.ph[PH_QKV].items, &flag);
             } else {
                 if (qkv_out) qkv_rows(C, Ld, l, qkv_out);
-                ok = wait_count(C, dl + DONE_GU, (uint32_t)C.ph[PH_GU].items, &flag);
+                ok = wait_count(C, counter(C, l, DONE_GU), (uint32_t)C.ph[PH_GU].items, &flag);
             }
             if (!ok) return;
-            norm_quant(C, l, ph, x, Ld.norm[ph], P.width, min(P.items, C.G), xq, &sx_lds, red_d, (float*)red_f, o_at);
+            // two runs per thread for widths up to 4096 (no work on padding)
+            if (P.width <= 2 * 4 * kThreads)
+                norm_quant<2>(C, l, ph, x, Ld.norm[ph], P.width, min(P.items, C.G), xq, &sx_lds, red_d, (float*)red_f, o_at);
+            else
+                norm_quant<kRuns>(C, l, ph, x, Ld.norm[ph], P.width, min(P.items, C.G), xq, &sx_lds, red_d, (float*)red_f, o_at);
             for (int item = first; item < P.items; item += C.G) {
                 int part;
                 if (item == first) {
@@ -560,14 +621,19 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     part = blk.p[0][0];
                 } else {
                     it = item_of(C, P, ph, item);
-                    const tq_prob_dev& Pq = Ld.p[it.proj + wp];
+                    const tq_prob_dev Pq = ld_uniform_struct(&Ld.p[it.proj + wp]);
                     wave_range(Pq.NC, P.splits, it.split, nw, ws, &c0, &c1);
+                    n_out = (int)ld_uniform_u32(&Ld.p[it.proj], offsetof(tq_prob_dev, N) / 4);
                     RB b2(Pq, it.rb, xq, nullptr);
                     b2.run(c0, c1, nullptr);
                     part = b2.p[0][0];
                 }
                 // the waves' partial sums, per projection, in wave order
                 red[wave][lane] = part;
+                // this wave's stores of norm_quant (designated rows, s_x)
+                // complete behind the product; they are out before any item
+                // of the workgroup is counted
+                wait_stores();
                 __syncthreads();
                 if (wave == 0) {
                     int sa = 0, sb = 0;
@@ -575,18 +641,17 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
                     if (ph == PH_GU)
                         for (int k = nw; k < kWaves; ++k) sb += red[k][lane];
                     // the item's slot: its split's partial sums of the block's rows
-                    const tq_prob_dev& Pa = Ld.p[it.proj];
                     int32_t* slot = C.part + P.pbase + it.split * P.prow + it.off;
-                    if (it.rb * 64 + lane < Pa.N) {
+                    if (it.rb * 64 + lane < n_out) {
                         st_shared_i32(slot + lane, sa);
                         if (ph == PH_GU) st_shared_i32(slot + C.inter + lane, sb);
                     }
                     wait_stores();   // the slot is written before the count says so
                     if (lane == 0) {
                         const int c = ph == PH_QKV ? DONE_QKV : (ph == PH_O ? DONE_O : (ph == PH_GU ? DONE_GU : DONE_DOWN));
-                        __hip_atomic_fetch_add(dl + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_fetch_add(counter(C, l, c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         if (ph == PH_QKV && it.proj == W_V)
-                            __hip_atomic_fetch_add(dl + DONE_V, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            __hip_atomic_fetch_add(counter(C, l, DONE_V), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
                 __syncthreads();
@@ -596,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
     // the hidden state after the last layer, x = x1 + down: wave w of every
     // workgroup takes the 64-row blocks b with b = blockIdx + G (w + kWaves i)
     const int L = C.n_layers - 1;
-    if (!wait_count(C, C.done + L * DONE_N + DONE_DOWN, (uint32_t)C.ph[PH_DOWN].items, &flag)) return;
+    if (!wait_count(C, counter(C, L, DONE_DOWN), (uint32_t)C.ph[PH_DOWN].items, &flag)) return;
     const float cd = epi_scale(C, C.layers[L], W_DOWN, L, PH_DOWN);
     const PhaseDev& D = C.ph[PH_DOWN];
     for (int blk = blockIdx.x + C.G * wave; blk * 64 < C.hidden; blk += C.G * kWaves) {
@@ -616,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void k_bitnet_chain(const ChainDev* __res
 __global__ void k_chain_reset(ChainDev* C)
 {
     const ChainDev c = *C;
-    for (int i = threadIdx.x; i < c.n_layers * DONE_N; i += blockDim.x) c.done[i] = 0;
+    for (int i = threadIdx.x; i < c.n_layers * DONE_N; i += blockDim.x) c.done[i * kCtrStride] = 0;
     if (threadIdx.x == 0) *c.err = 0;
 }
 
@@ -673,7 +738,7 @@ Sizes sizes_of(const tq_bitnet_dims* d, int32_t n_layers)
     s.off_sxs = o;
     o = tq_align256(o + 4 * 4 * (int64_t)n_layers);
     s.off_done = o;
-    o = tq_align256(o + 4 * (int64_t)n_layers * DONE_N);
+    o = tq_align256(o + 4 * (int64_t)n_layers * DONE_N * kCtrStride);
     s.off_err = o;
     s.total = tq_align256(o + 4);
     return s;
