@@ -65,7 +65,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxWidth = 8192;          // longest phase input (held in registers, 16 per thread)
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls of one wait before giving up (~seconds)
 #ifndef TQ_CHAIN_SLEEP
-#define TQ_CHAIN_SLEEP 16                    // s_sleep between two polls of a wait (units of 64 cycles)
+#define TQ_CHAIN_SLEEP 32                    // s_sleep between two polls of a wait (units of 64 cycles)
 #endif
 
 enum { PH_QKV = 0, PH_O = 1, PH_GU = 2, PH_DOWN = 3 };
@@ -208,6 +208,14 @@ __device__ __forceinline__ uint32_t* counter(const ChainDev& C, int l, int c)
 
 // Wait until counter ctr reaches target.  Returns false when the wait gave
 // up, or another workgroup's did (every wait is bounded).
+// A counter poll: a relaxed agent-scope load through the global address
+// space (a flat load also waits on the LDS counter).
+__device__ __forceinline__ uint32_t poll(const uint32_t* p)
+{
+    return __hip_atomic_load((const __attribute__((address_space(1))) uint32_t*)p, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t target, int* flag_lds)
 {
     __syncthreads();   // every thread has read the previous wait's flag
@@ -215,12 +223,10 @@ __device__ bool wait_count(const ChainDev& C, const uint32_t* ctr, uint32_t targ
         uint32_t spins = 0;
         int ok = 1;
         for (;;) {
-            const uint32_t c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (c >= target) break;
+            if (poll(ctr) >= target) break;
             // the error flag, which every waiting workgroup would otherwise
             // poll on one line, only every kErrEvery polls
-            if ((spins & (kErrEvery - 1)) == kErrEvery - 1 &&
-                __hip_atomic_load(C.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+            if ((spins & (kErrEvery - 1)) == kErrEvery - 1 && poll((const uint32_t*)C.err)) {
                 ok = 0;
                 break;
             }

@@ -125,10 +125,15 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     constexpr int KPC = 64 / KS;                 // MFMA steps per chunk
     using SS = SkinnyStage<LAYOUT, K, KS>;
     constexpr int CDS = SS::CDS, SWN = SS::SWN, WST = SS::WST;
-    // chunks in flight: four (Llama-8B-shaped K = 3 stack, 16 tokens: 1.30
-    // against 1.34 ms with two; the compact codes 1.43 against 1.64 ms), two
-    // where four would not fit the registers of two waves per SIMD
-    constexpr int NBUF = K == 4 ? 2 : TQ_SKINNY_NBUF;
+    // chunks in flight: four (Llama-8B-shaped K = 3 stack, 16 tokens: 1.23
+    // against 1.28 ms with two; the compact codes 1.29 against 1.54 ms), two
+    // where four would not fit the registers of two waves per SIMD, and two
+    // for int8 with group scales (111 instead of 189 registers, four waves
+    // per SIMD instead of two; routed experts, K = 3, 64 tokens: 4.37
+    // against 4.46 ms) and for the codec's two-bit planes (16 tokens: 1.80
+    // against 1.87 ms; 4 tokens: the same)
+    constexpr int NBUF = (K == 4 || (XT == TQ_I8 && LAYOUT == TQ_SCALE_GROUP_F16) || LAYOUT == TQ_SCALE_CODEBOOK)
+                             ? 2 : TQ_SKINNY_NBUF;
     static_assert(NBUF % 2 == 0 && NBUF >= 2, "chunks in flight");
     constexpr int XL = 64 / KS;                  // x loads per chunk (one MFMA step's fragment each)
     using XF = typename std::conditional<KS * ESZ == 64, u32x4, u32x2>::type;
