@@ -205,7 +205,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int TN = 16 * FN * (4 / WM);
     constexpr int CW = kLds ? (XT == TQ_I8 ? 4 : 2) : 1;
     constexpr int CPT = kLds ? TN * CW / kThreads : 1;
-    static_assert(!kLds || (CPT >= 1 && CW % CPT == 0), "code dwords per thread");
+    static_assert(!kLds || ((CPT == 1 || CPT == 2 || CPT == 4) && CW % CPT == 0), "code dwords per thread");
     // Codes through a stage of the wave's own: the bf16 kernels without the
     // workgroup stage (the one-tile kernels, and 16-column steps), whose wave
     // owns one whole 64-row block.  Lane l loads row l's code dwords of the
@@ -263,13 +263,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // rotation rot = 2 ((R / 8) % 2) putting the 32 lanes of one LDS pass
     // (rows R .. R + 15, two dwords each) in distinct banks
     __shared__ __attribute__((aligned(16))) uint32_t clds[kLds ? 2 : 1][kLds ? TN * CW : 4];
-    uint32_t ccoff = 0, clds_w = 0, clds_r[FN];
+    uint32_t ccoff = 0, clds_w = 0, clds_w2 = 0, clds_r[FN];
     {
         const uint32_t T = threadIdx.x, R = T * CPT / CW, d0 = T * CPT % CW;
         const uint32_t n = tn * TN + R;
         const uint32_t rot = CW == 4 ? 2 * ((R >> 3) & 1) : 0;
         ccoff = ((n >> 6) * NC * K * 64 + (n & 63)) * 16 + d0 * 4;
         clds_w = R * CW + ((d0 + rot) % CW);
+        clds_w2 = R * CW + ((d0 + 2 + rot) % CW);   // CPT = 4: the row's second half
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const uint32_t Rr = (wave / WM) * (16 * FN) + 16 * fn + r;
@@ -354,7 +355,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         }
         const uint32_t cs = ((uint32_t)MF::chunk(ks) * K + c.k) * 1024 + MF::dword_step(ks) * 4;
         if constexpr (kLds) {
-            if constexpr (CPT == 2) {
+            if constexpr (CPT == 4) {
+                const u32x4 v = buffer_load<u32x4>(rc, ccoff, cs);
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) w[i] = v[i];
+            } else if constexpr (CPT == 2) {
                 const u32x2 v = buffer_load<u32x2>(rc, ccoff, cs);
                 w[0] = v[0];
                 w[CPT - 1] = v[1];
@@ -477,7 +482,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     auto lds_write = [&](int stage, const Frag (&a)[AREG], const uint32_t (&w)[WREG]) {
 #pragma unroll
         for (int i = 0; i < AREG; ++i) *(LDS_AS Frag*)((LDS_AS uint8_t*)xlds[stage] + xlds_w[i]) = a[i];
-        if constexpr (CPT == 2) {
+        if constexpr (CPT == 4) {
+            // the row's four dwords, rotated: two halves at their rotated places
+            *(LDS_AS u32x2*)((LDS_AS uint32_t*)clds[stage] + clds_w) = u32x2{w[0], w[1]};
+            *(LDS_AS u32x2*)((LDS_AS uint32_t*)clds[stage] + clds_w2) = u32x2{w[2], w[CPT - 1]};
+        } else if constexpr (CPT == 2) {
             *(LDS_AS u32x2*)((LDS_AS uint32_t*)clds[stage] + clds_w) = u32x2{w[0], w[CPT - 1]};
         } else {
             ((LDS_AS uint32_t*)clds[stage])[clds_w] = w[0];
