@@ -44,6 +44,9 @@ constexpr int kThreads = 256;   // 4 waves
 #ifndef TQ_GEMM_NBUF
 #define TQ_GEMM_NBUF 4             // steps in flight of the prefill kernels
 #endif
+#ifndef TQ_GEMM_PAIR
+#define TQ_GEMM_PAIR 1             // two steps per barrier where the registers allow
+#endif
 #ifndef TQ_GEMM_B3_NBUF
 #define TQ_GEMM_B3_NBUF 4          // steps in flight of the compact codec's kernels
 #endif
@@ -53,6 +56,12 @@ constexpr int kThreads = 256;   // 4 waves
 #endif
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Outputs of at most 1 GiB are stored through a buffer resource; kYPast is
+// the offset of an output past M or N: at or above the resource's size even
+// when added to a row or column offset that is itself in range.
+constexpr int64_t kYLean = (int64_t)1 << 30;
+constexpr uint32_t kYPast = 1u << 30;
 
 // The MFMA of one step of KS columns for activation type XT: operand
 // fragments (16 tokens or 16 weight rows by KS columns, KS / 4 columns per
@@ -184,8 +193,6 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     using Frag = typename MF::Frag;
     constexpr int ESZ = XT == TQ_I8 ? 1 : 2;             // bytes per activation
     constexpr int QCOLS = KS / 4;                         // columns per lane group
-    // steps in flight (loads issued NBUF - 1 steps ahead)
-    constexpr int NBUF = LAYOUT == TQ_SCALE_CODEBOOK_B3 ? TQ_GEMM_B3_NBUF : TQ_GEMM_NBUF;
     // int8, one plane, per-tensor scale: the int32 sum is the result
     constexpr bool kDirect = XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1;
     // the scale word of a (segment, plane) block: two f16 group scales, or six 5-bit codebook indices
@@ -197,6 +204,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr int TM = 16 * FM * WM;
     constexpr bool kLds = WM == 2 && KS * ESZ == 64 && TM * 4 % kThreads == 0;
     constexpr int XCH = kLds ? TM * 4 / kThreads : 1;     // 16-byte chunks per thread and step
+    // Two steps per barrier (the int8 one-plane kernel, whose registers allow
+    // six steps in flight): the workgroup stage is a ring of NBUF steps, and
+    // at every other step the waves meet once and stage the two steps after
+    // the next.  Otherwise one barrier per step and a double-buffered stage.
+    constexpr bool kPair = kLds && kDirect && TQ_GEMM_PAIR;
+    // steps in flight (loads issued NBUF - 1 steps ahead)
+    constexpr int NBUF = kPair ? 6 : LAYOUT == TQ_SCALE_CODEBOOK_B3 ? TQ_GEMM_B3_NBUF : TQ_GEMM_NBUF;
+    constexpr int NST = kPair ? NBUF : 2;                  // stages of the workgroup's LDS ring
     // The codes go through LDS as well: the workgroup's TN rows' code dwords
     // of a step are CW per row (the whole 16-byte slot for int8, half of it
     // for bf16), loaded CPT consecutive dwords per thread.  Read in the MFMA
@@ -258,11 +273,11 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         const uint32_t R = (wave % WM) * (16 * FM) + 16 * fm + r;
         xlds_r[fm] = R * 64 + 16 * (q ^ ((R >> 1) & 3));
     }
-    __shared__ __attribute__((aligned(16))) uint8_t xlds[kLds ? 2 : 1][kLds ? TM * 64 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[kLds ? NST : 1][kLds ? TM * 64 : 16];
     // code stage: row R's dword d at R * CW + ((d + rot(R)) % CW), the int8
     // rotation rot = 2 ((R / 8) % 2) putting the 32 lanes of one LDS pass
     // (rows R .. R + 15, two dwords each) in distinct banks
-    __shared__ __attribute__((aligned(16))) uint32_t clds[kLds ? 2 : 1][kLds ? TN * CW : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t clds[kLds ? NST : 1][kLds ? TN * CW : 4];
     uint32_t ccoff = 0, clds_w = 0, clds_w2 = 0, clds_r[FN];
     {
         const uint32_t T = threadIdx.x, R = T * CPT / CW, d0 = T * CPT % CW;
@@ -548,9 +563,22 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         if constexpr (kLds) {
             Frag a[FM];
             uint32_t w[FN];
-            barrier();
-            lds_write((u + 1) & 1, abuf[(u + 1) % NBUF], wbuf[(u + 1) % NBUF]);
-            lds_read(u & 1, a, w);
+            if constexpr (kPair) {
+                // even steps: stages u + 2 and u + 3 were last read at steps
+                // u - 4 and u - 3, and stages u, u + 1 were written at step
+                // u - 2, all before this barrier; their loads were issued at
+                // steps u - 3 and u - 2
+                if (u % 2 == 0) {
+                    barrier();
+                    lds_write((u + 2) % NST, abuf[(u + 2) % NBUF], wbuf[(u + 2) % NBUF]);
+                    lds_write((u + 3) % NST, abuf[(u + 3) % NBUF], wbuf[(u + 3) % NBUF]);
+                }
+                lds_read(u % NST, a, w);
+            } else {
+                barrier();
+                lds_write((u + 1) & 1, abuf[(u + 1) % NBUF], wbuf[(u + 1) % NBUF]);
+                lds_read(u & 1, a, w);
+            }
             // bf16 with a per-tensor scale and a ragged last step: x columns
             // past Kin (the next token's first ones) are zeroed, so that an
             // infinity there adds nothing to this token
@@ -582,8 +610,10 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         ld.advance(seg_steps, K);
     }
     if constexpr (kLds) lds_write(0, abuf[0], wbuf[0]);
+    if constexpr (kPair) lds_write(1, abuf[1], wbuf[1]);
     if constexpr (kWave) wave_write(0, wbuf[0], swbuf[0]);
     static_assert(!(kLds || kWave) || NBUF % 2 == 0, "stage parity follows the buffer index");
+    static_assert(!kPair || (NBUF == NST && NBUF >= 6), "the ring's stage of a step is its buffer index");
     int t = 0;
     for (; t + NBUF <= total; t += NBUF) {
 #pragma unroll
@@ -597,6 +627,56 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // epilogue: lane holds weight row n = n0 + 16 fn + r of tokens m0 + 16 fm + 4 q + e
     float s_w = 0.0f;
     if (kDirect) s_w = ld_uniform((const float*)P.scales);
+    const int64_t ybytes = (int64_t)M * N * 4;
+    if (ybytes <= kYLean) {
+        // y (and acc) through buffer stores: an output past M or N gets an
+        // offset at or above 1 GiB, past the resource's size, so the store is
+        // dropped -- one offset per row and per column, no branch per store
+        // (y of at most 1 GiB)
+        const __amdgpu_buffer_rsrc_t ry = rsrc(P.y, ybytes);
+        const __amdgpu_buffer_rsrc_t ra = rsrc(P.acc, P.acc ? ybytes : 0);
+        uint32_t colv[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = n0 + 16 * fn + r;
+            colv[fn] = n < N ? (uint32_t)n * 4u : kYPast;
+        }
+        // every token scale's load in flight at once
+        float cm[FM][4];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + 16 * fm + 4 * q + e;
+                cm[fm][e] = XT == TQ_I8 ? P.x_scale[m < M ? m : M - 1] : 1.0f;   // past M: stored nowhere
+            }
+        auto store_all = [&](const bool with_acc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + 16 * fm + 4 * q + e;
+                    const uint32_t rowv = m < M ? (uint32_t)m * (uint32_t)N * 4u : kYPast;
+                    const float c = kDirect ? s_w * cm[fm][e] : cm[fm][e];   // fl32(s_w * x_scale[m]), one rounding
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        float v;
+                        if (kDirect) {
+                            const int a = part[fm][fn][e];
+                            v = (float)a * c;
+                            if (with_acc)
+                                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)a, ra, rowv + colv[fn], 0, 0);
+                        } else {
+                            v = XT == TQ_I8 ? acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e] * c
+                                            : acc[kDirect ? 0 : fm][kDirect ? 0 : fn][e];
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, rowv + colv[fn], 0, 0);
+                    }
+                }
+        };
+        store_all(kDirect && P.acc);
+        return;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
