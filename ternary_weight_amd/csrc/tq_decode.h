@@ -121,6 +121,26 @@ struct B3Table {
     static __device__ __forceinline__ uint32_t copy_offset() { return (uint32_t)(threadIdx.x % C) * 4u; }
 };
 
+// The combined-digit table of the codec's two-bit digit planes (three
+// planes, plane k weighing 3^(2 - k)): a column's 6-bit code g holds plane
+// k's digit code at bits 2k, 2k + 1 (01 = +1, 10 = -1, 00 and 11 = 0), and
+// the bf16 at byte 2 g is the column's combined value 9 d0 + 3 d1 + d2, an
+// integer in [-13, 13], exact in bf16 (d3 card, "Quantization details").
+// 128 bytes: 32 dwords, one per bank, so no two lanes' reads conflict.
+struct D3Table {
+    static constexpr int kBytes = 128;
+    static __device__ __forceinline__ int digit(uint32_t c) { return c == 1u ? 1 : (c == 2u ? -1 : 0); }
+    static __device__ __forceinline__ void fill(uint8_t* lut)
+    {
+        const uint32_t g = threadIdx.x;
+        if (g < 64) {
+            const int v = 9 * digit(g & 3u) + 3 * digit((g >> 2) & 3u) + digit((g >> 4) & 3u);
+            // a small integer: the fp32 value's upper half is the exact bf16
+            *(LDS_AS uint16_t*)((LDS_AS uint8_t*)lut + 2 * g) = (uint16_t)(__float_as_uint((float)v) >> 16);
+        }
+    }
+};
+
 __device__ __forceinline__ float f16_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 }  // namespace tqk

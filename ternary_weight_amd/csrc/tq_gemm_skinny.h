@@ -22,7 +22,11 @@
 //   - per plane and chunk, 2 steps of v_mfma_f32_16x16x32_bf16 (groups of 32
 //     and more, per-tensor scale) or 4 of v_mfma_f32_16x16x16_bf16 (groups
 //     of 16, the codec), 4 MFMAs each (tiles fn = 0..3), into a partial sum
-//     per plane and tile; a group's scales are applied once when it ends.
+//     per plane and tile; a group's scales are applied once when it ends;
+//   - the codec's three two-bit digit planes are combined per column into
+//     one operand of exact values 9 d0 + 3 d1 + d2 (a 64-entry table of bf16
+//     values in LDS), so a group takes one MFMA and one codebook scale per
+//     tile, not one per plane.
 // Loads run NBUF - 1 chunks ahead.  The per-chunk bookkeeping (offsets, the
 // chunk's groups) is a few scalar instructions per chunk, where a kernel
 // stepping one MFMA step of one plane at a time spends them on every step.
@@ -39,6 +43,14 @@ namespace tqm {
 #ifndef TQ_SKINNY_NBUF
 #define TQ_SKINNY_NBUF 4   // chunks in flight (even: the stage parity follows the buffer index)
 #endif
+// The codec's combined-digit kernel: two chunks in flight at three waves per
+// SIMD (136 VGPRs; Llama-8B-shaped codec stack, 16 tokens: 1.53 ms, against
+// 1.58 ms with four chunks at two waves per SIMD and 1.60 ms with six; four
+// chunks at three waves per SIMD spill).
+#ifndef TQ_SKINNY_COMB_NBUF
+#define TQ_SKINNY_COMB_NBUF 2
+#endif
+#define TQ_SKINNY_COMB_NBUF_OR(comb, other) ((comb) ? TQ_SKINNY_COMB_NBUF : (other))
 
 // The two-bit decode of these kernels.  One field of a code dword (one
 // 2-bit code per byte: columns 4p .. 4p + 3, tq_layout.h) gives four bf16
@@ -104,6 +116,28 @@ struct SkinnyStage {
     static constexpr int WST = 64 * (CDS + SWN);   // dwords per wave and stage
 };
 
+// The codec's two-bit digit planes combined into one operand per group
+// (skinny_tile), and the table size that takes.
+template <int XT, int LAYOUT, int K, int KS>
+constexpr bool skinny_comb() { return XT == TQ_BF16 && LAYOUT == TQ_SCALE_CODEBOOK && K == 3 && KS == 16; }
+template <int XT, int LAYOUT, int K, int KS>
+constexpr int skinny_lut_bytes()
+{
+    return skinny_comb<XT, LAYOUT, K, KS>() ? D3Table::kBytes : b3_lut_bytes<LAYOUT>();
+}
+// The codebook (and the table of the compact codes or of the combined digits) in LDS.
+template <int XT, int LAYOUT, int K, int KS>
+__device__ __forceinline__ void skinny_stage_tables(const tq_prob_dev& P, float* cb_lds, uint8_t* lut)
+{
+    if constexpr (skinny_comb<XT, LAYOUT, K, KS>()) {
+        if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+        D3Table::fill(lut);
+        __syncthreads();
+    } else {
+        stage_codebook<LAYOUT>(P, cb_lds, lut);
+    }
+}
+
 template <int XT, int LAYOUT, int K, int KS, int GM>
 __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const LDS_AS float* cb_lds,
                                             const LDS_AS uint8_t* b3_lut, LDS_AS uint32_t* wlds)
@@ -121,7 +155,12 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     static_assert(!kB3 || (!kI8 && K == 1 && KS == 16), "compact base-3 codes: one stream, 16-column steps");
     static_assert(kI8 ? (KS == 64 && !kCb) : (KS == 32 || KS == 16), "MFMA step");
     static_assert((GM == kGroupNone) == kTensor, "group mode");
-    constexpr int KP = K;                        // code streams per chunk: planes, or the one B3 stream
+    // The codec's three two-bit digit planes (d = 3): each 16-column group's
+    // digits are combined into one operand of exact values 9 d0 + 3 d1 + d2
+    // through the combined-digit table, one MFMA and one codebook scale per
+    // group and tile instead of one per plane.
+    constexpr bool kComb = skinny_comb<XT, LAYOUT, K, KS>();
+    constexpr int KP = kComb ? 1 : K;            // partial sums per tile: planes, or the one combined operand
     constexpr int KPC = 64 / KS;                 // MFMA steps per chunk
     using SS = SkinnyStage<LAYOUT, K, KS>;
     constexpr int CDS = SS::CDS, SWN = SS::SWN, WST = SS::WST;
@@ -130,15 +169,17 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     // where four would not fit the registers of two waves per SIMD, and two
     // for int8 with group scales (111 instead of 189 registers, four waves
     // per SIMD instead of two; routed experts, K = 3, 64 tokens: 4.37
-    // against 4.46 ms) and for the codec's two-bit planes (16 tokens: 1.80
-    // against 1.87 ms; 4 tokens: the same)
-    constexpr int NBUF = (K == 4 || (XT == TQ_I8 && LAYOUT == TQ_SCALE_GROUP_F16) || LAYOUT == TQ_SCALE_CODEBOOK)
-                             ? 2 : TQ_SKINNY_NBUF;
+    // against 4.46 ms) and for codebook scales on digit planes other than
+    // the three the combined kernel takes (measured when the three-digit
+    // codec still ran one plane at a time: 16 tokens 1.80 against 1.87 ms)
+    constexpr int NBUF = (K == 4 || (XT == TQ_I8 && LAYOUT == TQ_SCALE_GROUP_F16) ||
+                          (LAYOUT == TQ_SCALE_CODEBOOK && !kComb))
+                             ? 2 : TQ_SKINNY_COMB_NBUF_OR(kComb, TQ_SKINNY_NBUF);
     static_assert(NBUF % 2 == 0 && NBUF >= 2, "chunks in flight");
     constexpr int XL = 64 / KS;                  // x loads per chunk (one MFMA step's fragment each)
     using XF = typename std::conditional<KS * ESZ == 64, u32x4, u32x2>::type;
     static_assert(sizeof(XF) == sizeof(Frag), "an x load is one MFMA step's fragment");
-    constexpr int CL = kB3 ? 3 : KP;             // code loads per chunk
+    constexpr int CL = kB3 ? 3 : K;              // code loads per chunk (a slot per plane; B3: three parts)
     using B3T = B3Table<8>;   // pair-code table, 8 copies (32 KiB)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -184,6 +225,13 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         b3_h[s] = bit & 31u;
     }
     const uint32_t b3_copy = kB3 ? B3T::copy_offset() : 0u;
+    // kComb: rotations that bring field q (bits 2q, 2q + 1 of every byte) of
+    // plane k to bits 2k + 1, 2k + 2, so that each byte becomes 2 g, the
+    // byte offset of its column's combined value in the table
+    const uint32_t rot0 = (2u * (uint32_t)q - 1u) & 31u, rot1 = (2u * (uint32_t)q - 3u) & 31u,
+                   rot2 = (2u * (uint32_t)q - 5u) & 31u;
+    // kComb: the code dwords of the chunk, row 16 fn + r, plane k (read once per chunk)
+    u32x4 cwv[kComb ? 4 : 1][kComb ? 3 : 1];
 
     u32x4 cbuf[NBUF][CL];                         // B3: parts 0, 1 and (low half) 2
     uint32_t sbuf[NBUF][SWN > 0 ? SWN : 1];
@@ -213,7 +261,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         } else {
             const uint32_t so = (uint32_t)c * K * 1024u;
 #pragma unroll
-            for (int k = 0; k < KP; ++k) cb[k] = buffer_load<u32x4, kCacheNT>(rc, cv + (uint32_t)k * 1024u, so);
+            for (int k = 0; k < CL; ++k) cb[k] = buffer_load<u32x4, kCacheNT>(rc, cv + (uint32_t)k * 1024u, so);
         }
         if constexpr (SWN > 0) {
             const uint32_t so = scale_soff(c);
@@ -229,7 +277,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             *(LDS_AS u32x2*)(row + 8) = u32x2{cb[2][0], cb[2][1]};
         } else {
 #pragma unroll
-            for (int k = 0; k < KP; ++k) *(LDS_AS u32x4*)(row + 4 * k) = cb[k];
+            for (int k = 0; k < CL; ++k) *(LDS_AS u32x4*)(row + 4 * k) = cb[k];
         }
 #pragma unroll
         for (int j = 0; j < SWN; ++j) st[64 * CDS + 64 * j + lane] = sw[j];
@@ -258,6 +306,24 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             Frag f;
             f[0] = *(const LDS_AS uint32_t*)(b3_lut + a0);
             f[1] = *(const LDS_AS uint32_t*)(b3_lut + a1);
+            return f;
+        } else if constexpr (kComb) {
+            // step s: dword s of each plane's slot, field q: the lane's four
+            // columns' codes as table offsets 2 g, one per byte; then the
+            // pairs (1, 3) and (0, 2) (the odd-even order of x)
+            const uint32_t g = (__builtin_amdgcn_alignbit(cwv[fn][2][s], cwv[fn][2][s], rot2) & 0x60606060u) |
+                               (__builtin_amdgcn_alignbit(cwv[fn][1][s], cwv[fn][1][s], rot1) & 0x18181818u) |
+                               (__builtin_amdgcn_alignbit(cwv[fn][0][s], cwv[fn][0][s], rot0) & 0x06060606u);
+            const LDS_AS uint16_t* t = (const LDS_AS uint16_t*)b3_lut;
+            typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 p13, p02;
+            p13[0] = *(const LDS_AS uint16_t*)((const LDS_AS uint8_t*)t + __builtin_amdgcn_ubfe(g, 8, 8));
+            p13[1] = *(const LDS_AS uint16_t*)((const LDS_AS uint8_t*)t + (g >> 24));
+            p02[0] = *(const LDS_AS uint16_t*)((const LDS_AS uint8_t*)t + (g & 0xFFu));
+            p02[1] = *(const LDS_AS uint16_t*)((const LDS_AS uint8_t*)t + __builtin_amdgcn_ubfe(g, 16, 8));
+            Frag f;
+            f[0] = __builtin_bit_cast(uint32_t, p13);
+            f[1] = __builtin_bit_cast(uint32_t, p02);
             return f;
         } else if constexpr (KS == 32) {
             // step s: dword 2 s + q / 2 of the plane's slot, half q % 2
@@ -290,7 +356,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             const int j = idx0 + grp - ((c << 6) >> lg);         // 0 .. 7: word j / 6, field j % 6
             const uint32_t w = j >= 6 ? idxw[fn][1] : idxw[fn][0];
             const float cb = cb_lds[(w >> (5 * (j >= 6 ? j - 6 : j))) & 31u];
-            if constexpr (kB3) {
+            if constexpr (kB3 || kComb) {
                 return cb;                                         // the table holds the combined values
             } else {
                 float wgt = MF::kScale;                            // digit plane k weighs 3^(K - 1 - k)
@@ -339,6 +405,12 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         const int nv = nks - c * KPC;              // valid steps of the chunk (>= 1; more than KPC: all)
         if (kTensor && c == NC - 1 && Kin % KS != 0) mask_x(c, xa);
         read_idx(st, c);
+        if constexpr (kComb) {
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) cwv[fn][k] = *(const LDS_AS u32x4*)(st + (16 * fn + r) * CDS + 4 * k);
+        }
         auto one_step = [&](int s, bool zero) {
             // x in the weight fragments' column order (the compact codes'
             // table gives consecutive columns)
@@ -448,27 +520,34 @@ __device__ __forceinline__ void skinny_dispatch(const tq_prob_dev& P, int tn, co
     }
 }
 
+#ifndef TQ_SKINNY_COMB_WPS
+#define TQ_SKINNY_COMB_WPS 3
+#endif
+// Waves per SIMD the register budget is sized for.
 template <int XT, int LAYOUT, int K, int KS>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny(tq_prob_dev P, int /*tiles_m*/)
+constexpr int skinny_waves() { return skinny_comb<XT, LAYOUT, K, KS>() ? TQ_SKINNY_COMB_WPS : 2; }
+
+template <int XT, int LAYOUT, int K, int KS>
+__global__ __launch_bounds__(kThreads, (skinny_waves<XT, LAYOUT, K, KS>())) void k_gemm_skinny(tq_prob_dev P, int /*tiles_m*/)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[skinny_lut_bytes<XT, LAYOUT, K, KS>()];
     __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
-    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
+    skinny_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
     skinny_dispatch<XT, LAYOUT, K, KS>(P, blockIdx.x, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
                                    (LDS_AS uint32_t*)wlds);
 }
 
 // Grouped: item i = (problem, tile); one token tile per problem.
 template <int XT, int LAYOUT, int K, int KS>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny_grouped(const tq_prob_dev* probs, const int2* items)
+__global__ __launch_bounds__(kThreads, (skinny_waves<XT, LAYOUT, K, KS>())) void k_gemm_skinny_grouped(const tq_prob_dev* probs, const int2* items)
 {
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[skinny_lut_bytes<XT, LAYOUT, K, KS>()];
     __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
-    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
+    skinny_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
     skinny_dispatch<XT, LAYOUT, K, KS>(P, it.y, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
                                    (LDS_AS uint32_t*)wlds);
 }

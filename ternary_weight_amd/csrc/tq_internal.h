@@ -51,15 +51,18 @@ tq_prob_dev tq_make_prob(const tq_layout& L, const void* blob, int64_t M, const 
 tq_status tq_fail_problem(tq_status s, int32_t i);
 
 // bf16 decode with at least this many tokens runs on the matrix cores (the
-// prefill kernels' one-tile variant) when x is 16-byte aligned: 3, or 5 for
-// the codec in either packing, whose matrix-core kernels apply a scale after
-// every 16 columns (measured crossovers; compact codes: 4 tokens 0.98 ms on
-// the vector ALUs, 5 tokens 1.83 ms there against 1.5 ms on the matrix cores).
+// few-token kernels) when x is 16-byte aligned: 3, also for the codec's
+// two-bit digit planes, whose matrix-core kernel combines the three digits
+// into one operand (Llama-8B-shaped codec stack: 3 tokens 1.52 ms there
+// against 1.63 ms on the vector ALUs, 2 tokens 1.5 against 1.31 ms), and 5
+// for the compact codes, whose matrix-core kernel applies a scale after
+// every 16 columns (4 tokens 0.98 ms on the vector ALUs, 5 tokens 1.83 ms
+// there against 1.5 ms on the matrix cores).
 #ifndef TQ_BF16_MFMA_MIN_M
 #define TQ_BF16_MFMA_MIN_M 3
 #endif
 #ifndef TQ_BF16_MFMA_MIN_M_CODEC
-#define TQ_BF16_MFMA_MIN_M_CODEC 5
+#define TQ_BF16_MFMA_MIN_M_CODEC 3
 #endif
 #ifndef TQ_BF16_MFMA_MIN_M_B3
 #define TQ_BF16_MFMA_MIN_M_B3 5

@@ -15,7 +15,7 @@ import pytest
 import oracle
 from oracle import BF16, CODEBOOK, F32, GROUP_F16, I8, TENSOR
 from synth import gen
-from tests.gpu_util import TOL, dev, gemv, host, pack, rel_err, torch
+from tests.gpu_util import TOL, dev, gemv, host, pack, read_blob, rel_err, torch
 from tests.test_gpu_parity import rand_problem, rand_x
 
 pytestmark = pytest.mark.gpu
@@ -232,10 +232,10 @@ def test_gemm_grouped_equals_single(xt, K, g, layout):
 @pytest.mark.parametrize("layout,K,g", [(CODEBOOK, 3, 16), (GROUP_F16, 3, 256), (GROUP_F16, 2, 16)])
 @pytest.mark.parametrize("M", [2, 3, 4, 5, 9, 16])
 def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
-    """tq_gemv and the grouped decode plan route bf16 with 3 or more tokens (5
-    or more for the codec) to the one-tile matrix-core kernels, fewer to the
-    vector ALUs in slices of 4; both agree with the oracle, and on the matrix
-    cores the grouped plan bit for bit with the single call."""
+    """tq_gemv and the grouped decode plan route bf16 with 3 or more tokens
+    (the codec's digit planes included) to the one-tile matrix-core kernels,
+    fewer to the vector ALUs in slices of 4; both agree with the oracle, and on
+    the matrix cores the grouped plan bit for bit with the single call."""
     from ternary_weight_amd import tq
     t = torch()
     rng = np.random.default_rng(M * 10 + g + K)
@@ -256,7 +256,7 @@ def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
     n = tq.gemv_grouped_workspace_size(probs, M)
     ws = t.empty(n, dtype=t.uint8, device="cuda")
     plan = tq.gemv_grouped_prepare(probs, M, BF16, ws, n)
-    on_mfma = M >= (5 if layout == CODEBOOK else 3)
+    on_mfma = M >= 3
     assert (plan.family >= 1000) == on_mfma          # a matrix-core plan, or the vector ALUs
     tq.gemv_grouped_run(plan)
     t.cuda.synchronize()
@@ -265,6 +265,33 @@ def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
             assert np.array_equal(host(y).view(np.uint32), w.view(np.uint32))
         else:
             assert rel_err(host(y), w) <= TOL
+
+
+@pytest.mark.parametrize("M", [3, 16])
+def test_codec_digit_planes_code_11_and_ragged_chunk(M):
+    """The codec's three two-bit digit planes on the matrix cores, combined
+    per column into one operand (d3 card, "Quantization details": value
+    9 t2 + 3 t1 + t0): digit code 11 planted at random in every plane reads
+    as 0 (the layout's rule, applied by the independent blob reader), and rows
+    of 464 columns end 16 columns into their eighth 64-column chunk."""
+    rng = np.random.default_rng(71 + M)
+    K, g, N, Kin = 3, 16, 200, 464
+    trits, scales, cb = rand_problem(K, g, CODEBOOK, N, Kin, rng)
+    d, blob = pack(K, g, CODEBOOK, trits, scales, cb)
+    raw = host(blob).view(np.uint8).copy()
+    NB, NC = (N + 63) // 64, (Kin + 63) // 64
+    nbytes = NB * NC * K * 64 * 16
+    region = raw[256:256 + nbytes]
+    hit = rng.random(nbytes) < 0.25
+    field = rng.integers(0, 4, size=nbytes).astype(np.uint8)
+    region[hit] |= (np.uint8(3) << (2 * field[hit])).astype(np.uint8)
+    raw[256:256 + nbytes] = region
+    rb = read_blob(raw, K, N, Kin, CODEBOOK, g=g)
+    assert np.any(rb["codes"][:, :N, :Kin] == 3)
+    assert np.array_equal(rb["scales"], scales)
+    x = rand_x(M, Kin, BF16, rng)
+    y = gemv(d, dev(raw), BF16, x)
+    assert rel_err(y, oracle.gemv_fp(K, g, CODEBOOK, rb["trits"], scales, x, BF16, cb)) <= TOL
 
 
 def test_bf16_several_tokens_weight_over_4gib_runs_on_vector_alus():
