@@ -170,6 +170,11 @@ __device__ __forceinline__ F zero_frag()
 // The host keeps every operand of a launch below 4 GiB.
 // Position in the step sequence: segment (a group, or the whole row for a
 // per-tensor scale), then plane, then the segment's MFMA steps.
+// The codec's three two-bit digit planes combined into one operand per
+// 16-column group (gemm_tile), and the table that takes.
+template <int XT, int LAYOUT, int K, int KS>
+constexpr bool gemm_comb() { return XT == TQ_BF16 && LAYOUT == TQ_SCALE_CODEBOOK && K == 3 && KS == 16; }
+
 struct Cursor {
     int seg, k, j;
     __device__ __forceinline__ void advance(int seg_steps, int K)
@@ -238,7 +243,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     constexpr bool kB3 = LAYOUT == TQ_SCALE_CODEBOOK_B3;
     constexpr bool kCb = LAYOUT == TQ_SCALE_CODEBOOK || kB3;
     static_assert(!kB3 || (kWave && K == 1 && KS == 16), "compact base-3 codes: the per-wave stage, 16-column steps");
-    constexpr int CWW = kB3 ? 3 : KS / 16;                // code dwords of a row per step
+    // The codec's three two-bit digit planes: a step stages the group's
+    // dword of each plane, and each column's three digits become one operand
+    // of exact values 9 d0 + 3 d1 + d2 (the combined-digit table): one MFMA
+    // and one codebook scale per group, as for the compact codes.
+    constexpr bool kComb = gemm_comb<XT, LAYOUT, K, KS>();
+    static_assert(!kComb || kWave, "combined digits: the per-wave stage");
+    constexpr int KC = kComb ? 1 : K;                     // planes the steps walk (the combined operand: one)
+    constexpr int CWW = kB3 || kComb ? 3 : KS / 16;       // code dwords of a row per step
     constexpr int WST = 64 * CWW + (kWord ? 64 : 0) + (kB3 ? 4 : 0);   // dwords per wave and stage (B3: a
                                                                       // pad dword read past the last row)
 
@@ -325,6 +337,9 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     }
     using B3T = B3Table<8>;   // pair-code table, 8 copies (32 KiB: more workgroups per unit, measured)
     const uint32_t b3_copy = kB3 ? B3T::copy_offset() : 0u;
+    // combined digits: plane k's rotation, field q to bits 2k + 1, 2k + 2
+    const uint32_t crot[3] = {(2u * (uint32_t)q - 1u) & 31u, (2u * (uint32_t)q - 3u) & 31u,
+                              (2u * (uint32_t)q - 5u) & 31u};
     __shared__ __attribute__((aligned(16))) uint32_t wlds[kWave ? 2 : 1][kWave ? 4 * WST : 4];
     LDS_AS uint32_t* const wst0 = (LDS_AS uint32_t*)wlds[0] + (kWave ? wave * WST : 0);
     LDS_AS uint32_t* const wst1 = (LDS_AS uint32_t*)wlds[kWave ? 1 : 0] + (kWave ? wave * WST : 0);
@@ -332,7 +347,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     const int nks = (Kin + KS - 1) / KS;                       // MFMA steps per row
     const int seg_steps = LAYOUT == TQ_SCALE_TENSOR ? nks : P.g / KS;
     const int nseg = LAYOUT == TQ_SCALE_TENSOR ? 1 : Kin / P.g;
-    const int total = nseg * K * seg_steps;
+    const int total = nseg * KC * seg_steps;
 
     Part part[FM][FN];
     f32x4 acc[kDirect ? 1 : FM][kDirect ? 1 : FN];
@@ -355,7 +370,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         // a cursor past the last step (the prefetch runs ahead of the end)
         // loads the last step again: the data is in cache and never used
         const bool past = cur.seg >= nseg;
-        const Cursor c{past ? nseg - 1 : cur.seg, past ? K - 1 : cur.k, past ? seg_steps - 1 : cur.j};
+        const Cursor c{past ? nseg - 1 : cur.seg, past ? KC - 1 : cur.k, past ? seg_steps - 1 : cur.j};
         const int ks = c.seg * seg_steps + c.j;                 // MFMA step along the row
         const uint32_t xs = (uint32_t)ks * (KS * ESZ);
         // x through a window from the step's first column to the end of x, so
@@ -392,6 +407,10 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
                 const uint32_t so = chunk * TQ_B3_CHUNK_BYTES + (third ? (D - 8) * 4 : (D >> 2) * 1024 + (D & 3) * 4);
                 w[i] = buffer_load<uint32_t>(rc, third ? cwoff2 : cwoff, so);
             }
+        } else if constexpr (kComb) {
+            // the step's dword (16 columns) of each digit plane
+#pragma unroll
+            for (int i = 0; i < 3; ++i) w[i] = buffer_load<uint32_t>(rc, cwoff, cs + (uint32_t)i * 1024u);
         } else if constexpr (kWave) {
             if constexpr (CWW == 2) {
                 const u32x2 v = buffer_load<u32x2>(rc, cwoff, cs);
@@ -425,6 +444,20 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
             Frag f;
             f[0] = *(const LDS_AS uint32_t*)(b3_lut + a0);
             f[1] = *(const LDS_AS uint32_t*)(b3_lut + a1);
+            return f;
+        } else if constexpr (kComb) {
+            // wv: the lane's four columns' 6-bit codes as table offsets 2 g,
+            // one per byte; pairs (0, 1) and (2, 3) in column order
+            typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+            const LDS_AS uint8_t* t = b3_lut;
+            u16x2 p01, p23;
+            p01[0] = *(const LDS_AS uint16_t*)(t + (wv & 0xFFu));
+            p01[1] = *(const LDS_AS uint16_t*)(t + __builtin_amdgcn_ubfe(wv, 8, 8));
+            p23[0] = *(const LDS_AS uint16_t*)(t + __builtin_amdgcn_ubfe(wv, 16, 8));
+            p23[1] = *(const LDS_AS uint16_t*)(t + (wv >> 24));
+            Frag f;
+            f[0] = __builtin_bit_cast(uint32_t, p01);
+            f[1] = __builtin_bit_cast(uint32_t, p23);
             return f;
         } else {
             return MF::decode(wv, q);
@@ -460,7 +493,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         for (int fn = 0; fn < FN; ++fn) {
             if (LAYOUT == TQ_SCALE_TENSOR) {
                 sc[fn] = ld_uniform(((const float*)P.scales) + c.k) * MF::kScale;
-            } else if (kB3) {
+            } else if (kB3 || kComb) {
                 // the table holds the combined values exactly: the group's scale alone
                 sc[fn] = cb_lds[(sw[fn] >> (5 * (c.seg % 6))) & 31u];
             } else if (LAYOUT == TQ_SCALE_CODEBOOK) {
@@ -518,7 +551,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
     // writes row l's code dwords and scale word; the fragments are read back
     // in the MFMA layout, row 16 fn + r, the lane group's dword
     auto wave_write = [&](int stage, const uint32_t (&w)[WREG], const uint32_t (&sw)[SREG]) {
-        if constexpr (kB3) {
+        if constexpr (kB3 || kComb) {
             LDS_AS uint32_t* st = stage ? wst1 : wst0;
 #pragma unroll
             for (int i = 0; i < 3; ++i) st[3 * lane + i] = w[i];   // stride 3: no bank conflicts
@@ -544,6 +577,18 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
                 const uint32_t base = (16 * fn + r) * 3 + lo;
                 w[fn] = __builtin_amdgcn_alignbit(st[base + 1], st[base], sh);
             }
+        } else if constexpr (kComb) {
+            // row 16 fn + r's dword of each plane, field q (bits 2q, 2q + 1 of
+            // every byte) of plane k rotated to bits 2k + 1, 2k + 2: each byte
+            // becomes 2 g, the offset of its column's value in the table
+            const LDS_AS uint32_t* st = stage ? wst1 : wst0;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const LDS_AS uint32_t* row = st + (16 * fn + r) * 3;
+                w[fn] = (__builtin_amdgcn_alignbit(row[2], row[2], crot[2]) & 0x60606060u) |
+                        (__builtin_amdgcn_alignbit(row[1], row[1], crot[1]) & 0x18181818u) |
+                        (__builtin_amdgcn_alignbit(row[0], row[0], crot[0]) & 0x06060606u);
+            }
         } else if constexpr (kWave) {
             const LDS_AS uint32_t* st = stage ? wst1 : wst0;
 #pragma unroll
@@ -557,7 +602,7 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         const int v = (u + kAhead) % NBUF;
         if (issue) {
             load(ld, abuf[v], wbuf[v], swbuf[v]);
-            ld.advance(seg_steps, K);
+            ld.advance(seg_steps, KC);
         }
         __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's MFMAs
         if constexpr (kLds) {
@@ -600,14 +645,14 @@ __device__ __forceinline__ void gemm_tile(const tq_prob_dev& P, int tm, int tn, 
         } else {
             compute(cp, abuf[u], wbuf[u], swbuf[u], wst0);
         }
-        cp.advance(seg_steps, K);
+        cp.advance(seg_steps, KC);
     };
 
     Cursor ld{0, 0, 0}, cp{0, 0, 0};
 #pragma unroll
     for (int u = 0; u + 1 < NBUF; ++u) {
         load(ld, abuf[u], wbuf[u], swbuf[u]);
-        ld.advance(seg_steps, K);
+        ld.advance(seg_steps, KC);
     }
     if constexpr (kLds) lds_write(0, abuf[0], wbuf[0]);
     if constexpr (kPair) lds_write(1, abuf[1], wbuf[1]);
@@ -718,6 +763,22 @@ __device__ __forceinline__ void stage_codebook(const tq_prob_dev& P, float* cb_l
 template <int LAYOUT>
 constexpr int b3_lut_bytes() { return LAYOUT == TQ_SCALE_CODEBOOK_B3 ? B3Table<8>::kBytes : 16; }
 
+// The prefill kernels' tables: the codebook, and the table of the compact
+// codes or of the combined digits.
+template <int XT, int LAYOUT, int K, int KS>
+constexpr int gemm_lut_bytes() { return gemm_comb<XT, LAYOUT, K, KS>() ? D3Table::kBytes : b3_lut_bytes<LAYOUT>(); }
+template <int XT, int LAYOUT, int K, int KS>
+__device__ __forceinline__ void gemm_stage_tables(const tq_prob_dev& P, float* cb_lds, uint8_t* lut)
+{
+    if constexpr (gemm_comb<XT, LAYOUT, K, KS>()) {
+        if (threadIdx.x < TQ_CB_SLOTS) cb_lds[threadIdx.x] = f16_to_f32(P.cb[threadIdx.x]);
+        D3Table::fill(lut);
+        __syncthreads();
+    } else {
+        stage_codebook<LAYOUT>(P, cb_lds, lut);
+    }
+}
+
 // Waves per SIMD the register budget is sized for: the compact codec's
 // few-token kernel (98 VGPRs) takes four, as its table leaves room for them.
 template <int LAYOUT, int FM>
@@ -727,8 +788,8 @@ template <int XT, int LAYOUT, int K, int FM, int FN, int KS, int WM>
 __global__ __launch_bounds__(kThreads, (waves_per_simd<LAYOUT, FM>())) void k_gemm_single(tq_prob_dev P, int tiles_m)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
-    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[gemm_lut_bytes<XT, LAYOUT, K, KS>()];
+    gemm_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
     const int tile = blockIdx.x;
     gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, tile % tiles_m, tile / tiles_m, (const LDS_AS float*)cb_lds,
                                              (const LDS_AS uint8_t*)b3_lut);
@@ -741,8 +802,8 @@ __global__ __launch_bounds__(kThreads, (waves_per_simd<LAYOUT, FM>())) void k_ge
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
     __shared__ float cb_lds[TQ_CB_SLOTS];
-    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[b3_lut_bytes<LAYOUT>()];
-    stage_codebook<LAYOUT>(P, cb_lds, b3_lut);
+    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[gemm_lut_bytes<XT, LAYOUT, K, KS>()];
+    gemm_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
     const int tiles_m = (P.M + 16 * FM * WM - 1) / (16 * FM * WM);
     gemm_tile<XT, LAYOUT, K, FM, FN, KS, WM>(P, it.y % tiles_m, it.y / tiles_m, (const LDS_AS float*)cb_lds,
                                              (const LDS_AS uint8_t*)b3_lut);

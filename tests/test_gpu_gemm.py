@@ -267,11 +267,12 @@ def test_decode_bf16_several_tokens_on_matrix_cores(layout, K, g, M):
             assert rel_err(host(y), w) <= TOL
 
 
-@pytest.mark.parametrize("M", [3, 16])
+@pytest.mark.parametrize("M", [3, 16, 40])
 def test_codec_digit_planes_code_11_and_ragged_chunk(M):
     """The codec's three two-bit digit planes on the matrix cores, combined
     per column into one operand (d3 card, "Quantization details": value
-    9 t2 + 3 t1 + t0): digit code 11 planted at random in every plane reads
+    9 t2 + 3 t1 + t0), in the few-token kernel (3 and 16 tokens) and the
+    prefill kernel (40): digit code 11 planted at random in every plane reads
     as 0 (the layout's rule, applied by the independent blob reader), and rows
     of 464 columns end 16 columns into their eighth 64-column chunk."""
     rng = np.random.default_rng(71 + M)
@@ -290,7 +291,7 @@ def test_codec_digit_planes_code_11_and_ragged_chunk(M):
     assert np.any(rb["codes"][:, :N, :Kin] == 3)
     assert np.array_equal(rb["scales"], scales)
     x = rand_x(M, Kin, BF16, rng)
-    y = gemv(d, dev(raw), BF16, x)
+    y = gemv(d, dev(raw), BF16, x, gemm=M > 16)
     assert rel_err(y, oracle.gemv_fp(K, g, CODEBOOK, rb["trits"], scales, x, BF16, cb)) <= TOL
 
 
