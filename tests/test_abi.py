@@ -174,8 +174,12 @@ def test_gemm_grouped_validation():
     d3 = tq.desc(3, 256, tq.SCALE_GROUP_F16, 640, 2560)
     good = 0x70000
     n = tq.gemm_grouped_workspace_size(tq.problems([(d1, good, good, good, good, None)]), 2048, tq.I8)
-    # one item per 128 x 128 output tile (16 x 5), after the problem table
-    assert n == 256 + ((16 * 5 * 8 + 255) // 256) * 256
+    # one item per output tile after the problem table: int8 with one plane
+    # and a per-tensor scale takes 128-token x 256-row tiles (16 x 3)
+    assert n == 256 + ((16 * 3 * 8 + 255) // 256) * 256
+    n3 = tq.gemm_grouped_workspace_size(tq.problems([(d3, good, good, good, good, None)]), 2048, tq.I8)
+    # group scales: 128 x 128 tiles (16 x 5)
+    assert n3 == 256 + ((16 * 5 * 8 + 255) // 256) * 256
     mixed = tq.problems([(d1, good, good, good, good, None), (d3, good, good, good, good, None)])
     with pytest.raises(tq.TQError) as e:
         tq.gemm_grouped_prepare(mixed, 64, tq.I8, good, 1 << 20, stream=0)
