@@ -295,6 +295,48 @@ def test_codec_digit_planes_code_11_and_ragged_chunk(M):
     assert rel_err(y, oracle.gemv_fp(K, g, CODEBOOK, rb["trits"], scales, x, BF16, cb)) <= TOL
 
 
+@pytest.mark.parametrize("x_type,K,g,layout", [
+    (I8, 1, 0, TENSOR), (I8, 3, 256, GROUP_F16), (BF16, 3, 256, GROUP_F16), (BF16, 3, 16, CODEBOOK),
+    (BF16, 1, 16, CODEBOOK),
+])
+@pytest.mark.parametrize("M,N", [(17, 200), (129, 513), (300, 640), (40, 1)])
+def test_gemm_writes_nothing_past_y(x_type, K, g, layout, M, N):
+    """The prefill kernels store y (and the int32 sums) through a buffer
+    resource the size of y and drop every output past M or N: a guard region
+    after y (and after acc) keeps its sentinel, and y is right, for ragged
+    token and row counts in every kernel family."""
+    from ternary_weight_amd import tq
+    t = torch()
+    Kin = 512
+    rng = np.random.default_rng(M * 31 + N + K)
+    trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
+    d, blob = pack(K, g, layout, trits, scales, cb)
+    guard = 8192
+    ybuf = t.full((M * N + guard,), float("nan"), dtype=t.float32, device="cuda")
+    abuf = t.full((M * N + guard,), -777, dtype=t.int32, device="cuda")
+    want_acc = x_type == I8 and K == 1 and layout == TENSOR
+    if x_type == I8:
+        q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
+        tq.gemm(d, blob, M, I8, dev(q), dev(s), ybuf, abuf if want_acc else None)
+        ref = oracle.gemv_i8(K, g, layout, trits, scales, q, s)
+        want = ref["y32"] if want_acc else ref["y64"]
+    else:
+        x = rand_x(M, Kin, BF16, rng)
+        tq.gemm(d, blob, M, BF16, dev(x), None, ybuf, None)
+        want = oracle.gemv_fp(K, g, layout, trits, scales, x, BF16, cb)
+    t.cuda.synchronize()
+    yh = host(ybuf)
+    assert np.all(np.isnan(yh[M * N:])), "a store past y"
+    y = yh[:M * N].reshape(M, N)
+    if want_acc:
+        assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+        ah = host(abuf)
+        assert np.all(ah[M * N:] == -777), "a store past acc"
+        assert np.array_equal(ah[:M * N].reshape(M, N), ref["acc"].astype(np.int32))
+    else:
+        assert rel_err(y, want) <= TOL
+
+
 def test_bf16_several_tokens_weight_over_4gib_runs_on_vector_alus():
     """A bf16 call with several tokens whose codes exceed the 4 GiB that the
     matrix-core kernels address goes to the vector-ALU kernels (tq_gemv and
