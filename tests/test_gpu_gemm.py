@@ -191,7 +191,8 @@ def test_gemm_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("xt,K,g,layout", [(I8, 1, 0, TENSOR), (BF16, 3, 256, GROUP_F16), (I8, 2, 64, GROUP_F16)])
+@pytest.mark.parametrize("xt,K,g,layout", [(I8, 1, 0, TENSOR), (BF16, 3, 256, GROUP_F16), (I8, 2, 64, GROUP_F16),
+                                            (BF16, 3, 16, CODEBOOK)])
 def test_gemm_grouped_equals_single(xt, K, g, layout):
     from ternary_weight_amd import tq
     t = torch()
@@ -200,8 +201,8 @@ def test_gemm_grouped_equals_single(xt, K, g, layout):
     shapes = [(256, 512), (64, 1024), (700, 256), (130, 768)]
     keep, items, want = [], [], []
     for (N, Kin) in shapes:
-        trits, scales, _ = rand_problem(K, g, layout, N, Kin, rng)
-        d, blob = pack(K, g, layout, trits, scales)
+        trits, scales, cb = rand_problem(K, g, layout, N, Kin, rng)
+        d, blob = pack(K, g, layout, trits, scales, cb)
         if xt == I8:
             q, s = oracle.act_quant_i8(rand_x(M, Kin, F32, rng))
             xd, xs = dev(q), dev(s)
