@@ -893,8 +893,11 @@ def measure_stack(args, config, M, fused, waves, row_blocks, spin_up_ms, seconda
     gbytes, qbytes = stack.gemv_bytes(), stack.quant_bytes()
     if stack.prefill:
         step = 64 if case.x_type == I8 else (32 if case.layout == TENSOR or case.group % 32 == 0 else 16)
+        # 16 x 16 tiles per wave: 4 x 8 for int8 with one plane and a per-tensor
+        # scale (its int32 sums are the result), 4 x 4 otherwise
+        fn = 8 if case.x_type == I8 and case.layout == TENSOR and case.planes == 1 else 4
         kernel_name = ("k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, CODEBOOK_B3, 1, 16) if stack.b3 else
-                       "k_gemm_grouped<%d, %d, %d, 4, 4, %d, 2>" % (stack.run_type, case.layout, case.planes, step))
+                       "k_gemm_grouped<%d, %d, %d, 4, %d, %d, 2>" % (stack.run_type, case.layout, case.planes, fn, step))
         ops = stack.ops()
         value = ops / (ms_step / 1e3) / 1e12
         achieved = ops / (gemv_avg / 1e3) / 1e12
