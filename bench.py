@@ -345,7 +345,10 @@ def decode_kernel_name(plan, run_type, layout, planes, group) -> str:
             ks = 64
         else:
             ks = 32 if layout in (TENSOR, GROUP_F16) and (layout == TENSOR or group % 32 == 0) else 16
-        return "k_gemm_skinny_grouped<%d, %d, %d, %d>" % (run_type, layout, planes, ks)
+        # int8 with one plane and a per-tensor scale from 8 tokens: the wide
+        # kernel (two 64-row blocks per wave)
+        wide = run_type == I8 and layout == TENSOR and planes == 1 and plan.M >= 8
+        return "k_gemm_skinny%s_grouped<%d, %d, %d, %d>" % ("_wide" if wide else "", run_type, layout, planes, ks)
     mt = 1 if plan.M <= 1 else 4
     kind = "k_gemv_wave_items" if plan.mode == 1 else "k_gemv_grouped"   # an item per wave, or per workgroup
     return "%s<%d, %d, %d, %d>" % (kind, run_type, layout, planes, mt)

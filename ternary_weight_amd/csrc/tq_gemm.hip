@@ -22,12 +22,13 @@ int gemm_row(const tq_layout& L, int x_type)
 }
 
 // Kernel tables: 0 int8, 1 bf16, 2 bf16 with at most 16 tokens, 3 int8 with
-// at most 16 tokens.
-constexpr int kTables = 4;
+// at most 16 tokens, 4 int8 with TQ_I8_WIDE_MIN_M to 16 tokens.
+constexpr int kTables = 5;
 int table_index(int x_type, int64_t M)
 {
     const bool few = M <= TQ_MAX_M_GEMV;
-    return x_type == TQ_I8 ? (few ? 3 : 0) : (few ? 2 : 1);
+    if (x_type == TQ_I8) return few ? (M >= TQ_I8_WIDE_MIN_M ? 4 : 3) : 0;
+    return few ? 2 : 1;
 }
 
 const tq_gemm_kernel (*gemm_table(int index))[4]
@@ -36,7 +37,8 @@ const tq_gemm_kernel (*gemm_table(int index))[4]
     case 0: return tq_gemm_table_i8();
     case 1: return tq_gemm_table_bf16();
     case 2: return tq_gemm_table_bf16_skinny();
-    default: return tq_gemm_table_i8_skinny();
+    case 3: return tq_gemm_table_i8_skinny();
+    default: return tq_gemm_table_i8_skinny_wide();
     }
 }
 

@@ -17,3 +17,16 @@ const tq_gemm_kernel (*tq_gemm_table_i8_skinny())[4]
     };
     return t;
 }
+
+const tq_gemm_kernel (*tq_gemm_table_i8_skinny_wide())[4]
+{
+    static const tq_gemm_kernel t[TQ_GEMM_ROWS][4] = {
+        {TQ_SKINNY_WIDE_ENTRY(TQ_I8, TQ_SCALE_TENSOR, 1, 64), TQ_SKINNY_ENTRY(TQ_I8, TQ_SCALE_TENSOR, 2, 64),
+         TQ_SKINNY_ENTRY(TQ_I8, TQ_SCALE_TENSOR, 3, 64), TQ_SKINNY_ENTRY(TQ_I8, TQ_SCALE_TENSOR, 4, 64)},
+        TQ_SKINNY_ROW(TQ_I8, TQ_SCALE_GROUP_F16, 64),
+        TQ_GEMM_NONE,
+        TQ_GEMM_NONE,
+        TQ_GEMM_NONE,
+    };
+    return t;
+}

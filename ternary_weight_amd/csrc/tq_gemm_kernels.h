@@ -23,6 +23,9 @@ const tq_gemm_kernel (*tq_gemm_table_bf16())[4];
 // Kernels for a few tokens (M <= 16): one 16-token tile, 4 waves along the rows.
 const tq_gemm_kernel (*tq_gemm_table_bf16_skinny())[4];
 const tq_gemm_kernel (*tq_gemm_table_i8_skinny())[4];
+// int8 with 8 to 16 tokens: one plane with a per-tensor scale on the wide
+// kernels (two 64-row blocks per wave), the rest as with fewer tokens.
+const tq_gemm_kernel (*tq_gemm_table_i8_skinny_wide())[4];
 
 #define TQ_GEMM_ENTRY(XT, LAYOUT, K, FM, FN, KS, WM)                                               \
     {tqm::k_gemm_single<XT, LAYOUT, K, FM, FN, KS, WM>, tqm::k_gemm_grouped<XT, LAYOUT, K, FM, FN, KS, WM>, \
@@ -38,9 +41,12 @@ const tq_gemm_kernel (*tq_gemm_table_i8_skinny())[4];
     {TQ_GEMM_NONE_ENTRY, TQ_GEMM_NONE_ENTRY, TQ_GEMM_ENTRY(TQ_BF16, TQ_SCALE_CODEBOOK_B3, 1, FM, FN, 16, WM), \
      TQ_GEMM_NONE_ENTRY}
 // The few-token kernels (tq_gemm_skinny.h): one 16-token tile, 4 waves of
-// 64 rows each, a 64-column chunk of every plane per step.
+// 64 rows each, a 64-column chunk of every plane per step; the wide ones
+// 128 rows per wave.
 #define TQ_SKINNY_ENTRY(XT, LAYOUT, K, KS) \
     {tqm::k_gemm_skinny<XT, LAYOUT, K, KS>, tqm::k_gemm_skinny_grouped<XT, LAYOUT, K, KS>, 1, 4, KS, 1}
+#define TQ_SKINNY_WIDE_ENTRY(XT, LAYOUT, K, KS) \
+    {tqm::k_gemm_skinny_wide<XT, LAYOUT, K, KS>, tqm::k_gemm_skinny_wide_grouped<XT, LAYOUT, K, KS>, 1, 8, KS, 1}
 #define TQ_SKINNY_ROW(XT, LAYOUT, KS)                                                                     \
     {TQ_SKINNY_ENTRY(XT, LAYOUT, 1, KS), TQ_SKINNY_ENTRY(XT, LAYOUT, 2, KS), TQ_SKINNY_ENTRY(XT, LAYOUT, 3, KS), \
      TQ_SKINNY_ENTRY(XT, LAYOUT, 4, KS)}

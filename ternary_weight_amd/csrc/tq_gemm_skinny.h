@@ -9,7 +9,10 @@
 // 3 and 1 and a group's scale is its codebook entry).
 //
 // Mapping onto CDNA4.  A workgroup is 4 waves; wave w owns the 64-row block
-// 4 tile + w and one MFMA tile of 16 tokens (rows past M read zeros).  The
+// 4 tile + w (the wide kernels, for int8 with one plane and a per-tensor
+// scale and 8 or more tokens: the two blocks 2 (4 tile + w) and the next,
+// with the same x fragments) and one MFMA tile of 16 tokens (rows past M
+// read zeros).  The
 // wave walks its block one 64-column chunk at a time, every plane of the
 // chunk in one step:
 //   - lane l loads row l's 16-byte slot of each plane (one coalesced 1 KiB
@@ -120,6 +123,13 @@ struct SkinnyStage {
 // (skinny_tile), and the table size that takes.
 template <int XT, int LAYOUT, int K, int KS>
 constexpr bool skinny_comb() { return XT == TQ_BF16 && LAYOUT == TQ_SCALE_CODEBOOK && K == 3 && KS == 16; }
+// 64-row blocks per wave (RB): one, or two -- the "wide" kernels, for int8
+// with one plane and a per-tensor scale and 8 or more tokens: the same x
+// fragments serve both blocks, so a wave loads half as many x bytes per code
+// byte (BitNet-2B-shaped stack, 16 tokens: 57.7 -> 60.7% of HBM, 8 tokens
+// 64.6 -> 66.4%; 4 tokens the same, 2 tokens 77.8 -> 75.9%).
+template <int XT, int LAYOUT, int K, int KS>
+constexpr bool skinny_wide_ok() { return XT == TQ_I8 && LAYOUT == TQ_SCALE_TENSOR && K == 1; }
 template <int XT, int LAYOUT, int K, int KS>
 constexpr int skinny_lut_bytes()
 {
@@ -138,7 +148,7 @@ __device__ __forceinline__ void skinny_stage_tables(const tq_prob_dev& P, float*
     }
 }
 
-template <int XT, int LAYOUT, int K, int KS, int GM>
+template <int XT, int LAYOUT, int K, int KS, int GM, int RB>
 __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const LDS_AS float* cb_lds,
                                             const LDS_AS uint8_t* b3_lut, LDS_AS uint32_t* wlds)
 {
@@ -163,7 +173,9 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     constexpr int KP = kComb ? 1 : K;            // partial sums per tile: planes, or the one combined operand
     constexpr int KPC = 64 / KS;                 // MFMA steps per chunk
     using SS = SkinnyStage<LAYOUT, K, KS>;
-    constexpr int CDS = SS::CDS, SWN = SS::SWN, WST = SS::WST;
+    constexpr int NFN = 4 * RB;                           // 16-row tiles per wave
+    static_assert(RB == 1 || (RB == 2 && skinny_wide_ok<XT, LAYOUT, K, KS>()), "two blocks per wave: int8, one plane");
+    constexpr int CDS = SS::CDS, SWN = SS::SWN, WST = SS::WST * RB;
     // chunks in flight: four (Llama-8B-shaped K = 3 stack, 16 tokens: 1.23
     // against 1.28 ms with two; the compact codes 1.29 against 1.54 ms), two
     // where four would not fit the registers of two waves per SIMD, and two
@@ -186,7 +198,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     const int r = lane & 15, q = lane >> 4;
     const int M = P.M, N = P.N, Kin = P.Kin, NC = P.NC;
     const int NB = (N + 63) >> 6;
-    const int rb = tn * 4 + wave;                 // the wave's row block
+    const int rb = (tn * 4 + wave) * RB;          // the wave's first row block
     const int n0 = rb * 64;
 
     // Buffer resources (tq_decode.h): a lane whose VGPR offset is at or past
@@ -233,7 +245,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     // kComb: the code dwords of the chunk, row 16 fn + r, plane k (read once per chunk)
     u32x4 cwv[kComb ? 4 : 1][kComb ? 3 : 1];
 
-    u32x4 cbuf[NBUF][CL];                         // B3: parts 0, 1 and (low half) 2
+    u32x4 cbuf[NBUF][CL * RB];                    // B3: parts 0, 1 and (low half) 2; block-major
     uint32_t sbuf[NBUF][SWN > 0 ? SWN : 1];
     XF xbuf[NBUF][XL];
 
@@ -247,7 +259,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         else if constexpr (KS == 16) return (uint32_t)(2 * c) * K * 256u;
         else return (uint32_t)(((c << 6) >> lg) >> 1) * K * 256u;
     };
-    auto load = [&](int c, u32x4 (&cb)[CL], uint32_t (&sw)[SWN > 0 ? SWN : 1], XF (&xa)[XL]) {
+    auto load = [&](int c, u32x4 (&cb)[CL * RB], uint32_t (&sw)[SWN > 0 ? SWN : 1], XF (&xa)[XL]) {
         c = c < NC ? c : NC - 1;   // a prefetch past the last chunk loads the last again (never used)
         const uint32_t xv = xv0 + (uint32_t)c * (64u * ESZ);
 #pragma unroll
@@ -261,7 +273,11 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         } else {
             const uint32_t so = (uint32_t)c * K * 1024u;
 #pragma unroll
-            for (int k = 0; k < CL; ++k) cb[k] = buffer_load<u32x4, kCacheNT>(rc, cv + (uint32_t)k * 1024u, so);
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int k = 0; k < CL; ++k)
+                    cb[b * CL + k] = buffer_load<u32x4, kCacheNT>(
+                        rc, cv + (uint32_t)b * (uint32_t)NC * K * 1024u + (uint32_t)k * 1024u, so);
         }
         if constexpr (SWN > 0) {
             const uint32_t so = scale_soff(c);
@@ -269,7 +285,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             for (int j = 0; j < SWN; ++j) sw[j] = buffer_load<uint32_t>(rs, sv + (uint32_t)j * 256u, so);
         }
     };
-    auto stage_write = [&](LDS_AS uint32_t* st, const u32x4 (&cb)[CL], const uint32_t (&sw)[SWN > 0 ? SWN : 1]) {
+    auto stage_write = [&](LDS_AS uint32_t* st, const u32x4 (&cb)[CL * RB], const uint32_t (&sw)[SWN > 0 ? SWN : 1]) {
         LDS_AS uint32_t* row = st + lane * CDS;
         if constexpr (kB3) {
             *(LDS_AS u32x4*)(row) = cb[0];
@@ -277,16 +293,18 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
             *(LDS_AS u32x2*)(row + 8) = u32x2{cb[2][0], cb[2][1]};
         } else {
 #pragma unroll
-            for (int k = 0; k < CL; ++k) *(LDS_AS u32x4*)(row + 4 * k) = cb[k];
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int k = 0; k < CL; ++k) *(LDS_AS u32x4*)(row + 64 * CDS * b + 4 * k) = cb[b * CL + k];
         }
 #pragma unroll
         for (int j = 0; j < SWN; ++j) st[64 * CDS + 64 * j + lane] = sw[j];
     };
 
-    Part part[KP][4];
-    f32x4 acc[4];
+    Part part[KP][NFN];
+    f32x4 acc[NFN];
 #pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
+    for (int fn = 0; fn < NFN; ++fn) {
         acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KP; ++k) part[k][fn] = Part{0, 0, 0, 0};
@@ -376,7 +394,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
     };
     auto apply = [&](const LDS_AS uint32_t* st, int c, int grp) {
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn)
+        for (int fn = 0; fn < NFN; ++fn)
 #pragma unroll
             for (int k = 0; k < KP; ++k) {
                 const float sc = group_scale(st, c, grp, k, fn);
@@ -407,7 +425,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         read_idx(st, c);
         if constexpr (kComb) {
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn)
+            for (int fn = 0; fn < NFN; ++fn)
 #pragma unroll
                 for (int k = 0; k < 3; ++k) cwv[fn][k] = *(const LDS_AS u32x4*)(st + (16 * fn + r) * CDS + 4 * k);
         }
@@ -418,7 +436,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 #pragma unroll
             for (int k = 0; k < KP; ++k)
 #pragma unroll
-                for (int fn = 0; fn < 4; ++fn) {
+                for (int fn = 0; fn < NFN; ++fn) {
                     const Frag b = frag(st, k, fn, s);
                     part[k][fn] = MF::run(a, b, zero ? Part{0, 0, 0, 0} : part[k][fn]);
                 }
@@ -439,7 +457,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 #pragma unroll
                     for (int k = 0; k < KP; ++k)
 #pragma unroll
-                        for (int fn = 0; fn < 4; ++fn) part[k][fn] = Part{0, 0, 0, 0};
+                        for (int fn = 0; fn < NFN; ++fn) part[k][fn] = Part{0, 0, 0, 0};
                 }
             }
         }
@@ -473,7 +491,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         for (int k = 0; k < KP; ++k) {
             const float sc = ld_uniform(((const float*)P.scales) + k) * MF::kScale;
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn)
+            for (int fn = 0; fn < NFN; ++fn)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[fn][e] = fmaf(sc, (float)part[k][fn][e], acc[fn][e]);
         }
@@ -490,7 +508,7 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
         const float xs = kI8 ? P.x_scale[m] : 1.0f;
         const float cm = kDirect ? s_w * xs : xs;
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) {
+        for (int fn = 0; fn < NFN; ++fn) {
             const int n = n0 + 16 * fn + r;
             if (n >= N) continue;
             const int64_t o = (int64_t)m * N + n;
@@ -508,15 +526,15 @@ __device__ __forceinline__ void skinny_tile(const tq_prob_dev& P, int tn, const 
 // The group mode of a launch: groups of the step's width end with every
 // step, larger ones after g / KS steps (one kernel takes both; the branch is
 // uniform).
-template <int XT, int LAYOUT, int K, int KS>
+template <int XT, int LAYOUT, int K, int KS, int RB>
 __device__ __forceinline__ void skinny_dispatch(const tq_prob_dev& P, int tn, const LDS_AS float* cb_lds,
                                                 const LDS_AS uint8_t* b3_lut, LDS_AS uint32_t* wlds)
 {
     if constexpr (LAYOUT == TQ_SCALE_TENSOR) {
-        skinny_tile<XT, LAYOUT, K, KS, kGroupNone>(P, tn, cb_lds, b3_lut, wlds);
+        skinny_tile<XT, LAYOUT, K, KS, kGroupNone, RB>(P, tn, cb_lds, b3_lut, wlds);
     } else {
-        if (P.g == KS) skinny_tile<XT, LAYOUT, K, KS, kGroupStep>(P, tn, cb_lds, b3_lut, wlds);
-        else skinny_tile<XT, LAYOUT, K, KS, kGroupSteps>(P, tn, cb_lds, b3_lut, wlds);
+        if (P.g == KS) skinny_tile<XT, LAYOUT, K, KS, kGroupStep, RB>(P, tn, cb_lds, b3_lut, wlds);
+        else skinny_tile<XT, LAYOUT, K, KS, kGroupSteps, RB>(P, tn, cb_lds, b3_lut, wlds);
     }
 }
 
@@ -527,15 +545,22 @@ __device__ __forceinline__ void skinny_dispatch(const tq_prob_dev& P, int tn, co
 template <int XT, int LAYOUT, int K, int KS>
 constexpr int skinny_waves() { return skinny_comb<XT, LAYOUT, K, KS>() ? TQ_SKINNY_COMB_WPS : 2; }
 
-template <int XT, int LAYOUT, int K, int KS>
-__global__ __launch_bounds__(kThreads, (skinny_waves<XT, LAYOUT, K, KS>())) void k_gemm_skinny(tq_prob_dev P, int /*tiles_m*/)
+// The kernels' body: the tables, then the tile of 64 RB rows per wave.
+template <int XT, int LAYOUT, int K, int KS, int RB>
+__device__ __forceinline__ void skinny_body(const tq_prob_dev& P, int tn)
 {
     __shared__ float cb_lds[TQ_CB_SLOTS];
     __shared__ __attribute__((aligned(16))) uint8_t b3_lut[skinny_lut_bytes<XT, LAYOUT, K, KS>()];
-    __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
+    __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST * RB];
     skinny_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
-    skinny_dispatch<XT, LAYOUT, K, KS>(P, blockIdx.x, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
-                                   (LDS_AS uint32_t*)wlds);
+    skinny_dispatch<XT, LAYOUT, K, KS, RB>(P, tn, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
+                                           (LDS_AS uint32_t*)wlds);
+}
+
+template <int XT, int LAYOUT, int K, int KS>
+__global__ __launch_bounds__(kThreads, (skinny_waves<XT, LAYOUT, K, KS>())) void k_gemm_skinny(tq_prob_dev P, int /*tiles_m*/)
+{
+    skinny_body<XT, LAYOUT, K, KS, 1>(P, blockIdx.x);
 }
 
 // Grouped: item i = (problem, tile); one token tile per problem.
@@ -544,12 +569,22 @@ __global__ __launch_bounds__(kThreads, (skinny_waves<XT, LAYOUT, K, KS>())) void
 {
     const int2 it = items[blockIdx.x];
     const tq_prob_dev P = ld_uniform_struct(probs + it.x);
-    __shared__ float cb_lds[TQ_CB_SLOTS];
-    __shared__ __attribute__((aligned(16))) uint8_t b3_lut[skinny_lut_bytes<XT, LAYOUT, K, KS>()];
-    __shared__ __attribute__((aligned(16))) uint32_t wlds[8 * SkinnyStage<LAYOUT, K, KS>::WST];
-    skinny_stage_tables<XT, LAYOUT, K, KS>(P, cb_lds, b3_lut);
-    skinny_dispatch<XT, LAYOUT, K, KS>(P, it.y, (const LDS_AS float*)cb_lds, (const LDS_AS uint8_t*)b3_lut,
-                                   (LDS_AS uint32_t*)wlds);
+    skinny_body<XT, LAYOUT, K, KS, 1>(P, it.y);
+}
+
+// Two 64-row blocks per wave (skinny_wide_ok).
+template <int XT, int LAYOUT, int K, int KS>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny_wide(tq_prob_dev P, int /*tiles_m*/)
+{
+    skinny_body<XT, LAYOUT, K, KS, 2>(P, blockIdx.x);
+}
+
+template <int XT, int LAYOUT, int K, int KS>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_skinny_wide_grouped(const tq_prob_dev* probs, const int2* items)
+{
+    const int2 it = items[blockIdx.x];
+    const tq_prob_dev P = ld_uniform_struct(probs + it.x);
+    skinny_body<XT, LAYOUT, K, KS, 2>(P, it.y);
 }
 
 }  // namespace tqm

@@ -189,7 +189,7 @@ def test_gemm_grouped_validation():
     assert e.value.status == tq.ERR_UNSUPPORTED
     plan = tq.tq_grouped_plan(workspace=good, n_items=3, family=5, n_problems=1)
     assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG   # a decode family
-    plan.family = 1000 + 4 * 5 * 4                                                 # past the last family
+    plan.family = 1000 + 5 * 5 * 4                                                 # past the last family
     assert tq.lib().tq_gemm_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     assert tq.lib().tq_gemv_grouped_run(ctypes.byref(plan), None) == tq.ERR_ARG
     plan.family = 1000 + 2 * 4 + 0                                                 # int8 with groups of 16: none

@@ -145,7 +145,9 @@ def test_act_quant_bit_exact(x_type, M, Kin):
 # Decode products.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("N,Kin,M", [(64, 64, 1), (2560, 2560, 1), (640, 2560, 1), (100, 6912, 1),
-                                     (96, 80, 3), (200, 1040, 4), (130, 512, 7), (64, 256, 16)])
+                                     (96, 80, 3), (200, 1040, 4), (130, 512, 7), (64, 256, 16),
+                                     # 8 tokens and more: the wide kernels, 512 rows a workgroup
+                                     (640, 2560, 8), (1000, 1040, 12), (2560, 2560, 16), (513, 512, 9)])
 def test_gemv_int8_per_tensor_bit_exact(N, Kin, M):
     trits, scales, _ = rand_problem(1, 0, TENSOR, N, Kin)
     x = rand_x(M, Kin, F32)
