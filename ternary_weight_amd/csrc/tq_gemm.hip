@@ -10,6 +10,11 @@
 namespace {
 
 constexpr int64_t kMaxM = 1 << 24;
+// int8 with one plane and a per-tensor scale and at least this many tokens
+// (up to 16) runs on the wide few-token kernels, two 64-row blocks per wave.
+#ifndef TQ_I8_WIDE_MIN_M
+#define TQ_I8_WIDE_MIN_M 8
+#endif
 constexpr int kFamilyBase = 1000;   // grouped plans of tq_gemm carry family >= this
 
 int gemm_row(const tq_layout& L, int x_type)

@@ -74,11 +74,6 @@ tq_status tq_fail_problem(tq_status s, int32_t i);
 #ifndef TQ_I8_MFMA_MIN_M
 #define TQ_I8_MFMA_MIN_M 2
 #endif
-// int8 with one plane and a per-tensor scale and at least this many tokens
-// (up to 16) runs on the wide few-token kernels, two 64-row blocks per wave.
-#ifndef TQ_I8_WIDE_MIN_M
-#define TQ_I8_WIDE_MIN_M 8
-#endif
 static inline int64_t tq_bf16_mfma_min_m(int layout)
 {
     return layout == TQ_SCALE_CODEBOOK ? TQ_BF16_MFMA_MIN_M_CODEC
